@@ -1,0 +1,357 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against a closed form, an identity stated on the pages,
+a reduction to an independent definition, brute force, or a hand-worked fixture under
+tests/golden/.  Page references: PARK, paperpeel.com/paper/2609.38978 (sections and
+equations as printed there); SCOPE, paperpeel.com/paper/2608.12780.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rand_qk(L, d, seed=0, centres=4):
+    rng = np.random.default_rng(seed)
+    mu = rng.normal(0, 2, (centres, d))
+    z = rng.integers(0, centres, L)
+    Q = (mu[z] + rng.normal(0, 0.5, (L, d))).astype(np.float32)
+    K = (mu[z] + rng.normal(0, 0.5, (L, d))).astype(np.float32)
+    V = rng.normal(0, 1, (L, d)).astype(np.float32)
+    return Q, K, V
+
+
+# ---------------------------------------------------------------- metric (a1-a3)
+
+def test_gram_quadratic_form(orc):
+    """App. D.2 'Euclidean realization': x^T G_Q x = ||Q x||^2 / L >= 0."""
+    Q, K, _ = _rand_qk(300, 16, 1)
+    G, _, _, ok = orc.query_metric(Q)
+    assert ok
+    rng = np.random.default_rng(5)
+    Q64 = Q.astype(np.float64)
+    for _ in range(5):
+        x = rng.normal(size=16)
+        lhs = x @ G @ x
+        rhs = np.sum((Q64 @ x) ** 2) / Q.shape[0]
+        assert lhs >= 0
+        assert abs(lhs - rhs) <= 1e-12 * rhs
+
+
+def test_cholesky_factor(orc):
+    """App. D.2: Gs = R R^T with R lower triangular, positive diagonal (unique factor)."""
+    Q, _, _ = _rand_qk(200, 24, 2)
+    G, Gs, R, ok = orc.query_metric(Q)
+    assert ok
+    assert np.all(np.triu(R, 1) == 0)
+    assert np.all(np.diag(R) > 0)
+    assert np.abs(R @ R.T - Gs).max() <= 1e-12 * np.abs(Gs).max()
+
+
+def test_shrinkage_limits(orc):
+    """App. D.2 last paragraph: alpha = 1 is isotropic up to scale; alpha = 0 is the query
+    metric up to the stability term.  s_Q = tr(G_Q)/d = ||Q||_F^2 / (L d)."""
+    Q, _, _ = _rand_qk(150, 12, 3)
+    L, d = Q.shape
+    s = np.sum(Q.astype(np.float64) ** 2) / (L * d)
+    _, Gs1, R1, ok = orc.query_metric(Q, alpha=1.0)
+    assert ok
+    np.testing.assert_allclose(R1, np.sqrt((1 + orc.EPS) * s) * np.eye(d), rtol=1e-12, atol=0)
+    G0, Gs0, _, ok = orc.query_metric(Q, alpha=0.0)
+    assert ok
+    np.testing.assert_allclose(Gs0 - G0, orc.EPS * s * np.eye(d), rtol=1e-9, atol=1e-18)
+
+
+def test_euclidean_metric_is_identity(orc):
+    Q, _, _ = _rand_qk(50, 8, 4)
+    _, _, R, ok = orc.query_metric(Q, metric="euclidean")
+    assert ok and np.array_equal(R, np.eye(8))
+
+
+def test_metric_failure_reported(orc):
+    """A factorisation that cannot succeed (non-finite queries) is reported, not hidden."""
+    Q, _, _ = _rand_qk(40, 8, 5)
+    Q[3, 2] = np.nan
+    *_, ok = orc.query_metric(Q)
+    assert not ok
+
+
+def test_qrkc_objective_identity(orc):
+    """Section 5.2, the J_QRKC identity: with k~ = R^T k,
+    sum_j ||k~_j - c~_{a_j}||^2 = (1-alpha) (1/L) sum_i sum_j [q_i^T (k_j - c_{a_j})]^2
+                                  + (alpha+eps) s_Q sum_j ||k_j - c_{a_j}||^2."""
+    Q, K, _ = _rand_qk(120, 10, 6)
+    L, d = Q.shape
+    rng = np.random.default_rng(7)
+    labels = rng.integers(0, 5, L)
+    C = rng.normal(0, 2, (5, d))
+    _, _, R, ok = orc.query_metric(Q)
+    assert ok
+    Kt = orc.transform(K, R).astype(np.float64)
+    Ct = orc.transform(C.astype(np.float32), R).astype(np.float64)
+    lhs = np.sum((Kt - Ct[labels]) ** 2)
+    Dlt = K.astype(np.float64) - C.astype(np.float32).astype(np.float64)[labels]
+    jq = 0.0
+    for i in range(L):
+        for j in range(L):
+            jq += float(Q[i].astype(np.float64) @ Dlt[j]) ** 2
+    jq /= L
+    je = np.sum(Dlt ** 2)
+    s = np.sum(Q.astype(np.float64) ** 2) / (L * d)
+    rhs = (1 - orc.ALPHA) * jq + (orc.ALPHA + orc.EPS) * s * je
+    assert abs(lhs - rhs) <= 1e-5 * rhs   # float rounding of the transformed keys
+
+
+# ---------------------------------------------------------------- k-means (a4-a6)
+
+def test_kmeans_golden_line(orc):
+    g = _gold("kmeans_line.json")
+    Kt = np.array(g["Kt"], np.float32)
+    km = orc.kmeans(Kt, 2, 2, init_idx=g["init_idx"])
+    assert km["labels_hist"][0].tolist() == g["labels"]
+    np.testing.assert_array_equal(km["C_hist"][1], np.array(g["centroids"], np.float32))
+    assert km["J_assign"][0] == g["J_assign_1"]
+    assert km["J_update"][0] == g["J_update_1"]
+    assert abs(km["margins"][0][1] - g["margin_key1_step1"]) < 1e-15
+
+
+def test_kmeans_objective_non_increasing(orc):
+    """Lloyd steps never increase the objective (k-means, App. D.2 'K-means optimizes the
+    specified objective iteratively')."""
+    import park_synth
+    Q, K, _ = park_synth.generate(park_synth.CONFIGS[0])
+    cl = orc.cluster_keys(Q[0, 0], K[0, 0], 32, 10)
+    ja, ju = cl["km"]["J_assign"], cl["km"]["J_update"]
+    for t in range(len(ja)):
+        assert ju[t] <= ja[t] * (1 + 1e-9)
+        if t + 1 < len(ja):
+            assert ja[t + 1] <= ju[t] * (1 + 1e-9)
+
+
+def test_kmeans_singletons_identity(orc):
+    """N_K = L with strided anchors: every key is its own cluster."""
+    Q, K, _ = _rand_qk(64, 8, 8)
+    cl = orc.cluster_keys(Q, K, 64, 3)
+    assert cl["labels"].tolist() == list(range(64))
+    assert cl["counts"].tolist() == [1] * 64
+
+
+def test_alpha_one_matches_euclidean(orc):
+    """alpha = 1 makes the metric isotropic, so labels equal plain Euclidean k-means on
+    the raw keys up to near-ties."""
+    Q, K, _ = _rand_qk(400, 16, 9, centres=6)
+    a = orc.cluster_keys(Q, K, 12, 4, alpha=1.0)
+    b = orc.cluster_keys(Q, K, 12, 4, metric="euclidean")
+    ok = (a["labels"] == b["labels"]) | (b["km"]["margins"][-1] < 1e-5)
+    assert ok.all()
+
+
+def test_finalize_invariants(orc):
+    Q, K, _ = _rand_qk(333, 8, 10)
+    cl = orc.cluster_keys(Q, K, 7, 3)
+    off, perm, lab, cnt = cl["offsets"], cl["perm"], cl["labels"], cl["counts"]
+    assert off[0] == 0 and off[-1] == 333
+    assert sorted(perm.tolist()) == list(range(333))
+    keys = [(lab[p], p) for p in perm]
+    assert keys == sorted(keys)
+    assert np.array_equal(np.diff(off), cnt)
+
+
+# ---------------------------------------------------------------- PAMA (a8)
+
+def test_pama_golden(orc):
+    g = _gold("pama_closed_form.json")
+    for case in ("case_a", "case_b"):
+        c = g[case]
+        Q = np.array(c["Q"], np.float32)
+        W = orc.pama(Q, np.array(c["C"], np.float32), np.array(c["counts"]), len(Q), 1.0)
+        np.testing.assert_allclose(W[0], c["W"], rtol=1e-7, atol=0)
+
+
+def test_pama_rows_sum_to_one(orc):
+    """E8: each query's distribution over key blocks sums to 1, so each W_u sums to 1."""
+    Q, K, _ = _rand_qk(300, 16, 11)
+    cl = orc.cluster_keys(Q, K, 9, 3)
+    W = orc.pama(Q, cl["centroids"], cl["counts"], 64, 0.25)
+    np.testing.assert_allclose(W.sum(1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_pama_singletons_equal_exact_importance(orc):
+    """With one key per block, c_v = k_v and log n_v = 0, so PAMA is the exact block
+    importance of section 3.2 Eq. (3) (computed by an independent dense routine)."""
+    Q, K, _ = _rand_qk(96, 8, 12)
+    labels = np.arange(96, dtype=np.int32)
+    cent, counts, _, _ = orc.finalize(K, labels, 96)
+    W = orc.pama(Q, cent, counts, 32, 0.3)
+    Wx = orc.exact_block_importance(Q, K, labels, 96, 32, 0.3)
+    np.testing.assert_allclose(W, Wx, rtol=1e-10, atol=1e-15)
+
+
+def test_pama_identical_keys_equal_exact_importance(orc):
+    """App. D.2 exact decomposition: S*_iv = log n_v + q_i^T c_v scale + Delta^K_iv, and
+    Delta^K vanishes when a block's keys are identical; PAMA then equals Eq. (3)."""
+    rng = np.random.default_rng(13)
+    base = rng.normal(0, 1, (6, 8)).astype(np.float32)
+    labels = rng.integers(0, 6, 150).astype(np.int32)
+    labels[:6] = np.arange(6)
+    K = base[labels]
+    Q = rng.normal(0, 1, (150, 8)).astype(np.float32)
+    cent, counts, _, _ = orc.finalize(K, labels, 6)
+    W = orc.pama(Q, cent, counts, 50, 0.7)
+    Wx = orc.exact_block_importance(Q, K, labels, 6, 50, 0.7)
+    np.testing.assert_allclose(W, Wx, rtol=1e-9, atol=1e-15)
+
+
+def test_pooled_identical_queries_equal_pama(orc):
+    """App. D.1: if all queries in a block are identical the query-centroid estimate is
+    exact, i.e. the pooled scores equal PAMA."""
+    rng = np.random.default_rng(14)
+    q = rng.normal(0, 1, (4, 8)).astype(np.float32)
+    Q = np.repeat(q, 16, axis=0)
+    _, K, _ = _rand_qk(64, 8, 15)
+    cl = orc.cluster_keys(Q, K, 5, 2)
+    Wp = orc.pooled_scores(Q, cl["centroids"], cl["counts"], 16, 0.5)
+    Wa = orc.pama(Q, cl["centroids"], cl["counts"], 16, 0.5)
+    np.testing.assert_allclose(Wp, Wa, rtol=1e-10, atol=1e-15)
+
+
+# ---------------------------------------------------------------- selection (a9)
+
+def test_select_golden(orc):
+    for c in _gold("select_rows.json")["cases"]:
+        W = np.array([c["W"]])
+        mask, lst, cnt, _, _ = orc.select(W, np.array(c["counts"]), c["p"], c["k"])
+        assert cnt[0] == c["count"], c["why"]
+        assert lst[0, :cnt[0]].tolist() == c["list"], c["why"]
+        assert np.all(lst[0, cnt[0]:] == -1)
+        assert mask[0].nonzero()[0].tolist() == c["list"]
+
+
+def _brute_force_select(w, counts, p, k):
+    """Smallest set of non-empty blocks holding at least p of the mass; among those the
+    larger mass, then the lexicographically smallest id list; then grown to k blocks by
+    the largest remaining masses (ids ascending on ties)."""
+    ne = [v for v in range(len(w)) if counts[v] > 0]
+    total = float(sum(w[v] for v in ne))
+    best = None
+    if p > 0:
+        for r in range(1, len(ne) + 1):
+            for sub in itertools.combinations(ne, r):
+                m = float(np.sum(w[list(sub)]))
+                if m >= p * total:
+                    key = (-m, list(sub))
+                    if best is None or key < best[0]:
+                        best = (key, list(sub))
+            if best is not None:
+                break
+    chosen = [] if best is None else best[1]
+    rest = sorted([v for v in ne if v not in chosen], key=lambda v: (-w[v], v))
+    while len(chosen) < min(k, len(ne)):
+        chosen.append(rest.pop(0))
+    return sorted(chosen)
+
+
+def test_select_brute_force(orc):
+    rng = np.random.default_rng(16)
+    for trial in range(300):
+        nk = int(rng.integers(1, 10))
+        counts = rng.integers(0, 3, nk)
+        if counts.sum() == 0:
+            counts[0] = 1
+        # small integer masses: every subset sum is exact, and ties are frequent
+        w = (rng.integers(0, 9, nk) ** 2 * (counts > 0)).astype(np.float64)
+        p = float(rng.choice([0.0, 0.3, 0.5, 0.9, 1.0]))
+        k = int(rng.integers(0, nk + 2))
+        _, lst, cnt, _, _ = orc.select(w[None, :], counts, p, k)
+        bf = _brute_force_select(w, counts, p, k)
+        assert lst[0, :cnt[0]].tolist() == bf, (w, counts, p, k)
+
+
+# ---------------------------------------------------------------- attention (a10)
+
+def test_attention_golden(orc):
+    g = _gold("attention_closed_form.json")
+    Q, K, V = (np.array(g[x], np.float32) for x in "QKV")
+    perm = np.array([0, 1]); off = np.array([0, 2]); lst = np.array([[0]]); cnt = np.array([1])
+    O, lse = orc.block_sparse_attn(Q, K, V, perm, off, lst, cnt, 1, 1.0)
+    np.testing.assert_allclose(O[0], g["O"], rtol=1e-7)
+    assert abs(lse[0] - g["lse"]) < 1e-7
+    Q2 = np.concatenate([Q, np.zeros_like(Q)])          # the dense routine takes L queries and L keys
+    Od, lsed = orc.dense_attn(Q2, K, V, 1.0, rows=[0])
+    np.testing.assert_allclose(Od[0], g["O"], rtol=1e-7)
+    assert abs(lsed[0] - g["lse"]) < 1e-7
+
+
+def test_density_one_equals_dense(orc):
+    """Section 3.1: with every block selected, sparse attention is dense attention
+    (the dense routine is an independent textbook triple loop)."""
+    Q, K, V = _rand_qk(200, 16, 17)
+    cl = orc.cluster_keys(Q, K, 6, 2)
+    nq = (200 + 63) // 64
+    lst = np.tile(np.arange(6, dtype=np.int32), (nq, 1))
+    cnt = np.full(nq, 6, np.int32)
+    O, lse = orc.block_sparse_attn(Q, K, V, cl["perm"], cl["offsets"], lst, cnt, 64, 0.25)
+    Od, lsed = orc.dense_attn(Q, K, V, 0.25)
+    np.testing.assert_allclose(O, Od, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lsed, rtol=1e-12, atol=1e-12)
+
+
+def test_singleton_selection_returns_value(orc):
+    """A single selected one-key block: the softmax has one term, O_i = v_j."""
+    Q, K, V = _rand_qk(10, 4, 18)
+    perm = np.array([3, 0, 1, 2, 4, 5, 6, 7, 8, 9], np.int32)
+    off = np.array([0, 1, 10], np.int32)
+    lst = np.array([[0, -1]], np.int32); cnt = np.array([1], np.int32)
+    O, lse = orc.block_sparse_attn(Q, K, V, perm, off, lst, cnt, 10, 0.5)
+    np.testing.assert_allclose(O, np.repeat(V[3:4].astype(np.float64), 10, 0), rtol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * (Q.astype(np.float64) @ K[3].astype(np.float64)), rtol=1e-12)
+
+
+def test_empty_selection(orc):
+    Q, K, V = _rand_qk(8, 4, 19)
+    O, lse = orc.block_sparse_attn(Q, K, V, np.arange(8), np.array([0, 8]), np.array([[-1]]),
+                                   np.array([0]), 8, 0.5)
+    assert np.all(O == 0) and np.all(np.isneginf(lse))
+
+
+def test_top_p_on_exact_importance_gives_recall(orc):
+    """Table 1 'Full/Full' rows: top-p over the exact block importance keeps at least p of
+    each query block's attention mass.  Recall per block is the mean over its queries of
+    exp(lse_sparse - lse_dense) (section 3.2, Recall), and it equals the kept mass."""
+    Q, K, V = _rand_qk(256, 16, 20, centres=8)
+    cl = orc.cluster_keys(Q, K, 10, 3)
+    scale = 0.25
+    Wx = orc.exact_block_importance(Q, K, cl["labels"], 10, 64, scale)
+    _, lst, cnt, _, _ = orc.select(Wx, cl["counts"], 0.9, 0)
+    O, lse = orc.block_sparse_attn(Q, K, V, cl["perm"], cl["offsets"], lst, cnt, 64, scale)
+    _, lsed = orc.dense_attn(Q, K, V, scale)
+    rec = np.exp(lse - lsed)
+    for u in range(4):
+        r = rec[64 * u:64 * u + 64].mean()
+        kept = Wx[u, lst[u, :cnt[u]]].sum()
+        assert r >= 0.9 - 1e-12
+        assert abs(r - kept) < 1e-10
+
+
+def test_literal_masked_attention_is_recall_times_output(orc):
+    """Section 3.1: the literal O^sp = (A .* M) V equals recall_i times the renormalised
+    sparse output (A from the dense definition, written out here for a tiny case)."""
+    Q, K, V = _rand_qk(40, 6, 21)
+    cl = orc.cluster_keys(Q, K, 4, 2)
+    lst = np.array([[0, 2, -1, -1]], np.int32); cnt = np.array([2], np.int32)
+    O, lse = orc.block_sparse_attn(Q, K, V, cl["perm"], cl["offsets"], lst, cnt, 40, 0.3)
+    _, lsed = orc.dense_attn(Q, K, V, 0.3)
+    sel = np.isin(cl["labels"], [0, 2])
+    Z = 0.3 * Q.astype(np.float64) @ K.astype(np.float64).T
+    A = np.exp(Z - Z.max(1, keepdims=True)); A /= A.sum(1, keepdims=True)
+    lit = (A * sel[None, :]) @ V.astype(np.float64)
+    np.testing.assert_allclose(lit, np.exp(lse - lsed)[:, None] * O, rtol=1e-9, atol=1e-12)
