@@ -1,0 +1,243 @@
+"""Python binding of libpark (ctypes): argument marshalling only.
+
+Every step of the path runs in the HIP kernels of libpark.so; PyTorch supplies device
+memory and the current stream.  The functions carry the names of the C entry points
+declared in include/park.h:
+
+  park_cluster_keys        query-response key clustering (PARK, section 5.2)
+  park_retrieve_blocks     PAMA block scores + top-p / top-k selection (section 5.1, 6.1)
+  park_retrieve_blocks_pooled  the pooled-query baseline (section 4.1)
+  park_block_sparse_attn   attention over the selected blocks (section 3.1)
+
+There is no fallback: if libpark.so is missing or was built for another GPU the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
+    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn",
+    "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
+    "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpark.so")
+
+PARK_OK, PARK_ERR_INVALID, PARK_ERR_UNSUPPORTED, PARK_ERR_WORKSPACE, PARK_ERR_HIP, PARK_ERR_NUMERIC = range(6)
+OP_CLUSTER_KEYS, OP_RETRIEVE_BLOCKS, OP_BLOCK_SPARSE_ATTN = range(3)
+_METRIC = {"qrkc": 0, "euclidean": 1}
+
+
+class ParkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} returned {_lib_status_string(status)} ({status})")
+
+
+_lib = None
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def lib():
+    """The loaded libpark.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_response_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.park_abi_version.restype = _I
+        L.park_status_string.argtypes = [_I]
+        L.park_status_string.restype = ctypes.c_char_p
+        L.park_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+        L.park_workspace_bytes.restype = _S
+        L.park_cluster_keys.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _S, _P]
+        L.park_cluster_keys.restype = _I
+        for name in ("park_retrieve_blocks", "park_retrieve_blocks_pooled"):
+            f = getattr(L, name)
+            f.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P, _P, _P, _S, _P]
+            f.restype = _I
+        L.park_block_sparse_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _P, _P,
+                                             _P, _S, _P]
+        L.park_block_sparse_attn.restype = _I
+        _lib = L
+    return _lib
+
+
+def _lib_status_string(status: int) -> str:
+    try:
+        return lib().park_status_string(status).decode()
+    except Exception:  # pragma: no cover - only while the library is unusable
+        return f"status {status}"
+
+
+def park_abi_version() -> int:
+    return lib().park_abi_version()
+
+
+def workspace_bytes(op: int, B: int, H: int, N: int, d: int, n_clusters: int) -> int:
+    return int(lib().park_workspace_bytes(op, B, H, N, d, n_clusters))
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype == torch.float32:
+        return 0
+    raise ValueError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _workspace(nbytes: int, device, given=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        return given, given.numel() * given.element_size()
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes], nbytes
+
+
+def _bhnd(x, name):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    return x.shape
+
+
+def _check(st: int, where: str):
+    if st != PARK_OK:
+        raise ParkError(st, where)
+
+
+# ------------------------------------------------------------------------- entry points
+
+def park_cluster_keys(Q, K, n_clusters: int, iters: int, metric: str = "qrkc", alpha: float = 0.05,
+                      init_idx=None, workspace=None):
+    """Cluster the keys of every (b, h).  Returns a dict of GPU tensors:
+    centroids [B,H,nk,d] float32, counts [B,H,nk], labels [B,H,N], perm [B,H,N],
+    offsets [B,H,nk+1], status [B,H] (int32)."""
+    torch = _torch()
+    _dev(Q, "Q"); _dev(K, "K")
+    B, H, N, d = _bhnd(Q, "Q")
+    if K.shape != Q.shape or K.dtype != Q.dtype:
+        raise ValueError("K must match Q in shape and dtype")
+    dev = Q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(centroids=torch.empty(B, H, n_clusters, d, dtype=torch.float32, device=dev),
+               counts=torch.empty(B, H, n_clusters, **i32), labels=torch.empty(B, H, N, **i32),
+               perm=torch.empty(B, H, N, **i32), offsets=torch.empty(B, H, n_clusters + 1, **i32),
+               status=torch.empty(B, H, **i32))
+    if init_idx is not None:
+        _dev(init_idx, "init_idx")
+        if init_idx.dtype != torch.int32 or init_idx.numel() != n_clusters:
+            raise ValueError("init_idx must be int32 [n_clusters]")
+    ws, wsb = _workspace(workspace_bytes(OP_CLUSTER_KEYS, B, H, N, d, n_clusters), dev, workspace)
+    st = lib().park_cluster_keys(_ptr(Q), _ptr(K), _dtype_code(Q), B, H, N, d, n_clusters, iters,
+                                 _METRIC[metric], alpha, _ptr(init_idx), _ptr(out["centroids"]),
+                                 _ptr(out["counts"]), _ptr(out["labels"]), _ptr(out["perm"]),
+                                 _ptr(out["offsets"]), _ptr(out["status"]), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_cluster_keys")
+    return out
+
+
+def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace):
+    torch = _torch()
+    _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
+    B, H, N, d = _bhnd(Q, "Q")
+    nk = centroids.shape[2]
+    if centroids.shape != (B, H, nk, d) or centroids.dtype != torch.float32:
+        raise ValueError("centroids must be float32 [B, H, n_clusters, d]")
+    if counts.shape != (B, H, nk) or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [B, H, n_clusters]")
+    NQ = (N + 63) // 64
+    dev = Q.device
+    out = dict(mask=torch.empty(B, H, NQ, nk, dtype=torch.uint8, device=dev),
+               block_list=torch.empty(B, H, NQ, nk, dtype=torch.int32, device=dev),
+               block_count=torch.empty(B, H, NQ, dtype=torch.int32, device=dev))
+    if scores:
+        out["scores"] = torch.empty(B, H, NQ, nk, dtype=torch.float32, device=dev)
+    need = workspace_bytes(OP_RETRIEVE_BLOCKS, B, H, N, d, nk)
+    ws, wsb = _workspace(need, dev, workspace)
+    sc = -1.0 if scale is None else float(scale)
+    st = fn(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts), nk, 64, float(top_p),
+            int(top_k), sc, _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
+            _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
+    _check(st, where)
+    return out
+
+
+def park_retrieve_blocks(Q, centroids, counts, top_p: float, top_k: int, scale=None, scores: bool = True,
+                         workspace=None):
+    """PAMA scores and top-p / top-k selection.  Returns dict(scores?, mask, block_list,
+    block_count)."""
+    return _retrieve(lib().park_retrieve_blocks, "park_retrieve_blocks", Q, centroids, counts, top_p, top_k,
+                     scale, scores, workspace)
+
+
+def park_retrieve_blocks_pooled(Q, centroids, counts, top_p: float, top_k: int, scale=None,
+                                scores: bool = True, workspace=None):
+    """Pooled-query baseline scores and the same selection."""
+    return _retrieve(lib().park_retrieve_blocks_pooled, "park_retrieve_blocks_pooled", Q, centroids, counts,
+                     top_p, top_k, scale, scores, workspace)
+
+
+def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scale=None, want_lse: bool = True,
+                           out=None, lse=None):
+    """Attention over the selected blocks.  Returns (O [B,H,N,d] in Q's dtype, lse [B,H,N]
+    float32 or None)."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (perm, "perm"), (offsets, "offsets"),
+                 (block_list, "block_list"), (block_count, "block_count")):
+        _dev(t, n)
+    B, H, N, d = _bhnd(Q, "Q")
+    if K.shape != Q.shape or V.shape != Q.shape or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("K and V must match Q in shape and dtype")
+    nk = offsets.shape[-1] - 1
+    NQ = (N + 63) // 64
+    if block_list.shape != (B, H, NQ, nk) or block_count.shape != (B, H, NQ):
+        raise ValueError("block_list must be [B, H, NQ, n_clusters] and block_count [B, H, NQ]")
+    if perm.shape != (B, H, N) or offsets.shape != (B, H, nk + 1):
+        raise ValueError("perm must be [B, H, N] and offsets [B, H, n_clusters + 1]")
+    O = torch.empty_like(Q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_block_sparse_attn(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, N, d, _ptr(perm),
+                                      _ptr(offsets), nk, _ptr(block_list), _ptr(block_count), 64, sc, _ptr(O),
+                                      _ptr(lse if want_lse else None), None, 0, _stream(Q))
+    _check(st, "park_block_sparse_attn")
+    return O, (lse if want_lse else None)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

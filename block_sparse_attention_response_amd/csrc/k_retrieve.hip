@@ -1,0 +1,442 @@
+// Block retrieval kernels: PAMA scores (PARK section 5.1, E7/E8), the pooled-query
+// baseline (section 4.1), and top-p selection with a top-k floor (section 6.1; floor rule
+// from the SCOPE appendix "Online Per-Head Top-k Selection").
+#include "park_device.h"
+#include "park_internal.h"
+
+namespace park {
+
+// ---------------------------------------------------------------------------------------
+// Centroids as an unevaluated sum of two bf16 matrices (hi + lo), so that a bf16 product
+// with the exact-bf16 queries carries about 16 mantissa bits of each centroid; plus the
+// log2 of the cluster size (-inf for an empty cluster).  Rows nk..nkp-1 are zero padding.
+__global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __restrict__ counts,
+                                 int nk, int nkp, int d, bf16* __restrict__ Chi,
+                                 bf16* __restrict__ Clo, float* __restrict__ lg) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < nkp * d) {
+    const int v = e / d;
+    const float x = v < nk ? C[(size_t)bh * nk * d + e] : 0.0f;
+    const bf16 hi = (bf16)x;
+    const bf16 lo = (bf16)(x - (float)hi);
+    Chi[(size_t)bh * nkp * d + e] = hi;
+    Clo[(size_t)bh * nkp * d + e] = lo;
+  }
+  if (e < nkp) {
+    const int n = e < nk ? counts[(size_t)bh * nk + e] : 0;
+    lg[(size_t)bh * nkp + e] = n > 0 ? __log2f((float)n) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused PAMA: one workgroup per (query block, head), 64 queries, nw waves; wave w owns
+// clusters [32 VT w, 32 VT (w+1)).  The 64 x (32 VT) logit slab of a wave stays in
+// registers (MFMA accumulators) through the softmax and the block mean; only W goes out.
+//   S_iv (log2 units) = scale log2(e) q_i . c_v + log2 n_v
+//   P_iv = 2^(S_iv - max_r S_ir) / sum_r 2^(S_ir - max_r S_ir)
+//   W_uv = (1/n_u) sum_i P_iv
+template <int D, int VT, bool QF32>
+__global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const bf16* __restrict__ Chi,
+                                              const bf16* __restrict__ Clo, const float* __restrict__ lg,
+                                              int N, int nk, int nkp, int NQ, float scale2,
+                                              float* __restrict__ W) {
+  constexpr int QP = D + 8;
+  __shared__ bf16 qs[64 * QP];
+  __shared__ bf16 qlo[QF32 ? 64 * QP : 8];
+  __shared__ float red[8][64];
+  __shared__ float rowm[64];
+  __shared__ float rowinv[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int u = blockIdx.x, bh = blockIdx.y;
+  const int q0 = u * 64;
+  const int nu = min(64, N - q0);
+
+  for (int e = tid; e < 64 * (D / 8); e += blockDim.x) {
+    const int row = e / (D / 8), seg = e % (D / 8);
+    bf16x8 hi, lo;
+    if (row < nu) {
+      const size_t off = ((size_t)bh * N + q0 + row) * D + seg * 8;
+      if constexpr (QF32) {
+        const float* q = reinterpret_cast<const float*>(Qv) + off;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          hi[i] = (bf16)q[i];
+          lo[i] = (bf16)(q[i] - (float)hi[i]);
+        }
+      } else {
+        hi = load_bf16x8(reinterpret_cast<const bf16*>(Qv) + off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { hi[i] = (bf16)0.0f; lo[i] = (bf16)0.0f; }
+    }
+    *reinterpret_cast<bf16x8*>(&qs[row * QP + seg * 8]) = hi;
+    if constexpr (QF32) *reinterpret_cast<bf16x8*>(&qlo[row * QP + seg * 8]) = lo;
+  }
+  __syncthreads();
+
+  const int v0 = w * VT * 32;
+  f32x16 acc[2][VT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = 0.0f;
+
+#pragma unroll 2
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const int col = kc * 16 + 8 * h;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qs[l32 * QP + col]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qs[(32 + l32) * QP + col]);
+    bf16x8 a0l, a1l;
+    if constexpr (QF32) {
+      a0l = *reinterpret_cast<const bf16x8*>(&qlo[l32 * QP + col]);
+      a1l = *reinterpret_cast<const bf16x8*>(&qlo[(32 + l32) * QP + col]);
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      if (v0 + 32 * vt < nkp) {
+        const size_t crow = ((size_t)bh * nkp + v0 + 32 * vt + l32) * D + col;
+        const bf16x8 bhi = load_bf16x8(Chi + crow);
+        const bf16x8 blo = load_bf16x8(Clo + crow);
+        acc[0][vt] = mfma32(a0, bhi, acc[0][vt]);
+        acc[1][vt] = mfma32(a1, bhi, acc[1][vt]);
+        acc[0][vt] = mfma32(a0, blo, acc[0][vt]);
+        acc[1][vt] = mfma32(a1, blo, acc[1][vt]);
+        if constexpr (QF32) {
+          acc[0][vt] = mfma32(a0l, bhi, acc[0][vt]);
+          acc[1][vt] = mfma32(a1l, bhi, acc[1][vt]);
+        }
+      }
+    }
+  }
+
+  // logits in log2 units; columns outside [0, nkp) are -inf
+  float lgv[VT];
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt)
+    lgv[vt] = (v0 + 32 * vt < nkp) ? lg[(size_t)bh * nkp + v0 + 32 * vt + l32] : -INFINITY;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = fmaf(acc[qt][vt][r], scale2, lgv[vt]);
+
+  // row maxima over this wave's clusters, then over the waves
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float mx = acc[qt][0][r];
+#pragma unroll
+      for (int vt = 1; vt < VT; ++vt) mx = fmaxf(mx, acc[qt][vt][r]);
+      mx = max32(mx);
+      if (l32 == 0) red[w][32 * qt + c_row(r, lane)] = mx;
+    }
+  __syncthreads();
+  if (tid < 64) {
+    float m = -INFINITY;
+    for (int i = 0; i < nw; ++i) m = fmaxf(m, red[i][tid]);
+    rowm[tid] = (m == -INFINITY) ? 0.0f : m;
+  }
+  __syncthreads();
+
+  // probabilities (unnormalised) and row sums
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float m = rowm[32 * qt + c_row(r, lane)];
+      float ps = 0.0f;
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const float p = fast_exp2(acc[qt][vt][r] - m);
+        acc[qt][vt][r] = p;
+        ps += p;
+      }
+      ps = sum32(ps);
+      if (l32 == 0) red[w][32 * qt + c_row(r, lane)] = ps;
+    }
+  __syncthreads();
+  if (tid < 64) {
+    float l = 0.0f;
+    for (int i = 0; i < nw; ++i) l += red[i][tid];
+    rowinv[tid] = (tid < nu && l > 0.0f) ? 1.0f / l : 0.0f;
+  }
+  __syncthreads();
+
+  // block mean over the queries: each lane owns one cluster column per tile
+  const float inv_nu = 1.0f / (float)nu;
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    float cs = 0.0f;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs = fmaf(acc[qt][vt][r], rowinv[32 * qt + c_row(r, lane)], cs);
+    cs += __shfl_xor(cs, 32);
+    const int v = v0 + 32 * vt + l32;
+    if (h == 0 && v < nk) W[((size_t)bh * NQ + u) * nk + v] = cs * inv_nu;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Pooled-query baseline: qbar_u = mean of the block's queries; W_uv = softmax_v(scale
+// qbar_u . c_v + log n_v).  One workgroup per (query block, head).
+template <typename T>
+__global__ __launch_bounds__(256) void k_pooled(const T* __restrict__ Q, const float* __restrict__ C,
+                                                const float* __restrict__ lg, int N, int d, int nk,
+                                                int nkp, int NQ, float scale2, float* __restrict__ W) {
+  extern __shared__ float sm[];
+  float* qbar = sm;          // d
+  float* s = sm + 128;       // nk
+  __shared__ float redv[4];
+  const int tid = threadIdx.x, u = blockIdx.x, bh = blockIdx.y;
+  const int q0 = u * 64, nu = min(64, N - q0);
+  for (int a = tid; a < d; a += blockDim.x) {
+    double acc = 0.0;
+    for (int i = 0; i < nu; ++i) acc += (double)to_f32(Q[((size_t)bh * N + q0 + i) * d + a]);
+    qbar[a] = (float)(acc / nu);
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int v = tid; v < nk; v += blockDim.x) {
+    const float* c = C + ((size_t)bh * nk + v) * d;
+    float dot = 0.0f;
+    for (int a = 0; a < d; ++a) dot = fmaf(qbar[a], c[a], dot);
+    const float x = fmaf(dot, scale2, lg[(size_t)bh * nkp + v]);
+    s[v] = x;
+    mx = fmaxf(mx, x);
+  }
+  mx = max64(mx);
+  if ((tid & 63) == 0) redv[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(redv[0], redv[1]), fmaxf(redv[2], redv[3]));
+  __syncthreads();
+  float ps = 0.0f;
+  for (int v = tid; v < nk; v += blockDim.x) {
+    const float p = fast_exp2(s[v] - mx);
+    s[v] = p;
+    ps += p;
+  }
+  ps = sum64(ps);
+  if ((tid & 63) == 0) redv[tid >> 6] = ps;
+  __syncthreads();
+  const float inv = 1.0f / (redv[0] + redv[1] + redv[2] + redv[3]);
+  for (int v = tid; v < nk; v += blockDim.x) W[((size_t)bh * NQ + u) * nk + v] = s[v] * inv;
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection per (query block, head): bitonic sort of (rank key, id) in LDS, fixed-point
+// prefix mass, cut t_p, floor k, then the mask, the ascending id list and the count.
+// Masses are summed as integers in units of 2^-56, so the prefix sums are exact and do not
+// depend on the order of the additions.
+template <int NP>
+__global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, const int32_t* __restrict__ counts,
+                                                int nk, int NQ, float top_p, int top_k,
+                                                uint8_t* __restrict__ mask, int32_t* __restrict__ list,
+                                                int32_t* __restrict__ count) {
+  __shared__ uint64_t key[NP];
+  __shared__ uint64_t pre[NP];
+  __shared__ uint64_t part[256];
+  __shared__ int sel_scan[NP];
+  __shared__ int s_nonempty, s_tp;
+  const int tid = threadIdx.x;
+  const size_t row = (size_t)blockIdx.y * NQ + blockIdx.x;
+  const int bh = blockIdx.y;
+  const float* Wr = W + row * nk;
+  if (tid == 0) { s_nonempty = 0; s_tp = 0; }
+  __syncthreads();
+  int ne = 0;
+  for (int i = tid; i < NP; i += 256) {
+    uint64_t k = ~0ull;
+    if (i < nk) {
+      const int c = counts[(size_t)bh * nk + i];
+      float wv = Wr[i];
+      wv = (wv > 0.0f) ? wv : 0.0f;  // also maps NaN to 0
+      const uint32_t hi = c > 0 ? (0x7F800000u - __float_as_uint(wv)) : 0xFFFFFFFFu;
+      ne += c > 0;
+      k = ((uint64_t)hi << 32) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  atomicAdd(&s_nonempty, ne);
+  __syncthreads();
+  for (int k = 2; k <= NP; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < NP; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t a = key[i], b = key[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { key[i] = b; key[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // fixed-point masses in ranking order, then an inclusive scan
+  constexpr int SEG = NP >= 256 ? NP / 256 : 1;
+  const int b0 = tid * SEG;
+  uint64_t run = 0;
+  if (b0 < NP) {
+    for (int i = b0; i < b0 + SEG; ++i) {
+      const uint64_t k = key[i];
+      uint64_t m = 0;
+      if ((uint32_t)(k >> 32) != 0xFFFFFFFFu) {
+        const float wv = __uint_as_float(0x7F800000u - (uint32_t)(k >> 32));
+        const double x = (double)fminf(wv, 64.0f) * 72057594037927936.0;  // 2^56
+        m = (uint64_t)x;
+      }
+      run += m;
+      pre[i] = run;
+    }
+  }
+  part[tid] = (b0 < NP) ? run : 0;
+  __syncthreads();
+  if (tid < 64) {
+    uint64_t s = 0;
+    for (int i = 0; i < 4; ++i) s += part[4 * tid + i];
+    uint64_t incl = s;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t o = __shfl_up(incl, off);
+      if (tid >= off) incl += o;
+    }
+    uint64_t ex = incl - s;
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t v = part[4 * tid + i];
+      part[4 * tid + i] = ex;
+      ex += v;
+    }
+  }
+  __syncthreads();
+  if (b0 < NP)
+    for (int i = b0; i < b0 + SEG; ++i) pre[i] += part[tid];
+  __syncthreads();
+  const double total = (double)pre[NP - 1];
+  if (top_p > 0.0f) {
+    const double target = (double)top_p * total;
+    for (int i = tid; i < NP; i += 256) {
+      if ((double)pre[i] >= target && (i == 0 || (double)pre[i - 1] < target)) s_tp = i + 1;
+    }
+  }
+  __syncthreads();
+  int cnt = s_tp > top_k ? s_tp : top_k;
+  cnt = min(cnt, s_nonempty);
+  // selection flags in id order
+  for (int i = tid; i < NP; i += 256) sel_scan[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nk; i += 256) sel_scan[(uint32_t)key[i]] = (i < cnt) ? 1 : 0;
+  __syncthreads();
+  for (int i = tid; i < nk; i += 256) mask[row * nk + i] = (uint8_t)sel_scan[i];
+  // exclusive scan of the flags -> list positions
+  int f = 0;
+  if (b0 < NP)
+    for (int i = b0; i < b0 + SEG; ++i) f += sel_scan[i];
+  __syncthreads();
+  part[tid] = (b0 < NP) ? (uint64_t)f : 0;
+  __syncthreads();
+  if (tid < 64) {
+    uint64_t s = 0;
+    for (int i = 0; i < 4; ++i) s += part[4 * tid + i];
+    uint64_t incl = s;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t o = __shfl_up(incl, off);
+      if (tid >= off) incl += o;
+    }
+    uint64_t ex = incl - s;
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t v = part[4 * tid + i];
+      part[4 * tid + i] = ex;
+      ex += v;
+    }
+  }
+  __syncthreads();
+  if (b0 < NP) {
+    int pos = (int)part[tid];
+    for (int i = b0; i < b0 + SEG && i < nk; ++i)
+      if (sel_scan[i]) list[row * nk + pos++] = i;
+  }
+  for (int i = cnt + tid; i < nk; i += 256) list[row * nk + i] = -1;
+  if (tid == 0) count[row] = cnt;
+}
+
+// ---------------------------------------------------------------------------------------
+size_t retrieve_workspace(const Shape& s, bool need_scores) {
+  const int nkp = nk_pad32(s.nk);
+  size_t b = 0;
+  b += align256((size_t)s.BH * nkp * s.d * sizeof(bf16)) * 2;  // Chi, Clo
+  b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
+  if (need_scores) b += align256((size_t)s.BH * n_qblocks(s.N) * s.nk * sizeof(float));
+  return b;
+}
+
+template <int D, bool QF32>
+static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo,
+                                const float* lg, float scale2, float* W, hipStream_t st) {
+  const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
+  const int vt = (nkp + 255) / 256;
+  const int nw = (nkp + 32 * vt - 1) / (32 * vt);
+  dim3 grid(NQ, s.BH), block(64 * nw);
+  switch (vt) {
+#define PARK_PAMA_CASE(V) \
+  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, lg, s.N, s.nk, nkp, NQ, scale2, W); break;
+    PARK_PAMA_CASE(1) PARK_PAMA_CASE(2) PARK_PAMA_CASE(3) PARK_PAMA_CASE(4) PARK_PAMA_CASE(5) PARK_PAMA_CASE(6)
+#undef PARK_PAMA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
+                           float scale, float top_p, int top_k, bool pooled, float* scores,
+                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st) {
+  const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
+  char* p = static_cast<char*>(ws);
+  bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
+  bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
+  float* lg = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * nkp * sizeof(float));
+  float* W = scores ? scores : reinterpret_cast<float*>(p);
+  {
+    dim3 grid((nkp * s.d + 255) / 256, s.BH);
+    k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, Chi, Clo, lg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const float scale2 = scale * kLog2e;
+  hipError_t e;
+  if (pooled) {
+    dim3 grid(NQ, s.BH);
+    const size_t shm = (128 + (size_t)s.nk) * sizeof(float);
+    if (s.dtype == 1)
+      k_pooled<bf16><<<grid, 256, shm, st>>>(reinterpret_cast<const bf16*>(Q), cent, lg, s.N, s.d, s.nk, nkp, NQ, scale2, W);
+    else
+      k_pooled<float><<<grid, 256, shm, st>>>(reinterpret_cast<const float*>(Q), cent, lg, s.N, s.d, s.nk, nkp, NQ, scale2, W);
+    e = hipGetLastError();
+  } else if (s.d == 128) {
+    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, scale2, W, st)
+                     : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, scale2, W, st);
+  } else {
+    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, scale2, W, st)
+                     : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, scale2, W, st);
+  }
+  if (e != hipSuccess) return e;
+  dim3 grid(NQ, s.BH);
+  int np = 32;
+  while (np < s.nk) np <<= 1;
+  switch (np) {
+#define PARK_SEL_CASE(P) \
+  case P: k_select<P><<<grid, 256, 0, st>>>(W, counts, s.nk, NQ, top_p, top_k, mask, list, count); break;
+    PARK_SEL_CASE(32) PARK_SEL_CASE(64) PARK_SEL_CASE(128) PARK_SEL_CASE(256) PARK_SEL_CASE(512)
+    PARK_SEL_CASE(1024) PARK_SEL_CASE(2048)
+#undef PARK_SEL_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace park

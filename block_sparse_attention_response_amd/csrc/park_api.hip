@@ -1,0 +1,137 @@
+// libpark C ABI: argument validation, workspace sizing and kernel launches.
+#include <math.h>
+#include "../../include/park.h"
+#include "park_internal.h"
+
+using park::Shape;
+
+namespace {
+
+bool finite_f(float x) { return isfinite(x) != 0; }
+
+int check_common(int dtype, int B, int H, int N, int d, int n_clusters, bool* unsupported) {
+  *unsupported = false;
+  if (dtype != PARK_F32 && dtype != PARK_BF16) return PARK_ERR_INVALID;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || n_clusters < 1 || n_clusters > N) return PARK_ERR_INVALID;
+  if ((long long)B * H * N * d >= (1LL << 31)) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
+  if (d != 64 && d != 128) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
+  if (n_clusters > PARK_MAX_CLUSTERS) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
+  return PARK_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return PARK_OK;
+  if (ws == nullptr || have < need) return PARK_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return PARK_ERR_WORKSPACE;
+  return PARK_OK;
+}
+
+Shape make_shape(int dtype, int B, int H, int N, int d, int nk) {
+  Shape s;
+  s.BH = B * H; s.N = N; s.d = d; s.nk = nk; s.dtype = dtype;
+  return s;
+}
+
+int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                  const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k, float scale,
+                  float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !centroids || !counts || !mask || !block_list || !block_count) return PARK_ERR_INVALID;
+  if (!finite_f(top_p) || top_p < 0.0f || top_p > 1.0f || top_k < 0 || !finite_f(scale)) return PARK_ERR_INVALID;
+  if (q_block != PARK_QUERY_BLOCK) return PARK_ERR_UNSUPPORTED;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::retrieve_workspace(s, scores == nullptr));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  hipError_t e = park::launch_retrieve(s, Q, centroids, counts, scale, top_p, top_k, pooled, scores, mask,
+                                       block_list, block_count, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int park_abi_version(void) { return PARK_ABI_VERSION; }
+
+const char* park_status_string(int status) {
+  switch (status) {
+    case PARK_OK: return "PARK_OK";
+    case PARK_ERR_INVALID: return "PARK_ERR_INVALID";
+    case PARK_ERR_UNSUPPORTED: return "PARK_ERR_UNSUPPORTED";
+    case PARK_ERR_WORKSPACE: return "PARK_ERR_WORKSPACE";
+    case PARK_ERR_HIP: return "PARK_ERR_HIP";
+    case PARK_ERR_NUMERIC: return "PARK_ERR_NUMERIC";
+    default: return "PARK_ERR_UNKNOWN";
+  }
+}
+
+size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_clusters) {
+  bool uns;
+  if (check_common(PARK_BF16, B, H, N, d, n_clusters, &uns) != PARK_OK) return 0;
+  const Shape s = make_shape(PARK_BF16, B, H, N, d, n_clusters);
+  switch (op) {
+    case PARK_OP_CLUSTER_KEYS: return park::cluster_workspace(s);
+    case PARK_OP_RETRIEVE_BLOCKS: return park::retrieve_workspace(s, true);
+    case PARK_OP_BLOCK_SPARSE_ATTN: return park::attn_workspace(s);
+    default: return 0;
+  }
+}
+
+int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int N, int d, int n_clusters,
+                      int iters, int metric, float alpha, const int32_t* init_idx, float* centroids,
+                      int32_t* counts, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !K || !centroids || !counts || !labels || !perm || !offsets) return PARK_ERR_INVALID;
+  if (iters < 1 || (metric != PARK_METRIC_QRKC && metric != PARK_METRIC_EUCLIDEAN)) return PARK_ERR_INVALID;
+  if (!finite_f(alpha) || alpha < 0.0f || alpha > 1.0f) return PARK_ERR_INVALID;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::cluster_workspace(s));
+  if (st != PARK_OK) return st;
+  hipError_t e = park::launch_cluster(s, Q, K, iters, metric, alpha, init_idx, centroids, counts, labels, perm,
+                                      offsets, status, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+int park_retrieve_blocks(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                         const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k, float scale,
+                         float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return retrieve_impl(false, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
+                       scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
+}
+
+int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                                const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k,
+                                float scale, float* scores, uint8_t* mask, int32_t* block_list,
+                                int32_t* block_count, void* workspace, size_t workspace_bytes, void* stream) {
+  return retrieve_impl(true, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
+                       scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
+}
+
+int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,
+                           const int32_t* perm, const int32_t* offsets, int n_clusters, const int32_t* block_list,
+                           const int32_t* block_count, int q_block, float scale, void* O, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !K || !V || !perm || !offsets || !block_list || !block_count || !O) return PARK_ERR_INVALID;
+  if (!finite_f(scale)) return PARK_ERR_INVALID;
+  if (q_block != PARK_QUERY_BLOCK) return PARK_ERR_UNSUPPORTED;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::attn_workspace(s));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  hipError_t e = park::launch_attn(s, Q, K, V, perm, offsets, block_list, block_count, scale, O, lse, workspace,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+}  // extern "C"

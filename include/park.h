@@ -1,0 +1,172 @@
+/*
+ * park.h - C ABI of libpark: query-response key clustering, per-query attention-mass
+ * block retrieval and block-sparse attention for one attention layer, on one MI355X
+ * (gfx950) GPU.
+ *
+ * The method is PARK, "Accurate Block Retrieval for Sparse Attention in Video Diffusion
+ * Transformers" (paperpeel.com/paper/2609.38978).  Section and equation names below refer
+ * to that page.
+ *
+ * Conventions for every entry point
+ *   - Tensors are caller-owned DEVICE memory, contiguous, in [B, H, N, d] (or the stated
+ *     shape) row-major order; nothing is copied to or from the host.
+ *   - libpark allocates no device memory.  Scratch space comes from the caller's
+ *     `workspace` (device memory, 256-byte aligned, at least park_workspace_bytes()).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and the
+ *     call returns without synchronising.  Device-side faults surface at the caller's next
+ *     synchronisation.  Calls hold no global state and may run concurrently on different
+ *     streams with different workspaces.
+ *   - Arguments are validated on the host before anything is launched; a failing check
+ *     returns its status and launches nothing.  No C++ exception crosses the ABI.
+ *   - dtype: PARK_F32 (inputs are float) or PARK_BF16 (inputs are bfloat16).
+ *   - Head dimension d must be 64 or 128; the query block is 64 tokens; the number of
+ *     key clusters is at most PARK_MAX_CLUSTERS.
+ */
+#ifndef PARK_H
+#define PARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PARK_API __attribute__((visibility("default")))
+#else
+#define PARK_API
+#endif
+
+#define PARK_ABI_VERSION 1
+#define PARK_MAX_CLUSTERS 1536
+#define PARK_QUERY_BLOCK 64
+
+typedef enum park_status {
+  PARK_OK = 0,
+  PARK_ERR_INVALID = 1,      /* a required pointer is NULL or a size/parameter is out of range */
+  PARK_ERR_UNSUPPORTED = 2,  /* valid, but not built: d not in {64,128}, q_block != 64, ... */
+  PARK_ERR_WORKSPACE = 3,    /* workspace NULL, misaligned or smaller than required */
+  PARK_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError after the launch) */
+  PARK_ERR_NUMERIC = 5       /* reserved for the host-side check of per-head status flags */
+} park_status;
+
+typedef enum park_dtype { PARK_F32 = 0, PARK_BF16 = 1 } park_dtype;
+
+typedef enum park_metric {
+  PARK_METRIC_QRKC = 0,      /* query-response key clustering (section 5.2) */
+  PARK_METRIC_EUCLIDEAN = 1  /* plain Euclidean k-means on the raw keys ("w/o QRKC", section 6.3) */
+} park_metric;
+
+typedef enum park_op {
+  PARK_OP_CLUSTER_KEYS = 0,
+  PARK_OP_RETRIEVE_BLOCKS = 1,
+  PARK_OP_BLOCK_SPARSE_ATTN = 2
+} park_op;
+
+/* PARK_ABI_VERSION of the loaded library. */
+PARK_API int park_abi_version(void);
+
+/* Static, NUL-terminated name of a park_status value ("PARK_OK", ...). */
+PARK_API const char* park_status_string(int status);
+
+/* Bytes of workspace the given entry point needs for these sizes (0 if none); returns 0
+ * also for invalid sizes, which the entry point itself then rejects. */
+PARK_API size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_clusters);
+
+/*
+ * park_cluster_keys - query-response key clustering (section 5.2, App. D.2), per (b, h):
+ *   G_Q = (1/N) Q^T Q;  s_Q = max(tr(G_Q)/d, 1e-6);
+ *   Gs  = (1 - alpha) G_Q + (alpha + 1e-6) s_Q I = R R^T  (Cholesky, R lower triangular);
+ *   k~_j = R^T k_j;  Lloyd k-means with `iters` steps of (assign, update) on k~ from the
+ *   anchors k~_{floor(v N / n_clusters)} (or k~_{init_idx[v]});  argmin ties go to the
+ *   lowest cluster; an empty cluster keeps its centroid.  metric EUCLIDEAN uses R = I.
+ * Outputs (all per (b, h)):
+ *   centroids [B,H,n_clusters,d] float: c_v = mean of the ORIGINAL keys of cluster v
+ *             (section 5.1, E7), 0 for an empty cluster;
+ *   counts    [B,H,n_clusters]   int32: n_v;
+ *   labels    [B,H,N]            int32: cluster of each key after the last step;
+ *   perm      [B,H,N]            int32: key indices in (label, index) order, so cluster v
+ *             is perm[offsets[v] .. offsets[v+1]);
+ *   offsets   [B,H,n_clusters+1] int32: exclusive prefix sum of counts, offsets[n] = N;
+ *   status    [B,H] int32 or NULL: 0, or 1 when the Cholesky factorisation failed (the
+ *             head is then clustered with R = I); written asynchronously on `stream`.
+ * init_idx: NULL or device int32 [n_clusters] of key indices in [0, N), shared by all heads.
+ * Errors: INVALID for NULL required pointers, B,H < 1, N < 1, n_clusters outside [1, N],
+ * iters < 1, alpha outside [0, 1] or not finite, unknown dtype/metric; UNSUPPORTED for d
+ * not in {64,128} or n_clusters > PARK_MAX_CLUSTERS; WORKSPACE; HIP.
+ */
+PARK_API int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int N, int d,
+                      int n_clusters, int iters, int metric, float alpha, const int32_t* init_idx,
+                      float* centroids, int32_t* counts, int32_t* labels, int32_t* perm,
+                      int32_t* offsets, int32_t* status, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * park_retrieve_blocks - per-query attention-mass aggregation (PAMA, section 5.1, E7/E8)
+ * followed by top-p selection with a top-k floor (section 6.1; the floor as in SCOPE,
+ * paperpeel.com/paper/2608.12780, appendix "Online Per-Head Top-k Selection"), per (b, h):
+ *   S_iv = scale q_i . c_v + log n_v  (-inf for n_v = 0);  P_iv = softmax_v S_iv;
+ *   W_uv = (1/n_u) sum_{i in query block u} P_iv, query block u = tokens [64u, 64u+64) of N
+ *   (the last block may be shorter);
+ *   ranking of blocks v by (W_uv descending, v ascending), empty clusters last;
+ *   t_p = shortest prefix with mass >= top_p * sum_v W_uv (0 if top_p = 0);
+ *   count_u = min(max(t_p, top_k), number of non-empty clusters).
+ * Inputs: Q [B,H,N,d]; centroids [B,H,n_clusters,d] float and counts [B,H,n_clusters] as
+ * written by park_cluster_keys.  scale <= 0 selects 1/sqrt(d).
+ * Outputs (NQ = ceil(N/64)):
+ *   scores      [B,H,NQ,n_clusters] float or NULL: W^PAMA;
+ *   mask        [B,H,NQ,n_clusters] uint8: 1 for selected (query block, cluster) pairs;
+ *   block_list  [B,H,NQ,n_clusters] int32: selected cluster ids ascending, then -1;
+ *   block_count [B,H,NQ] int32: count_u.
+ * Errors: INVALID (NULL required pointers, sizes, top_p outside [0,1], top_k < 0, scale not
+ * finite), UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS), WORKSPACE, HIP.
+ */
+PARK_API int park_retrieve_blocks(const void* Q, int dtype, int B, int H, int N, int d,
+                         const float* centroids, const int32_t* counts, int n_clusters,
+                         int q_block, float top_p, int top_k, float scale, float* scores,
+                         uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * park_retrieve_blocks_pooled - the query-centroid estimate that PAMA replaces (section 4.1
+ * and the "w/o PAMA" ablation of section 6.3), kept as a measurement baseline:
+ *   qbar_u = mean of block u's queries;  W_uv = softmax_v(scale qbar_u . c_v + log n_v);
+ * then the same selection as park_retrieve_blocks.  Same arguments, layouts and errors.
+ */
+PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, int d,
+                                const float* centroids, const int32_t* counts, int n_clusters,
+                                int q_block, float top_p, int top_k, float scale, float* scores,
+                                uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * park_block_sparse_attn - attention restricted to the selected blocks (section 3.1, E1/E2
+ * with the softmax renormalised over the selected keys), per (b, h) and query i in block u:
+ *   J_u = union over r < block_count[u] of cluster block_list[u][r], i.e. the keys
+ *         perm[offsets[v] .. offsets[v+1]);
+ *   O_i = sum_{j in J_u} exp(s_ij - m_i) v_j / sum_{j in J_u} exp(s_ij - m_i),
+ *   s_ij = scale q_i . k_j,  lse_i = m_i + log sum_{j in J_u} exp(s_ij - m_i);
+ * an empty J_u gives O_i = 0 and lse_i = -inf.  Keys and values are read in place through
+ * perm (no reordered copy is made); O is in the original query order.
+ * Inputs: Q, K, V [B,H,N,d] of `dtype`; perm/offsets from park_cluster_keys; block_list /
+ * block_count from park_retrieve_blocks (ids must lie in [0, n_clusters); listing every
+ * cluster gives dense attention).  scale <= 0 selects 1/sqrt(d).
+ * Outputs: O [B,H,N,d] of `dtype`; lse [B,H,N] float or NULL (natural-log log-sum-exp).
+ * Numerics: bf16 inputs use bf16 matrix products with float accumulation and a float
+ * online softmax (probabilities rounded to bf16 before the PV product); float inputs are
+ * computed in float throughout.
+ * Errors: INVALID, UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS),
+ * WORKSPACE, HIP.
+ */
+PARK_API int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtype, int B, int H,
+                           int N, int d, const int32_t* perm, const int32_t* offsets,
+                           int n_clusters, const int32_t* block_list, const int32_t* block_count,
+                           int q_block, float scale, void* O, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARK_H */
