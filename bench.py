@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the PARK hot path on one MI355X.
+
+One step = park_cluster_keys (query-response key clustering, 10 k-means steps) +
+park_retrieve_blocks (PAMA scores + top-p / top-k selection) + park_block_sparse_attn
+for one attention layer of the Wan2.1-14B-720p shape (40 heads, 75,600 tokens as a
+21x45x80 latent grid, d = 128, bf16, 1024 key clusters, top-p 0.9, top-k floor 8) on
+seeded synthetic Q/K/V.  Inputs are resident on the GPU before timing starts.
+
+Prints one JSON line.  `value` is the whole-step throughput expressed as effective
+sparse-attention TFLOP/s: 4 d x (selected query-key pairs) per step divided by the
+whole step time (clustering + retrieval + attention).  Per-entry-point times, the
+attention kernel's own TFLOP/s against the bf16 MFMA peak, recall against dense
+attention and the CPU oracle's time on a bounded sample are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def effective_pairs(torch, counts, block_list, block_count, N):
+    """Sum over (b, h, query block u) of n_u * sum_{v selected} n_v."""
+    B, H, NQ, nk = block_list.shape
+    valid = block_list >= 0
+    idx = block_list.clamp(min=0).long()
+    sizes = torch.gather(counts.long().unsqueeze(2).expand(B, H, NQ, nk), 3, idx) * valid
+    keys_per_block = sizes.sum(-1)                               # [B, H, NQ]
+    nu = torch.full((NQ,), 64, dtype=torch.long, device=counts.device)
+    nu[-1] = N - 64 * (NQ - 1)
+    return int((keys_per_block * nu).sum().item()), keys_per_block
+
+
+def cpu_baseline(cfg, Q, K, V, budget_heads=1):
+    """The oracle on head 0 of batch 0, attention on every 16th query block (plus the last);
+    per-layer time extrapolated to all heads and blocks."""
+    import numpy as np
+    import oracle
+    oracle.lib()
+    d = cfg.d
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = Q[0, 0], K[0, 0], V[0, 0]
+    t0 = time.perf_counter()
+    cl = oracle.cluster_keys(q, k, cfg.n_clusters, cfg.iters)
+    t1 = time.perf_counter()
+    W = oracle.pama(q, cl["centroids"], cl["counts"], 64, scale)
+    _, lst, cnt, _, _ = oracle.select(W, cl["counts"], cfg.top_p, cfg.top_k)
+    t2 = time.perf_counter()
+    NQ = cfg.n_qblocks
+    ub = np.unique(np.r_[np.arange(0, NQ, 16), NQ - 1])
+    oracle.block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], lst, cnt, 64, scale, ub)
+    t3 = time.perf_counter()
+    sizes = np.diff(cl["offsets"])
+    nu = np.full(NQ, 64); nu[-1] = cfg.N - 64 * (NQ - 1)
+    pairs_head = float(sum(nu[u] * sizes[lst[u, :cnt[u]]].sum() for u in range(NQ)))
+    heads = cfg.B * cfg.H
+    layer_s = heads * ((t1 - t0) + (t2 - t1) + (t3 - t2) * NQ / len(ub))
+    flops = 4.0 * d * pairs_head * heads
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": flops / layer_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"batch 0 head 0 of {heads}: full clustering ({cfg.iters} k-means steps) and retrieval, "
+                   f"attention on {len(ub)} of {NQ} query blocks; per-layer time extrapolated x{heads} heads "
+                   f"(attention x{NQ / len(ub):.1f})"),
+        "sample_s": round(t3 - t0, 2),
+        "layer_s_extrapolated": round(layer_s, 1),
+        "cluster_s_per_head": round(t1 - t0, 2), "retrieve_s_per_head": round(t2 - t1, 2),
+        "attn_s_per_head_extrapolated": round((t3 - t2) * NQ / len(ub), 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="workload index of park_synth.CONFIGS")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--recall", choices=["on", "off"], default="on")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (heads would be "
+              "sharded across GPUs with no exchange inside the layer).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import park_synth
+    cfg = park_synth.CONFIGS[args.config]
+    log(f"generating {cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} {cfg.dtype}")
+    t = time.perf_counter()
+    Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
+    log(f"inputs ready in {time.perf_counter() - t:.1f}s")
+
+    import torch
+    import block_sparse_attention_response_amd as park
+    park.lib()
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(Q).to(dt).cuda()
+    k = torch.from_numpy(K).to(dt).cuda()
+    v = torch.from_numpy(V).to(dt).cuda()
+    B, H, N, d = q.shape
+    nk = cfg.n_clusters
+    top_p, top_k = cfg.top_p, (cfg.top_k if not cfg.forced_k else cfg.forced_k[1])
+    ws_c = torch.empty(park.workspace_bytes(park.OP_CLUSTER_KEYS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(park.workspace_bytes(park.OP_RETRIEVE_BLOCKS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        cl = park.park_cluster_keys(q, k, nk, cfg.iters, workspace=ws_c)
+        if ev: ev[1].record(stream)
+        rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)
+        if ev: ev[2].record(stream)
+        O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"])
+        if ev: ev[3].record(stream)
+        return cl, rb, O, lse
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cl, rb, O, lse = out
+    ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
+    cluster_ms, retrieve_ms, attn_ms = ms.mean(0)
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"step {ms_per_step:.2f} ms: cluster {cluster_ms:.2f} retrieve {retrieve_ms:.2f} attention {attn_ms:.2f}")
+
+    pairs, keys_per_block = effective_pairs(torch, cl["counts"], rb["block_list"], rb["block_count"], N)
+    attn_flops = 4.0 * d * pairs
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    value = attn_flops / (ms_per_step * 1e-3) / 1e12
+    block_density = float(rb["block_count"].float().mean().item()) / nk
+    pair_density = pairs / (B * H * float(N) * N)
+
+    result = {
+        "metric": "retrieval ms/layer + sparse-attn effective TFLOP/s (75.6k tok, 40 heads)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded clustered Gaussian Q/K with 3D RoPE, V ~ N(0,1)); no trained weights",
+        "config": {"workload": cfg.name, "batch": B, "heads": H, "tokens": N, "head_dim": d,
+                   "key_clusters": nk, "kmeans_iters": cfg.iters, "top_p": top_p, "top_k_floor": top_k,
+                   "query_block": 64, "parallelism": "single GPU"},
+        "retrieval_ms_per_layer": round(float(retrieve_ms), 3),
+        "cluster_ms_per_layer": round(float(cluster_ms), 3),
+        "attn_ms_per_layer": round(float(attn_ms), 3),
+        "attn_effective_tflops": round(attn_tflops, 2),
+        "block_density": round(block_density, 4),
+        "pair_density": round(pair_density, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+    if args.recall == "on":
+        allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()
+        allc = torch.full_like(rb["block_count"], nk)
+        _, lse_dense = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], allb, allc)
+        torch.cuda.synchronize()
+        rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
+        result["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
+                            "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+
+    if args.cpu_baseline == "on":
+        log("CPU oracle baseline on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, Q, K, V)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,7 +110,29 @@ def head_rng(seed: int, b: int, h: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(b, h))))
 
 
-def generate(cfg: Config, seed: int = 0, heads=None):
+def _one_head(cfg: Config, seed: int, b: int, h: int, tabs):
+    T, Hh, Ww = cfg.grid
+    nv = T * Hh * Ww
+    N, d, M = cfg.N, cfg.d, cfg.n_centres
+    rng = head_rng(seed, b, h)
+    mu = 2.0 * rng.standard_normal((M, d), dtype=np.float32)
+    z = rng.integers(0, M, size=nv)
+    q = mu[z] + 0.5 * rng.standard_normal((nv, d), dtype=np.float32)
+    k = mu[z] + 0.5 * rng.standard_normal((nv, d), dtype=np.float32)
+    v = rng.standard_normal((N, d), dtype=np.float32)
+    Q = np.empty((N, d), np.float32)
+    K = np.empty((N, d), np.float32)
+    Q[:nv] = rope_3d(q, cfg.grid, cfg.split, tables=tabs)
+    K[:nv] = rope_3d(k, cfg.grid, cfg.split, tables=tabs)
+    if cfg.n_text:
+        Q[nv:] = rng.standard_normal((cfg.n_text, d), dtype=np.float32)
+        K[nv:] = rng.standard_normal((cfg.n_text, d), dtype=np.float32)
+    if cfg.dtype == "bf16":
+        Q, K, v = round_bf16(Q), round_bf16(K), round_bf16(v)
+    return Q, K, v
+
+
+def generate(cfg: Config, seed: int = 0, heads=None, workers: int = 0):
     """Q, K, V as float32 arrays [B, H', N, d] (bf16-exact values for bf16 configs).
 
     Each (batch b, head h) draws from its own PCG64 stream ``head_rng(seed, b, h)``:
@@ -120,29 +142,25 @@ def generate(cfg: Config, seed: int = 0, heads=None):
     Normal draws are float32.  3D RoPE is applied to the video part of Q and K, then
     everything is rounded to bf16 for bf16 configs.  ``heads`` (head indices) restricts
     the output to those heads (H' = len(heads)); each head's values do not depend on
-    which other heads are generated.
+    which other heads are generated.  ``workers`` > 1 generates heads on that many threads.
     """
-    T, Hh, Ww = cfg.grid
-    nv = T * Hh * Ww
-    N, d, M = cfg.N, cfg.d, cfg.n_centres
     keep = list(range(cfg.H)) if heads is None else sorted(set(int(h) for h in heads))
     tabs = _rope_tables(cfg.grid, cfg.split, 10000.0)
+    N, d = cfg.N, cfg.d
     Q = np.empty((cfg.B, len(keep), N, d), np.float32)
     K = np.empty_like(Q)
     V = np.empty_like(Q)
-    for b in range(cfg.B):
-        for hi, h in enumerate(keep):
-            rng = head_rng(seed, b, h)
-            mu = 2.0 * rng.standard_normal((M, d), dtype=np.float32)
-            z = rng.integers(0, M, size=nv)
-            q = mu[z] + 0.5 * rng.standard_normal((nv, d), dtype=np.float32)
-            k = mu[z] + 0.5 * rng.standard_normal((nv, d), dtype=np.float32)
-            V[b, hi] = rng.standard_normal((N, d), dtype=np.float32)
-            Q[b, hi, :nv] = rope_3d(q, cfg.grid, cfg.split, tables=tabs)
-            K[b, hi, :nv] = rope_3d(k, cfg.grid, cfg.split, tables=tabs)
-            if cfg.n_text:
-                Q[b, hi, nv:] = rng.standard_normal((cfg.n_text, d), dtype=np.float32)
-                K[b, hi, nv:] = rng.standard_normal((cfg.n_text, d), dtype=np.float32)
-    if cfg.dtype == "bf16":
-        Q, K, V = round_bf16(Q), round_bf16(K), round_bf16(V)
+    jobs = [(b, hi, h) for b in range(cfg.B) for hi, h in enumerate(keep)]
+
+    def run(job):
+        b, hi, h = job
+        Q[b, hi], K[b, hi], V[b, hi] = _one_head(cfg, seed, b, h, tabs)
+
+    if workers and workers > 1 and len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(workers, len(jobs))) as ex:
+            list(ex.map(run, jobs))
+    else:
+        for j in jobs:
+            run(j)
     return Q, K, V
