@@ -116,6 +116,7 @@ def main():
     top_p, top_k = cfg.top_p, (cfg.top_k if not cfg.forced_k else cfg.forced_k[1])
     ws_c = torch.empty(park.workspace_bytes(park.OP_CLUSTER_KEYS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     ws_r = torch.empty(park.workspace_bytes(park.OP_RETRIEVE_BLOCKS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(park.workspace_bytes(park.OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -124,7 +125,8 @@ def main():
         if ev: ev[1].record(stream)
         rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)
         if ev: ev[2].record(stream)
-        O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"])
+        O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
+                                             workspace=ws_a)
         if ev: ev[3].record(stream)
         return cl, rb, O, lse
 
@@ -175,7 +177,7 @@ def main():
         "attn_effective_tflops": round(attn_tflops, 2),
         "block_density": round(block_density, 4),
         "pair_density": round(pair_density, 4),
-        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "park_block_sparse_attn (pack + k_attn_bf16<128>)", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
     }
@@ -183,7 +185,7 @@ def main():
     if args.recall == "on":
         allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()
         allc = torch.full_like(rb["block_count"], nk)
-        _, lse_dense = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], allb, allc)
+        _, lse_dense = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], allb, allc, workspace=ws_a)
         torch.cuda.synchronize()
         rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
         result["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),

@@ -212,7 +212,7 @@ def park_retrieve_blocks_pooled(Q, centroids, counts, top_p: float, top_k: int, 
 
 
 def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scale=None, want_lse: bool = True,
-                           out=None, lse=None):
+                           out=None, lse=None, workspace=None):
     """Attention over the selected blocks.  Returns (O [B,H,N,d] in Q's dtype, lse [B,H,N]
     float32 or None)."""
     torch = _torch()
@@ -232,9 +232,10 @@ def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scal
     if want_lse and lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
     sc = -1.0 if scale is None else float(scale)
+    ws, wsb = _workspace(workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), Q.device, workspace)
     st = lib().park_block_sparse_attn(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, N, d, _ptr(perm),
                                       _ptr(offsets), nk, _ptr(block_list), _ptr(block_count), 64, sc, _ptr(O),
-                                      _ptr(lse if want_lse else None), None, 0, _stream(Q))
+                                      _ptr(lse if want_lse else None), _ptr(ws), wsb, _stream(Q))
     _check(st, "park_block_sparse_attn")
     return O, (lse if want_lse else None)
 
