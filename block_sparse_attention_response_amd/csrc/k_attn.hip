@@ -101,8 +101,19 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
   const int32_t* pm = perm + (size_t)bh * N + a;
   const bf16* Kh = K + (size_t)bh * N * D;
   const bf16* Vh = V + (size_t)bh * N * D;
-  bf16* Kph = Kp + ((size_t)bh * Gcap + g0) * 8 * D;
-  bf16* Vph = Vp + ((size_t)bh * Gcap + g0) * 8 * D;
+  bf16* Kph = Kp + (size_t)bh * (Gcap + 1) * 8 * D;
+  bf16* Vph = Vp + (size_t)bh * (Gcap + 1) * 8 * D;
+  if (v == 0) {  // group Gcap of every head is all zeros: the filler of partial tiles
+    for (int e = tid; e < D; e += 128) {
+      bf16x8 z;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+      *reinterpret_cast<bf16x8*>(Kph + (size_t)Gcap * 8 * D + e * 8) = z;
+      *reinterpret_cast<bf16x8*>(Vph + (size_t)Gcap * 8 * D + e * 8) = z;
+    }
+  }
+  Kph += (size_t)g0 * 8 * D;
+  Vph += (size_t)g0 * 8 * D;
   for (int e = tid; e < ng * 8 * NS; e += 128) {
     const int slot = e / NS, sg = e % NS;
     bf16x8 val;
@@ -137,142 +148,156 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
   }
 }
 
-// Row swap inside each 16-row chunk (rows 4..7 <-> 8..11): with it, the 8 rows of S^T that
-// an MFMA lane holds for one 16-key chunk are 8 consecutive keys, so the matching V^T
-// operand is one 16-byte read.
-__device__ __forceinline__ int sigma16(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
-
-// bf16 path, step 2.  One workgroup (4 waves) per (query block, head).  Wave w = 2 kw + qw
-// owns queries 32 qw .. 32 qw + 31 of the block and keys 32 kw .. 32 kw + 31 of every
-// 64-key tile (8 groups); each wave keeps its own online-softmax state and the two key
-// halves are merged at the end.  Tiles are double-buffered in LDS: the loads of tile t+1
-// are issued before the MFMA work on tile t.
-//   S^T = K Q^T  (A: K rows from LDS in sigma16 order, B: Q^T fragments in registers)
-//   O^T += V^T P^T  (A: V^T rows from LDS, B: P^T straight from the S^T accumulators)
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
-                                                      const bf16* __restrict__ Vp, const int32_t* __restrict__ gstart,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ list,
-                                                      const int32_t* __restrict__ count, int N, int nk, int NQ,
-                                                      int Gcap, float scale2, bf16* __restrict__ O,
-                                                      float* __restrict__ lse) {
-  constexpr int KP = D + 8;
-  constexpr int VP = 64 + 8;
-  constexpr int NS = D / 8;
-  constexpr int KCH = 64 * NS / 256;  // 16-byte K chunks per thread per tile
-  constexpr int VCH = 8 * D / 256;    // 16-byte V chunks per thread per tile
-  __shared__ bf16 Ks[2][64 * KP];
-  __shared__ bf16 Vt[2][D * VP];
-  __shared__ int pre[PARK_MAX_CLUSTERS + 1];
-  __shared__ int tgrp[3][8];
-  __shared__ int tval[3][8];
-  __shared__ int wsum[4];
-
-  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lb / NQ, u = lb % NQ;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
-  const int qw = w & 1, kw = w >> 1;
-  const size_t row = (size_t)bh * NQ + u;
+// ---------------------------------------------------------------------------------------
+// bf16 path, step 2: the tile plan.  For every (head, query block) the concatenation of its
+// selected clusters' groups is cut into 64-key tiles of 8 groups; plan entry (g << 4) | nv
+// names a packed group g and its number of real keys nv (0..8).  The last tile of a block is
+// filled with the all-zero group Gcap.  tbase is the exclusive scan of tiles per block.
+__global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ list, const int32_t* __restrict__ count,
+                                                    const int32_t* __restrict__ offsets, int nk, int NQ, int rows,
+                                                    int32_t* __restrict__ ntiles) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int bh = row / NQ;
   const int cnt = min(max(count[row], 0), nk);
-  const int32_t* lst = list + row * nk;
+  const int32_t* lst = list + (size_t)row * nk;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
-  const int32_t* gst = gstart + (size_t)bh * (nk + 1);
-  const bf16* Kph = Kp + (size_t)bh * Gcap * 8 * D;
-  const bf16* Vph = Vp + (size_t)bh * Gcap * 8 * D;
-
-  // prefix of the group counts of the selected clusters (ids outside [0, nk) count as empty)
-  auto csize = [&](int i) {
+  int s = 0;
+  for (int i = lane; i < cnt; i += 64) {
     const int v = lst[i];
-    return (v >= 0 && v < nk) ? off[v + 1] - off[v] : 0;
-  };
-  int TG;
-  {
-    const int per = (cnt + 255) / 256;
-    const int b0 = min(tid * per, cnt), b1 = min(b0 + per, cnt);
-    int s = 0;
-    for (int i = b0; i < b1; ++i) s += (csize(i) + 7) >> 3;
-    int incl = s;
+    if (v >= 0 && v < nk) s += (off[v + 1] - off[v] + 7) >> 3;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) ntiles[row] = (s + 7) >> 3;
+}
+
+__global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ ntiles, int rows,
+                                                    int32_t* __restrict__ tbase) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (rows + 1023) / 1024;
+  const int b0 = min(tid * per, rows), b1 = min(b0 + per, rows);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += ntiles[i];
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int ex = incl - s;
+  for (int i = 0; i < w; ++i) ex += wsum[i];
+  for (int i = b0; i < b1; ++i) {
+    tbase[i] = ex;
+    ex += ntiles[i];
+  }
+  if (tid == 1023) tbase[rows] = ex;
+}
+
+__global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ list, const int32_t* __restrict__ count,
+                                                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ gstart,
+                                                   int nk, int NQ, int rows, int Gcap, const int32_t* __restrict__ tbase,
+                                                   int32_t* __restrict__ plan) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int bh = row / NQ;
+  const int cnt = min(max(count[row], 0), nk);
+  const int32_t* lst = list + (size_t)row * nk;
+  const int32_t* off = offsets + (size_t)bh * (nk + 1);
+  const int32_t* gs = gstart + (size_t)bh * (nk + 1);
+  int32_t* pl = plan + (size_t)tbase[row] * 8;
+  int run = 0;
+  for (int i0 = 0; i0 < cnt; i0 += 64) {
+    const int i = i0 + lane;
+    int n = 0, g0 = 0;
+    if (i < cnt) {
+      const int v = lst[i];
+      if (v >= 0 && v < nk) { n = off[v + 1] - off[v]; g0 = gs[v]; }
+    }
+    const int ng = (n + 7) >> 3;
+    int incl = ng;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int t = __shfl_up(incl, o);
       if (lane >= o) incl += t;
     }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    int ex = incl - s;
-    for (int i = 0; i < w; ++i) ex += wsum[i];
-    for (int i = b0; i < b1; ++i) {
-      pre[i] = ex;
-      ex += (csize(i) + 7) >> 3;
-    }
-    TG = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (tid == 0) pre[cnt] = TG;
-    __syncthreads();
+    const int ex = run + incl - ng;
+    for (int jj = 0; jj < ng; ++jj) pl[ex + jj] = ((g0 + jj) << 4) | min(8, n - 8 * jj);
+    run += __shfl(incl, 63);
   }
-  const int ntiles = (TG + 7) >> 3;
+  const int end = (run + 7) & ~7;
+  for (int j = run + lane; j < end; j += 64) pl[j] = Gcap << 4;
+}
 
-  // group ids and valid-key counts of tile t into ring slot t % 3 (threads 0..7)
-  auto tile_info = [&](int t) {
-    if (tid < 8) {
-      const int j = 8 * t + tid;
-      int g = -1, nv = 0;
-      if (j < TG) {
-        int lo = 0, hi = cnt - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= j) lo = mid; else hi = mid - 1;
-        }
-        const int jj = j - pre[lo];
-        const int v = lst[lo];          // non-empty, hence a valid id
-        g = gst[v] + jj;
-        nv = min(8, off[v + 1] - off[v] - 8 * jj);
-      }
-      tgrp[t % 3][tid] = g;
-      tval[t % 3][tid] = nv;
-    }
-  };
+// ---------------------------------------------------------------------------------------
+// bf16 path, step 3: attention over the planned tiles.  One workgroup (4 waves) per
+// (query block, head); wave w = 2 kw + qw owns queries 32 qw .. 32 qw + 31 of the block and
+// keys 32 kw .. 32 kw + 31 of every 64-key tile, with its own online-softmax state (the two
+// key halves are merged at the end).  Tiles are copied global -> LDS by the LDS DMA path
+// (global_load_lds_dwordx4), double-buffered: the copy of tile t+1 runs under the MFMA
+// work of tile t.  LDS holds K group-major and row-major with an XOR swizzle of the
+// 16-byte chunks (conflict-free A reads), and V^T group-major exactly as packed.
+//   S^T = K Q^T  (A: K rows in sigma16 order, B: Q^T fragments in registers; the MFMA
+//                 accumulator starts at 0 / -inf so padding keys are masked for free)
+//   O^T += V^T P^T  (A: V^T from LDS, B: P^T straight from the S^T accumulators)
+// Row swap inside each 16-row chunk (rows 4..7 <-> 8..11): with it, the 8 rows of S^T that
+// an MFMA lane holds for one 16-key chunk are 8 consecutive keys, so the matching V^T
+// operand is one 16-byte read.
+__device__ __forceinline__ int sigma16(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 
-  bf16x8 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int t) {
-    const int sl = t % 3;
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* gbl_vptr;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_wave_base, 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
+                                                      const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
+                                                      const int32_t* __restrict__ tbase, int N, int NQ, int Gcap,
+                                                      float scale2, bf16* __restrict__ O, float* __restrict__ lse) {
+  constexpr int NS = D / 8;        // 16-byte chunks per K row
+  constexpr int GE = 8 * D;        // bf16 elements per group (K or V)
+  constexpr int CPG = GE / 8 / 64; // DMA instructions (64 lanes x 16 B) per group
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 64 * D + 2 * 64 * D];
+  __shared__ __attribute__((aligned(16))) float btab[9][8];
+  bf16* Ks = smem;                 // [2][64 rows][D], chunk c of row R at (c ^ (R % NS))
+  bf16* Vt = smem + 2 * 64 * D;    // [2][8 groups][D][8]
+
+  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lb / NQ, u = lb % NQ;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = w & 1, kw = w >> 1;
+  const int row = bh * NQ + u;
+  const int t0 = tbase[row];
+  const int nt = tbase[row + 1] - t0;
+  const int32_t* pl = plan + (size_t)t0 * 8;
+  const bf16* Kph = Kp + (size_t)bh * (Gcap + 1) * GE;
+  const bf16* Vph = Vp + (size_t)bh * (Gcap + 1) * GE;
+
+  if (tid < 72) btab[tid >> 3][tid & 7] = (tid & 7) < (tid >> 3) ? 0.0f : -INFINITY;
+
+  // copy tile t into buffer b: wave w moves groups 2w and 2w+1 (K and V)
+  auto issue = [&](int t, int b) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int e = tid + 256 * c;          // 0 .. 64*NS-1
-      const int gi = e / (8 * NS);          // group within the tile
-      const int g = tgrp[sl][gi];
-      if (g >= 0) {
-        kreg[c] = load_bf16x8(Kph + (size_t)g * 8 * D + (e % (8 * NS)) * 8);
-      } else {
+    for (int j = 0; j < 2; ++j) {
+      const int gi = 2 * w + j;
+      const int g = pl[8 * t + gi] >> 4;
+      const bf16* ksrc = Kph + (size_t)g * GE;
+      const bf16* vsrc = Vph + (size_t)g * GE;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kreg[c][i] = (bf16)0.0f;
+      for (int c = 0; c < CPG; ++c) {
+        const int pc = 64 * c + lane;            // physical chunk within the group
+        const int r = pc / NS, R = 8 * gi + r;   // row within group / tile
+        const int seg = (pc % NS) ^ (R % NS);    // logical chunk stored there
+        dma16(ksrc + r * D + seg * 8, Ks + (size_t)b * 64 * D + (size_t)gi * GE + c * 512);
+        dma16(vsrc + pc * 8, Vt + (size_t)b * 64 * D + (size_t)gi * GE + c * 512);
       }
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int e = tid + 256 * c;          // 0 .. 8*D-1
-      const int gi = e / D, d = e % D;
-      const int g = tgrp[sl][gi];
-      if (g >= 0) {
-        vreg[c] = load_bf16x8(Vph + (size_t)g * 8 * D + (size_t)d * 8);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vreg[c][i] = (bf16)0.0f;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int e = tid + 256 * c;
-      const int r = e / NS, sg = e % NS;    // key slot (group-major) and segment
-      *reinterpret_cast<bf16x8*>(&Ks[buf][r * KP + sg * 8]) = kreg[c];
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int e = tid + 256 * c;
-      const int gi = e / D, d = e % D;
-      *reinterpret_cast<bf16x8*>(&Vt[buf][d * VP + 8 * gi]) = vreg[c];
     }
   };
 
@@ -296,42 +321,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
   constexpr float kNoMax = -1e30f;
   float m = kNoMax, lsum = 0.0f;
 
-  if (ntiles > 0) {
-    tile_info(0);
-    if (ntiles > 1) tile_info(1);
-    __syncthreads();
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
+  if (nt > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   const int arow = 32 * kw + 16 * (l32 >> 4) + sigma16(l32 & 15);
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    if (t + 2 < ntiles) tile_info(t + 2);
-
+  const bf16* karow = Ks + arow * D;
+  const int aswz = arow % NS;
+  for (int t = 0; t < nt; ++t) {
+    const int b = t & 1;
+    if (t + 1 < nt) issue(t + 1, b ^ 1);
+    // lane element r = 8c + i is key 32 kw + 16 c + 8 h + i: slot i of group 4 kw + 2 c + h
+    const int nv0 = pl[8 * t + 4 * kw + h] & 15, nv1 = pl[8 * t + 4 * kw + 2 + h] & 15;
     f32x16 sacc;
+    {
+      const f32x4* b0 = reinterpret_cast<const f32x4*>(&btab[nv0][0]);
+      const f32x4* b1 = reinterpret_cast<const f32x4*>(&btab[nv1][0]);
+      const f32x4 x0 = b0[0], x1 = b0[1], x2 = b1[0], x3 = b1[1];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+      for (int i = 0; i < 4; ++i) { sacc[i] = x0[i]; sacc[4 + i] = x1[i]; sacc[8 + i] = x2[i]; sacc[12 + i] = x3[i]; }
+    }
+    const bf16* kb = karow + (size_t)b * 64 * D;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[cur][arow * KP + kc * 16 + 8 * h]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (((2 * kc + h) ^ aswz) * 8));
       sacc = mfma32(a, qf[kc], sacc);
     }
-    // lane element r = 8c + i is key 32 kw + 16 c + 8 h + i, i.e. slot i of group 4 kw + 2 c + h
-    const int nv0 = tval[t % 3][4 * kw + h], nv1 = tval[t % 3][4 * kw + 2 + h];
-    float mx = -INFINITY;
+    float mx = sacc[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int nv = r < 8 ? nv0 : nv1;
-      const float x = (r & 7) < nv ? sacc[r] * scale2 : -INFINITY;
-      sacc[r] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
     // rescale only when the running maximum grows by more than 2^8
-    const bool grow = mx > m + 8.0f;
-    if (__any(grow)) {
+    if (__any(mx > m + 8.0f)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = fast_exp2(m - mnew);
       lsum *= alpha;
@@ -344,28 +364,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
     float ps = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(sacc[r] - m);
+      const float p = fast_exp2(fmaf(sacc[r], scale2, -m));
       sacc[r] = p;
       ps += p;
     }
     lsum += ps;
+    const bf16* vb = Vt + (size_t)b * 64 * D;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = (bf16)sacc[8 * c + i];
+      const bf16* vg = vb + (size_t)(4 * kw + 2 * c + h) * GE;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[cur][(32 * dt + l32) * VP + 32 * kw + 16 * c + 8 * h]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vg + (32 * dt + l32) * 8);
         oacc[dt] = mfma32(a, pb, oacc[dt]);
       }
     }
-    if (t + 1 < ntiles) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // merge the two key halves: waves kw = 1 hand (m, l, O^T) to waves kw = 0 through LDS
-  float* xch = reinterpret_cast<float*>(&Ks[0][0]);  // 2 waves x 64 lanes x (2 + D/2) floats
+  float* xch = reinterpret_cast<float*>(smem);  // 2 waves x 64 lanes x (2 + D/2) floats
   constexpr int XS = 2 + D / 2;
   if (kw == 1) {
     float* x = xch + ((size_t)qw * 64 + lane) * XS;
@@ -476,11 +498,35 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q, c
 }
 
 static inline int group_cap(const Shape& s) { return (s.N + 7) / 8 + s.nk; }
+// most 64-key tiles one query block can need (every cluster selected)
+static inline int max_tiles_per_block(const Shape& s) { return (group_cap(s) + 7) / 8; }
+
+struct AttnWs {
+  int32_t *gstart, *ntiles, *tbase, *plan;
+  bf16 *Kp, *Vp;
+};
+
+static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
+  const int rows = s.BH * n_qblocks(s.N);
+  const size_t kv = (size_t)s.BH * (group_cap(s) + 1) * 8 * s.d * sizeof(bf16);
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  AttnWs w;
+  w.gstart = reinterpret_cast<int32_t*>(take((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)));
+  w.ntiles = reinterpret_cast<int32_t*>(take((size_t)rows * sizeof(int32_t)));
+  w.tbase = reinterpret_cast<int32_t*>(take((size_t)(rows + 1) * sizeof(int32_t)));
+  w.plan = reinterpret_cast<int32_t*>(take((size_t)rows * max_tiles_per_block(s) * 8 * sizeof(int32_t)));
+  w.Kp = reinterpret_cast<bf16*>(take(kv));
+  w.Vp = reinterpret_cast<bf16*>(take(kv));
+  if (total) *total = (size_t)(p - static_cast<char*>(base));
+  return w;
+}
 
 size_t attn_workspace(const Shape& s) {
   if (s.dtype != 1) return 0;
-  const size_t kv = (size_t)s.BH * group_cap(s) * 8 * s.d * sizeof(bf16);
-  return align256((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)) + 2 * align256(kv);
+  size_t total = 0;
+  carve_attn(s, nullptr, &total);
+  return total;
 }
 
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
@@ -490,29 +536,32 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
   const float scale2 = scale * kLog2e;
   if (s.dtype == 1) {
     const int Gcap = group_cap(s);
-    char* p = static_cast<char*>(ws);
-    int32_t* gstart = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)s.BH * (s.nk + 1) * sizeof(int32_t));
-    bf16* Kp = reinterpret_cast<bf16*>(p);
-    p += align256((size_t)s.BH * Gcap * 8 * s.d * sizeof(bf16));
-    bf16* Vp = reinterpret_cast<bf16*>(p);
+    const int rows = s.BH * NQ;
+    AttnWs w = carve_attn(s, ws, nullptr);
     auto k = reinterpret_cast<const bf16*>(K);
     auto v = reinterpret_cast<const bf16*>(V);
-    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, gstart);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+#define PARK_CHECK() do { e = hipGetLastError(); if (e != hipSuccess) return e; } while (0)
+    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, w.gstart);
+    PARK_CHECK();
     dim3 pgrid(s.nk, s.BH);
-    if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, gstart, s.N, s.nk, Gcap, Kp, Vp);
-    else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, gstart, s.N, s.nk, Gcap, Kp, Vp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(NQ * s.BH));
+    if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
+    else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
+    PARK_CHECK();
+    k_plan_count<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, s.nk, NQ, rows, w.ntiles);
+    PARK_CHECK();
+    k_plan_scan<<<1, 1024, 0, st>>>(w.ntiles, rows, w.tbase);
+    PARK_CHECK();
+    k_plan_fill<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.gstart, s.nk, NQ, rows, Gcap, w.tbase, w.plan);
+    PARK_CHECK();
+#undef PARK_CHECK
+    dim3 grid((unsigned)rows);
     auto q = reinterpret_cast<const bf16*>(Q);
     auto o = reinterpret_cast<bf16*>(O);
     if (s.d == 128)
-      k_attn_bf16<128><<<grid, 256, 0, st>>>(q, Kp, Vp, gstart, offsets, list, count, s.N, s.nk, NQ, Gcap, scale2, o, lse);
+      k_attn_bf16<128><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
     else
-      k_attn_bf16<64><<<grid, 256, 0, st>>>(q, Kp, Vp, gstart, offsets, list, count, s.N, s.nk, NQ, Gcap, scale2, o, lse);
+      k_attn_bf16<64><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
   } else {
     dim3 grid(NQ, s.BH);
     auto q = reinterpret_cast<const float*>(Q);
