@@ -263,13 +263,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
   constexpr int NS = D / 8;        // 16-byte chunks per K row
   constexpr int GE = 8 * D;        // bf16 elements per group (K or V)
   constexpr int CPG = GE / 8 / 64; // DMA instructions (64 lanes x 16 B) per group
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 64 * D + 2 * 64 * D];
+  // Four distinct LDS objects, so the compiler can tell the tile being computed from the one
+  // the DMA is filling and does not wait for the copy before reading.
+  __shared__ __attribute__((aligned(16))) bf16 K0[64 * D];   // rows, chunk c of row R at (c ^ (R % NS))
+  __shared__ __attribute__((aligned(16))) bf16 K1[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16 V0[64 * D];   // [8 groups][D][8]
+  __shared__ __attribute__((aligned(16))) bf16 V1[64 * D];
   __shared__ __attribute__((aligned(16))) float btab[9][8];
-  bf16* Ks = smem;                 // [2][64 rows][D], chunk c of row R at (c ^ (R % NS))
-  bf16* Vt = smem + 2 * 64 * D;    // [2][8 groups][D][8]
 
-  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lb / NQ, u = lb % NQ;
+  int bh, u;
+  if (!xcd_head_sync(blockIdx.x, NQ, &bh, &u)) return;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qw = w & 1, kw = w >> 1;
@@ -282,8 +285,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
 
   if (tid < 72) btab[tid >> 3][tid & 7] = (tid & 7) < (tid >> 3) ? 0.0f : -INFINITY;
 
-  // copy tile t into buffer b: wave w moves groups 2w and 2w+1 (K and V)
-  auto issue = [&](int t, int b) {
+  // copy tile t into (Kb, Vb): wave w moves groups 2w and 2w+1 (K and V)
+  auto issue = [&](int t, bf16* Kb, bf16* Vb) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int gi = 2 * w + j;
@@ -295,8 +298,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
         const int pc = 64 * c + lane;            // physical chunk within the group
         const int r = pc / NS, R = 8 * gi + r;   // row within group / tile
         const int seg = (pc % NS) ^ (R % NS);    // logical chunk stored there
-        dma16(ksrc + r * D + seg * 8, Ks + (size_t)b * 64 * D + (size_t)gi * GE + c * 512);
-        dma16(vsrc + pc * 8, Vt + (size_t)b * 64 * D + (size_t)gi * GE + c * 512);
+        dma16(ksrc + r * D + seg * 8, Kb + (size_t)gi * GE + c * 512);
+        dma16(vsrc + pc * 8, Vb + (size_t)gi * GE + c * 512);
       }
     }
   };
@@ -320,18 +323,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
   constexpr float kNoMax = -1e30f;
   float m = kNoMax, lsum = 0.0f;
-
-  if (nt > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const int arow = 32 * kw + 16 * (l32 >> 4) + sigma16(l32 & 15);
-  const bf16* karow = Ks + arow * D;
   const int aswz = arow % NS;
-  for (int t = 0; t < nt; ++t) {
-    const int b = t & 1;
-    if (t + 1 < nt) issue(t + 1, b ^ 1);
+
+  auto compute = [&](int t, const bf16* Kb, const bf16* Vb) {
+    // plan entries through the scalar path (wave-uniform addresses)
+    const int* pt = pl + __builtin_amdgcn_readfirstlane(8 * t + 4 * kw);
+    const int e0 = pt[0], e1 = pt[1], e2 = pt[2], e3 = pt[3];
     // lane element r = 8c + i is key 32 kw + 16 c + 8 h + i: slot i of group 4 kw + 2 c + h
-    const int nv0 = pl[8 * t + 4 * kw + h] & 15, nv1 = pl[8 * t + 4 * kw + 2 + h] & 15;
+    const int nv0 = (h ? e1 : e0) & 15, nv1 = (h ? e3 : e2) & 15;
     f32x16 sacc;
     {
       const f32x4* b0 = reinterpret_cast<const f32x4*>(&btab[nv0][0]);
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
 #pragma unroll
       for (int i = 0; i < 4; ++i) { sacc[i] = x0[i]; sacc[4 + i] = x1[i]; sacc[8 + i] = x2[i]; sacc[12 + i] = x3[i]; }
     }
-    const bf16* kb = karow + (size_t)b * 64 * D;
+    const bf16* kb = Kb + arow * D;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (((2 * kc + h) ^ aswz) * 8));
@@ -369,39 +369,53 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
       ps += p;
     }
     lsum += ps;
-    const bf16* vb = Vt + (size_t)b * 64 * D;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = (bf16)sacc[8 * c + i];
-      const bf16* vg = vb + (size_t)(4 * kw + 2 * c + h) * GE;
+      const bf16* vg = Vb + (size_t)(4 * kw + 2 * c + h) * GE;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(vg + (32 * dt + l32) * 8);
         oacc[dt] = mfma32(a, pb, oacc[dt]);
       }
     }
+  };
+
+  if (nt > 0) issue(0, K0, V0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < nt; t += 2) {
+    if (t + 1 < nt) issue(t + 1, K1, V1);
+    compute(t, K0, V0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 >= nt) break;
+    if (t + 2 < nt) issue(t + 2, K0, V0);
+    compute(t + 1, K1, V1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // merge the two key halves: waves kw = 1 hand (m, l, O^T) to waves kw = 0 through LDS
-  float* xch = reinterpret_cast<float*>(smem);  // 2 waves x 64 lanes x (2 + D/2) floats
-  constexpr int XS = 2 + D / 2;
+  float* xo = reinterpret_cast<float*>(K0);  // K0 and K1 hold 2 waves x 64 lanes x D/2 floats
+  float* xm = reinterpret_cast<float*>(V0);  // 2 waves x 64 lanes x (m, l)
+  auto xo_at = [&](int qq, int ln, int k) -> float* {  // lane-contiguous: no bank conflicts
+    const int idx = k * 128 + qq * 64 + ln;
+    return idx < 32 * D ? xo + idx : reinterpret_cast<float*>(K1) + (idx - 32 * D);
+  };
   if (kw == 1) {
-    float* x = xch + ((size_t)qw * 64 + lane) * XS;
-    x[0] = m;
-    x[1] = lsum;
+    xm[(qw * 64 + lane) * 2] = m;
+    xm[(qw * 64 + lane) * 2 + 1] = lsum;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[2 + 16 * dt + r] = oacc[dt][r];
+      for (int r = 0; r < 16; ++r) *xo_at(qw, lane, 16 * dt + r) = oacc[dt][r];
   }
   __syncthreads();
   if (kw == 0) {
-    const float* x = xch + ((size_t)qw * 64 + lane) * XS;
-    const float m1 = x[0], l1 = x[1];
+    const float m1 = xm[(qw * 64 + lane) * 2], l1 = xm[(qw * 64 + lane) * 2 + 1];
     const float mt = fmaxf(m, m1);
     const float a0 = fast_exp2(m - mt), a1 = fast_exp2(m1 - mt);
     float l = lsum * a0 + l1 * a1;
@@ -417,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
-            o[i] = (bf16)((oacc[dt][r] * a0 + x[2 + 16 * dt + r] * a1) * inv);
+            o[i] = (bf16)((oacc[dt][r] * a0 + *xo_at(qw, lane, 16 * dt + r) * a1) * inv);
           }
           *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
@@ -555,7 +569,7 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     k_plan_fill<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.gstart, s.nk, NQ, rows, Gcap, w.tbase, w.plan);
     PARK_CHECK();
 #undef PARK_CHECK
-    dim3 grid((unsigned)rows);
+    dim3 grid((unsigned)(s.BH * 8 * ((NQ + 7) / 8)));
     auto q = reinterpret_cast<const bf16*>(Q);
     auto o = reinterpret_cast<bf16*>(O);
     if (s.d == 128)

@@ -5,12 +5,15 @@
 //   counts and original-space centroids.
 #include "park_device.h"
 #include "park_internal.h"
+#include "../../include/park.h"
 
 namespace park {
 
+typedef __attribute__((address_space(3))) void* lds_vptr_c;
+typedef __attribute__((address_space(1))) void* gbl_vptr_c;
+
 constexpr int kGramChunk = 4096;   // tokens per Gram partial
 constexpr int kSortChunk = 256;    // keys per counting-sort chunk
-constexpr int kCandPerKey = 16;    // screened candidates kept per key before the slow path
 constexpr double kEps = 1e-6;      // Cholesky stability term (times s_Q)
 constexpr double kSMin = 1e-6;     // floor of s_Q
 
@@ -24,6 +27,9 @@ struct ClusterWs {
   float* ctil;    // [BH][nkp][D] centroids in the transformed space
   bf16* gneg2;    // [BH][nkp][D] bf16(-2 R c~)
   float4* cinfo;  // [BH][nkp] (|c~|^2, |R c~|, |R c~ - bf16(R c~)|, 0)
+  float* ccv;     // [BH][nkp] |c~|^2 (+inf for padding rows)
+  double* cmean;  // [BH][nkp][D] original-space member means
+  uint32_t* hmax; // [BH][4] float bits of max |R c~|, max bf16 error of R c~, max |c~|^2
   int32_t* hist;  // [BH][nch_s][nk] counting-sort histograms, then bases
   int nch_g, nch_s, nkp;
 };
@@ -45,6 +51,9 @@ static ClusterWs carve(const Shape& s, void* base) {
   w.ctil = reinterpret_cast<float*>(take(BH * w.nkp * D * sizeof(float)));
   w.gneg2 = reinterpret_cast<bf16*>(take(BH * w.nkp * D * sizeof(bf16)));
   w.cinfo = reinterpret_cast<float4*>(take(BH * w.nkp * sizeof(float4)));
+  w.ccv = reinterpret_cast<float*>(take(BH * w.nkp * sizeof(float)));
+  w.cmean = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
+  w.hmax = reinterpret_cast<uint32_t*>(take(BH * 4 * sizeof(uint32_t)));
   w.hist = reinterpret_cast<int32_t*>(take(BH * (size_t)w.nch_s * s.nk * sizeof(int32_t)));
   if (base == nullptr) w.gpart = reinterpret_cast<double*>(p);  // total size in the pointer
   return w;
@@ -296,24 +305,30 @@ __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ K, cons
 // Centroid preparation (D threads): from c~_v (float, in LDS) compute g = R c~ in double,
 // gneg2 = bf16(-2 g), |c~|^2, |g| and |g - bf16(g)|.  Pad rows (v >= nk) get cc = +inf.
 template <int D>
-__device__ void centroid_prep(int bh, int v, int nk, int nkp, const float* cs, const double* __restrict__ Rt64,
-                              bf16* __restrict__ gneg2, float4* __restrict__ cinfo, double* red) {
+__device__ void centroid_prep(int bh, int v, int nkp, const float* cs, const double* __restrict__ Rt64,
+                              bf16* __restrict__ gneg2, float4* __restrict__ cinfo, float* __restrict__ ccv,
+                              double* red) {
   const int i = threadIdx.x;
-  const double* Rt = Rt64 + (size_t)bh * D * D;
-  double g = 0.0;
-  for (int k = 0; k < D; ++k) g += Rt[(size_t)k * D + i] * (double)cs[k];
-  const bf16 gb = (bf16)(float)g;
-  gneg2[((size_t)bh * nkp + v) * D + i] = (bf16)(-2.0f * (float)gb);
-  const double df = g - (double)(float)gb;
-  double cc = (double)cs[i] * cs[i], gn = g * g, f = df * df;
-  cc = sum64d(cc); gn = sum64d(gn); f = sum64d(f);
-  const int w = i >> 6;
-  if ((i & 63) == 0) { red[3 * w] = cc; red[3 * w + 1] = gn; red[3 * w + 2] = f; }
+  if (i < D) {
+    const double* Rt = Rt64 + (size_t)bh * D * D;
+    double g = 0.0;
+    for (int k = 0; k < D; ++k) g += Rt[(size_t)k * D + i] * (double)cs[k];
+    const bf16 gb = (bf16)(float)g;
+    gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)gb);
+    const double df = g - (double)(float)gb;
+    double cc = (double)cs[i] * cs[i], gn = g * g, f = df * df;
+    cc = sum64d(cc); gn = sum64d(gn); f = sum64d(f);
+    const int w = i >> 6;
+    if ((i & 63) == 0) { red[3 * w] = cc; red[3 * w + 1] = gn; red[3 * w + 2] = f; }
+  }
   __syncthreads();
   if (i == 0) {
+    double cc = red[0], gn = red[1], f = red[2];
     for (int k = 1; k < D / 64; ++k) { cc += red[3 * k]; gn += red[3 * k + 1]; f += red[3 * k + 2]; }
     const float up = 1.0f + 1.0f / 1048576.0f;
-    cinfo[(size_t)bh * nkp + v] = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
+    const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
+    cinfo[(size_t)bh * nkp + v] = ci;
+    ccv[(size_t)bh * nkp + v] = ci.x;
   }
   __syncthreads();
 }
@@ -323,14 +338,17 @@ template <int D>
 __global__ __launch_bounds__(D) void k_km_init(const float* __restrict__ Kt, const int32_t* __restrict__ init_idx,
                                                int N, int nk, int nkp, const double* __restrict__ Rt64,
                                                float* __restrict__ ctil, bf16* __restrict__ gneg2,
-                                               float4* __restrict__ cinfo) {
+                                               float4* __restrict__ cinfo, float* __restrict__ ccv) {
   __shared__ float cs[D];
   __shared__ double red[6];
   const int v = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
-  if (v >= nk) {  // padding rows
+  if (v >= nk) {  // padding rows: never the nearest centroid
     ctil[((size_t)bh * nkp + v) * D + i] = 0.0f;
-    gneg2[((size_t)bh * nkp + v) * D + i] = (bf16)0.0f;
-    if (i == 0) cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
+    gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
+    if (i == 0) {
+      cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
+      ccv[(size_t)bh * nkp + v] = INFINITY;
+    }
     return;
   }
   long j = init_idx ? (long)init_idx[v] : (long)(((long long)v * N) / nk);
@@ -339,170 +357,285 @@ __global__ __launch_bounds__(D) void k_km_init(const float* __restrict__ Kt, con
   cs[i] = x;
   ctil[((size_t)bh * nkp + v) * D + i] = x;
   __syncthreads();
-  centroid_prep<D>(bh, v, nk, nkp, cs, Rt64, gneg2, cinfo, red);
+  centroid_prep<D>(bh, v, nkp, cs, Rt64, gneg2, cinfo, ccv, red);
+}
+
+// Per-head maxima of |R c~|, its bf16 error and |c~|^2 over all clusters (empty ones
+// included: they keep their centroid and stay candidates), read by the next assignment.
+__global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ cinfo, int nk, int nkp,
+                                                   uint32_t* __restrict__ hmax) {
+  __shared__ float red[3][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, bh = blockIdx.x;
+  float g = 0.0f, f = 0.0f, cc = 0.0f;
+  for (int v = tid; v < nk; v += 256) {
+    const float4 c = cinfo[(size_t)bh * nkp + v];
+    cc = fmaxf(cc, c.x); g = fmaxf(g, c.y); f = fmaxf(f, c.z);
+  }
+  g = max64(g); f = max64(f); cc = max64(cc);
+  if (lane == 0) { red[0][w] = g; red[1][w] = f; red[2][w] = cc; }
+  __syncthreads();
+  if (tid < 3) {
+    const float m = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
+    hmax[4 * bh + tid] = __float_as_uint(tid == 2 ? m * (1.0f + 1.0f / 1048576.0f) : m);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // a5: assignment a_j = argmin_v |k~_j - c~_v|^2, ties to the lowest v.
 // Screen: score_jv = |c~_v|^2 - 2 k_j . bf16(R c~_v) on bf16 MFMA (S^T layout: rows are
 // clusters, columns keys), which equals |k~_j - c~_v|^2 - |k~_j|^2 up to a per-key bound
-//   E_j = 2 (e_j G + a_j F + e_j F) + 2^-12 (2 a_j G + CC + t_j^2)
+//   E_j = 2 (e_j G + a_j F + e_j F) + 2^-14 (2 a_j G + CC + t_j^2)
 // (a_j = |k_j|, e_j = |k_j - bf16(k_j)|, t_j = |k~_j|, G = max |R c~|, F = max bf16 error of
 // R c~, CC = max |c~|^2).  Every cluster whose score is within 2 E_j of the key's minimum is
-// a candidate; the true argmin always is one.  A single candidate is the answer; otherwise
-// the candidates are compared with exact float distances (k~ and c~ as stored), then by id.
-template <int D, int VT, bool KF32>
-__global__ __launch_bounds__(512) void k_km_assign(const void* __restrict__ Kv, const float* __restrict__ Kt,
-                                                   const float4* __restrict__ knorm, const float* __restrict__ ctil,
-                                                   const bf16* __restrict__ gneg2, const float4* __restrict__ cinfo,
-                                                   int N, int nk, int nkp, int32_t* __restrict__ labels) {
-  constexpr int KP = D + 8;
-  __shared__ bf16 Ks[64 * KP];
-  __shared__ float red[8][64];
-  __shared__ float thr[64];
-  __shared__ unsigned int bmax[3];
-  __shared__ int ccount[64];
-  __shared__ int cand[64][kCandPerKey];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.y, k0 = blockIdx.x * 64;
-  const float4* ci = cinfo + (size_t)bh * nkp;
+// a candidate; the true argmin always is one.
+// One workgroup: 4 waves x 64 keys.  The cluster operand streams through LDS in 32-cluster
+// tiles (LDS DMA, double-buffered, shared by the 4 waves); each wave keeps its keys' B
+// fragments in registers and a running minimum per key, and records every score within 2 E_j
+// of the running minimum in a small per-key list (a value that ends within 2 E_j of the final
+// minimum was within 2 E_j of the running minimum when it was seen).  A single surviving
+// candidate is the answer; otherwise the candidates are compared with exact float distances
+// (k~ and c~ as stored, summed in dimension order), then by id; a key whose list overflowed
+// compares every cluster.
+constexpr int kAsgWaves = 4;
+constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
+constexpr int kAsgCap = 16;                // list entries per key (compacted when half full)
 
-  if (tid < 3) bmax[tid] = 0u;
-  if (tid < 64) ccount[tid] = 0;
-  __syncthreads();
-  {
-    float g = 0.0f, f = 0.0f, cc = 0.0f;
-    for (int v = tid; v < nk; v += blockDim.x) {
-      const float4 c = ci[v];
-      cc = fmaxf(cc, c.x); g = fmaxf(g, c.y); f = fmaxf(f, c.z);
+template <int D, bool KF32>
+__global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ Kv, const float* __restrict__ Kt,
+                                                      const float4* __restrict__ knorm, const float* __restrict__ ctil,
+                                                      const bf16* __restrict__ gneg2, const float* __restrict__ ccv,
+                                                      const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
+                                                      int have_prev, int32_t* __restrict__ labels) {
+  constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
+  __shared__ int lcnt[kAsgKeys];
+  __shared__ int lovf[kAsgKeys];
+  __shared__ int2 lst[kAsgKeys][kAsgCap];
+  __shared__ float ths[kAsgKeys];
+  __shared__ unsigned long long best[kAsgKeys];
+  __shared__ int2 pairs[kAsgKeys * 4];
+  __shared__ int npairs;
+  __shared__ __attribute__((aligned(16))) float ccs[PARK_MAX_CLUSTERS];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, k0 = blockIdx.x * kAsgKeys;
+  const int nT = nkp >> 5;
+  const bf16* gA = gneg2 + (size_t)bh * nkp * D + (size_t)lane * 8;  // this lane's piece of fragment 0
+  for (int v = tid; v < nkp; v += kAsgKeys) ccs[v] = ccv[(size_t)bh * nkp + v];
+  lcnt[tid] = 0;
+  lovf[tid] = 0;
+  best[tid] = ~0ull;
+  if (tid == 0) npairs = 0;
+
+  // B fragments of this wave's 64 keys (two 32-key tiles)
+  bf16x8 bfr[2][NF];
+  float E[2];
+  const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
+  const float CC = __uint_as_float(hmax[4 * bh + 2]);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = k0 + 64 * w + 32 * kt + l32;
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) {
+      if (key < N) {
+        const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
+        if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
+        else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = (bf16)0.0f;
+      }
     }
-    g = max64(g); f = max64(f); cc = max64(cc);
-    if (lane == 0) {
-      atomicMax(&bmax[0], __float_as_uint(g));
-      atomicMax(&bmax[1], __float_as_uint(f));
-      atomicMax(&bmax[2], __float_as_uint(cc));
+    E[kt] = 0.0f;
+    if (key < N) {
+      const float4 kn = knorm[(size_t)bh * N + key];
+      // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
+      // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
+      E[kt] = 2.0f * (kn.y * G + kn.x * F + kn.y * F) + (1.0f / 16384.0f) * (2.0f * kn.x * G + CC + kn.z * kn.z);
+      E[kt] *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
     }
   }
-  for (int e = tid; e < 64 * (D / 8); e += blockDim.x) {
-    const int r = e / (D / 8), sg = e % (D / 8);
-    bf16x8 val;
-    if (k0 + r < N) {
-      const size_t off = ((size_t)bh * N + k0 + r) * D + sg * 8;
-      if constexpr (KF32) val = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
-      else val = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
-    } else {
+  // Running minimum.  From the second step on it starts at the screen score of the key's
+  // previous cluster (plus half the window, which covers the different summation order), an
+  // upper bound of the final minimum: far fewer scores then fall inside the window.
+  float mr[2] = {INFINITY, INFINITY};
+  if (have_prev) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) val[i] = (bf16)0.0f;
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = k0 + 64 * w + 32 * kt + l32;
+      if (key < N) {
+        const int vp = labels[(size_t)bh * N + key];
+        float dot = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < NF; ++kc) {
+          const bf16x8 g = load_bf16x8(gneg2 + (size_t)bh * nkp * D + frag_offset(vp, 16 * kc + 8 * h, D));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = fmaf((float)bfr[kt][kc][i], (float)g[i], dot);
+        }
+        dot += __shfl_xor(dot, 32);
+        mr[kt] = ccv[(size_t)bh * nkp + vp] + dot + 0.5f * E[kt];
+      } else {
+        mr[kt] = INFINITY;
+      }
     }
-    *reinterpret_cast<bf16x8*>(&Ks[r * KP + sg * 8]) = val;
   }
   __syncthreads();
 
-  const int v0 = w * VT * 32;
-  f32x16 acc[2][VT];
+  // stream the 32-cluster tiles straight from memory (fragment-major: 1 KB per fragment),
+  // two tiles of A fragments in flight ahead of the MFMA work
+  bf16x8 an[NF], an2[NF];
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt) {
+  for (int kc = 0; kc < NF; ++kc) an[kc] = load_bf16x8(gA + (size_t)kc * 512);
+  if (nT > 1) {
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) an2[kc] = load_bf16x8(gA + ((size_t)NF + kc) * 512);
+  }
+  for (int t = 0; t < nT; ++t) {
+    bf16x8 a[NF];
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) { a[kc] = an[kc]; an[kc] = an2[kc]; }
+    if (t + 2 < nT) {
+#pragma unroll
+      for (int kc = 0; kc < NF; ++kc) an2[kc] = load_bf16x8(gA + ((size_t)(t + 2) * NF + kc) * 512);
+    }
     float init[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = v0 + 32 * vt + c_row(r, lane);
-      init[r] = v < nkp ? ci[v].x : INFINITY;
+    for (int g = 0; g < 4; ++g) {  // rows 8g + 4h + 0..3 of the tile
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&ccs[32 * t + 8 * g + 4 * h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) init[4 * g + i] = c[i];
+    }
+    f32x16 acc[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { acc[0][r] = init[r]; acc[1][r] = init[r]; }
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) {
+      acc[0] = mfma32(a[kc], bfr[0][kc], acc[0]);
+      acc[1] = mfma32(a[kc], bfr[1][kc], acc[1]);
     }
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int kt = 0; kt < 2; ++kt) {
+      float tm = acc[kt][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = init[r];
-  }
-#pragma unroll 2
-  for (int kc = 0; kc < D / 16; ++kc) {
-    const int col = 16 * kc + 8 * h;
-    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&Ks[l32 * KP + col]);
-    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&Ks[(32 + l32) * KP + col]);
+      for (int r = 1; r < 16; ++r) tm = fminf(tm, acc[kt][r]);
+      tm = fminf(tm, __shfl_xor(tm, 32));
+      mr[kt] = fminf(mr[kt], tm);
+      const float th = mr[kt] + E[kt];
+      if (__any(tm <= th)) {
+        const int slot = 64 * w + 32 * kt + l32;
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-      if (v0 + 32 * vt < nkp) {
-        const bf16x8 a = load_bf16x8(gneg2 + ((size_t)bh * nkp + v0 + 32 * vt + l32) * D + col);
-        acc[0][vt] = mfma32(a, b0, acc[0][vt]);
-        acc[1][vt] = mfma32(a, b1, acc[1][vt]);
-      }
-    }
-  }
-  // per-key minimum over this wave's clusters, then over the waves
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float mn = INFINITY;
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mn = fminf(mn, acc[qt][vt][r]);
-    mn = fminf(mn, __shfl_xor(mn, 32));
-    if (h == 0) red[w][32 * qt + l32] = mn;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float mn = INFINITY;
-    for (int i = 0; i < nw; ++i) mn = fminf(mn, red[i][tid]);
-    const float G = __uint_as_float(bmax[0]), F = __uint_as_float(bmax[1]), CC = __uint_as_float(bmax[2]);
-    float E = 0.0f;
-    if (k0 + tid < N) {
-      const float4 kn = knorm[(size_t)bh * N + k0 + tid];
-      E = 2.0f * (kn.y * G + kn.x * F + kn.y * F) +
-          (1.0f / 4096.0f) * (2.0f * kn.x * G + CC + kn.z * kn.z);
-    }
-    thr[tid] = mn + 2.0f * E * (1.0f + 1.0f / 65536.0f);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int kl = 32 * qt + l32;
-    const float t = thr[kl];
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v0 + 32 * vt + c_row(r, lane);
-        if (acc[qt][vt][r] <= t && v < nk) {
-          const int c = atomicAdd(&ccount[kl], 1);
-          if (c < kCandPerKey) cand[kl][c] = v;
+        for (int r = 0; r < 16; ++r) {
+          const int v = 32 * t + c_row(r, lane);
+          if (acc[kt][r] <= th && v < nk) {
+            const int c = atomicAdd(&lcnt[slot], 1);
+            if (c < kAsgCap) lst[slot][c] = make_int2(v, __float_as_int(acc[kt][r]));
+            else lovf[slot] = 1;
+          }
+        }
+        // the window only shrinks: drop entries that left it once a list is half full
+        if (__any(lcnt[slot] > kAsgCap / 2)) {
+          if (h == 0 && lcnt[slot] > kAsgCap / 2) {
+            const int n = min(lcnt[slot], kAsgCap);
+            int m = 0;
+            for (int c = 0; c < n; ++c) {
+              const int2 e = lst[slot][c];
+              if (__int_as_float(e.y) <= th) lst[slot][m++] = e;
+            }
+            lcnt[slot] = m;
+          }
         }
       }
+    }
+  }
+  if (h == 0) {
+    ths[64 * w + l32] = mr[0] + E[0];
+    ths[64 * w + 32 + l32] = mr[1] + E[1];
   }
   __syncthreads();
-  // refine: one wave per key, exact float distance, (distance, id) minimum
-  for (int kl = w; kl < 64; kl += nw) {
-    const int j = k0 + kl;
-    if (j >= N) break;
-    const int n = ccount[kl];
-    int best;
-    if (n == 1) {
-      best = cand[kl][0];
-    } else {
-      const float* x = Kt + ((size_t)bh * N + j) * D;
-      float xv[D / 64];
+  // survivors per key: list entries within the window of the final minimum; keys with two
+  // or more add their (key, cluster) pairs to the refine list
+  int n_surv = 0, only = 0;
+  const int j = k0 + tid;
+  {
+    const int n = min(lcnt[tid], kAsgCap);
+    const float th = ths[tid];
+    for (int c = 0; c < n; ++c) {
+      const int2 e = lst[tid][c];
+      if (__int_as_float(e.y) <= th) { ++n_surv; only = e.x; }
+    }
+    if (j < N && !lovf[tid] && n_surv >= 2) {
+      const int base = atomicAdd(&npairs, n_surv);
+      int m = 0;
+      for (int c = 0; c < n; ++c) {
+        const int2 e = lst[tid][c];
+        if (__int_as_float(e.y) <= th) {
+          if (base + m < kAsgKeys * 4) pairs[base + m] = make_int2(tid, e.x);
+          ++m;
+        }
+      }
+    }
+  }
+  // exact comparison of every cluster where the list overflowed, the pair list is full or no
+  // entry survived (only possible with non-finite data)
+  bool slow = lovf[tid] != 0 || n_surv == 0;
+  __syncthreads();
+  const int np = npairs;
+  if (np > kAsgKeys * 4 && n_surv >= 2) slow = true;
+  lovf[tid] = slow ? 1 : 0;
+  __syncthreads();
+  // refine: 4 lanes per (key, cluster) pair, exact float distance; each lane sums D/4
+  // consecutive dimensions in order and the 4 partial sums are added in a fixed tree
+  const int npl = min(np, kAsgKeys * 4);
+  for (int p0 = 0; p0 < npl; p0 += kAsgKeys / 4) {
+    const int p = p0 + tid / 4, q = tid & 3;
+    float s = 0.0f;
+    int2 pr = make_int2(0, 0);
+    if (p < npl) {
+      pr = pairs[p];
+      const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + k0 + pr.x) * D + q * (D / 4));
+      const f32x4* y = reinterpret_cast<const f32x4*>(ctil + ((size_t)bh * nkp + pr.y) * D + q * (D / 4));
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) xv[i] = x[lane + 64 * i];
-      // no candidate (only with non-finite data) or too many: compare every cluster
-      const bool listed = n >= 1 && n <= kCandPerKey;
-      const int nc = listed ? n : nk;
-      uint64_t bk = ~0ull;
-      for (int c = 0; c < nc; ++c) {
-        const int v = listed ? cand[kl][c] : c;
-        const float* y = ctil + ((size_t)bh * nkp + v) * D;
-        float s = 0.0f;
+      for (int i = 0; i < D / 16; ++i) {
+        const f32x4 a = x[i], b = y[i];
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) {
-          const float dd = xv[i] - y[lane + 64 * i];
+        for (int z = 0; z < 4; ++z) {
+          const float dd = a[z] - b[z];
           s = fmaf(dd, dd, s);
         }
-        s = sum64(s);
-        const uint64_t k = ((uint64_t)__float_as_uint(s) << 32) | (uint32_t)v;
-        bk = k < bk ? k : bk;
       }
-      best = (int)(uint32_t)bk;
     }
-    if (lane == 0) labels[(size_t)bh * N + j] = best;
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (p < npl && q == 0 && !lovf[pr.x])
+      atomicMin(&best[pr.x], ((unsigned long long)__float_as_uint(s) << 32) | (uint32_t)pr.y);
   }
+  for (int kl = w; kl < kAsgKeys; kl += kAsgWaves) {
+    if (k0 + kl >= N) break;
+    if (!lovf[kl]) continue;
+    const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + k0 + kl) * D);
+    unsigned long long bk = ~0ull;
+    for (int v = lane; v < nk; v += 64) {
+      const f32x4* y = reinterpret_cast<const f32x4*>(ctil + ((size_t)bh * nkp + v) * D);
+      float s = 0.0f;
+      for (int i = 0; i < D / 4; ++i) {
+        const f32x4 a = x[i], b = y[i];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const float dd = a[z] - b[z];
+          s = fmaf(dd, dd, s);
+        }
+      }
+      const unsigned long long k = ((unsigned long long)__float_as_uint(s) << 32) | (uint32_t)v;
+      bk = k < bk ? k : bk;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long t = __shfl_xor(bk, o);
+      bk = t < bk ? t : bk;
+    }
+    if (lane == 0) best[kl] = bk;
+  }
+  __syncthreads();
+  if (j < N) labels[(size_t)bh * N + j] = (!slow && n_surv == 1) ? only : (int)(uint32_t)best[tid];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -594,64 +727,152 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// a6/a7: per-cluster update.  The members (a contiguous run of perm) are summed in double in
-// key order; the original-space mean is the cluster centroid output, and c~_v = R^T mean
-// (the same value as the mean of R^T k_j).  Empty clusters keep c~ and output 0.
+// a6/a7: per-cluster update, step 1: member sums.  One 256-thread workgroup per cluster;
+// the members (a run of perm) are read 16 bytes per thread, RPI rows at a time; each thread
+// sums its dimensions in double over its rows, and the RPI partial sums are added in a
+// fixed order, so the result does not depend on scheduling.  Writes the original-space mean
+// (double) for step 2 and, on the last iteration, the float centroid output (0 if empty).
 template <int D, typename T>
-__global__ __launch_bounds__(D) void k_km_update(const T* __restrict__ K, const int32_t* __restrict__ perm,
+__global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ offsets, int N, int nk, int nkp,
-                                                 const double* __restrict__ R64, const double* __restrict__ Rt64,
-                                                 float* __restrict__ ctil, bf16* __restrict__ gneg2,
-                                                 float4* __restrict__ cinfo, float* __restrict__ cent) {
-  __shared__ double mean[D];
-  __shared__ float cs[D];
-  __shared__ double red[6];
-  const int v = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
+                                                 double* __restrict__ cmean, float* __restrict__ cent) {
+  constexpr int TPR = D / 8;         // threads per row (8 dimensions each)
+  constexpr int RPI = 256 / TPR;     // rows in flight per step
+  __shared__ double part[RPI][D];
+  const int v = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int a = offsets[(size_t)bh * (nk + 1) + v], b = offsets[(size_t)bh * (nk + 1) + v + 1];
-  const int32_t* pm = perm + (size_t)bh * N;
-  const T* Kh = K + (size_t)bh * N * D;
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  int p = a;
-  for (; p + 3 < b; p += 4) {
-    s0 += (double)to_f32(Kh[(size_t)pm[p] * D + i]);
-    s1 += (double)to_f32(Kh[(size_t)pm[p + 1] * D + i]);
-    s2 += (double)to_f32(Kh[(size_t)pm[p + 2] * D + i]);
-    s3 += (double)to_f32(Kh[(size_t)pm[p + 3] * D + i]);
-  }
-  for (; p < b; ++p) s0 += (double)to_f32(Kh[(size_t)pm[p] * D + i]);
   const int n = b - a;
-  const double m = n > 0 ? ((s0 + s1) + (s2 + s3)) / (double)n : 0.0;
-  if (cent) cent[((size_t)bh * nk + v) * D + i] = (float)m;
-  if (n == 0) return;  // block-uniform
-  mean[i] = m;
+  if (n == 0) {
+    if (cent && tid < D) cent[((size_t)bh * nk + v) * D + tid] = 0.0f;
+    return;
+  }
+  const int32_t* pm = perm + (size_t)bh * N + a;
+  const T* Kh = K + (size_t)bh * N * D;
+  const int rg = tid / TPR, c8 = (tid % TPR) * 8;
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int r = rg; r < n; r += RPI) {
+    const T* src = Kh + (size_t)pm[r] * D + c8;
+    float x[8];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 q = load_bf16x8(reinterpret_cast<const bf16*>(src));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)q[i];
+    } else {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { x[i] = q0[i]; x[4 + i] = q1[i]; }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[rg][c8 + i] = acc[i];
   __syncthreads();
-  const double* R = R64 + (size_t)bh * D * D;
-  double t = 0.0;
-  for (int k = 0; k < D; ++k) t += R[(size_t)k * D + i] * mean[k];  // (R^T m)_i
-  const float tf = (float)t;
-  cs[i] = tf;
-  ctil[((size_t)bh * nkp + v) * D + i] = tf;
+  if (tid < D) {
+    double sum = 0.0;
+    for (int g = 0; g < RPI; ++g) sum += part[g][tid];
+    const double m = sum / (double)n;
+    cmean[((size_t)bh * nkp + v) * D + tid] = m;
+    if (cent) cent[((size_t)bh * nk + v) * D + tid] = (float)m;
+  }
+}
+
+// Step 2, per (32-cluster tile, head): c~_v = R^T mean_v rounded to float, then the screen
+// operand g_v = R c~_v, gneg2 = bf16(-2 g) (fragment-major), |c~|^2, |g|, |g - bf16(g)|.
+// Clusters without keys keep everything from the previous step.  Thread (i, vh) owns
+// output dimension i of the clusters 2j + vh of the tile, so each R element read from
+// memory serves 16 clusters.
+template <int D>
+__global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
+                                                int nk, int nkp, const double* __restrict__ R64,
+                                                const double* __restrict__ Rt64, float* __restrict__ ctil,
+                                                bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
+                                                float* __restrict__ ccv) {
+  constexpr int VPT = 32 / (256 / D);  // clusters per thread
+  constexpr int NVH = 256 / D;         // thread groups over the clusters of the tile
+  __shared__ double ms[32][D + 1];
+  __shared__ float cs[32][D + 1];
+  __shared__ double red[3][32][4];
+  const int tid = threadIdx.x, lane = tid & 63, bh = blockIdx.y, v0 = blockIdx.x * 32;
+  const int i = tid % D, vh = tid / D;
+  const int wq = (tid % D) >> 6;       // wave index within the group of D threads
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int vv = e / D, k = e % D;
+    const int v = v0 + vv;
+    ms[vv][k] = v < nk ? cmean[((size_t)bh * nkp + v) * D + k] : 0.0;
+  }
   __syncthreads();
-  centroid_prep<D>(bh, v, nk, nkp, cs, Rt64, gneg2, cinfo, red);
+  bool live[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = v0 + NVH * j + vh;
+    live[j] = v < nk && counts[(size_t)bh * nk + v] > 0;
+  }
+  {
+    const double* R = R64 + (size_t)bh * D * D;
+    double t[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) t[j] = 0.0;
+    for (int k = 0; k < D; ++k) {
+      const double r = R[(size_t)k * D + i];       // R[k][i]: (R^T m)_i = sum_k R[k][i] m_k
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) t[j] += r * ms[NVH * j + vh][k];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) cs[NVH * j + vh][i] = (float)t[j];
+  }
+  __syncthreads();
+  {
+    const double* Rt = Rt64 + (size_t)bh * D * D;
+    double g[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) g[j] = 0.0;
+    for (int k = 0; k < D; ++k) {
+      const double r = Rt[(size_t)k * D + i];      // Rt[k][i] = R[i][k]: (R c~)_i
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) g[j] += r * (double)cs[NVH * j + vh][k];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int vv = NVH * j + vh, v = v0 + vv;
+      const float c = cs[vv][i];
+      const bf16 gb = (bf16)(float)g[j];
+      if (live[j]) {
+        ctil[((size_t)bh * nkp + v) * D + i] = c;
+        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)gb);
+      }
+      const double df = g[j] - (double)(float)gb;
+      double cc = (double)c * c, gn = g[j] * g[j], f = df * df;
+      cc = sum64d(cc); gn = sum64d(gn); f = sum64d(f);
+      if (lane == 0) { red[0][vv][wq] = cc; red[1][vv][wq] = gn; red[2][vv][wq] = f; }
+    }
+  }
+  __syncthreads();
+  if (tid < 32) {
+    const int v = v0 + tid;
+    if (v < nk && counts[(size_t)bh * nk + v] > 0) {
+      double cc = 0.0, gn = 0.0, f = 0.0;
+      for (int q = 0; q < D / 64; ++q) { cc += red[0][tid][q]; gn += red[1][tid][q]; f += red[2][tid][q]; }
+      const float up = 1.0f + 1.0f / 1048576.0f;
+      const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
+      cinfo[(size_t)bh * nkp + v] = ci;
+      ccv[(size_t)bh * nkp + v] = ci.x;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 template <int D>
-static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, int32_t* labels, hipStream_t st) {
-  const int vt = (w.nkp + 255) / 256;
-  const int nw = (w.nkp + 32 * vt - 1) / (32 * vt);
-  dim3 grid((s.N + 63) / 64, s.BH), block(64 * nw);
-  const bool f32 = s.dtype == 0;
-  switch (vt) {
-#define PARK_ASSIGN_CASE(V)                                                                                   \
-  case V:                                                                                                     \
-    if (f32) k_km_assign<D, V, true><<<grid, block, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.cinfo, s.N, s.nk, w.nkp, labels); \
-    else k_km_assign<D, V, false><<<grid, block, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.cinfo, s.N, s.nk, w.nkp, labels); \
-    break;
-    PARK_ASSIGN_CASE(1) PARK_ASSIGN_CASE(2) PARK_ASSIGN_CASE(3) PARK_ASSIGN_CASE(4) PARK_ASSIGN_CASE(5) PARK_ASSIGN_CASE(6)
-#undef PARK_ASSIGN_CASE
-    default: return hipErrorInvalidValue;
-  }
+static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, int have_prev, int32_t* labels,
+                                hipStream_t st) {
+  dim3 grid((s.N + kAsgKeys - 1) / kAsgKeys, s.BH);
+  if (s.dtype == 0)
+    k_km_assign<D, true><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk, w.nkp, have_prev, labels);
+  else
+    k_km_assign<D, false><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk, w.nkp, have_prev, labels);
   return hipGetLastError();
 }
 
@@ -685,11 +906,14 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     else k_key_norms<bf16, D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Kt, s.N, w.knorm);
     PARK_CHECK();
   }
-  k_km_init<D><<<dim3(w.nkp, s.BH), D, 0, st>>>(w.Kt, init_idx, s.N, s.nk, w.nkp, w.Rt64, w.ctil, w.gneg2, w.cinfo);
+  k_km_init<D><<<dim3(w.nkp, s.BH), D, 0, st>>>(w.Kt, init_idx, s.N, s.nk, w.nkp, w.Rt64, w.ctil, w.gneg2, w.cinfo,
+                                                 w.ccv);
+  PARK_CHECK();
+  k_bound_max<<<s.BH, 256, 0, st>>>(w.cinfo, s.nk, w.nkp, w.hmax);
   PARK_CHECK();
   const size_t shm_nk = (size_t)s.nk * sizeof(int);
   for (int it = 0; it < iters; ++it) {
-    e = launch_assign<D>(s, w, K, labels, st);
+    e = launch_assign<D>(s, w, K, it > 0 ? 1 : 0, labels, st);
     if (e != hipSuccess) return e;
     k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
@@ -699,10 +923,18 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
     if (f32)
-      k_km_update<D, float><<<dim3(s.nk, s.BH), D, 0, st>>>(reinterpret_cast<const float*>(K), perm, offsets, s.N, s.nk, w.nkp, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, co);
+      k_km_sums<D, float><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const float*>(K), perm, offsets, s.N, s.nk, w.nkp, w.cmean, co);
     else
-      k_km_update<D, bf16><<<dim3(s.nk, s.BH), D, 0, st>>>(reinterpret_cast<const bf16*>(K), perm, offsets, s.N, s.nk, w.nkp, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, co);
+      k_km_sums<D, bf16><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm, offsets, s.N, s.nk, w.nkp, w.cmean, co);
     PARK_CHECK();
+    if (it + 1 < iters) {  // the transformed centroids only feed the next assignment
+      k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, w.ccv);
+      PARK_CHECK();
+    }
+    if (it + 1 < iters) {
+      k_bound_max<<<s.BH, 256, 0, st>>>(w.cinfo, s.nk, w.nkp, w.hmax);
+      PARK_CHECK();
+    }
   }
 #undef PARK_CHECK
   return hipSuccess;

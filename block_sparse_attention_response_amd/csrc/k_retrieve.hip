@@ -16,12 +16,13 @@ __global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __r
   const int bh = blockIdx.y;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e < nkp * d) {
-    const int v = e / d;
+    const int v = e / d, c = e % d;
     const float x = v < nk ? C[(size_t)bh * nk * d + e] : 0.0f;
     const bf16 hi = (bf16)x;
     const bf16 lo = (bf16)(x - (float)hi);
-    Chi[(size_t)bh * nkp * d + e] = hi;
-    Clo[(size_t)bh * nkp * d + e] = lo;
+    const size_t o = (size_t)bh * nkp * d + frag_offset(v, c, d);  // fragment-major
+    Chi[o] = hi;
+    Clo[o] = lo;
   }
   if (e < nkp) {
     const int n = e < nk ? counts[(size_t)bh * nk + e] : 0;
@@ -85,6 +86,14 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qt][vt][r] = 0.0f;
+  // B operand fragments (fragment-major Chi / Clo); spare tiles past nkp re-read tile 0
+  // (their logits are set to -inf)
+  size_t crow[VT];
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt) {
+    const int t = v0 + 32 * vt < nkp ? (v0 >> 5) + vt : 0;
+    crow[vt] = (size_t)bh * nkp * D + frag_lane(t, 0, lane, D);
+  }
 
 #pragma unroll 2
   for (int kc = 0; kc < D / 16; ++kc) {
@@ -98,18 +107,15 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     }
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      if (v0 + 32 * vt < nkp) {
-        const size_t crow = ((size_t)bh * nkp + v0 + 32 * vt + l32) * D + col;
-        const bf16x8 bhi = load_bf16x8(Chi + crow);
-        const bf16x8 blo = load_bf16x8(Clo + crow);
-        acc[0][vt] = mfma32(a0, bhi, acc[0][vt]);
-        acc[1][vt] = mfma32(a1, bhi, acc[1][vt]);
-        acc[0][vt] = mfma32(a0, blo, acc[0][vt]);
-        acc[1][vt] = mfma32(a1, blo, acc[1][vt]);
-        if constexpr (QF32) {
-          acc[0][vt] = mfma32(a0l, bhi, acc[0][vt]);
-          acc[1][vt] = mfma32(a1l, bhi, acc[1][vt]);
-        }
+      const bf16x8 bhi = load_bf16x8(Chi + crow[vt] + kc * 512);
+      const bf16x8 blo = load_bf16x8(Clo + crow[vt] + kc * 512);
+      acc[0][vt] = mfma32(a0, bhi, acc[0][vt]);
+      acc[1][vt] = mfma32(a1, bhi, acc[1][vt]);
+      acc[0][vt] = mfma32(a0, blo, acc[0][vt]);
+      acc[1][vt] = mfma32(a1, blo, acc[1][vt]);
+      if constexpr (QF32) {
+        acc[0][vt] = mfma32(a0l, bhi, acc[0][vt]);
+        acc[1][vt] = mfma32(a1l, bhi, acc[1][vt]);
       }
     }
   }

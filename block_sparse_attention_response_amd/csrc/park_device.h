@@ -28,6 +28,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// Fragment-major layout of a [rows][D] bf16 operand that is read as 32x16 MFMA fragments:
+// the 64 lanes' 16-byte pieces of one (32-row tile, 16-column chunk) sit in 1 KB of
+// contiguous memory, so every fragment load is fully coalesced.  Lane l of the fragment
+// holds row 32 t + (l % 32), columns 16 kc + 8 (l / 32) .. + 7.
+__device__ __forceinline__ size_t frag_offset(int row, int col, int D) {
+  const int t = row >> 5, r = row & 31, kc = col >> 4, hh = (col >> 3) & 1, i = col & 7;
+  return ((size_t)(t * (D / 16) + kc) * 64 + r + 32 * hh) * 8 + i;
+}
+// Start of the fragment (tile t, chunk kc) for lane `lane`.
+__device__ __forceinline__ size_t frag_lane(int t, int kc, int lane, int D) {
+  return ((size_t)(t * (D / 16) + kc) * 64 + lane) * 8;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
@@ -75,13 +88,19 @@ __device__ __forceinline__ float max64(float v) {
   return v;
 }
 
-// XCD-aware block order: the dispatcher hands consecutive workgroups to the 8 XCDs in turn;
-// this mapping gives each XCD one contiguous range of logical blocks so the blocks that run
-// together on an XCD share its L2.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
-  const uint32_t per = nblocks / 8u;
-  if (per == 0u || bid >= per * 8u) return bid;
-  return (bid % 8u) * per + bid / 8u;
+// XCD-aware block order for grids of per-head work items (NQ items per head).  The
+// dispatcher hands consecutive workgroups to the 8 XCDs in turn, so workgroup b runs on XCD
+// b % 8.  This mapping gives XCD x the items [x S, (x+1) S) of each head (S = ceil(NQ / 8))
+// and walks all XCDs through the heads together: the blocks in flight at any moment belong
+// to one or two heads (whose packed keys and values then stay in the shared cache), and the
+// neighbouring query blocks of one XCD share its L2.  The grid must have 8 S workgroups per
+// head; returns false for the padding slots.
+__device__ __forceinline__ bool xcd_head_sync(uint32_t bid, int NQ, int* head, int* item) {
+  const int S = (NQ + 7) / 8;
+  const int x = bid % 8u, slot = bid / 8u;
+  *head = slot / S;
+  *item = x * S + slot % S;
+  return *item < NQ;
 }
 
 }  // namespace park
