@@ -147,8 +147,11 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  *         perm[offsets[v] .. offsets[v+1]);
  *   O_i = sum_{j in J_u} exp(s_ij - m_i) v_j / sum_{j in J_u} exp(s_ij - m_i),
  *   s_ij = scale q_i . k_j,  lse_i = m_i + log sum_{j in J_u} exp(s_ij - m_i);
- * an empty J_u gives O_i = 0 and lse_i = -inf.  Keys and values are read in place through
- * perm (no reordered copy is made); O is in the original query order.
+ * an empty J_u gives O_i = 0 and lse_i = -inf.  O is in the original query order.
+ * For bf16 inputs the call first copies every cluster's keys and values, in cluster order, into
+ * the workspace as 8-key groups (the last group of a cluster zero-padded; values transposed per
+ * group), then lists each query block's 64-key tiles, then runs the attention kernel; float
+ * inputs are read in place through perm.
  * Inputs: Q, K, V [B,H,N,d] of `dtype`; perm/offsets from park_cluster_keys; block_list /
  * block_count from park_retrieve_blocks (ids must lie in [0, n_clusters); listing every
  * cluster gives dense attention).  scale <= 0 selects 1/sqrt(d).
@@ -156,6 +159,8 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  * Numerics: bf16 inputs use bf16 matrix products with float accumulation and a float
  * online softmax (probabilities rounded to bf16 before the PV product); float inputs are
  * computed in float throughout.
+ * Workspace: park_workspace_bytes(PARK_OP_BLOCK_SPARSE_ATTN, ...) bytes (sized for any selection,
+ * up to every cluster for every query block).
  * Errors: INVALID, UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS),
  * WORKSPACE, HIP.
  */

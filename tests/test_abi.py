@@ -1,0 +1,128 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point declared in
+include/park.h, and rejects invalid arguments on the host before anything is launched.
+(The pointers passed here are never dereferenced: every call fails a host-side check.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "park.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_response_amd", "libpark.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)   # a non-null address; never used by a rejected call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libpark.so is not built (run __graft_entry__.build())")
+    import block_sparse_attention_response_amd as park
+    return park.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"PARK_API\s+[\w\s\*]+?\b(park_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("park_cluster_keys", "park_retrieve_blocks", "park_retrieve_blocks_pooled",
+              "park_block_sparse_attn", "park_workspace_bytes", "park_abi_version", "park_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.park_abi_version() == 1
+    names = [lib.park_status_string(i).decode() for i in range(6)]
+    assert names == ["PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
+                     "PARK_ERR_NUMERIC"]
+    assert lib.park_status_string(99).decode() == "PARK_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    for op in range(3):
+        assert lib.park_workspace_bytes(op, 1, 2, 1000, 128, 24) > 0
+    assert lib.park_workspace_bytes(0, 1, 2, 1000, 96, 24) == 0      # unsupported d
+    assert lib.park_workspace_bytes(0, 1, 2, 10, 128, 24) == 0       # more clusters than tokens
+    assert lib.park_workspace_bytes(7, 1, 2, 1000, 128, 24) == 0     # unknown op
+    a = lib.park_workspace_bytes(0, 1, 40, 75600, 128, 1024)
+    b = lib.park_workspace_bytes(0, 1, 40, 75600, 128, 1536)
+    assert b > a > 0
+
+
+def _cluster(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, dtype=1, B=1, H=1, N=256, d=128, nk=8, iters=2, metric=0, alpha=0.05, init=None,
+             cent=FAKE, counts=FAKE, labels=FAKE, perm=FAKE, offsets=FAKE, status=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.park_cluster_keys(a["Q"], a["K"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["nk"], a["iters"],
+                                 a["metric"], a["alpha"], a["init"], a["cent"], a["counts"], a["labels"], a["perm"],
+                                 a["offsets"], a["status"], a["ws"], a["wsb"], None)
+
+
+def test_cluster_keys_rejects(lib):
+    assert _cluster(lib, Q=None) == INVALID
+    assert _cluster(lib, perm=None) == INVALID
+    assert _cluster(lib, N=0) == INVALID
+    assert _cluster(lib, nk=300) == INVALID
+    assert _cluster(lib, nk=0) == INVALID
+    assert _cluster(lib, iters=0) == INVALID
+    assert _cluster(lib, alpha=1.5) == INVALID
+    assert _cluster(lib, alpha=float("nan")) == INVALID
+    assert _cluster(lib, metric=5) == INVALID
+    assert _cluster(lib, dtype=7) == INVALID
+    assert _cluster(lib, d=96) == UNSUPPORTED
+    assert _cluster(lib, N=4000, nk=2000) == UNSUPPORTED
+    assert _cluster(lib, ws=None) == WORKSPACE
+    assert _cluster(lib, wsb=1024) == WORKSPACE
+    assert _cluster(lib, ws=ctypes.c_void_p(0x10008)) == WORKSPACE   # not 256-byte aligned
+
+
+def _retrieve(lib, fn="park_retrieve_blocks", **kw):
+    a = dict(Q=FAKE, dtype=1, B=1, H=1, N=256, d=128, cent=FAKE, counts=FAKE, nk=8, qb=64, p=0.9, k=2, scale=-1.0,
+             scores=FAKE, mask=FAKE, lst=FAKE, cnt=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return getattr(lib, fn)(a["Q"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["cent"], a["counts"], a["nk"],
+                            a["qb"], a["p"], a["k"], a["scale"], a["scores"], a["mask"], a["lst"], a["cnt"], a["ws"],
+                            a["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", ["park_retrieve_blocks", "park_retrieve_blocks_pooled"])
+def test_retrieve_rejects(lib, fn):
+    assert _retrieve(lib, fn, mask=None) == INVALID
+    assert _retrieve(lib, fn, p=1.5) == INVALID
+    assert _retrieve(lib, fn, p=-0.1) == INVALID
+    assert _retrieve(lib, fn, k=-1) == INVALID
+    assert _retrieve(lib, fn, scale=float("inf")) == INVALID
+    assert _retrieve(lib, fn, qb=32) == UNSUPPORTED
+    assert _retrieve(lib, fn, d=80) == UNSUPPORTED
+    assert _retrieve(lib, fn, ws=None) == WORKSPACE
+    assert _retrieve(lib, fn, wsb=16) == WORKSPACE
+
+
+def _attn(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=1, B=1, H=1, N=256, d=128, perm=FAKE, off=FAKE, nk=8, lst=FAKE, cnt=FAKE,
+             qb=64, scale=-1.0, O=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.park_block_sparse_attn(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["perm"],
+                                      a["off"], a["nk"], a["lst"], a["cnt"], a["qb"], a["scale"], a["O"], a["lse"],
+                                      a["ws"], a["wsb"], None)
+
+
+def test_attention_rejects(lib):
+    assert _attn(lib, V=None) == INVALID
+    assert _attn(lib, O=None) == INVALID
+    assert _attn(lib, B=0) == INVALID
+    assert _attn(lib, scale=float("nan")) == INVALID
+    assert _attn(lib, qb=128) == UNSUPPORTED
+    assert _attn(lib, d=32) == UNSUPPORTED
+    assert _attn(lib, ws=None) == WORKSPACE
+    assert _attn(lib, wsb=100) == WORKSPACE
