@@ -1,0 +1,129 @@
+"""Full-size parity at the benchmark shapes (all heads on the GPU, in the launch
+configuration bench.py times), checked on sampled heads and sampled query blocks that the
+CPU oracle can afford:
+  * k-means: the first step from the anchors, and the last step teacher-forced from the GPU's
+    previous labels (margin < 1e-5 exempt);
+  * clustering outputs (counts, offsets, perm, centroids) against the oracle's finalisation
+    of the GPU labels, for every head;
+  * PAMA scores (rel 1e-3) and the selection (bit-exact except margin < 1e-5), teacher-forced
+    on the GPU's own clustering;
+  * attention on sampled query blocks (max abs 2e-2 against the double oracle).
+"""
+import numpy as np
+import pytest
+
+import park_synth
+from parity_util import check_scores, compare_selection, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_response_amd as park
+    park.lib()
+    return park
+
+
+def _run(park, cfg, Q, K, V, iters, top_p, top_k, metric="qrkc", pooled=False):
+    import torch
+    q, k, v = (to_dev(x, cfg.dtype) for x in (Q, K, V))
+    cl = park.park_cluster_keys(q, k, cfg.n_clusters, iters, metric=metric)
+    f = park.park_retrieve_blocks_pooled if pooled else park.park_retrieve_blocks
+    rb = f(q, cl["centroids"], cl["counts"], top_p, top_k)
+    O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"])
+    torch.cuda.synchronize()
+    out = {kk: host(vv) for kk, vv in cl.items()}
+    out.update({kk: host(vv) for kk, vv in rb.items()})
+    out["O"], out["lse"] = host(O), host(lse)
+    del q, k, v, O, lse
+    return out
+
+
+def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc", pooled=False, ub_step=37):
+    q, k, v = Q[b, h], K[b, h], V[b, h]
+    nk = cfg.n_clusters
+    _, _, R, ok = orc.query_metric(q, metric=metric)
+    assert ok
+    Kt = orc.transform(k, R)
+    # first step from the strided anchors
+    lab_o, mar, _, _ = orc.assign(Kt, orc.init_centroids(Kt, nk))
+    d = lab_o != g1["labels"][b, h]
+    assert np.all(mar[d] < 1e-5), f"step 1: {d.sum()} labels differ"
+    # last step, teacher-forced from the GPU's previous labels (needs no empty cluster there)
+    prev = gT1["labels"][b, h]
+    if np.all(np.bincount(prev, minlength=nk) > 0):
+        C = orc.update(Kt, prev, np.zeros((nk, q.shape[1]), np.float32))
+        lab_o, mar, _, _ = orc.assign(Kt, C)
+        d = lab_o != gT["labels"][b, h]
+        assert np.all(mar[d] < 1e-5), f"last step: {d.sum()} labels differ"
+    # outputs of the final clustering
+    cent, counts, perm, offsets = orc.finalize(k, gT["labels"][b, h], nk)
+    assert np.array_equal(gT["counts"][b, h], counts)
+    assert np.array_equal(gT["offsets"][b, h], offsets)
+    assert np.array_equal(gT["perm"][b, h], perm)
+    assert np.abs(gT["centroids"][b, h] - cent).max() <= 1e-6 * max(1.0, np.abs(cent).max())
+    # retrieval on the GPU's clustering
+    scale = 1.0 / np.sqrt(q.shape[1])
+    ref = orc.pooled_scores if pooled else orc.pama
+    W = ref(q, cent, counts, 64, scale)
+    check_scores(gT["scores"][b, h], W)
+    _, ex = compare_selection(gT["scores"][b, h], counts, top_p, top_k, gT["mask"][b, h], gT["block_list"][b, h],
+                              gT["block_count"][b, h], orc)
+    # attention on sampled query blocks
+    NQ = W.shape[0]
+    ub = np.unique(np.r_[np.arange(0, NQ, ub_step), NQ - 1])
+    Oo, lo = orc.block_sparse_attn(q, k, v, perm, offsets, gT["block_list"][b, h], gT["block_count"][b, h], 64,
+                                   scale, ub)
+    rows = ~np.isnan(lo)
+    err = np.abs(gT["O"][b, h][rows] - Oo[rows]).max()
+    assert err <= 2e-2, f"attention max abs err {err}"
+    assert np.abs(gT["lse"][b, h][rows] - lo[rows]).max() <= 1e-3
+    return ex, err
+
+
+@pytest.mark.parametrize("cid,heads", [(1, (0, 11)), (2, (0, 39)), (3, (5, 23))])
+def test_fullsize_config(dev, orc, cid, heads):
+    cfg = park_synth.CONFIGS[cid]
+    Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
+    g1 = _run(dev, cfg, Q, K, V, 1, cfg.top_p, cfg.top_k)
+    gT1 = _run(dev, cfg, Q, K, V, cfg.iters - 1, cfg.top_p, cfg.top_k)
+    gT = _run(dev, cfg, Q, K, V, cfg.iters, cfg.top_p, cfg.top_k)
+    B, H = Q.shape[:2]
+    for b in range(B):
+        for h in range(H):   # every head: output invariants
+            off = gT["offsets"][b, h]
+            assert off[0] == 0 and off[-1] == cfg.N
+            assert np.array_equal(np.sort(gT["perm"][b, h]), np.arange(cfg.N))
+            assert np.array_equal(np.diff(off), gT["counts"][b, h])
+            assert np.all(gT["block_count"][b, h] >= np.minimum(cfg.top_k, (gT["counts"][b, h] > 0).sum()))
+    for h in heads:
+        ex, err = _check_head(orc, cfg, Q, K, V, g1, gT1, gT, 0, h, cfg.top_p, cfg.top_k)
+        print(f"config {cid} head {h}: {ex} selection rows exempt by margin, attention err {err:.2e}")
+
+
+@pytest.mark.parametrize("pooled", [False, True])
+def test_density_sweep_config4(dev, orc, pooled):
+    """Config 4: forced top-k (top_p = 0) at the config-2 shape; PARK and the pooled-query /
+    Euclidean-key baseline.  k = 1024 (every cluster) must reproduce dense attention."""
+    cfg = park_synth.CONFIGS[4]
+    Q, K, V = park_synth.generate(cfg, seed=0, heads=[0, 1, 2, 3], workers=4)
+    metric = "euclidean" if pooled else "qrkc"
+    import torch
+    for kk in cfg.forced_k:
+        g = _run(dev, cfg, Q, K, V, cfg.iters, 0.0, kk, metric=metric, pooled=pooled)
+        h = 1
+        counts = g["counts"][0, h]
+        nne = int((counts > 0).sum())
+        assert np.all(g["block_count"][0, h] == min(kk, nne))
+        compare_selection(g["scores"][0, h], counts, 0.0, kk, g["mask"][0, h], g["block_list"][0, h],
+                          g["block_count"][0, h], orc)
+        if kk == 1024:
+            rows = np.r_[np.arange(0, cfg.N, 997), cfg.N - 1]
+            Od, ld = orc.dense_attn(Q[0, h], K[0, h], V[0, h], 1.0 / np.sqrt(cfg.d), rows)
+            assert np.abs(g["O"][0, h][rows] - Od).max() <= 2e-2
+            assert np.abs(g["lse"][0, h][rows] - ld).max() <= 1e-3
+        torch.cuda.empty_cache()
