@@ -13,7 +13,7 @@ typedef __attribute__((address_space(3))) void* lds_vptr_c;
 typedef __attribute__((address_space(1))) void* gbl_vptr_c;
 
 constexpr int kGramChunk = 4096;   // tokens per Gram partial
-constexpr int kSortChunk = 256;    // keys per counting-sort chunk
+constexpr int kSortChunk = 1024;   // keys per counting-sort chunk
 constexpr double kEps = 1e-6;      // Cholesky stability term (times s_Q)
 constexpr double kSMin = 1e-6;     // floor of s_Q
 
@@ -153,14 +153,26 @@ __global__ __launch_bounds__(256) void k_gram_f32(const float* __restrict__ Q, i
 }
 
 // ---------------------------------------------------------------------------------------
-// a2: shrinkage and Cholesky factor, one workgroup per head, double precision in LDS.
-//   G = sum of partials / N;  s = max(tr G / D, s_min);  Gs = (1-alpha) G + (alpha+eps) s I;
-//   Gs = R R^T (left-looking, in place, row pitch D+1).  On failure (non-positive or
-//   non-finite pivot) the head gets R = I and status 1.  metric 1 (Euclidean) writes R = I.
+// a1 (end): G = (sum of the chunk partials, in chunk order) / N, one thread per entry.
 template <int D>
-__global__ __launch_bounds__(256) void k_chol(const double* __restrict__ gpart, int nch, int N, int metric,
-                                              double alpha, double* __restrict__ R64, double* __restrict__ Rt64,
-                                              bf16* __restrict__ Rsp, int32_t* __restrict__ status) {
+__global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ gpart, int nch, int N,
+                                                     double* __restrict__ G) {
+  const int bh = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * D) return;
+  double s = 0.0;
+  for (int c = 0; c < nch; ++c) s += gpart[((size_t)bh * nch + c) * D * D + e];
+  G[(size_t)bh * D * D + e] = s / (double)N;
+}
+
+// a2: shrinkage and Cholesky factor, one workgroup per head, double precision in LDS.
+//   s = max(tr G / D, s_min);  Gs = (1-alpha) G + (alpha+eps) s I;  Gs = R R^T computed
+//   right-looking in place (row pitch D+1): for each column the pivot is square-rooted, the
+//   column below it scaled, and the trailing lower triangle updated by all threads at once.
+//   On failure (non-positive or non-finite pivot) the head gets R = I and status 1.
+//   metric 1 (Euclidean) writes R = I.  G may alias Rt64 (it is read before Rt64 is written).
+template <int D>
+__global__ __launch_bounds__(256) void k_chol(const double* G, int metric, double alpha, double* __restrict__ R64,
+                                              double* Rt64, bf16* __restrict__ Rsp, int32_t* __restrict__ status) {
   constexpr int P = D + 1;
   __shared__ double A[D * P];
   __shared__ double red[4];
@@ -168,11 +180,7 @@ __global__ __launch_bounds__(256) void k_chol(const double* __restrict__ gpart, 
   const int tid = threadIdx.x, bh = blockIdx.x;
   if (tid == 0) fail = 0;
   if (metric == 0) {
-    for (int e = tid; e < D * D; e += 256) {
-      double s = 0.0;
-      for (int c = 0; c < nch; ++c) s += gpart[((size_t)bh * nch + c) * D * D + e];
-      A[(e / D) * P + e % D] = s / (double)N;
-    }
+    for (int e = tid; e < D * D; e += 256) A[(e / D) * P + e % D] = G[(size_t)bh * D * D + e];
     __syncthreads();
     double tr = 0.0;
     for (int i = tid; i < D; i += 256) tr += A[i * P + i];
@@ -187,18 +195,21 @@ __global__ __launch_bounds__(256) void k_chol(const double* __restrict__ gpart, 
     }
     __syncthreads();
     for (int j = 0; j < D; ++j) {
-      if (tid == 0) {
-        double s = A[j * P + j];
-        for (int k = 0; k < j; ++k) s -= A[j * P + k] * A[j * P + k];
-        if (!(s > 0.0) || !isfinite(s)) { fail = 1; s = 1.0; }
-        A[j * P + j] = sqrt(s);
+      double piv = A[j * P + j];
+      if (!(piv > 0.0) || !isfinite(piv)) {
+        if (tid == 0) fail = 1;
+        piv = 1.0;
       }
+      const double dj = sqrt(piv);
       __syncthreads();
-      const double piv = A[j * P + j];
-      for (int i = j + 1 + tid; i < D; i += 256) {
-        double s = A[i * P + j];
-        for (int k = 0; k < j; ++k) s -= A[i * P + k] * A[j * P + k];
-        A[i * P + j] = s / piv;
+      if (tid == 0) A[j * P + j] = dj;
+      for (int i = j + 1 + tid; i < D; i += 256) A[i * P + j] /= dj;
+      __syncthreads();
+      // trailing lower triangle, 16 x 16 thread grid
+      const int ty = tid >> 4, tx = tid & 15;
+      for (int i = j + 1 + ty; i < D; i += 16) {
+        const double lij = A[i * P + j];
+        for (int k = j + 1 + tx; k <= i; k += 16) A[i * P + k] -= lij * A[k * P + j];
       }
       __syncthreads();
     }
@@ -301,63 +312,19 @@ __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ K, cons
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// Centroid preparation (D threads): from c~_v (float, in LDS) compute g = R c~ in double,
-// gneg2 = bf16(-2 g), |c~|^2, |g| and |g - bf16(g)|.  Pad rows (v >= nk) get cc = +inf.
-template <int D>
-__device__ void centroid_prep(int bh, int v, int nkp, const float* cs, const double* __restrict__ Rt64,
-                              bf16* __restrict__ gneg2, float4* __restrict__ cinfo, float* __restrict__ ccv,
-                              double* red) {
-  const int i = threadIdx.x;
-  if (i < D) {
-    const double* Rt = Rt64 + (size_t)bh * D * D;
-    double g = 0.0;
-    for (int k = 0; k < D; ++k) g += Rt[(size_t)k * D + i] * (double)cs[k];
-    const bf16 gb = (bf16)(float)g;
-    gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)gb);
-    const double df = g - (double)(float)gb;
-    double cc = (double)cs[i] * cs[i], gn = g * g, f = df * df;
-    cc = sum64d(cc); gn = sum64d(gn); f = sum64d(f);
-    const int w = i >> 6;
-    if ((i & 63) == 0) { red[3 * w] = cc; red[3 * w + 1] = gn; red[3 * w + 2] = f; }
-  }
-  __syncthreads();
-  if (i == 0) {
-    double cc = red[0], gn = red[1], f = red[2];
-    for (int k = 1; k < D / 64; ++k) { cc += red[3 * k]; gn += red[3 * k + 1]; f += red[3 * k + 2]; }
-    const float up = 1.0f + 1.0f / 1048576.0f;
-    const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
-    cinfo[(size_t)bh * nkp + v] = ci;
-    ccv[(size_t)bh * nkp + v] = ci.x;
-  }
-  __syncthreads();
-}
-
-// a4: initial centroids c~_v = k~ at floor(v N / nk) (or init_idx[v], clamped to [0, N)).
+// a4: initial centroids c~_v = k~ at floor(v N / nk) (or init_idx[v], clamped to [0, N));
+// padding rows (v >= nk) are zero.  The screen operands follow from k_km_ctx.
 template <int D>
 __global__ __launch_bounds__(D) void k_km_init(const float* __restrict__ Kt, const int32_t* __restrict__ init_idx,
-                                               int N, int nk, int nkp, const double* __restrict__ Rt64,
-                                               float* __restrict__ ctil, bf16* __restrict__ gneg2,
-                                               float4* __restrict__ cinfo, float* __restrict__ ccv) {
-  __shared__ float cs[D];
-  __shared__ double red[6];
+                                               int N, int nk, int nkp, float* __restrict__ ctil) {
   const int v = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
-  if (v >= nk) {  // padding rows: never the nearest centroid
-    ctil[((size_t)bh * nkp + v) * D + i] = 0.0f;
-    gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
-    if (i == 0) {
-      cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
-      ccv[(size_t)bh * nkp + v] = INFINITY;
-    }
-    return;
+  float x = 0.0f;
+  if (v < nk) {
+    long j = init_idx ? (long)init_idx[v] : (long)(((long long)v * N) / nk);
+    j = j < 0 ? 0 : (j >= N ? N - 1 : j);
+    x = Kt[((size_t)bh * N + j) * D + i];
   }
-  long j = init_idx ? (long)init_idx[v] : (long)(((long long)v * N) / nk);
-  j = j < 0 ? 0 : (j >= N ? N - 1 : j);
-  const float x = Kt[((size_t)bh * N + j) * D + i];
-  cs[i] = x;
   ctil[((size_t)bh * nkp + v) * D + i] = x;
-  __syncthreads();
-  centroid_prep<D>(bh, v, nkp, cs, Rt64, gneg2, cinfo, ccv, red);
 }
 
 // Per-head maxima of |R c~|, its bf16 error and |c~|^2 over all clusters (empty ones
@@ -647,8 +614,8 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
   const int tid = threadIdx.x, bh = blockIdx.y, ch = blockIdx.x;
   for (int v = tid; v < nk; v += 256) hs[v] = 0;
   __syncthreads();
-  const int j = ch * kSortChunk + tid;
-  if (j < N) atomicAdd(&hs[labels[(size_t)bh * N + j]], 1);
+  for (int j = ch * kSortChunk + tid; j < min(N, (ch + 1) * kSortChunk); j += 256)
+    atomicAdd(&hs[labels[(size_t)bh * N + j]], 1);
   __syncthreads();
   for (int v = tid; v < nk; v += 256) hist[((size_t)bh * nch + ch) * nk + v] = hs[v];
 }
@@ -661,6 +628,7 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   int32_t* hb = hist + (size_t)bh * nch * nk;
   for (int v = tid; v < nk; v += 1024) {
     int s = 0;
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) s += hb[(size_t)c * nk + v];
     tot[v] = s;
     counts[(size_t)bh * nk + v] = s;
@@ -691,6 +659,7 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   __syncthreads();
   for (int v = tid; v < nk; v += 1024) {
     int b = tot[v];
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) {
       const int t = hb[(size_t)c * nk + v];
       hb[(size_t)c * nk + v] = b;
@@ -752,6 +721,7 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+#pragma unroll 4
   for (int r = rg; r < n; r += RPI) {
     const T* src = Kh + (size_t)pm[r] * D + c8;
     float x[8];
@@ -780,82 +750,94 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
   }
 }
 
-// Step 2, per (32-cluster tile, head): c~_v = R^T mean_v rounded to float, then the screen
-// operand g_v = R c~_v, gneg2 = bf16(-2 g) (fragment-major), |c~|^2, |g|, |g - bf16(g)|.
-// Clusters without keys keep everything from the previous step.  Thread (i, vh) owns
-// output dimension i of the clusters 2j + vh of the tile, so each R element read from
-// memory serves 16 clusters.
+// Step 2, per (32-cluster tile, head): c~_v = R^T mean_v rounded to float (or, for the
+// initial centroids, c~_v as stored), then the screen operand g_v = R c~_v in double,
+// gneg2 = bf16(-2 g) (fragment-major), |c~|^2, |g|, |g - bf16(g)|.  Clusters without keys
+// keep everything from the previous step; padding rows (v >= nk) get |c~|^2 = +inf.
+// Thread (i, vh) owns dimension i of the clusters NVH j + vh of the tile, so each R element
+// read from memory serves several clusters.
 template <int D>
 __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
-                                                int nk, int nkp, const double* __restrict__ R64,
+                                                int nk, int nkp, int init_mode, const double* __restrict__ R64,
                                                 const double* __restrict__ Rt64, float* __restrict__ ctil,
                                                 bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
                                                 float* __restrict__ ccv) {
-  constexpr int VPT = 32 / (256 / D);  // clusters per thread
   constexpr int NVH = 256 / D;         // thread groups over the clusters of the tile
-  __shared__ double ms[32][D + 1];
+  constexpr int VPT = 32 / NVH;        // clusters per thread
+  __shared__ double ms[32][D + 1];     // means, then g
   __shared__ float cs[32][D + 1];
-  __shared__ double red[3][32][4];
-  const int tid = threadIdx.x, lane = tid & 63, bh = blockIdx.y, v0 = blockIdx.x * 32;
+  const int tid = threadIdx.x, bh = blockIdx.y, v0 = blockIdx.x * 32;
   const int i = tid % D, vh = tid / D;
-  const int wq = (tid % D) >> 6;       // wave index within the group of D threads
-  for (int e = tid; e < 32 * D; e += 256) {
-    const int vv = e / D, k = e % D;
-    const int v = v0 + vv;
-    ms[vv][k] = v < nk ? cmean[((size_t)bh * nkp + v) * D + k] : 0.0;
-  }
-  __syncthreads();
   bool live[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int v = v0 + NVH * j + vh;
-    live[j] = v < nk && counts[(size_t)bh * nk + v] > 0;
+    live[j] = v < nk && (init_mode || counts[(size_t)bh * nk + v] > 0);
   }
-  {
+  if (init_mode) {
+    for (int e = tid; e < 32 * D; e += 256) {
+      const int vv = e / D, k = e % D;
+      cs[vv][k] = ctil[((size_t)bh * nkp + v0 + vv) * D + k];
+    }
+    __syncthreads();
+  } else {
+    for (int e = tid; e < 32 * D; e += 256) {
+      const int vv = e / D, k = e % D;
+      const int v = v0 + vv;
+      ms[vv][k] = v < nk ? cmean[((size_t)bh * nkp + v) * D + k] : 0.0;
+    }
+    __syncthreads();
     const double* R = R64 + (size_t)bh * D * D;
     double t[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) t[j] = 0.0;
+#pragma unroll 8
     for (int k = 0; k < D; ++k) {
-      const double r = R[(size_t)k * D + i];       // R[k][i]: (R^T m)_i = sum_k R[k][i] m_k
+      const double r = R[(size_t)k * D + i];       // (R^T m)_i = sum_k R[k][i] m_k
 #pragma unroll
       for (int j = 0; j < VPT; ++j) t[j] += r * ms[NVH * j + vh][k];
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) cs[NVH * j + vh][i] = (float)t[j];
+    __syncthreads();
   }
-  __syncthreads();
   {
     const double* Rt = Rt64 + (size_t)bh * D * D;
     double g[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) g[j] = 0.0;
+#pragma unroll 8
     for (int k = 0; k < D; ++k) {
       const double r = Rt[(size_t)k * D + i];      // Rt[k][i] = R[i][k]: (R c~)_i
 #pragma unroll
       for (int j = 0; j < VPT; ++j) g[j] += r * (double)cs[NVH * j + vh][k];
     }
+    __syncthreads();  // ms is reused for g
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int vv = NVH * j + vh, v = v0 + vv;
-      const float c = cs[vv][i];
-      const bf16 gb = (bf16)(float)g[j];
+      ms[vv][i] = g[j];
       if (live[j]) {
-        ctil[((size_t)bh * nkp + v) * D + i] = c;
-        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)gb);
+        ctil[((size_t)bh * nkp + v) * D + i] = cs[vv][i];
+        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[j]);
+      } else if (v >= nk) {
+        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
       }
-      const double df = g[j] - (double)(float)gb;
-      double cc = (double)c * c, gn = g[j] * g[j], f = df * df;
-      cc = sum64d(cc); gn = sum64d(gn); f = sum64d(f);
-      if (lane == 0) { red[0][vv][wq] = cc; red[1][vv][wq] = gn; red[2][vv][wq] = f; }
     }
   }
   __syncthreads();
   if (tid < 32) {
     const int v = v0 + tid;
-    if (v < nk && counts[(size_t)bh * nk + v] > 0) {
+    if (v >= nk) {
+      cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
+      ccv[(size_t)bh * nkp + v] = INFINITY;
+    } else if (init_mode || counts[(size_t)bh * nk + v] > 0) {
       double cc = 0.0, gn = 0.0, f = 0.0;
-      for (int q = 0; q < D / 64; ++q) { cc += red[0][tid][q]; gn += red[1][tid][q]; f += red[2][tid][q]; }
+      for (int k = 0; k < D; ++k) {
+        const double c = cs[tid][k], g = ms[tid][k];
+        const double df = g - (double)(float)(bf16)(float)g;
+        cc += c * c; gn += g * g; f += df * df;
+      }
       const float up = 1.0f + 1.0f / 1048576.0f;
       const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
       cinfo[(size_t)bh * nkp + v] = ci;
@@ -890,7 +872,11 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     else k_gram_bf16<D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(Q), s.N, w.nch_g, w.gpart);
     PARK_CHECK();
   }
-  k_chol<D><<<s.BH, 256, 0, st>>>(w.gpart, w.nch_g, s.N, metric, (double)alpha, w.R64, w.Rt64, w.Rsp, status);
+  if (metric == 0) {
+    k_gram_reduce<D><<<dim3((D * D + 255) / 256, s.BH), 256, 0, st>>>(w.gpart, w.nch_g, s.N, w.Rt64);
+    PARK_CHECK();
+  }
+  k_chol<D><<<s.BH, 256, 0, st>>>(w.Rt64, metric, (double)alpha, w.R64, w.Rt64, w.Rsp, status);
   PARK_CHECK();
   if (f32) {
     dim3 grid((unsigned)(((size_t)s.N * D + 255) / 256), s.BH);
@@ -906,8 +892,10 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     else k_key_norms<bf16, D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Kt, s.N, w.knorm);
     PARK_CHECK();
   }
-  k_km_init<D><<<dim3(w.nkp, s.BH), D, 0, st>>>(w.Kt, init_idx, s.N, s.nk, w.nkp, w.Rt64, w.ctil, w.gneg2, w.cinfo,
-                                                 w.ccv);
+  k_km_init<D><<<dim3(w.nkp, s.BH), D, 0, st>>>(w.Kt, init_idx, s.N, s.nk, w.nkp, w.ctil);
+  PARK_CHECK();
+  k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, 1, w.R64, w.Rt64, w.ctil,
+                                                      w.gneg2, w.cinfo, w.ccv);
   PARK_CHECK();
   k_bound_max<<<s.BH, 256, 0, st>>>(w.cinfo, s.nk, w.nkp, w.hmax);
   PARK_CHECK();
@@ -928,7 +916,7 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
       k_km_sums<D, bf16><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm, offsets, s.N, s.nk, w.nkp, w.cmean, co);
     PARK_CHECK();
     if (it + 1 < iters) {  // the transformed centroids only feed the next assignment
-      k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, w.ccv);
+      k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, 0, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, w.ccv);
       PARK_CHECK();
     }
     if (it + 1 < iters) {

@@ -95,7 +95,14 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     crow[vt] = (size_t)bh * nkp * D + frag_lane(t, 0, lane, D);
   }
 
-#pragma unroll 2
+  // B fragments are prefetched one 16-column step ahead when the registers allow it
+  constexpr bool kPrefetch = VT <= 4;
+  bf16x8 nhi[VT], nlo[VT];
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) { nhi[vt] = load_bf16x8(Chi + crow[vt]); nlo[vt] = load_bf16x8(Clo + crow[vt]); }
+  }
+#pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     const int col = kc * 16 + 8 * h;
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qs[l32 * QP + col]);
@@ -105,17 +112,33 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       a0l = *reinterpret_cast<const bf16x8*>(&qlo[l32 * QP + col]);
       a1l = *reinterpret_cast<const bf16x8*>(&qlo[(32 + l32) * QP + col]);
     }
+    bf16x8 bhi[VT], blo[VT];
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) { bhi[vt] = nhi[vt]; blo[vt] = nlo[vt]; }
+      if (kc + 1 < D / 16) {
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          nhi[vt] = load_bf16x8(Chi + crow[vt] + (kc + 1) * 512);
+          nlo[vt] = load_bf16x8(Clo + crow[vt] + (kc + 1) * 512);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        bhi[vt] = load_bf16x8(Chi + crow[vt] + kc * 512);
+        blo[vt] = load_bf16x8(Clo + crow[vt] + kc * 512);
+      }
+    }
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      const bf16x8 bhi = load_bf16x8(Chi + crow[vt] + kc * 512);
-      const bf16x8 blo = load_bf16x8(Clo + crow[vt] + kc * 512);
-      acc[0][vt] = mfma32(a0, bhi, acc[0][vt]);
-      acc[1][vt] = mfma32(a1, bhi, acc[1][vt]);
-      acc[0][vt] = mfma32(a0, blo, acc[0][vt]);
-      acc[1][vt] = mfma32(a1, blo, acc[1][vt]);
+      acc[0][vt] = mfma32(a0, bhi[vt], acc[0][vt]);
+      acc[1][vt] = mfma32(a1, bhi[vt], acc[1][vt]);
+      acc[0][vt] = mfma32(a0, blo[vt], acc[0][vt]);
+      acc[1][vt] = mfma32(a1, blo[vt], acc[1][vt]);
       if constexpr (QF32) {
-        acc[0][vt] = mfma32(a0l, bhi, acc[0][vt]);
-        acc[1][vt] = mfma32(a1l, bhi, acc[1][vt]);
+        acc[0][vt] = mfma32(a0l, bhi[vt], acc[0][vt]);
+        acc[1][vt] = mfma32(a1l, bhi[vt], acc[1][vt]);
       }
     }
   }
