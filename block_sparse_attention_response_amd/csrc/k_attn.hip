@@ -322,7 +322,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
   constexpr float kNoMax = -1e30f;
+  const float kBig = __builtin_amdgcn_ldexpf(1.0f, 60);
   float m = kNoMax, lsum = 0.0f;
+  // lacc: V^T P^T with V^T replaced by ones, i.e. the row sums of the bf16 weights that the
+  // PV product used (every element of a lane holds its query's sum); O is normalised by it,
+  // the log-sum-exp by the float sum lsum
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
   const int arow = 32 * kw + 16 * (l32 >> 4) + sigma16(l32 & 15);
   const int aswz = arow % NS;
 
@@ -346,40 +356,50 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (((2 * kc + h) ^ aswz) * 8));
       sacc = mfma32(a, qf[kc], sacc);
     }
-    float mx = sacc[0];
+    // probabilities against the running reference m; the reference only moves (with a
+    // rescale of the accumulators) when a row sum leaves [0, 2^60], which happens on the
+    // first tile (m starts at -1e30) and when a score exceeds m by about 60 (log2 units)
+    f32x16 pr;
+    float ps;
+    auto probs = [&]() {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
-    // rescale only when the running maximum grows by more than 2^8
-    if (__any(mx > m + 8.0f)) {
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[r], scale2, -m));
+      const float s0 = (pr[0] + pr[1]) + (pr[2] + pr[3]), s1 = (pr[4] + pr[5]) + (pr[6] + pr[7]);
+      const float s2 = (pr[8] + pr[9]) + (pr[10] + pr[11]), s3 = (pr[12] + pr[13]) + (pr[14] + pr[15]);
+      ps = (s0 + s1) + (s2 + s3);
+    };
+    probs();
+    if (__builtin_expect(__any(!(ps <= kBig)), 0)) {
+      asm volatile("" ::: "memory");   // keep this rare path a branch (no if-conversion)
+      float mx = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
       const float mnew = fmaxf(m, mx);
       const float alpha = fast_exp2(m - mnew);
       lsum *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m = mnew;
-    }
-    float ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(sacc[r], scale2, -m));
-      sacc[r] = p;
-      ps += p;
+      probs();
     }
     lsum += ps;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (bf16)sacc[8 * c + i];
+      for (int i = 0; i < 8; ++i) pb[i] = (bf16)pr[8 * c + i];
       const bf16* vg = Vb + (size_t)(4 * kw + 2 * c + h) * GE;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(vg + (32 * dt + l32) * 8);
         oacc[dt] = mfma32(a, pb, oacc[dt]);
       }
+      lacc = mfma32(ones, pb, lacc);
     }
   };
 
@@ -400,14 +420,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
 
   // merge the two key halves: waves kw = 1 hand (m, l, O^T) to waves kw = 0 through LDS
   float* xo = reinterpret_cast<float*>(K0);  // K0 and K1 hold 2 waves x 64 lanes x D/2 floats
-  float* xm = reinterpret_cast<float*>(V0);  // 2 waves x 64 lanes x (m, l)
+  float* xm = reinterpret_cast<float*>(V0);  // 2 waves x 64 lanes x (m, l, l of the bf16 weights)
   auto xo_at = [&](int qq, int ln, int k) -> float* {  // lane-contiguous: no bank conflicts
     const int idx = k * 128 + qq * 64 + ln;
     return idx < 32 * D ? xo + idx : reinterpret_cast<float*>(K1) + (idx - 32 * D);
   };
   if (kw == 1) {
-    xm[(qw * 64 + lane) * 2] = m;
-    xm[(qw * 64 + lane) * 2 + 1] = lsum;
+    xm[(qw * 64 + lane) * 3] = m;
+    xm[(qw * 64 + lane) * 3 + 1] = lsum;
+    xm[(qw * 64 + lane) * 3 + 2] = lacc[0];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -415,12 +436,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q
   }
   __syncthreads();
   if (kw == 0) {
-    const float m1 = xm[(qw * 64 + lane) * 2], l1 = xm[(qw * 64 + lane) * 2 + 1];
+    const float m1 = xm[(qw * 64 + lane) * 3], l1 = xm[(qw * 64 + lane) * 3 + 1];
+    const float lb1 = xm[(qw * 64 + lane) * 3 + 2];
     const float mt = fmaxf(m, m1);
     const float a0 = fast_exp2(m - mt), a1 = fast_exp2(m1 - mt);
     float l = lsum * a0 + l1 * a1;
     l += __shfl_xor(l, 32);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lb = lacc[0] * a0 + lb1 * a1;   // already summed over both lane halves
+    const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
     if (qvalid) {
       bf16* orow = O + ((size_t)bh * N + qrow) * D;
 #pragma unroll
