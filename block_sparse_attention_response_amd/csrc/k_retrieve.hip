@@ -260,138 +260,151 @@ __global__ __launch_bounds__(256) void k_pooled(const T* __restrict__ Q, const f
 }
 
 // ---------------------------------------------------------------------------------------
-// Selection per (query block, head): bitonic sort of (rank key, id) in LDS, fixed-point
-// prefix mass, cut t_p, floor k, then the mask, the ascending id list and the count.
-// Masses are summed as integers in units of 2^-56, so the prefix sums are exact and do not
-// depend on the order of the additions.
-template <int NP>
+// Selection per (query block, head), one wave per row.  Clusters are ranked by the key
+//   K = (hi << 11) | id,  hi = 0x7F800000 - bits(max(W, 0)) for a non-empty cluster, all ones
+// for an empty one, so ascending K is (W descending, id ascending, empty last).  Masses are
+// integers in units of 2^-56, so every prefix sum is exact and independent of the order of
+// the additions.  t_p is the smallest t whose ranking prefix reaches top_p * total; the
+// count is min(max(t_p, top_k), non-empty); the selected set is the `count` smallest keys.
+// Both cuts are found by a radix descent over K with 6-bit digits: a 64-bin LDS histogram of
+// the candidates' next digit (count and mass), a wave scan over the bins, and the first bin
+// that reaches the target; the descent stops as soon as one candidate is left.
+constexpr int kKeyBits = 43;   // 32 bits of hi + 11 bits of id (nk <= 2048)
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t t = __shfl_up(x, o);
+    if (lane >= o) x += t;
+  }
+  return x;
+}
+
+template <int EPL>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, const int32_t* __restrict__ counts,
-                                                int nk, int NQ, float top_p, int top_k,
+                                                int nk, int NQ, int rows, float top_p, int top_k,
                                                 uint8_t* __restrict__ mask, int32_t* __restrict__ list,
                                                 int32_t* __restrict__ count) {
-  __shared__ uint64_t key[NP];
-  __shared__ uint64_t pre[NP];
-  __shared__ uint64_t part[256];
-  __shared__ int sel_scan[NP];
-  __shared__ int s_nonempty, s_tp;
-  const int tid = threadIdx.x;
-  const size_t row = (size_t)blockIdx.y * NQ + blockIdx.x;
-  const int bh = blockIdx.y;
-  const float* Wr = W + row * nk;
-  if (tid == 0) { s_nonempty = 0; s_tp = 0; }
-  __syncthreads();
+  __shared__ uint32_t hcnt[4][64];
+  __shared__ uint64_t hmass[4][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  const int bh = row / NQ;
+  const float* Wr = W + (size_t)row * nk;
+  uint32_t* hc = hcnt[w];
+  uint64_t* hm = hmass[w];
+
+  uint64_t key[EPL], ms[EPL];
   int ne = 0;
-  for (int i = tid; i < NP; i += 256) {
-    uint64_t k = ~0ull;
-    if (i < nk) {
-      const int c = counts[(size_t)bh * nk + i];
+  uint64_t msum = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int i = lane + 64 * j;
+    uint32_t hi = 0xFFFFFFFFu;
+    uint64_t m = 0;
+    if (i < nk && counts[(size_t)bh * nk + i] > 0) {
       float wv = Wr[i];
-      wv = (wv > 0.0f) ? wv : 0.0f;  // also maps NaN to 0
-      const uint32_t hi = c > 0 ? (0x7F800000u - __float_as_uint(wv)) : 0xFFFFFFFFu;
-      ne += c > 0;
-      k = ((uint64_t)hi << 32) | (uint32_t)i;
+      wv = (wv > 0.0f) ? wv : 0.0f;   // also maps NaN to 0
+      hi = 0x7F800000u - __float_as_uint(wv);
+      m = (uint64_t)((double)fminf(wv, 64.0f) * 72057594037927936.0);   // 2^56
+      ++ne;
     }
-    key[i] = k;
+    key[j] = ((uint64_t)hi << 11) | (uint32_t)i;   // i < 2048
+    ms[j] = m;
+    msum += m;
   }
-  atomicAdd(&s_nonempty, ne);
-  __syncthreads();
-  for (int k = 2; k <= NP; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < NP; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = key[i], b = key[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) { key[i] = b; key[ixj] = a; }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ne += __shfl_xor(ne, o);
+    msum += __shfl_xor(msum, o);
+  }
+  const double total = (double)msum;
+
+  // smallest key kappa with (sum over keys <= kappa of the weight) >= target, where the
+  // weight is the mass (by_mass) or 1; returns kappa and the number of keys <= kappa
+  auto descend = [&](bool by_mass, double target, uint64_t* kappa, int* rank) {
+    uint64_t prefix = 0;          // key bits above `shift` fixed so far
+    uint64_t below = 0;           // weight of the keys below the candidate range
+    int nbelow = 0;               // number of keys below the candidate range
+    for (int shift = kKeyBits - 6; ; shift -= 6) {
+      const int sh = shift > 0 ? shift : 0;
+      const int width = shift + 6 - sh;              // digit bits at this level
+      const uint64_t hmask = (1ull << width) - 1;
+      hc[lane] = 0;
+      hm[lane] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        if ((key[j] >> (sh + width)) == prefix) {
+          const int d = (int)((key[j] >> sh) & hmask);
+          atomicAdd(&hc[d], 1u);
+          if (by_mass) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)ms[j]);
         }
       }
-      __syncthreads();
-    }
-  }
-  // fixed-point masses in ranking order, then an inclusive scan
-  constexpr int SEG = NP >= 256 ? NP / 256 : 1;
-  const int b0 = tid * SEG;
-  uint64_t run = 0;
-  if (b0 < NP) {
-    for (int i = b0; i < b0 + SEG; ++i) {
-      const uint64_t k = key[i];
-      uint64_t m = 0;
-      if ((uint32_t)(k >> 32) != 0xFFFFFFFFu) {
-        const float wv = __uint_as_float(0x7F800000u - (uint32_t)(k >> 32));
-        const double x = (double)fminf(wv, 64.0f) * 72057594037927936.0;  // 2^56
-        m = (uint64_t)x;
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t c = hc[lane];
+      const uint64_t wt = by_mass ? hm[lane] : (uint64_t)c;
+      const uint64_t cw = wave_incl_scan_u64(wt, lane);
+      int cc = (int)c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(cc, o);
+        if (lane >= o) cc += t;
       }
-      run += m;
-      pre[i] = run;
+      const bool reach = (double)(below + cw) >= target;
+      const uint64_t bal = __ballot(reach);
+      const int d = bal ? __ffsll((unsigned long long)bal) - 1 : 63;
+      const uint64_t cw_before = d > 0 ? __shfl(cw, d - 1) : 0;
+      const int cc_before = d > 0 ? __shfl(cc, d - 1) : 0;
+      const uint32_t cd = __shfl(c, d);
+      below += cw_before;
+      nbelow += cc_before;
+      prefix = (prefix << width) | (uint64_t)d;
+      if (sh == 0 || cd == 1) {
+        if (sh > 0) {
+          // one candidate left: its key completes the prefix
+          uint64_t k = 0;
+#pragma unroll
+          for (int j = 0; j < EPL; ++j)
+            if ((key[j] >> sh) == prefix) k = key[j];
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) k |= __shfl_xor(k, o);
+          prefix = k;
+        }
+        *kappa = prefix;
+        *rank = nbelow + 1;
+        return;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
+  };
+
+  int tp = 0;
+  uint64_t kp = 0;
+  if (top_p > 0.0f && ne > 0) descend(true, (double)top_p * total, &kp, &tp);
+  int cnt = tp > top_k ? tp : top_k;
+  cnt = min(cnt, ne);
+  uint64_t kc = kp;
+  if (cnt > 0 && cnt != tp) {
+    int rk;
+    descend(false, (double)cnt, &kc, &rk);
   }
-  part[tid] = (b0 < NP) ? run : 0;
-  __syncthreads();
-  if (tid < 64) {
-    uint64_t s = 0;
-    for (int i = 0; i < 4; ++i) s += part[4 * tid + i];
-    uint64_t incl = s;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t o = __shfl_up(incl, off);
-      if (tid >= off) incl += o;
-    }
-    uint64_t ex = incl - s;
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t v = part[4 * tid + i];
-      part[4 * tid + i] = ex;
-      ex += v;
-    }
+
+  // mask and ascending id list
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int i = lane + 64 * j;
+    const bool sel = cnt > 0 && key[j] <= kc;
+    if (i < nk) mask[(size_t)row * nk + i] = (uint8_t)sel;
+    const uint64_t b = __ballot(sel && i < nk);
+    const int pos = base + __popcll(b & ((1ull << lane) - 1));
+    if (sel && i < nk) list[(size_t)row * nk + pos] = i;
+    base += __popcll(b);
   }
-  __syncthreads();
-  if (b0 < NP)
-    for (int i = b0; i < b0 + SEG; ++i) pre[i] += part[tid];
-  __syncthreads();
-  const double total = (double)pre[NP - 1];
-  if (top_p > 0.0f) {
-    const double target = (double)top_p * total;
-    for (int i = tid; i < NP; i += 256) {
-      if ((double)pre[i] >= target && (i == 0 || (double)pre[i - 1] < target)) s_tp = i + 1;
-    }
-  }
-  __syncthreads();
-  int cnt = s_tp > top_k ? s_tp : top_k;
-  cnt = min(cnt, s_nonempty);
-  // selection flags in id order
-  for (int i = tid; i < NP; i += 256) sel_scan[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < nk; i += 256) sel_scan[(uint32_t)key[i]] = (i < cnt) ? 1 : 0;
-  __syncthreads();
-  for (int i = tid; i < nk; i += 256) mask[row * nk + i] = (uint8_t)sel_scan[i];
-  // exclusive scan of the flags -> list positions
-  int f = 0;
-  if (b0 < NP)
-    for (int i = b0; i < b0 + SEG; ++i) f += sel_scan[i];
-  __syncthreads();
-  part[tid] = (b0 < NP) ? (uint64_t)f : 0;
-  __syncthreads();
-  if (tid < 64) {
-    uint64_t s = 0;
-    for (int i = 0; i < 4; ++i) s += part[4 * tid + i];
-    uint64_t incl = s;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t o = __shfl_up(incl, off);
-      if (tid >= off) incl += o;
-    }
-    uint64_t ex = incl - s;
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t v = part[4 * tid + i];
-      part[4 * tid + i] = ex;
-      ex += v;
-    }
-  }
-  __syncthreads();
-  if (b0 < NP) {
-    int pos = (int)part[tid];
-    for (int i = b0; i < b0 + SEG && i < nk; ++i)
-      if (sel_scan[i]) list[row * nk + pos++] = i;
-  }
-  for (int i = cnt + tid; i < nk; i += 256) list[row * nk + i] = -1;
-  if (tid == 0) count[row] = cnt;
+  for (int i = cnt + lane; i < nk; i += 64) list[(size_t)row * nk + i] = -1;
+  if (lane == 0) count[row] = cnt;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -454,14 +467,13 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
                      : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, scale2, W, st);
   }
   if (e != hipSuccess) return e;
-  dim3 grid(NQ, s.BH);
-  int np = 32;
-  while (np < s.nk) np <<= 1;
-  switch (np) {
-#define PARK_SEL_CASE(P) \
-  case P: k_select<P><<<grid, 256, 0, st>>>(W, counts, s.nk, NQ, top_p, top_k, mask, list, count); break;
-    PARK_SEL_CASE(32) PARK_SEL_CASE(64) PARK_SEL_CASE(128) PARK_SEL_CASE(256) PARK_SEL_CASE(512)
-    PARK_SEL_CASE(1024) PARK_SEL_CASE(2048)
+  const int rows = s.BH * NQ;
+  const int sgrid = (rows + 3) / 4;
+  const int epl = (s.nk + 63) / 64;
+  switch (epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : epl <= 16 ? 16 : 32) {
+#define PARK_SEL_CASE(E) \
+  case E: k_select<E><<<sgrid, 256, 0, st>>>(W, counts, s.nk, NQ, rows, top_p, top_k, mask, list, count); break;
+    PARK_SEL_CASE(1) PARK_SEL_CASE(2) PARK_SEL_CASE(4) PARK_SEL_CASE(8) PARK_SEL_CASE(16) PARK_SEL_CASE(32)
 #undef PARK_SEL_CASE
     default: return hipErrorInvalidValue;
   }
