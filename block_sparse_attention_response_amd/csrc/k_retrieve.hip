@@ -7,20 +7,29 @@
 namespace park {
 
 // ---------------------------------------------------------------------------------------
-// Centroids as an unevaluated sum of two bf16 matrices (hi + lo), so that a bf16 product
-// with the exact-bf16 queries carries about 16 mantissa bits of each centroid; plus the
-// log2 of the cluster size (-inf for an empty cluster).  Rows nk..nkp-1 are zero padding.
+// Centroids for the PAMA product, pre-multiplied by scale2 = scale log2(e) and extended by one
+// 16-column chunk whose first column holds log2 n_v (-1e30 for an empty cluster), so that
+// one matrix product with the queries (extended by a column of ones) gives the logits
+//   S_iv (log2 units) = scale log2(e) q_i . c_v + log2 n_v.
+// Each value is stored as an unevaluated sum of two bf16 numbers (hi + lo), so a bf16 product
+// with the exact-bf16 queries carries about 16 mantissa bits of it.  Layout: fragment-major
+// over DK = d + 16 columns; rows nk..nkp-1 are empty clusters.  lg keeps log2 n_v (-inf if
+// empty) for the pooled baseline.
 __global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __restrict__ counts,
-                                 int nk, int nkp, int d, bf16* __restrict__ Chi,
+                                 int nk, int nkp, int d, float scale2, bf16* __restrict__ Chi,
                                  bf16* __restrict__ Clo, float* __restrict__ lg) {
   const int bh = blockIdx.y;
+  const int DK = d + 16;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < nkp * d) {
-    const int v = e / d, c = e % d;
-    const float x = v < nk ? C[(size_t)bh * nk * d + e] : 0.0f;
+  if (e < nkp * DK) {
+    const int v = e / DK, c = e % DK;
+    const int n = v < nk ? counts[(size_t)bh * nk + v] : 0;
+    float x = 0.0f;
+    if (c < d) x = v < nk ? C[((size_t)bh * nk + v) * d + c] * scale2 : 0.0f;
+    else if (c == d) x = n > 0 ? __log2f((float)n) : -1e30f;
     const bf16 hi = (bf16)x;
-    const bf16 lo = (bf16)(x - (float)hi);
-    const size_t o = (size_t)bh * nkp * d + frag_offset(v, c, d);  // fragment-major
+    const bf16 lo = (c == d && n <= 0) ? (bf16)0.0f : (bf16)(x - (float)hi);
+    const size_t o = (size_t)bh * nkp * DK + frag_offset(v, c, DK);
     Chi[o] = hi;
     Clo[o] = lo;
   }
@@ -30,19 +39,43 @@ __global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __r
   }
 }
 
+// Reduce-scatter over the 32 lanes of a wave half: v[i] (i < 32) of every lane is combined
+// with op across the 32 lanes, and lane l ends up holding the result for i = l % 32.
+template <bool MAX>
+__device__ __forceinline__ float reduce_scatter32(float (&v)[32], int l32) {
+#pragma unroll
+  for (int step = 0; step < 5; ++step) {
+    const int mask = 16 >> step, half = 16 >> step;
+    // lanes with the mask bit keep the upper half; the choice is a bitwise select on values
+    // (a ternary on array elements would become dynamic register indexing)
+    const uint32_t sel = (l32 & mask) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + half]);
+      const float send = __uint_as_float((lo & sel) | (hi & ~sel));
+      const float keep = __uint_as_float((hi & sel) | (lo & ~sel));
+      const float recv = __shfl_xor(send, mask);
+      v[i] = MAX ? fmaxf(keep, recv) : keep + recv;
+    }
+  }
+  return v[0];
+}
+
 // ---------------------------------------------------------------------------------------
 // Fused PAMA: one workgroup per (query block, head), 64 queries, nw waves; wave w owns
 // clusters [32 VT w, 32 VT (w+1)).  The 64 x (32 VT) logit slab of a wave stays in
 // registers (MFMA accumulators) through the softmax and the block mean; only W goes out.
-//   S_iv (log2 units) = scale log2(e) q_i . c_v + log2 n_v
 //   P_iv = 2^(S_iv - max_r S_ir) / sum_r 2^(S_ir - max_r S_ir)
 //   W_uv = (1/n_u) sum_i P_iv
+// Row maxima and sums: in-lane over the wave's tiles, a 32-lane reduce-scatter (one query
+// row per lane), then across the waves through LDS.
 template <int D, int VT, bool QF32>
 __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const bf16* __restrict__ Chi,
-                                              const bf16* __restrict__ Clo, const float* __restrict__ lg,
-                                              int N, int nk, int nkp, int NQ, float scale2,
+                                              const bf16* __restrict__ Clo, int N, int nk, int nkp, int NQ,
                                               float* __restrict__ W) {
-  constexpr int QP = D + 8;
+  constexpr int DK = D + 16;       // columns of the extended product
+  constexpr int KC = DK / 16;
+  constexpr int QP = DK + 8;       // padded LDS row
   __shared__ bf16 qs[64 * QP];
   __shared__ bf16 qlo[QF32 ? 64 * QP : 8];
   __shared__ float red[8][64];
@@ -54,24 +87,27 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
   const int q0 = u * 64;
   const int nu = min(64, N - q0);
 
-  for (int e = tid; e < 64 * (D / 8); e += blockDim.x) {
-    const int row = e / (D / 8), seg = e % (D / 8);
+  for (int e = tid; e < 64 * (DK / 8); e += blockDim.x) {
+    const int row = e / (DK / 8), seg = e % (DK / 8);
     bf16x8 hi, lo;
-    if (row < nu) {
-      const size_t off = ((size_t)bh * N + q0 + row) * D + seg * 8;
-      if constexpr (QF32) {
-        const float* q = reinterpret_cast<const float*>(Qv) + off;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = (bf16)q[i];
-          lo[i] = (bf16)(q[i] - (float)hi[i]);
+    for (int i = 0; i < 8; ++i) { hi[i] = (bf16)0.0f; lo[i] = (bf16)0.0f; }
+    if (seg * 8 < D) {
+      if (row < nu) {
+        const size_t off = ((size_t)bh * N + q0 + row) * D + seg * 8;
+        if constexpr (QF32) {
+          const float* q = reinterpret_cast<const float*>(Qv) + off;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            hi[i] = (bf16)q[i];
+            lo[i] = (bf16)(q[i] - (float)hi[i]);
+          }
+        } else {
+          hi = load_bf16x8(reinterpret_cast<const bf16*>(Qv) + off);
         }
-      } else {
-        hi = load_bf16x8(reinterpret_cast<const bf16*>(Qv) + off);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { hi[i] = (bf16)0.0f; lo[i] = (bf16)0.0f; }
+    } else if (seg * 8 == D) {
+      hi[0] = (bf16)1.0f;   // multiplies the log2 n_v column
     }
     *reinterpret_cast<bf16x8*>(&qs[row * QP + seg * 8]) = hi;
     if constexpr (QF32) *reinterpret_cast<bf16x8*>(&qlo[row * QP + seg * 8]) = lo;
@@ -87,12 +123,12 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qt][vt][r] = 0.0f;
   // B operand fragments (fragment-major Chi / Clo); spare tiles past nkp re-read tile 0
-  // (their logits are set to -inf)
+  // and are masked to -inf below
   size_t crow[VT];
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt) {
     const int t = v0 + 32 * vt < nkp ? (v0 >> 5) + vt : 0;
-    crow[vt] = (size_t)bh * nkp * D + frag_lane(t, 0, lane, D);
+    crow[vt] = (size_t)bh * nkp * DK + frag_lane(t, 0, lane, DK);
   }
 
   // B fragments are prefetched one 16-column step ahead when the registers allow it
@@ -103,7 +139,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     for (int vt = 0; vt < VT; ++vt) { nhi[vt] = load_bf16x8(Chi + crow[vt]); nlo[vt] = load_bf16x8(Clo + crow[vt]); }
   }
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < KC; ++kc) {
     const int col = kc * 16 + 8 * h;
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qs[l32 * QP + col]);
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qs[(32 + l32) * QP + col]);
@@ -116,7 +152,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     if constexpr (kPrefetch) {
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) { bhi[vt] = nhi[vt]; blo[vt] = nlo[vt]; }
-      if (kc + 1 < D / 16) {
+      if (kc + 1 < KC) {
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt) {
           nhi[vt] = load_bf16x8(Chi + crow[vt] + (kc + 1) * 512);
@@ -142,20 +178,19 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       }
     }
   }
-
-  // logits in log2 units; columns outside [0, nkp) are -inf
-  float lgv[VT];
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt)
-    lgv[vt] = (v0 + 32 * vt < nkp) ? lg[(size_t)bh * nkp + v0 + 32 * vt + l32] : -INFINITY;
+    if (v0 + 32 * vt >= nkp)
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = fmaf(acc[qt][vt][r], scale2, lgv[vt]);
+        for (int r = 0; r < 16; ++r) acc[qt][vt][r] = -INFINITY;
 
-  // row maxima over this wave's clusters, then over the waves
+  // this lane's query row after the reduce-scatter: index l32 = 16 qt + r
+  const int my_row = 32 * (l32 >> 4) + c_row(l32 & 15, lane);
+  float t[32];
+
+  // row maxima
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -163,9 +198,9 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       float mx = acc[qt][0][r];
 #pragma unroll
       for (int vt = 1; vt < VT; ++vt) mx = fmaxf(mx, acc[qt][vt][r]);
-      mx = max32(mx);
-      if (l32 == 0) red[w][32 * qt + c_row(r, lane)] = mx;
+      t[16 * qt + r] = mx;
     }
+  red[w][my_row] = reduce_scatter32<true>(t, l32);
   __syncthreads();
   if (tid < 64) {
     float m = -INFINITY;
@@ -178,18 +213,22 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float m = rowm[32 * qt + c_row(r, lane)];
-      float ps = 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(&rowm[32 * qt + 8 * g + 4 * h]);
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        const float p = fast_exp2(acc[qt][vt][r] - m);
-        acc[qt][vt][r] = p;
-        ps += p;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float ps = 0.0f;
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          const float p = fast_exp2(acc[qt][vt][r] - m4[i]);
+          acc[qt][vt][r] = p;
+          ps += p;
+        }
+        t[16 * qt + r] = ps;
       }
-      ps = sum32(ps);
-      if (l32 == 0) red[w][32 * qt + c_row(r, lane)] = ps;
     }
+  red[w][my_row] = reduce_scatter32<false>(t, l32);
   __syncthreads();
   if (tid < 64) {
     float l = 0.0f;
@@ -199,6 +238,15 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
   __syncthreads();
 
   // block mean over the queries: each lane owns one cluster column per tile
+  float ri[2][16];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&rowinv[32 * qt + 8 * g + 4 * h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ri[qt][4 * g + i] = x[i];
+    }
   const float inv_nu = 1.0f / (float)nu;
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt) {
@@ -206,7 +254,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cs = fmaf(acc[qt][vt][r], rowinv[32 * qt + c_row(r, lane)], cs);
+      for (int r = 0; r < 16; ++r) cs = fmaf(acc[qt][vt][r], ri[qt][r], cs);
     cs += __shfl_xor(cs, 32);
     const int v = v0 + 32 * vt + l32;
     if (h == 0 && v < nk) W[((size_t)bh * NQ + u) * nk + v] = cs * inv_nu;
@@ -411,7 +459,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, con
 size_t retrieve_workspace(const Shape& s, bool need_scores) {
   const int nkp = nk_pad32(s.nk);
   size_t b = 0;
-  b += align256((size_t)s.BH * nkp * s.d * sizeof(bf16)) * 2;  // Chi, Clo
+  b += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)) * 2;  // Chi, Clo
   b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
   if (need_scores) b += align256((size_t)s.BH * n_qblocks(s.N) * s.nk * sizeof(float));
   return b;
@@ -419,14 +467,14 @@ size_t retrieve_workspace(const Shape& s, bool need_scores) {
 
 template <int D, bool QF32>
 static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo,
-                                const float* lg, float scale2, float* W, hipStream_t st) {
+                                float* W, hipStream_t st) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   const int vt = (nkp + 255) / 256;
   const int nw = (nkp + 32 * vt - 1) / (32 * vt);
   dim3 grid(NQ, s.BH), block(64 * nw);
   switch (vt) {
 #define PARK_PAMA_CASE(V) \
-  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, lg, s.N, s.nk, nkp, NQ, scale2, W); break;
+  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W); break;
     PARK_PAMA_CASE(1) PARK_PAMA_CASE(2) PARK_PAMA_CASE(3) PARK_PAMA_CASE(4) PARK_PAMA_CASE(5) PARK_PAMA_CASE(6)
 #undef PARK_PAMA_CASE
     default: return hipErrorInvalidValue;
@@ -439,17 +487,17 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
                            uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   char* p = static_cast<char*>(ws);
-  bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
-  bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
+  bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
+  bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
   float* lg = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * nkp * sizeof(float));
   float* W = scores ? scores : reinterpret_cast<float*>(p);
+  const float scale2 = scale * kLog2e;
   {
-    dim3 grid((nkp * s.d + 255) / 256, s.BH);
-    k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, Chi, Clo, lg);
+    dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
+    k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, scale2, Chi, Clo, lg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const float scale2 = scale * kLog2e;
   hipError_t e;
   if (pooled) {
     dim3 grid(NQ, s.BH);
@@ -460,11 +508,11 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
       k_pooled<float><<<grid, 256, shm, st>>>(reinterpret_cast<const float*>(Q), cent, lg, s.N, s.d, s.nk, nkp, NQ, scale2, W);
     e = hipGetLastError();
   } else if (s.d == 128) {
-    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, scale2, W, st)
-                     : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, scale2, W, st);
+    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, W, st)
+                     : launch_pama_d<128, true>(s, Q, Chi, Clo, W, st);
   } else {
-    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, scale2, W, st)
-                     : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, scale2, W, st);
+    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, W, st)
+                     : launch_pama_d<64, true>(s, Q, Chi, Clo, W, st);
   }
   if (e != hipSuccess) return e;
   const int rows = s.BH * NQ;
