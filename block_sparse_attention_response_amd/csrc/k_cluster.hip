@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ ci
 // compares every cluster.
 constexpr int kAsgWaves = 4;
 constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
-constexpr int kAsgCap = 16;                // list entries per key (compacted when half full)
+constexpr int kAsgCap = 12;                // list entries per key and lane half (compacted when half full)
 
 template <int D, bool KF32>
 __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ Kv, const float* __restrict__ Kt,
@@ -374,9 +374,9 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
                                                       int have_prev, int32_t* __restrict__ labels) {
   constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
-  __shared__ int lcnt[kAsgKeys];
+  __shared__ int lcnt[kAsgKeys][2];
   __shared__ int lovf[kAsgKeys];
-  __shared__ int2 lst[kAsgKeys][kAsgCap];
+  __shared__ int2 lst[kAsgKeys][2][kAsgCap];   // one list per key and lane half (one writer each)
   __shared__ float ths[kAsgKeys];
   __shared__ unsigned long long best[kAsgKeys];
   __shared__ int2 pairs[kAsgKeys * 4];
@@ -388,7 +388,6 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   const int nT = nkp >> 5;
   const bf16* gA = gneg2 + (size_t)bh * nkp * D + (size_t)lane * 8;  // this lane's piece of fragment 0
   for (int v = tid; v < nkp; v += kAsgKeys) ccs[v] = ccv[(size_t)bh * nkp + v];
-  lcnt[tid] = 0;
   lovf[tid] = 0;
   best[tid] = ~0ull;
   if (tid == 0) npairs = 0;
@@ -425,6 +424,8 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   // previous cluster (plus half the window, which covers the different summation order), an
   // upper bound of the final minimum: far fewer scores then fall inside the window.
   float mr[2] = {INFINITY, INFINITY};
+  int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
+  bool ovf[2] = {false, false};
   if (have_prev) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -489,29 +490,34 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       const float th = mr[kt] + E[kt];
       if (__any(tm <= th)) {
         const int slot = 64 * w + 32 * kt + l32;
+        int c = cnt[kt];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int v = 32 * t + c_row(r, lane);
           if (acc[kt][r] <= th && v < nk) {
-            const int c = atomicAdd(&lcnt[slot], 1);
-            if (c < kAsgCap) lst[slot][c] = make_int2(v, __float_as_int(acc[kt][r]));
-            else lovf[slot] = 1;
+            if (c < kAsgCap) lst[slot][h][c] = make_int2(v, __float_as_int(acc[kt][r]));
+            else ovf[kt] = true;
+            ++c;
           }
         }
         // the window only shrinks: drop entries that left it once a list is half full
-        if (__any(lcnt[slot] > kAsgCap / 2)) {
-          if (h == 0 && lcnt[slot] > kAsgCap / 2) {
-            const int n = min(lcnt[slot], kAsgCap);
-            int m = 0;
-            for (int c = 0; c < n; ++c) {
-              const int2 e = lst[slot][c];
-              if (__int_as_float(e.y) <= th) lst[slot][m++] = e;
-            }
-            lcnt[slot] = m;
+        if (c > kAsgCap / 2 && !ovf[kt]) {
+          int m = 0;
+          for (int e = 0; e < c; ++e) {
+            const int2 x = lst[slot][h][e];
+            if (__int_as_float(x.y) <= th) lst[slot][h][m++] = x;
           }
+          c = m;
         }
+        cnt[kt] = c;
       }
     }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int slot = 64 * w + 32 * kt + l32;
+    lcnt[slot][h] = min(cnt[kt], kAsgCap);
+    if (ovf[kt]) lovf[slot] = 1;
   }
   if (h == 0) {
     ths[64 * w + l32] = mr[0] + E[0];
@@ -523,20 +529,25 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   int n_surv = 0, only = 0;
   const int j = k0 + tid;
   {
-    const int n = min(lcnt[tid], kAsgCap);
     const float th = ths[tid];
-    for (int c = 0; c < n; ++c) {
-      const int2 e = lst[tid][c];
-      if (__int_as_float(e.y) <= th) { ++n_surv; only = e.x; }
+    for (int hh = 0; hh < 2; ++hh) {
+      const int n = lcnt[tid][hh];
+      for (int c = 0; c < n; ++c) {
+        const int2 e = lst[tid][hh][c];
+        if (__int_as_float(e.y) <= th) { ++n_surv; only = e.x; }
+      }
     }
     if (j < N && !lovf[tid] && n_surv >= 2) {
       const int base = atomicAdd(&npairs, n_surv);
       int m = 0;
-      for (int c = 0; c < n; ++c) {
-        const int2 e = lst[tid][c];
-        if (__int_as_float(e.y) <= th) {
-          if (base + m < kAsgKeys * 4) pairs[base + m] = make_int2(tid, e.x);
-          ++m;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int n = lcnt[tid][hh];
+        for (int c = 0; c < n; ++c) {
+          const int2 e = lst[tid][hh][c];
+          if (__int_as_float(e.y) <= th) {
+            if (base + m < kAsgKeys * 4) pairs[base + m] = make_int2(tid, e.x);
+            ++m;
+          }
         }
       }
     }
@@ -791,7 +802,6 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
     double t[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) t[j] = 0.0;
-#pragma unroll 8
     for (int k = 0; k < D; ++k) {
       const double r = R[(size_t)k * D + i];       // (R^T m)_i = sum_k R[k][i] m_k
 #pragma unroll
@@ -806,7 +816,6 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
     double g[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) g[j] = 0.0;
-#pragma unroll 8
     for (int k = 0; k < D; ++k) {
       const double r = Rt[(size_t)k * D + i];      // Rt[k][i] = R[i][k]: (R c~)_i
 #pragma unroll
