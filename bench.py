@@ -82,6 +82,42 @@ def cpu_baseline(cfg, Q, K, V, budget_heads=1):
     }
 
 
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_response_amd", "csrc", "k_attn.hip")
+
+
+def traffic_bytes(workload):
+    """HBM bytes per launch of the attention kernel, from the committed rocprofv3 counter
+    summary for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
+    size); None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_attn_bf16_{workload}_traffic.txt")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(gib):
+    """A plain device-to-device copy of `gib` GiB (5 launches), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters: each launch reads and writes exactly that many bytes."""
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / 5
+    print(json.dumps({"copy_bytes": n, "launches": 5, "ms_per_copy": round(dt * 1e3, 3),
+                      "GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +126,12 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload index of park_synth.CONFIGS")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--recall", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (heads would be "
               "sharded across GPUs with no exchange inside the layer).", file=sys.stderr)
@@ -119,14 +160,14 @@ def main():
     ws_a = torch.empty(park.workspace_bytes(park.OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, kev=None):
         if ev: ev[0].record(stream)
         cl = park.park_cluster_keys(q, k, nk, cfg.iters, workspace=ws_c)
         if ev: ev[1].record(stream)
         rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)
         if ev: ev[2].record(stream)
         O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
-                                             workspace=ws_a)
+                                             workspace=ws_a, events=kev.handles if kev else None)
         if ev: ev[3].record(stream)
         return cl, rb, O, lse
 
@@ -135,22 +176,25 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    kevs = [park.HipEvents() for _ in range(args.steps)]   # around the attention kernel itself
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        out = step(evs[i])
+        out = step(evs[i], kevs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cl, rb, O, lse = out
     ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     cluster_ms, retrieve_ms, attn_ms = ms.mean(0)
+    kernel_ms = float(np.mean([e.elapsed_ms() for e in kevs]))
     ms_per_step = wall * 1e3 / args.steps
     log(f"step {ms_per_step:.2f} ms: cluster {cluster_ms:.2f} retrieve {retrieve_ms:.2f} attention {attn_ms:.2f}")
 
     pairs, keys_per_block = effective_pairs(torch, cl["counts"], rb["block_list"], rb["block_count"], N)
     attn_flops = 4.0 * d * pairs
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    kernel_tflops = attn_flops / (kernel_ms * 1e-3) / 1e12
     value = attn_flops / (ms_per_step * 1e-3) / 1e12
     block_density = float(rb["block_count"].float().mean().item()) / nk
     pair_density = pairs / (B * H * float(N) * N)
@@ -177,9 +221,10 @@ def main():
         "attn_effective_tflops": round(attn_tflops, 2),
         "block_density": round(block_density, 4),
         "pair_density": round(pair_density, 4),
-        "roofline": {"bound": "mfma", "kernel": "park_block_sparse_attn (pack + k_attn_bf16<128>)", "achieved": round(attn_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": round(kernel_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(cfg.name), "kernel_ms": round(kernel_ms, 3),
+                     "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch" % (attn_flops / 1e12)},
     }
 
     if args.recall == "on":

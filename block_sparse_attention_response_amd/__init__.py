@@ -20,7 +20,7 @@ import os
 
 __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
-    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn",
+    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
     "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
@@ -65,6 +65,8 @@ def lib():
         L.park_block_sparse_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _P, _P,
                                              _P, _S, _P]
         L.park_block_sparse_attn.restype = _I
+        L.park_block_sparse_attn_timed.argtypes = L.park_block_sparse_attn.argtypes + [_P, _P]
+        L.park_block_sparse_attn_timed.restype = _I
         _lib = L
     return _lib
 
@@ -212,9 +214,10 @@ def park_retrieve_blocks_pooled(Q, centroids, counts, top_p: float, top_k: int, 
 
 
 def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scale=None, want_lse: bool = True,
-                           out=None, lse=None, workspace=None):
+                           out=None, lse=None, workspace=None, events=None):
     """Attention over the selected blocks.  Returns (O [B,H,N,d] in Q's dtype, lse [B,H,N]
-    float32 or None)."""
+    float32 or None).  `events` = (begin, end) raw hipEvent_t handles selects
+    park_block_sparse_attn_timed, which records them around the attention kernel itself."""
     torch = _torch()
     for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (perm, "perm"), (offsets, "offsets"),
                  (block_list, "block_list"), (block_count, "block_count")):
@@ -233,11 +236,45 @@ def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scal
         lse = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
     sc = -1.0 if scale is None else float(scale)
     ws, wsb = _workspace(workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), Q.device, workspace)
-    st = lib().park_block_sparse_attn(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, N, d, _ptr(perm),
-                                      _ptr(offsets), nk, _ptr(block_list), _ptr(block_count), 64, sc, _ptr(O),
-                                      _ptr(lse if want_lse else None), _ptr(ws), wsb, _stream(Q))
-    _check(st, "park_block_sparse_attn")
+    args = (_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, N, d, _ptr(perm), _ptr(offsets), nk, _ptr(block_list),
+            _ptr(block_count), 64, sc, _ptr(O), _ptr(lse if want_lse else None), _ptr(ws), wsb, _stream(Q))
+    if events is None:
+        _check(lib().park_block_sparse_attn(*args), "park_block_sparse_attn")
+    else:
+        _check(lib().park_block_sparse_attn_timed(*args, events[0], events[1]), "park_block_sparse_attn_timed")
     return O, (lse if want_lse else None)
+
+
+class HipEvents:
+    """Two HIP events for timing one kernel through park_block_sparse_attn(events=...):
+    created and read through libamdhip64 directly (torch's events only see its own calls)."""
+
+    def __init__(self):
+        import ctypes.util
+        name = ctypes.util.find_library("amdhip64") or "libamdhip64.so"
+        self._hip = ctypes.CDLL(name)
+        self.begin, self.end = ctypes.c_void_p(), ctypes.c_void_p()
+        for ev in (self.begin, self.end):
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    @property
+    def handles(self):
+        return (self.begin, self.end)
+
+    def elapsed_ms(self) -> float:
+        ms = ctypes.c_float()
+        if self._hip.hipEventSynchronize(self.end) != 0 or \
+                self._hip.hipEventElapsedTime(ctypes.byref(ms), self.begin, self.end) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            for ev in (self.begin, self.end):
+                self._hip.hipEventDestroy(ev)
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 def default_scale(d: int) -> float:

@@ -568,7 +568,7 @@ size_t attn_workspace(const Shape& s) {
 
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
-                       void* O, float* lse, void* ws, hipStream_t st) {
+                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int NQ = n_qblocks(s.N);
   const float scale2 = scale * kLog2e;
   if (s.dtype == 1) {
@@ -591,14 +591,17 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     PARK_CHECK();
     k_plan_fill<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.gstart, s.nk, NQ, rows, Gcap, w.tbase, w.plan);
     PARK_CHECK();
-#undef PARK_CHECK
     dim3 grid((unsigned)(s.BH * 8 * ((NQ + 7) / 8)));
     auto q = reinterpret_cast<const bf16*>(Q);
     auto o = reinterpret_cast<bf16*>(O);
+    if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
     if (s.d == 128)
       k_attn_bf16<128><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
     else
       k_attn_bf16<64><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
+    PARK_CHECK();
+#undef PARK_CHECK
+    if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
   } else {
     dim3 grid(NQ, s.BH);
     auto q = reinterpret_cast<const float*>(Q);

@@ -115,10 +115,10 @@ int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, i
                        scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
 }
 
-int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,
-                           const int32_t* perm, const int32_t* offsets, int n_clusters, const int32_t* block_list,
-                           const int32_t* block_count, int q_block, float scale, void* O, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+static int attn_impl(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,
+                     const int32_t* perm, const int32_t* offsets, int n_clusters, const int32_t* block_list,
+                     const int32_t* block_count, int q_block, float scale, void* O, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end) {
   bool uns;
   int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
   if (st != PARK_OK) return st;
@@ -130,8 +130,26 @@ int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtyp
   if (st != PARK_OK) return st;
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   hipError_t e = park::launch_attn(s, Q, K, V, perm, offsets, block_list, block_count, scale, O, lse, workspace,
-                                   static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
+                                   static_cast<hipEvent_t>(ev_end));
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,
+                           const int32_t* perm, const int32_t* offsets, int n_clusters, const int32_t* block_list,
+                           const int32_t* block_count, int q_block, float scale, void* O, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_impl(Q, K, V, dtype, B, H, N, d, perm, offsets, n_clusters, block_list, block_count, q_block, scale, O,
+                   lse, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int park_block_sparse_attn_timed(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N,
+                                 int d, const int32_t* perm, const int32_t* offsets, int n_clusters,
+                                 const int32_t* block_list, const int32_t* block_count, int q_block, float scale,
+                                 void* O, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* ev_begin, void* ev_end) {
+  return attn_impl(Q, K, V, dtype, B, H, N, d, perm, offsets, n_clusters, block_list, block_count, q_block, scale, O,
+                   lse, workspace, workspace_bytes, stream, ev_begin, ev_end);
 }
 
 }  // extern "C"

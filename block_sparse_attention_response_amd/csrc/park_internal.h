@@ -26,7 +26,8 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
 size_t attn_workspace(const Shape& s);
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
-                       void* O, float* lse, void* ws, hipStream_t st);
+                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin = nullptr,
+                       hipEvent_t ev_end = nullptr);
 
 // ----- key clustering
 size_t cluster_workspace(const Shape& s);

@@ -170,6 +170,20 @@ PARK_API int park_block_sparse_attn(const void* Q, const void* K, const void* V,
                            int q_block, float scale, void* O, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * park_block_sparse_attn_timed - park_block_sparse_attn for measurement: records the HIP
+ * events ev_begin and ev_end (hipEvent_t, created by the caller; either may be NULL) on
+ * `stream` immediately before and after the attention kernel itself, i.e. after the packing
+ * and tile-planning launches, so that hipEventElapsedTime gives that kernel's duration.
+ * Otherwise identical to park_block_sparse_attn (arguments, results, errors); a failed
+ * hipEventRecord is reported as HIP.
+ */
+PARK_API int park_block_sparse_attn_timed(const void* Q, const void* K, const void* V, int dtype, int B, int H,
+                                 int N, int d, const int32_t* perm, const int32_t* offsets,
+                                 int n_clusters, const int32_t* block_list, const int32_t* block_count,
+                                 int q_block, float scale, void* O, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("park_cluster_keys", "park_retrieve_blocks", "park_retrieve_blocks_pooled",
-              "park_block_sparse_attn", "park_workspace_bytes", "park_abi_version", "park_status_string"):
+              "park_block_sparse_attn", "park_block_sparse_attn_timed", "park_workspace_bytes", "park_abi_version",
+              "park_status_string"):
         assert n in names
 
 
@@ -126,3 +127,16 @@ def test_attention_rejects(lib):
     assert _attn(lib, d=32) == UNSUPPORTED
     assert _attn(lib, ws=None) == WORKSPACE
     assert _attn(lib, wsb=100) == WORKSPACE
+
+
+def test_timed_attention_rejects_like_attention(lib):
+    # the measurement variant runs the same host checks before it records any event
+    base = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=1, B=1, H=1, N=128, d=128, perm=FAKE, off=FAKE, nk=2, lst=FAKE,
+                cnt=FAKE, qb=64, scale=0.0, O=FAKE, lse=None, ws=None, wsb=0)
+    for over, want in ((dict(V=None), INVALID), (dict(qb=128), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+                       (dict(), WORKSPACE)):
+        a = dict(base, **over)
+        st = lib.park_block_sparse_attn_timed(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"],
+                                              a["perm"], a["off"], a["nk"], a["lst"], a["cnt"], a["qb"], a["scale"],
+                                              a["O"], a["lse"], a["ws"], a["wsb"], None, FAKE, FAKE)
+        assert st == want, (over, st)
