@@ -68,6 +68,28 @@ size_t cluster_workspace(const Shape& s) {
 // a1: Gram partials of bf16 queries.  One workgroup per (4096-token chunk, head); 64-token
 // sub-chunks are staged transposed in LDS; products are exact in float, each sub-chunk is
 // summed in float by the MFMA and then added into double accumulators.
+constexpr int kTfKeys = 256;   // keys per workgroup of the bf16 key transform
+
+// Sum over the 32 lanes of a wave half of v[i] (i < 16): lanes l and l ^ 1 end up holding
+// the sum for i = (l % 32) / 2 (a reduce-scatter: 16 shuffles instead of 16 x 5).
+__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int l32) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    const int mask = 16 >> step, half = 8 >> step;
+    // lanes with the mask bit keep the upper half; bitwise selects on values (a ternary on
+    // array elements would become dynamic register indexing)
+    const uint32_t sel = (l32 & mask) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + half]);
+      const float send = __uint_as_float((lo & sel) | (hi & ~sel));
+      const float keep = __uint_as_float((hi & sel) | (lo & ~sel));
+      v[i] = keep + __shfl_xor(send, mask);
+    }
+  }
+  return v[0] + __shfl_xor(v[0], 1);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_gram_bf16(const bf16* __restrict__ Q, int N, int nch, double* __restrict__ gpart) {
   constexpr int TP = 64 + 8;
@@ -239,38 +261,74 @@ __global__ __launch_bounds__(256) void k_chol(const double* G, int metric, doubl
 // float accumulation sees R to ~24 bits).  64 keys per workgroup, 4 waves.
 template <int D>
 __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__ K, const bf16* __restrict__ Rsp,
-                                                        int N, float* __restrict__ Kt) {
-  constexpr int NT = D / 32;
-  constexpr int TPW = 2 * NT / 4;
+                                                        int N, float* __restrict__ Kt, float4* __restrict__ knorm) {
+  // k~ = R^T k for kTfKeys keys per workgroup, and the key norms (|k|, 0, |k~|) on the way.
+  // Wave w computes output columns [32 ct, 32 ct + 32) (ct = w % NT) of the key tiles with
+  // parity w / NT; its B fragments (three bf16 splits of R^T for those columns) stay in
+  // registers while the keys stream through.
+  constexpr int NT = D / 32;            // 32-column output tiles
+  constexpr int KC = D / 16;
+  constexpr int PAR = 4 / NT;           // waves per output tile
+  constexpr int KTILES = kTfKeys / 32;
+  __shared__ float tpart[NT][kTfKeys];  // |k~|^2 partial sums per output tile
+  __shared__ float ksq[kTfKeys];        // |k|^2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.y, k0 = blockIdx.x * 64;
-  const bf16* rs = Rsp + (size_t)bh * 3 * D * D;
+  const int ct = w % NT, par = w / NT;
+  const int bh = blockIdx.y, k0 = blockIdx.x * kTfKeys;
+  const bf16* rs = Rsp + (size_t)bh * 3 * D * D + (size_t)(32 * ct + l32) * D + 8 * h;
+  bf16x8 bfr[3][KC];
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int id = w * TPW + j, kt = id / NT, ct = id % NT;
+  for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) bfr[sp][kc] = load_bf16x8(rs + (size_t)sp * D * D + 16 * kc);
+  const int my_row = c_row(l32 >> 1, lane);   // tile row of this lane after the reduce-scatter
+  for (int kt = par; kt < KTILES; kt += PAR) {
     const int key = k0 + 32 * kt + l32;
+    bf16x8 a[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (key < N) {
+        a[kc] = load_bf16x8(K + ((size_t)bh * N + key) * D + 16 * kc + 8 * h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[kc][i] = (bf16)0.0f;
+      }
+    }
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      bf16x8 a;
-      if (key < N) {
-        a = load_bf16x8(K + ((size_t)bh * N + key) * D + 16 * kc + 8 * h);
-      } else {
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = (bf16)0.0f;
-      }
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const bf16x8 b = load_bf16x8(rs + (size_t)s * D * D + (size_t)(32 * ct + l32) * D + 16 * kc + 8 * h);
-        acc = mfma32(a, b, acc);
-      }
-    }
+      for (int sp = 0; sp < 3; ++sp) acc = mfma32(a[kc], bfr[sp][kc], acc);
+    float sq[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = k0 + 32 * kt + c_row(r, lane);
       if (kr < N) Kt[((size_t)bh * N + kr) * D + 32 * ct + l32] = acc[r];
+      sq[r] = acc[r] * acc[r];
+    }
+    // row sums of squares over this wave's 32 columns: lanes l and l ^ 1 get row my_row
+    const float t = reduce_scatter16(sq, l32);
+    if ((l32 & 1) == 0) tpart[ct][32 * kt + my_row] = t;
+    if (ct == 0) {   // |k|^2 from the A fragments: this lane's half of key l32's row
+      float s2 = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { const float x = (float)a[kc][i]; s2 = fmaf(x, x, s2); }
+      s2 += __shfl_xor(s2, 32);
+      if (h == 0) ksq[32 * kt + l32] = s2;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kTfKeys; i += 256) {
+    const int key = k0 + i;
+    if (key < N) {
+      float t2 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NT; ++c) t2 += tpart[c][i];
+      knorm[(size_t)bh * N + key] = make_float4(sqrtf(ksq[i]), 0.0f, sqrtf(t2), 0.0f);
     }
   }
 }
@@ -890,17 +948,14 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   if (f32) {
     dim3 grid((unsigned)(((size_t)s.N * D + 255) / 256), s.BH);
     k_transform_f32<D><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(K), w.R64, s.N, w.Kt);
+    PARK_CHECK();
+    dim3 ngrid((s.N + 63) / 64, s.BH);
+    k_key_norms<float, D><<<ngrid, 256, 0, st>>>(reinterpret_cast<const float*>(K), w.Kt, s.N, w.knorm);
   } else {
-    dim3 grid((s.N + 63) / 64, s.BH);
-    k_transform_bf16<D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Rsp, s.N, w.Kt);
+    dim3 grid((s.N + kTfKeys - 1) / kTfKeys, s.BH);
+    k_transform_bf16<D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Rsp, s.N, w.Kt, w.knorm);
   }
   PARK_CHECK();
-  {
-    dim3 grid((s.N + 63) / 64, s.BH);
-    if (f32) k_key_norms<float, D><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(K), w.Kt, s.N, w.knorm);
-    else k_key_norms<bf16, D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Kt, s.N, w.knorm);
-    PARK_CHECK();
-  }
   k_km_init<D><<<dim3(w.nkp, s.BH), D, 0, st>>>(w.Kt, init_idx, s.N, s.nk, w.nkp, w.ctil);
   PARK_CHECK();
   k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, 1, w.R64, w.Rt64, w.ctil,
