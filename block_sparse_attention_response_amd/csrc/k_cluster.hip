@@ -827,22 +827,45 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
 // read from memory serves several clusters.
 template <int D>
 __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
-                                                int nk, int nkp, int init_mode, const double* __restrict__ R64,
-                                                const double* __restrict__ Rt64, float* __restrict__ ctil,
-                                                bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
-                                                float* __restrict__ ccv) {
-  constexpr int NVH = 256 / D;         // thread groups over the clusters of the tile
-  constexpr int VPT = 32 / NVH;        // clusters per thread
+                                                 int nk, int nkp, int init_mode, const double* __restrict__ R64,
+                                                 const double* __restrict__ Rt64, float* __restrict__ ctil,
+                                                 bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
+                                                 float* __restrict__ ccv) {
+  // thread (cg, dg): clusters 4 cg .. 4 cg + 3 of the 32-cluster tile, columns DPT dg .. + DPT - 1
+  constexpr int DPT = D / 32;
   __shared__ double ms[32][D + 1];     // means, then g
   __shared__ float cs[32][D + 1];
+  __shared__ int live_s[32];
   const int tid = threadIdx.x, bh = blockIdx.y, v0 = blockIdx.x * 32;
-  const int i = tid % D, vh = tid / D;
-  bool live[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int v = v0 + NVH * j + vh;
-    live[j] = v < nk && (init_mode || counts[(size_t)bh * nk + v] > 0);
+  const int cg = tid >> 5, dg = tid & 31, c0 = 4 * cg, i0 = DPT * dg;
+  if (tid < 32) {
+    const int v = v0 + tid;
+    live_s[tid] = v < nk && (init_mode || counts[(size_t)bh * nk + v] > 0);
   }
+  // acc[c][d] = sum_k M[k][i0 + d] rhs(c0 + c, k), 8 rows of M loaded ahead of their use
+  auto matvec = [&](const double* M, auto&& rhs, double (&acc)[4][DPT]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) acc[c][d] = 0.0;
+    for (int k0 = 0; k0 < D; k0 += 8) {
+      double r[8][DPT];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) r[u][d] = M[(size_t)(k0 + u) * D + i0 + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        double x[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = rhs(c0 + c, k0 + u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) acc[c][d] = fma(r[u][d], x[c], acc[c][d]);
+      }
+    }
+  };
   if (init_mode) {
     for (int e = tid; e < 32 * D; e += 256) {
       const int vv = e / D, k = e % D;
@@ -856,59 +879,62 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
       ms[vv][k] = v < nk ? cmean[((size_t)bh * nkp + v) * D + k] : 0.0;
     }
     __syncthreads();
-    const double* R = R64 + (size_t)bh * D * D;
-    double t[VPT];
+    double t[4][DPT];   // (R^T m)_i = sum_k R[k][i] m_k
+    matvec(R64 + (size_t)bh * D * D, [&](int vv, int k) { return ms[vv][k]; }, t);
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) t[j] = 0.0;
-    for (int k = 0; k < D; ++k) {
-      const double r = R[(size_t)k * D + i];       // (R^T m)_i = sum_k R[k][i] m_k
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) t[j] += r * ms[NVH * j + vh][k];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) cs[NVH * j + vh][i] = (float)t[j];
+      for (int d = 0; d < DPT; ++d) cs[c0 + c][i0 + d] = (float)t[c][d];
     __syncthreads();
   }
   {
-    const double* Rt = Rt64 + (size_t)bh * D * D;
-    double g[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) g[j] = 0.0;
-    for (int k = 0; k < D; ++k) {
-      const double r = Rt[(size_t)k * D + i];      // Rt[k][i] = R[i][k]: (R c~)_i
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) g[j] += r * (double)cs[NVH * j + vh][k];
-    }
+    double g[4][DPT];   // Rt[k][i] = R[i][k]: (R c~)_i
+    matvec(Rt64 + (size_t)bh * D * D, [&](int vv, int k) { return (double)cs[vv][k]; }, g);
     __syncthreads();  // ms is reused for g
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int vv = NVH * j + vh, v = v0 + vv;
-      ms[vv][i] = g[j];
-      if (live[j]) {
-        ctil[((size_t)bh * nkp + v) * D + i] = cs[vv][i];
-        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[j]);
-      } else if (v >= nk) {
-        gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
+    for (int c = 0; c < 4; ++c) {
+      const int vv = c0 + c, v = v0 + vv;
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) {
+        const int i = i0 + d;
+        ms[vv][i] = g[c][d];
+        if (live_s[vv]) {
+          ctil[((size_t)bh * nkp + v) * D + i] = cs[vv][i];
+          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[c][d]);
+        } else if (v >= nk) {
+          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
+        }
       }
     }
   }
   __syncthreads();
-  if (tid < 32) {
-    const int v = v0 + tid;
-    if (v >= nk) {
-      cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
-      ccv[(size_t)bh * nkp + v] = INFINITY;
-    } else if (init_mode || counts[(size_t)bh * nk + v] > 0) {
-      double cc = 0.0, gn = 0.0, f = 0.0;
-      for (int k = 0; k < D; ++k) {
-        const double c = cs[tid][k], g = ms[tid][k];
-        const double df = g - (double)(float)(bf16)(float)g;
-        cc += c * c; gn += g * g; f += df * df;
+  // per cluster |c~|^2, |g| and the bf16 rounding residual of g: 8 threads per cluster, each
+  // summing D/8 consecutive columns in order, then a fixed butterfly
+  {
+    const int vv = tid >> 3, part = tid & 7;
+    double cc = 0.0, gn = 0.0, f = 0.0;
+    for (int k = part * (D / 8); k < (part + 1) * (D / 8); ++k) {
+      const double c = cs[vv][k], g = ms[vv][k];
+      const double df = g - (double)(float)(bf16)(float)g;
+      cc += c * c; gn += g * g; f += df * df;
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      cc += __shfl_xor(cc, o);
+      gn += __shfl_xor(gn, o);
+      f += __shfl_xor(f, o);
+    }
+    const int v = v0 + vv;
+    if (part == 0) {
+      if (v >= nk) {
+        cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
+        ccv[(size_t)bh * nkp + v] = INFINITY;
+      } else if (live_s[vv]) {
+        const float up = 1.0f + 1.0f / 1048576.0f;
+        const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
+        cinfo[(size_t)bh * nkp + v] = ci;
+        ccv[(size_t)bh * nkp + v] = ci.x;
       }
-      const float up = 1.0f + 1.0f / 1048576.0f;
-      const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
-      cinfo[(size_t)bh * nkp + v] = ci;
-      ccv[(size_t)bh * nkp + v] = ci.x;
     }
   }
 }
