@@ -430,7 +430,8 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
                                                       const float4* __restrict__ knorm, const float* __restrict__ ctil,
                                                       const bf16* __restrict__ gneg2, const float* __restrict__ ccv,
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
-                                                      int have_prev, int32_t* __restrict__ labels) {
+                                                      int have_prev, const int32_t* __restrict__ order,
+                                                      int32_t* __restrict__ labels) {
   constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
   __shared__ int lcnt[kAsgKeys][2];
   __shared__ int lovf[kAsgKeys];
@@ -440,6 +441,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   __shared__ int2 pairs[kAsgKeys * 4];
   __shared__ int npairs;
   __shared__ __attribute__((aligned(16))) float ccs[PARK_MAX_CLUSTERS];
+  __shared__ int kidx[kAsgKeys];   // key index of each slot (-1 past N)
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, k0 = blockIdx.x * kAsgKeys;
@@ -448,6 +450,12 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   for (int v = tid; v < nkp; v += kAsgKeys) ccs[v] = ccv[(size_t)bh * nkp + v];
   lovf[tid] = 0;
   best[tid] = ~0ull;
+  // Slots walk the keys in `order` (the previous step's label order, so that the keys of a
+  // tile share their nearest clusters and few tiles produce candidates) or in index order.
+  {
+    const int pos = k0 + tid;
+    kidx[tid] = pos < N ? (order ? order[(size_t)bh * N + pos] : pos) : -1;
+  }
   if (tid == 0) npairs = 0;
 
   // B fragments of this wave's 64 keys (two 32-key tiles)
@@ -457,10 +465,11 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   const float CC = __uint_as_float(hmax[4 * bh + 2]);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int key = k0 + 64 * w + 32 * kt + l32;
+    const int pos = k0 + 64 * w + 32 * kt + l32;
+    const int key = pos < N ? (order ? order[(size_t)bh * N + pos] : pos) : 0;
 #pragma unroll
     for (int kc = 0; kc < NF; ++kc) {
-      if (key < N) {
+      if (pos < N) {
         const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
         if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
         else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
@@ -470,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       }
     }
     E[kt] = 0.0f;
-    if (key < N) {
+    if (pos < N) {
       const float4 kn = knorm[(size_t)bh * N + key];
       // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
       // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
@@ -487,8 +496,9 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   if (have_prev) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int key = k0 + 64 * w + 32 * kt + l32;
-      if (key < N) {
+      const int pos = k0 + 64 * w + 32 * kt + l32;
+      if (pos < N) {
+        const int key = order ? order[(size_t)bh * N + pos] : pos;
         const int vp = labels[(size_t)bh * N + key];
         float dot = 0.0f;
 #pragma unroll
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     int2 pr = make_int2(0, 0);
     if (p < npl) {
       pr = pairs[p];
-      const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + k0 + pr.x) * D + q * (D / 4));
+      const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + kidx[pr.x]) * D + q * (D / 4));
       const f32x4* y = reinterpret_cast<const f32x4*>(ctil + ((size_t)bh * nkp + pr.y) * D + q * (D / 4));
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
@@ -647,7 +657,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   for (int kl = w; kl < kAsgKeys; kl += kAsgWaves) {
     if (k0 + kl >= N) break;
     if (!lovf[kl]) continue;
-    const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + k0 + kl) * D);
+    const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + kidx[kl]) * D);
     unsigned long long bk = ~0ull;
     for (int v = lane; v < nk; v += 64) {
       const f32x4* y = reinterpret_cast<const f32x4*>(ctil + ((size_t)bh * nkp + v) * D);
@@ -671,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     if (lane == 0) best[kl] = bk;
   }
   __syncthreads();
-  if (j < N) labels[(size_t)bh * N + j] = (!slow && n_surv == 1) ? only : (int)(uint32_t)best[tid];
+  if (j < N) labels[(size_t)bh * N + kidx[tid]] = (!slow && n_surv == 1) ? only : (int)(uint32_t)best[tid];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -941,13 +951,15 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
 
 // ---------------------------------------------------------------------------------------
 template <int D>
-static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, int have_prev, int32_t* labels,
-                                hipStream_t st) {
+static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, int have_prev,
+                                const int32_t* order, int32_t* labels, hipStream_t st) {
   dim3 grid((s.N + kAsgKeys - 1) / kAsgKeys, s.BH);
   if (s.dtype == 0)
-    k_km_assign<D, true><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk, w.nkp, have_prev, labels);
+    k_km_assign<D, true><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk,
+                                                         w.nkp, have_prev, order, labels);
   else
-    k_km_assign<D, false><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk, w.nkp, have_prev, labels);
+    k_km_assign<D, false><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N,
+                                                          s.nk, w.nkp, have_prev, order, labels);
   return hipGetLastError();
 }
 
@@ -991,7 +1003,8 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   PARK_CHECK();
   const size_t shm_nk = (size_t)s.nk * sizeof(int);
   for (int it = 0; it < iters; ++it) {
-    e = launch_assign<D>(s, w, K, it > 0 ? 1 : 0, labels, st);
+    // from the second step on, the keys are visited in the previous step's label order (perm)
+    e = launch_assign<D>(s, w, K, it > 0 ? 1 : 0, it > 0 ? perm : nullptr, labels, st);
     if (e != hipSuccess) return e;
     k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
