@@ -516,24 +516,16 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   }
   __syncthreads();
 
-  // stream the 32-cluster tiles straight from memory (fragment-major: 1 KB per fragment),
-  // two tiles of A fragments in flight ahead of the MFMA work
-  bf16x8 an[NF], an2[NF];
+  // stream the 32-cluster tiles straight from memory (fragment-major: 1 KB per fragment);
+  // three named fragment buffers rotate (the loop is unrolled by 3), so tile t + 3 is loaded
+  // into the buffer of tile t as soon as its products are issued, with no register copies
+  auto load_tile = [&](int t, bf16x8 (&buf)[NF]) {
+    const int tt = min(t, nT - 1);
 #pragma unroll
-  for (int kc = 0; kc < NF; ++kc) an[kc] = load_bf16x8(gA + (size_t)kc * 512);
-  if (nT > 1) {
-#pragma unroll
-    for (int kc = 0; kc < NF; ++kc) an2[kc] = load_bf16x8(gA + ((size_t)NF + kc) * 512);
-  }
-  for (int t = 0; t < nT; ++t) {
-    bf16x8 a[NF];
-#pragma unroll
-    for (int kc = 0; kc < NF; ++kc) { a[kc] = an[kc]; an[kc] = an2[kc]; }
-    if (t + 2 < nT) {
-#pragma unroll
-      for (int kc = 0; kc < NF; ++kc) an2[kc] = load_bf16x8(gA + ((size_t)(t + 2) * NF + kc) * 512);
-    }
-    float init[16];
+    for (int kc = 0; kc < NF; ++kc) buf[kc] = load_bf16x8(gA + ((size_t)tt * NF + kc) * 512);
+  };
+  auto tile = [&](int t, bf16x8 (&a)[NF]) {
+    f32x16 init;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {  // rows 8g + 4h + 0..3 of the tile
       const f32x4 c = *reinterpret_cast<const f32x4*>(&ccs[32 * t + 8 * g + 4 * h]);
@@ -541,18 +533,20 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       for (int i = 0; i < 4; ++i) init[4 * g + i] = c[i];
     }
     f32x16 acc[2];
+    acc[0] = mfma32(a[0], bfr[0][0], init);
+    acc[1] = mfma32(a[0], bfr[1][0], init);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { acc[0][r] = init[r]; acc[1][r] = init[r]; }
-#pragma unroll
-    for (int kc = 0; kc < NF; ++kc) {
+    for (int kc = 1; kc < NF; ++kc) {
       acc[0] = mfma32(a[kc], bfr[0][kc], acc[0]);
       acc[1] = mfma32(a[kc], bfr[1][kc], acc[1]);
     }
+    load_tile(t + 3, a);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      float tm = acc[kt][0];
+      float tm = fminf(fminf(acc[kt][0], acc[kt][1]), acc[kt][2]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tm = fminf(tm, acc[kt][r]);
+      for (int r = 3; r < 15; r += 2) tm = fminf(fminf(tm, acc[kt][r]), acc[kt][r + 1]);
+      tm = fminf(tm, acc[kt][15]);
       tm = fminf(tm, __shfl_xor(tm, 32));
       mr[kt] = fminf(mr[kt], tm);
       const float th = mr[kt] + E[kt];
@@ -580,7 +574,19 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
         cnt[kt] = c;
       }
     }
+  };
+  bf16x8 fa[NF], fb[NF], fc[NF];
+  load_tile(0, fa);
+  load_tile(1, fb);
+  load_tile(2, fc);
+  int t = 0;
+  for (; t + 2 < nT; t += 3) {
+    tile(t, fa);
+    tile(t + 1, fb);
+    tile(t + 2, fc);
   }
+  if (t < nT) tile(t, fa);
+  if (t + 1 < nT) tile(t + 1, fb);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int slot = 64 * w + 32 * kt + l32;
