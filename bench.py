@@ -90,7 +90,7 @@ def traffic_bytes(workload):
     summary for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
     size); None when there is none or the kernel source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"k_attn_bf16_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"k_attn_items_{workload}_traffic.txt")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
@@ -221,7 +221,7 @@ def main():
         "attn_effective_tflops": round(attn_tflops, 2),
         "block_density": round(block_density, 4),
         "pair_density": round(pair_density, 4),
-        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16<128>", "achieved": round(kernel_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_attn_items<128>", "achieved": round(kernel_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(cfg.name), "kernel_ms": round(kernel_ms, 3),
                      "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch" % (attn_flops / 1e12)},

@@ -55,15 +55,26 @@ __device__ __forceinline__ int selected_key(int p, const int* pre, int cnt, cons
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 path, step 1: pack the keys and values of every cluster, in cluster order, into
-// 8-key groups (a cluster of n keys takes ceil(n / 8) groups; the tail of its last group is
-// zero padding).  Kp[g] is 8 key rows of D; Vp[g] is the same 8 values transposed, D rows
-// of 8 keys, which is the operand layout of the P V product.  gstart[v] is the first group
-// of cluster v (exclusive scan of ceil(n_v / 8)).
+// bf16 path.  Three kernels prepare the work:
+//  * the keys and values of every cluster are packed, in cluster order, into 8-key groups
+//    in the operand layouts of the two MFMA products;
+//  * the clusters of every head are dealt to kRanges key ranges of about equal work;
+//    range r of every head is computed on XCD r (the dispatcher deals consecutive
+//    workgroups to the 8 XCDs in turn), so each XCD's L2 serves one eighth of a head's keys
+//    and values to all query blocks of that head;
+//  * every (query block, range) pair is a work item: the groups of its selected clusters in
+//    that range, in list order, cut into 32-key tiles of 4 groups.
+// One wave per item computes a partial softmax state over its tiles (k_attn_items) and a last
+// kernel merges the kRanges partial states of every query (k_attn_merge).
+constexpr int kRanges = 8;
+
+// Step 1: gstart[v] = first group of cluster v (exclusive scan of ceil(n_v / 8)); a cluster
+// of n keys takes ceil(n / 8) groups and the tail of its last group is zero padding.
 __global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ offsets, int nk,
-                                                    int32_t* __restrict__ gstart) {
+                                                    int32_t* __restrict__ gstart, float* __restrict__ vmax) {
   __shared__ int wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, bh = blockIdx.x;
+  if (tid == 0) vmax[bh] = 0.0f;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
   const int per = (nk + 255) / 256;
   const int b0 = min(tid * per, nk), b1 = min(b0 + per, nk);
@@ -87,6 +98,38 @@ __global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ 
   if (tid == 255) gs[nk] = ex;
 }
 
+// Per-head unit of the fp16 partial outputs: the smallest power of two >= the largest |value|
+// of the head (1 for an all-zero head); a partial output is a convex combination of values,
+// so in this unit its entries lie in [-1, 1].
+__device__ __forceinline__ float value_unit(float vmax) {
+  if (!(vmax > 0.0f)) return 1.0f;
+  int ex;
+  frexpf(vmax, &ex);   // vmax = f 2^ex, f in [0.5, 1)
+  return ldexpf(1.0f, ex);
+}
+
+// vmax[bh] (zeroed by k_group_scan) = largest |value| of head bh.  Grid (blocks, BH).
+__global__ __launch_bounds__(256) void k_vmax(const bf16* __restrict__ V, size_t per_head, float* __restrict__ vmax) {
+  const int bh = blockIdx.y;
+  const bf16* Vh = V + (size_t)bh * per_head;
+  float m = 0.0f;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_head; i += (size_t)gridDim.x * 256 * 8) {
+    const bf16x8 x = load_bf16x8(Vh + i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)x[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // non-negative floats order like their bit patterns
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(reinterpret_cast<int*>(vmax) + bh, __float_as_int(m));
+}
+
+// Packed group layouts (8 keys, D columns):
+//   Kp[g] (bf16): D/16 column chunks, each 8 keys x 16 values (chunk c of key slot s at
+//          128 c + 16 s), so the A operand of S^T = K Q^T (16 columns of one key per lane)
+//          is one 16-byte load and the four groups of a tile give 1 KB per chunk;
+//   Vp[g] (bf16): D rows of 8 keys (V^T), the A operand of O^T += V^T P^T.
+// Group Gcap of every head is all zeros: the filler of partial tiles.
 template <int D>
 __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                  const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
@@ -103,7 +146,7 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
   const bf16* Vh = V + (size_t)bh * N * D;
   bf16* Kph = Kp + (size_t)bh * (Gcap + 1) * 8 * D;
   bf16* Vph = Vp + (size_t)bh * (Gcap + 1) * 8 * D;
-  if (v == 0) {  // group Gcap of every head is all zeros: the filler of partial tiles
+  if (v == 0) {
     for (int e = tid; e < D; e += 128) {
       bf16x8 z;
 #pragma unroll
@@ -123,7 +166,8 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
 #pragma unroll
       for (int i = 0; i < 8; ++i) val[i] = (bf16)0.0f;
     }
-    *reinterpret_cast<bf16x8*>(Kph + (size_t)slot * D + sg * 8) = val;
+    const int j = slot >> 3, s = slot & 7;
+    *reinterpret_cast<bf16x8*>(Kph + (size_t)j * 8 * D + (sg >> 1) * 128 + s * 16 + (sg & 1) * 8) = val;
   }
   for (int e = tid; e < ng * NS; e += 128) {
     const int j = e / NS, sg = e % NS;
@@ -148,39 +192,104 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// bf16 path, step 2: the tile plan.  For every (head, query block) the concatenation of its
-// selected clusters' groups is cut into 64-key tiles of 8 groups; plan entry (g << 4) | nv
-// names a packed group g and its number of real keys nv (0..8).  The last tile of a block is
-// filled with the all-zero group Gcap.  tbase is the exclusive scan of tiles per block.
+// Step 2: the range of every cluster.  work(v) = (query blocks selecting v) x (groups of v);
+// clusters sorted by work (ties by id) are dealt to the ranges in serpentine order
+// 0..7, 7..0, 0..7, ..., so every range gets about the same work and every query block's
+// selection spreads about evenly over the ranges.  One workgroup per head.
+__global__ __launch_bounds__(1024) void k_range_assign(const int32_t* __restrict__ list,
+                                                       const int32_t* __restrict__ count,
+                                                       const int32_t* __restrict__ offsets, int nk, int NQ,
+                                                       int32_t* __restrict__ rng) {
+  constexpr int P = 2048;   // power of two >= PARK_MAX_CLUSTERS
+  static_assert(P >= PARK_MAX_CLUSTERS, "sort size");
+  __shared__ unsigned long long key[P];
+  __shared__ int freq[PARK_MAX_CLUSTERS];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  for (int v = tid; v < nk; v += 1024) freq[v] = 0;
+  __syncthreads();
+  const int32_t* L = list + (size_t)bh * NQ * nk;
+  const int32_t* C = count + (size_t)bh * NQ;
+  for (int e = tid; e < NQ * 64; e += 1024) {
+    const int u = e >> 6;
+    const int cnt = min(max(C[u], 0), nk);
+    for (int i = e & 63; i < cnt; i += 64) {
+      const int v = L[(size_t)u * nk + i];
+      if (v >= 0 && v < nk) atomicAdd(&freq[v], 1);
+    }
+  }
+  __syncthreads();
+  const int32_t* off = offsets + (size_t)bh * (nk + 1);
+  for (int p = tid; p < P; p += 1024) {
+    unsigned long long w = 0;
+    if (p < nk) w = (unsigned long long)freq[p] * (unsigned long long)((off[p + 1] - off[p] + 7) >> 3);
+    key[p] = (w << 32) | (unsigned)(P - 1 - p);   // larger work first; equal work: lower id first
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = key[i], y = key[l];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) { key[i] = y; key[l] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int p = tid; p < P; p += 1024) {
+    const int v = P - 1 - (int)(key[p] & 0xffffffffu);
+    const int blk = p / kRanges, pos = p % kRanges;
+    if (v < nk) rng[(size_t)bh * nk + v] = (blk & 1) ? kRanges - 1 - pos : pos;
+  }
+}
+
+// Step 3: the tile plan.  Items are numbered ((b h) NQ + u) kRanges + r.  Plan entry
+// (g << 4) | nv names a packed group g and its number of real keys nv (0..8); 4 entries make
+// a 32-key tile and the last tile of an item is filled with the all-zero group Gcap.
+// tbase is the exclusive scan of tiles per item.
 __global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ list, const int32_t* __restrict__ count,
-                                                    const int32_t* __restrict__ offsets, int nk, int NQ, int rows,
-                                                    int32_t* __restrict__ ntiles) {
+                                                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ rng,
+                                                    int nk, int NQ, int rows, int32_t* __restrict__ ntiles) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const int bh = row / NQ;
   const int cnt = min(max(count[row], 0), nk);
   const int32_t* lst = list + (size_t)row * nk;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
-  int s = 0;
+  const int32_t* rg = rng + (size_t)bh * nk;
+  int s[kRanges];
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j) s[j] = 0;
   for (int i = lane; i < cnt; i += 64) {
     const int v = lst[i];
-    if (v >= 0 && v < nk) s += (off[v + 1] - off[v] + 7) >> 3;
+    if (v >= 0 && v < nk) {
+      const int ng = (off[v + 1] - off[v] + 7) >> 3, r = rg[v];
+#pragma unroll
+      for (int j = 0; j < kRanges; ++j) s[j] += r == j ? ng : 0;
+    }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) ntiles[row] = (s + 7) >> 3;
+  for (int j = 0; j < kRanges; ++j) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s[j] += __shfl_xor(s[j], o);
+  }
+  if (lane < kRanges) {
+    int x = s[0];
+#pragma unroll
+    for (int j = 1; j < kRanges; ++j) x = lane == j ? s[j] : x;
+    ntiles[(size_t)row * kRanges + lane] = (x + 3) >> 2;
+  }
 }
 
-__global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ ntiles, int rows,
-                                                    int32_t* __restrict__ tbase) {
-  __shared__ int wsum[16];
+// Exclusive scan of n ints in three launches: per-block sums (kScanBlock values per
+// workgroup), a scan of the block sums, then the in-block scans plus the block offsets.
+constexpr int kScanBlock = 4096;
+
+__device__ __forceinline__ int block_excl_scan(int x, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (rows + 1023) / 1024;
-  const int b0 = min(tid * per, rows), b1 = min(b0 + per, rows);
-  int s = 0;
-  for (int i = b0; i < b1; ++i) s += ntiles[i];
-  int incl = s;
+  int incl = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o);
@@ -188,19 +297,65 @@ __global__ __launch_bounds__(1024) void k_plan_scan(const int32_t* __restrict__ 
   }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  int ex = incl - s;
-  for (int i = 0; i < w; ++i) ex += wsum[i];
-  for (int i = b0; i < b1; ++i) {
-    tbase[i] = ex;
-    ex += ntiles[i];
+  int ex = incl - x, tot = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+    ex += i < w ? wsum[i] : 0;
+    tot += wsum[i];
   }
-  if (tid == 1023) tbase[rows] = ex;
+  *total = tot;
+  return ex;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_blocks(const int32_t* __restrict__ x, int n, int32_t* __restrict__ bsum) {
+  __shared__ int wsum[16];
+  const int b0 = blockIdx.x * kScanBlock + threadIdx.x * 4;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += b0 + i < n ? x[b0 + i] : 0;
+  int tot;
+  block_excl_scan(s, wsum, &tot);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_top(int32_t* __restrict__ bsum, int nb) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int c = 0; c < nb; c += 1024) {
+    const int i = c + threadIdx.x;
+    const int x = i < nb ? bsum[i] : 0;
+    int tot;
+    const int ex = block_excl_scan(x, wsum, &tot);
+    const int base = carry;
+    if (i < nb) bsum[i] = base + ex;
+    __syncthreads();
+    if (threadIdx.x == 0) carry = base + tot;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_scan_final(const int32_t* __restrict__ x, int n,
+                                                     const int32_t* __restrict__ boff, int32_t* __restrict__ out) {
+  __shared__ int wsum[16];
+  const int b0 = blockIdx.x * kScanBlock + threadIdx.x * 4;
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = b0 + i < n ? x[b0 + i] : 0; s += v[i]; }
+  int tot;
+  int ex = block_excl_scan(s, wsum, &tot) + boff[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (b0 + i < n) out[b0 + i] = ex;
+    ex += v[i];
+  }
+  if (b0 <= n - 1 && n - 1 < b0 + 4) out[n] = ex;   // the thread holding the last value
 }
 
 __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ list, const int32_t* __restrict__ count,
                                                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ gstart,
-                                                   int nk, int NQ, int rows, int Gcap, const int32_t* __restrict__ tbase,
-                                                   int32_t* __restrict__ plan) {
+                                                   const int32_t* __restrict__ rng, int nk, int NQ, int rows, int Gcap,
+                                                   const int32_t* __restrict__ tbase, int32_t* __restrict__ plan) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const int bh = row / NQ;
@@ -208,259 +363,528 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
   const int32_t* lst = list + (size_t)row * nk;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
   const int32_t* gs = gstart + (size_t)bh * (nk + 1);
-  int32_t* pl = plan + (size_t)tbase[row] * 8;
-  int run = 0;
+  const int32_t* rg = rng + (size_t)bh * nk;
+  const int32_t* tb = tbase + (size_t)row * kRanges;
+  int run[kRanges];   // groups placed so far in each range
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j) run[j] = 0;
   for (int i0 = 0; i0 < cnt; i0 += 64) {
     const int i = i0 + lane;
-    int n = 0, g0 = 0;
+    int n = 0, g0 = 0, r = 0;
     if (i < cnt) {
       const int v = lst[i];
-      if (v >= 0 && v < nk) { n = off[v + 1] - off[v]; g0 = gs[v]; }
+      if (v >= 0 && v < nk) { n = off[v + 1] - off[v]; g0 = gs[v]; r = rg[v]; }
     }
     const int ng = (n + 7) >> 3;
-    int incl = ng;
+    int pos = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
+    for (int j = 0; j < kRanges; ++j) {
+      const int x = r == j ? ng : 0;
+      int incl = x;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      if (r == j) pos = run[j] + incl - x;
+      run[j] += __shfl(incl, 63);
     }
-    const int ex = run + incl - ng;
-    for (int jj = 0; jj < ng; ++jj) pl[ex + jj] = ((g0 + jj) << 4) | min(8, n - 8 * jj);
-    run += __shfl(incl, 63);
+    int32_t* pl = plan + (size_t)tb[r] * 4 + pos;
+    for (int jj = 0; jj < ng; ++jj) pl[jj] = ((g0 + jj) << 4) | min(8, n - 8 * jj);
   }
-  const int end = (run + 7) & ~7;
-  for (int j = run + lane; j < end; j += 64) pl[j] = Gcap << 4;
+  // fill the tail of each range's last tile
+  if (lane < kRanges) {
+    int used = run[0];
+#pragma unroll
+    for (int j = 1; j < kRanges; ++j) used = lane == j ? run[j] : used;
+    int32_t* pl = plan + (size_t)tb[lane] * 4;
+    for (int j = used; j < 4 * (tb[lane + 1] - tb[lane]); ++j) pl[j] = Gcap << 4;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 path, step 3: attention over the planned tiles.  One workgroup (4 waves) per
-// (query block, head); wave w = 2 kw + qw owns queries 32 qw .. 32 qw + 31 of the block and
-// keys 32 kw .. 32 kw + 31 of every 64-key tile, with its own online-softmax state (the two
-// key halves are merged at the end).  Tiles are copied global -> LDS by the LDS DMA path
-// (global_load_lds_dwordx4), double-buffered: the copy of tile t+1 runs under the MFMA
-// work of tile t.  LDS holds K group-major and row-major with an XOR swizzle of the
-// 16-byte chunks (conflict-free A reads), and V^T group-major exactly as packed.
-//   S^T = K Q^T  (A: K rows in sigma16 order, B: Q^T fragments in registers; the MFMA
-//                 accumulator starts at 0 / -inf so padding keys are masked for free)
-//   O^T += V^T P^T  (A: V^T from LDS, B: P^T straight from the S^T accumulators)
-// Row swap inside each 16-row chunk (rows 4..7 <-> 8..11): with it, the 8 rows of S^T that
-// an MFMA lane holds for one 16-key chunk are 8 consecutive keys, so the matching V^T
-// operand is one 16-byte read.
+// Step 4: attention over one item's tiles.  One wave per (head, query block, key range),
+// holding all 64 queries of the block, so every K or V fragment it reads feeds two MFMAs:
+//   S^T = K Q^T      (A: 32 keys x 16 columns in bf16; B: Q^T fragments of query halves 0 and
+//                     1 in registers; the accumulators start at 0 / -inf, which masks padding)
+//   O^T += V^T P^T   (A: V^T in fp16; B: P^T straight from the S^T accumulators, as fp16)
+// Keys and values are copied memory -> LDS (global_load_lds, two tiles deep per wave) in MFMA
+// fragment order and read back one fragment per lane per MFMA.
+// Row swap inside each 16-row chunk of a tile (rows 4..7 <-> 8..11): with it, the 8 rows of
+// S^T an MFMA lane holds for one 16-key chunk are 8 consecutive keys of one group, which is
+// the P^T operand layout.
+// Softmax: probabilities are taken against a per-query reference m, set to the row maximum
+// of the first tile.  They are rounded to bf16 for the P V product; the sum of exactly those
+// bf16 weights (v_dot2, accumulated in float) normalises O, and the float sum of the
+// unrounded probabilities gives the log-sum-exp.  The reference only moves (with a rescale of
+// the accumulators) when a lane's float sum for a tile leaves [0, 2^60]; the row maximum is
+// then recovered from the probabilities themselves (m + log2 of the largest), and only if
+// one overflowed float are the scores recomputed.  The partial state of the item is
+// O_r = O^T / lb in fp16 (in units of the head's value unit, so |O_r| <= 1), and
+// (m, l, unit) with l the float sum.
 __device__ __forceinline__ int sigma16(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 
-typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef __attribute__((address_space(1))) void* gbl_vptr;
-
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_wave_base, 16, 0, 0);
+// global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
+// Written as inline assembly so that the compiler does not guard every later LDS read with
+// a wait for all outstanding copies: the kernel waits for exactly the copies it needs
+// (s_waitcnt vmcnt; copies complete in issue order).  The instruction has no register
+// results; the scalar base carries the per-instruction displacement, so a batch of copies
+// needs one lane offset and no vector address arithmetic.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
+// the same with 4 bytes per lane (lane i writes lds + 4 i)
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// all LDS reads issued so far have returned (before a copy overwrites what they read)
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
-                                                      const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
-                                                      const int32_t* __restrict__ tbase, int N, int NQ, int Gcap,
-                                                      float scale2, bf16* __restrict__ O, float* __restrict__ lse) {
-  constexpr int NS = D / 8;        // 16-byte chunks per K row
-  constexpr int GE = 8 * D;        // bf16 elements per group (K or V)
-  constexpr int CPG = GE / 8 / 64; // DMA instructions (64 lanes x 16 B) per group
-  // Four distinct LDS objects, so the compiler can tell the tile being computed from the one
-  // the DMA is filling and does not wait for the copy before reading.
-  __shared__ __attribute__((aligned(16))) bf16 K0[64 * D];   // rows, chunk c of row R at (c ^ (R % NS))
-  __shared__ __attribute__((aligned(16))) bf16 K1[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16 V0[64 * D];   // [8 groups][D][8]
-  __shared__ __attribute__((aligned(16))) bf16 V1[64 * D];
+__global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
+                                                   const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
+                                                   const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
+                                                   int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
+                                                   float4* __restrict__ ML) {
+  constexpr int KC = D / 16, DT = D / 32;
+  constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
+  static_assert(KC == 2 * DT, "K and V batches have the same size");
+  // Two tiles of keys and values in MFMA fragment order (fragment f of lane i at [b][f][i] for
+  // buffer b = tile parity)
+  __shared__ bf16x8 Ks[2][KC][64];
+  __shared__ bf16x8 Vs[2][2 * DT][64];
+  // plan entries in flight: slot s holds the 16 tiles from the one its copy started at
+  __shared__ __attribute__((aligned(16))) int32_t pring[4][64];
   __shared__ __attribute__((aligned(16))) float btab[9][8];
-
-  int bh, u;
-  if (!xcd_head_sync(blockIdx.x, NQ, &bh, &u)) return;
-  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw = w & 1, kw = w >> 1;
-  const int row = bh * NQ + u;
-  const int t0 = tbase[row];
-  const int nt = tbase[row + 1] - t0;
-  const int32_t* pl = plan + (size_t)t0 * 8;
-  const bf16* Kph = Kp + (size_t)bh * (Gcap + 1) * GE;
-  const bf16* Vph = Vp + (size_t)bh * (Gcap + 1) * GE;
-
-  if (tid < 72) btab[tid >> 3][tid & 7] = (tid & 7) < (tid >> 3) ? 0.0f : -INFINITY;
-
-  // copy tile t into (Kb, Vb): wave w moves groups 2w and 2w+1 (K and V)
-  auto issue = [&](int t, bf16* Kb, bf16* Vb) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gi = 2 * w + j;
-      const int g = pl[8 * t + gi] >> 4;
-      const bf16* ksrc = Kph + (size_t)g * GE;
-      const bf16* vsrc = Vph + (size_t)g * GE;
-#pragma unroll
-      for (int c = 0; c < CPG; ++c) {
-        const int pc = 64 * c + lane;            // physical chunk within the group
-        const int r = pc / NS, R = 8 * gi + r;   // row within group / tile
-        const int seg = (pc % NS) ^ (R % NS);    // logical chunk stored there
-        dma16(ksrc + r * D + seg * 8, Kb + (size_t)gi * GE + c * 512);
-        dma16(vsrc + pc * 8, Vb + (size_t)gi * GE + c * 512);
-      }
-    }
-  };
-
-  const int qrow = 64 * u + 32 * qw + l32;
-  const bool qvalid = qrow < N;
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    if (qvalid) {
-      qf[kc] = load_bf16x8(Q + ((size_t)bh * N + qrow) * D + kc * 16 + 8 * h);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[kc][i] = (bf16)0.0f;
-    }
+  const int item = blockIdx.x;
+  const int rr = item % kRanges, row = item / kRanges;
+  const int bh = row / NQ, u = row - bh * NQ;
+  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
+  for (int i = lane; i < 72; i += 64) btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
+  const int t0 = tbase[item];
+  const int nt = tbase[item + 1] - t0;
+  const size_t hrow = (size_t)bh * N;
+  if (nt <= 0) {
+    const int q = 64 * u + lane;
+    if (q < N) ML[(hrow + q) * kRanges + rr] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+    return;
   }
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-  constexpr float kNoMax = -1e30f;
-  const float kBig = __builtin_amdgcn_ldexpf(1.0f, 60);
-  float m = kNoMax, lsum = 0.0f;
-  // lacc: V^T P^T with V^T replaced by ones, i.e. the row sums of the bf16 weights that the
-  // PV product used (every element of a lane holds its query's sum); O is normalised by it,
-  // the log-sum-exp by the float sum lsum
-  f32x16 lacc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
-  const int arow = 32 * kw + 16 * (l32 >> 4) + sigma16(l32 & 15);
-  const int aswz = arow % NS;
+  const int32_t* pl = plan + (size_t)t0 * 4;
+  const char* Kb = reinterpret_cast<const char*>(Kp + (size_t)bh * (Gcap + 1) * 8 * D);
+  const char* Vb = reinterpret_cast<const char*>(Vp + (size_t)bh * (Gcap + 1) * 8 * D);
+  // A row l32 of S^T is tile key kk: group kk / 8 of the tile, slot kk % 8
+  const int kk = 16 * (l32 >> 4) + sigma16(l32 & 15);
+  const int kj = kk >> 3;
+  const uint32_t koff = (uint32_t)((kk & 7) * 32 + h * 16);
+  const uint32_t voff = (uint32_t)(l32 * 16);
 
-  auto compute = [&](int t, const bf16* Kb, const bf16* Vb) {
-    // plan entries through the scalar path (wave-uniform addresses)
-    const int* pt = pl + __builtin_amdgcn_readfirstlane(8 * t + 4 * kw);
-    const int e0 = pt[0], e1 = pt[1], e2 = pt[2], e3 = pt[3];
-    // lane element r = 8c + i is key 32 kw + 16 c + 8 h + i: slot i of group 4 kw + 2 c + h
-    const int nv0 = (h ? e1 : e0) & 15, nv1 = (h ? e3 : e2) & 15;
-    f32x16 sacc;
-    {
-      const f32x4* b0 = reinterpret_cast<const f32x4*>(&btab[nv0][0]);
-      const f32x4* b1 = reinterpret_cast<const f32x4*>(&btab[nv1][0]);
-      const f32x4 x0 = b0[0], x1 = b0[1], x2 = b1[0], x3 = b1[1];
+  // plan entries of tile t (clamped to the item, so copies past its last tile read that tile
+  // again; they are never used)
+  auto entries = [&](int t) __attribute__((always_inline)) {
+    const int4 e = *reinterpret_cast<const int4*>(pl + 4 * min(t, nt - 1));
+    return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                     __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+  };
+  // group ids are clamped to the head's packed groups: entries copied from past an item's
+  // plan (only ever used for unused copies) may hold anything
+  auto key_offset = [&](const int4& e) __attribute__((always_inline)) {
+    const int g01 = (kj & 1) ? e.y : e.x, g23 = (kj & 1) ? e.w : e.z;
+    return (uint32_t)min((uint32_t)((kj & 2) ? g23 : g01) >> 4, (uint32_t)Gcap) * GB + koff;
+  };
+  auto lds_addr = [](const void* p) __attribute__((always_inline)) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  };
+  // copies of a tile's keys (A operands of S^T) and values (A operands of O^T)
+  auto copy_k = [&](int t, const int4& e) __attribute__((always_inline)) {
+    const uint32_t off = key_offset(e);
+    const uint32_t dst = lds_addr(&Ks[t & 1][0][0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { sacc[i] = x0[i]; sacc[4 + i] = x1[i]; sacc[8 + i] = x2[i]; sacc[12 + i] = x3[i]; }
-    }
-    const bf16* kb = Kb + arow * D;
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (((2 * kc + h) ^ aswz) * 8));
-      sacc = mfma32(a, qf[kc], sacc);
-    }
-    // probabilities against the running reference m; the reference only moves (with a
-    // rescale of the accumulators) when a row sum leaves [0, 2^60], which happens on the
-    // first tile (m starts at -1e30) and when a score exceeds m by about 60 (log2 units)
-    f32x16 pr;
-    float ps;
-    auto probs = [&]() {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[r], scale2, -m));
-      const float s0 = (pr[0] + pr[1]) + (pr[2] + pr[3]), s1 = (pr[4] + pr[5]) + (pr[6] + pr[7]);
-      const float s2 = (pr[8] + pr[9]) + (pr[10] + pr[11]), s3 = (pr[12] + pr[13]) + (pr[14] + pr[15]);
-      ps = (s0 + s1) + (s2 + s3);
-    };
-    probs();
-    if (__builtin_expect(__any(!(ps <= kBig)), 0)) {
-      asm volatile("" ::: "memory");   // keep this rare path a branch (no if-conversion)
-      float mx = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
-      const float mnew = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      m = mnew;
-      probs();
-    }
-    lsum += ps;
+    for (int kc = 0; kc < KC; ++kc) dma16(Kb + kc * 256, off, dst + kc * 1024);
+  };
+  auto copy_v = [&](int t, const int4& e) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      bf16x8 pb;
+      const int g = c ? (h ? e.w : e.z) : (h ? e.y : e.x);
+      const uint32_t off = min((uint32_t)g >> 4, (uint32_t)Gcap) * GB + voff;
+      const uint32_t dst = lds_addr(&Vs[t & 1][c * DT][0]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (bf16)pr[8 * c + i];
-      const bf16* vg = Vb + (size_t)(4 * kw + 2 * c + h) * GE;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vg + (32 * dt + l32) * 8);
-        oacc[dt] = mfma32(a, pb, oacc[dt]);
-      }
-      lacc = mfma32(ones, pb, lacc);
+      for (int dt = 0; dt < DT; ++dt) dma16(Vb + dt * 512, off, dst + dt * 1024);
     }
   };
 
-  if (nt > 0) issue(0, K0, V0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < nt; t += 2) {
-    if (t + 1 < nt) issue(t + 1, K1, V1);
-    compute(t, K0, V0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 >= nt) break;
-    if (t + 2 < nt) issue(t + 2, K0, V0);
-    compute(t + 1, K1, V1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // copy of the plan entries of tiles t .. t + 15 into ring slot t & 3 (one dword per lane)
+  auto copy_plan = [&](int t) __attribute__((always_inline)) {
+    dma4(pl, (uint32_t)(4 * t + lane) * 4u, lds_addr(&pring[t & 3][0]));
+  };
+  auto ring_entries = [&](int slot, int j) __attribute__((always_inline)) {
+    return *reinterpret_cast<const int4*>(&pring[slot][4 * j]);
+  };
+
+  // Q^T fragments of query halves 0 and 1 in registers
+  bf16x8 qf[2][KC];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int qrow = 64 * u + 32 * h2 + l32;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (qrow < N) {
+        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow) * D + kc * 16 + 8 * h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[h2][kc][i] = (bf16)0.0f;
+      }
+    }
   }
 
-  // merge the two key halves: waves kw = 1 hand (m, l, O^T) to waves kw = 0 through LDS
-  float* xo = reinterpret_cast<float*>(K0);  // K0 and K1 hold 2 waves x 64 lanes x D/2 floats
-  float* xm = reinterpret_cast<float*>(V0);  // 2 waves x 64 lanes x (m, l, l of the bf16 weights)
-  auto xo_at = [&](int qq, int ln, int k) -> float* {  // lane-contiguous: no bank conflicts
-    const int idx = k * 128 + qq * 64 + ln;
-    return idx < 32 * D ? xo + idx : reinterpret_cast<float*>(K1) + (idx - 32 * D);
+  f32x16 oacc[2][DT];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[h2][dt][r] = 0.0f;
+  // per lane and query half: reference m (log2 units), float sum of the probabilities (for
+  // the log-sum-exp) and sum of the bf16 weights the P V product used (O normalisation)
+  float m[2], lsum[2], lb[2];
+  const float kBig = __builtin_amdgcn_ldexpf(1.0f, 60);
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+
+  // Scores and probabilities share registers: sc holds S^T of a tile after its MFMAs and,
+  // after the exponentials (taken in place), its probabilities.  The accumulators start at 0
+  // for real keys and -inf for padding (lane element r < 8 is slot r of group h, element
+  // 8 + r slot r of group 2 + h).
+  f32x16 sc[2];
+  auto init_scores = [&](const int4& e) __attribute__((always_inline)) {
+    const int nva = (h ? e.y : e.x) & 15, nvb = (h ? e.w : e.z) & 15;
+    const f32x4* b0 = reinterpret_cast<const f32x4*>(&btab[nva][0]);
+    const f32x4* b1 = reinterpret_cast<const f32x4*>(&btab[nvb][0]);
+    const f32x4 x0 = b0[0], x1 = b0[1], x2 = b1[0], x3 = b1[1];
+    f32x16 init;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { init[i] = x0[i]; init[4 + i] = x1[i]; init[8 + i] = x2[i]; init[12 + i] = x3[i]; }
+    return init;
   };
-  if (kw == 1) {
-    xm[(qw * 64 + lane) * 3] = m;
-    xm[(qw * 64 + lane) * 3 + 1] = lsum;
-    xm[(qw * 64 + lane) * 3 + 2] = lacc[0];
+  // scores of tile t into out; from_lds: keys from the tile's LDS buffer, otherwise straight
+  // from the packed groups (the rare rescale path, when the buffer may be refilled already)
+  auto scores = [&](int t, bool from_lds, f32x16 (&out)[2]) __attribute__((always_inline)) {
+    const int4 e = entries(t);
+    out[0] = init_scores(e);
+    out[1] = out[0];
+    const char* src = Kb + key_offset(e);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int kc = 0; kc < KC; ++kc) {
+      const bf16x8 a = from_lds ? Ks[t & 1][kc][lane] : *reinterpret_cast<const bf16x8*>(src + kc * 256);
+      out[0] = mfma32(a, qf[0][kc], out[0]);
+      out[1] = mfma32(a, qf[1][kc], out[1]);
+    }
+  };
+  auto prob = [&](float x, int h2) __attribute__((always_inline)) { return fast_exp2(fmaf(x, scale2, -m[h2])); };
+  // bf16 weights of the probabilities in sc
+  auto to_bf16 = [&](bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) *xo_at(qw, lane, 16 * dt + r) = oacc[dt][r];
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[h2][c][i] = (bf16)sc[h2][8 * c + i];
+  };
+  auto weight_sums = [&](const bf16x8 (&pb)[2][2], float (&wb)[2], int h2) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pair = {pb[h2][c][2 * i], pb[h2][c][2 * i + 1]};
+        wb[h2] = __builtin_amdgcn_fdot2_f32_bf16(pair, one2, wb[h2], false);
+      }
+  };
+  // Tile t's probabilities are in sc, their per-lane float sums in ps, their bf16 weights in pb
+  // with sums wb.  Final unless a float sum left [0, 2^60]: then m moves to the row maximum
+  // where that is larger (recovered from the probabilities, or from recomputed scores if one
+  // overflowed), the accumulators are rescaled, and the tile's weights are rescaled with them.
+  // Adds the tile to lsum and lb.
+  auto settle = [&](int t, bf16x8 (&pb)[2][2], float (&ps)[2], float (&wb)[2]) __attribute__((always_inline)) {
+    if (__builtin_expect(__any(!(ps[0] <= kBig) || !(ps[1] <= kBig)), 0)) {
+      asm volatile("" ::: "memory");   // keep this rare path a branch (no if-conversion)
+      float pmax[2];
+      bool finite = true;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float x = sc[h2][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) x = fmaxf(x, sc[h2][r]);
+        pmax[h2] = fmaxf(x, __shfl_xor(x, 32));
+        finite = finite && pmax[h2] <= 3.0e38f;
+      }
+      float mx[2];
+      if (__all(finite)) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) mx[h2] = m[h2] + __log2f(pmax[h2]);
+      } else {
+        f32x16 st[2];
+        scores(t, false, st);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float x = st[h2][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) x = fmaxf(x, st[h2][r]);
+          mx[h2] = fmaxf(x, __shfl_xor(x, 32)) * scale2;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[h2][r] = fast_exp2(fmaf(st[h2][r], scale2, -mx[h2]));
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float mnew = fmaxf(m[h2], mx[h2]);
+        const float alpha = fast_exp2(m[h2] - mnew);
+        const float beta = __all(finite) ? alpha : fast_exp2(mx[h2] - mnew);
+        lsum[h2] *= alpha;
+        lb[h2] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[h2][dt][r] *= alpha;
+        m[h2] = mnew;
+        ps[h2] = 0.0f;
+        wb[h2] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[h2][r] *= beta;
+          ps[h2] += sc[h2][r];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pb[h2][c][i] = (bf16)sc[h2][8 * c + i];
+      }
+      weight_sums(pb, wb, 0);
+      weight_sums(pb, wb, 1);
+    }
+    lsum[0] += ps[0];
+    lsum[1] += ps[1];
+    lb[0] += wb[0];
+    lb[1] += wb[1];
+  };
+
+  // One pipeline step (tile t + 1 exists): tile t's fp16 weights are in pb (settled) and its
+  // values in LDS buffer t & 1, tile t + 1's keys in buffer (t + 1) & 1.  In the order written
+  // (scheduling fences keep it; with one wave per SIMD the matrix and vector units overlap
+  // only through this interleave):
+  //   A1: S^T MFMAs of tile t + 1, query half 0;
+  //   A2: S^T MFMAs of tile t + 1, query half 1, with the exponentials of half 0;
+  //   B:  P V MFMAs of tile t (O^T += V^T P^T) with the exponentials of half 1 and the fp16
+  //       conversion and weight sums of half 0;
+  //   then the conversion and sums of half 1 and the check of tile t + 1's weights (the rare
+  //   rescale), leaving them settled in pb.
+  // Each buffer is refilled as soon as its reads have returned: the keys of t + 3 in A1, the
+  // values of t + 2 in B.  Copies are issued in the order P1 P2 P3 K0 V0 K1 V1 K2 | P4 K3 V2 |
+  // P5 K4 V3 | ... (K, V: batches of KC instructions; P: one plan copy), so at the start of
+  // step t, after its plan copy, leaving 2 KC + 1 copies in flight completes K(t + 1), V(t) and
+  // the plan copy of tile t + 1 (issued three steps before).
+  constexpr int kNPV = 4 * DT;             // P V MFMAs: 2 key chunks x DT x 2 query halves
+  constexpr int kCopyK = KC / 2;           // A1 chunk that refills the key buffer
+  constexpr int kCopyV = kNPV / 2 + 2;     // B chunk that refills the value buffer
+  bf16x8 pb[2][2];
+  auto step = [&](int t) __attribute__((always_inline)) {
+    const bf16x8 (&Vx)[2 * DT][64] = Vs[t & 1];
+    const bf16x8 (&Ky)[KC][64] = Ks[(t + 1) & 1];
+    copy_plan(t + 4);
+    wait_copies<2 * KC + 1>();
+    const int4 e1 = ring_entries((t + 1) & 3, 0), e2 = ring_entries((t + 1) & 3, 1),
+               e3 = ring_entries((t + 1) & 3, 2);
+    const f32x16 init = init_scores(e1);
+    bf16x8 kf[KC], vf[2 * DT];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) kf[kc] = Ky[kc][lane];
+    __builtin_amdgcn_sched_barrier(0);
+    // A1
+    sc[0] = init;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (kc == kCopyK) {
+        wait_lds_reads();
+        copy_k(t + 3, e3);
+      }
+      sc[0] = mfma32(kf[kc], qf[0][kc], sc[0]);
+      if (kc < 2) vf[kc] = Vx[kc][lane];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // A2: the 16 exponentials (and float sums) of half 0
+    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    sc[1] = init;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      sc[1] = mfma32(kf[kc], qf[1][kc], sc[1]);
+#pragma unroll
+      for (int r = kc * 16 / KC; r < (kc + 1) * 16 / KC; ++r) {
+        sc[0][r] = prob(sc[0][r], 0);
+        acc[0][r & 1] += sc[0][r];
+      }
+      if (kc + 2 < 2 * DT && kc < 2) vf[kc + 2] = Vx[kc + 2][lane];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B: 16 exponentials (and sums) of half 1, then 8 conversions (pairs) and 8 weight sums of
+    // half 0
+    bf16x8 pn[2][2];
+    float wn[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kNPV; ++j) {
+      const int c = j / (2 * DT), dt = (j / 2) % DT, h2 = j & 1;
+      if ((j & 1) == 0 && j / 2 + 4 < 2 * DT) vf[j / 2 + 4] = Vx[j / 2 + 4][lane];
+      if (j == kCopyV) {
+        wait_lds_reads();
+        copy_v(t + 2, e2);
+      }
+      oacc[h2][dt] = mfma32(vf[c * DT + dt], pb[h2][c], oacc[h2][dt]);
+#pragma unroll
+      for (int w = j * 32 / kNPV; w < (j + 1) * 32 / kNPV; ++w) {
+        if (w < 16) {
+          sc[1][w] = prob(sc[1][w], 1);
+          acc[1][w & 1] += sc[1][w];
+        } else if (w < 24) {
+          const int cc = (w - 16) >> 2, i = (w - 16) & 3;
+          pn[0][cc][2 * i] = (bf16)sc[0][8 * cc + 2 * i];
+          pn[0][cc][2 * i + 1] = (bf16)sc[0][8 * cc + 2 * i + 1];
+        } else {
+          const int cc = (w - 24) >> 2, i = (w - 24) & 3;
+          const bf16x2 pair = {pn[0][cc][2 * i], pn[0][cc][2 * i + 1]};
+          wn[0] = __builtin_amdgcn_fdot2_f32_bf16(pair, one2, wn[0], false);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pn[1][c][i] = (bf16)sc[1][8 * c + i];
+    weight_sums(pn, wn, 1);
+    float ps[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
+    settle(t + 1, pn, ps, wn);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pb[h2][c] = pn[h2][c];
+  };
+  // the last tile t: P V
+  auto last = [&](int t) __attribute__((always_inline)) {
+    const bf16x8 (&Vx)[2 * DT][64] = Vs[t & 1];
+    wait_copies<2 * KC>();
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = Vx[c * DT + dt][lane];
+        oacc[0][dt] = mfma32(a, pb[0][c], oacc[0][dt]);
+        oacc[1][dt] = mfma32(a, pb[1][c], oacc[1][dt]);
+      }
+  };
+
+  {
+    const int4 e0 = entries(0), e1 = entries(1);
+    copy_plan(1);
+    copy_plan(2);
+    copy_plan(3);
+    copy_k(0, e0);
+    copy_v(0, e0);
+    copy_k(1, e1);
+    copy_v(1, e1);
   }
-  __syncthreads();
-  if (kw == 0) {
-    const float m1 = xm[(qw * 64 + lane) * 3], l1 = xm[(qw * 64 + lane) * 3 + 1];
-    const float lb1 = xm[(qw * 64 + lane) * 3 + 2];
-    const float mt = fmaxf(m, m1);
-    const float a0 = fast_exp2(m - mt), a1 = fast_exp2(m1 - mt);
-    float l = lsum * a0 + l1 * a1;
-    l += __shfl_xor(l, 32);
-    const float lb = lacc[0] * a0 + lb1 * a1;   // already summed over both lane halves
-    const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
-    if (qvalid) {
-      bf16* orow = O + ((size_t)bh * N + qrow) * D;
+  wait_copies<3 * KC>();
+  // tile 0: m starts at the row maximum of its scores (every tile holds a real key), so its
+  // probabilities are at most 1 and need no check
+  scores(0, true, sc);
+  wait_lds_reads();
+  copy_k(2, entries(2));
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float mx = sc[h2][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[h2][r]);
+    m[h2] = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
+    lsum[h2] = 0.0f;
+    lb[h2] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[h2][r] = prob(sc[h2][r], h2);
+      lsum[h2] += sc[h2][r];
+    }
+  }
+  to_bf16(pb);
+  weight_sums(pb, lb, 0);
+  weight_sums(pb, lb, 1);
+  for (int t = 0; t + 1 < nt; ++t) step(t);
+  last(nt - 1);
+  // no copy may still be writing this workgroup's LDS when the wave ends
+  wait_copies<0>();
+
+  // partial state: O_r = O^T / lb stored as fp16 in units of the head's value unit (so
+  // |stored| <= 1), and (m, l, unit) in float
+  const float unit = value_unit(vmax[bh]);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const float l = lsum[h2] + __shfl_xor(lsum[h2], 32);
+    const float lbs = lb[h2] + __shfl_xor(lb[h2], 32);
+    const int qrow = 64 * u + 32 * h2 + l32;
+    if (qrow < N) {
+      const float inv = lbs > 0.0f ? 1.0f / (lbs * unit) : 0.0f;
+      f16* orow = Opart + ((hrow + qrow) * kRanges + rr) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          bf16x4 o;
+          f16x4 o;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            o[i] = (bf16)((oacc[dt][r] * a0 + *xo_at(qw, lane, 16 * dt + r) * a1) * inv);
-          }
-          *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
+          for (int i = 0; i < 4; ++i) o[i] = (f16)(oacc[h2][dt][4 * g + i] * inv);
+          *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
-      if (lse && h == 0) lse[(size_t)bh * N + qrow] = l > 0.0f ? (mt + __log2f(l)) * kLn2 : -INFINITY;
+      if (h == 0) ML[(hrow + qrow) * kRanges + rr] = make_float4(m[h2], l, unit, 0.0f);
     }
   }
+}
+
+// Step 5: merge the kRanges partial states of every query:
+//   M = max_r m_r,  w_r = l_r 2^(m_r - M),  O = sum_r w_r O_r / sum_r w_r,
+//   lse = ln 2 (M + log2 sum_r w_r); ranges with l_r = 0 contribute nothing (their O_r is
+// never read).  D / 8 threads per query, 8 columns each.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_merge(const f16* __restrict__ Opart, const float4* __restrict__ ML,
+                                                    int rows, bf16* __restrict__ O, float* __restrict__ lse) {
+  constexpr int TPQ = D / 8;
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  const int q = gt / TPQ, part = gt % TPQ;
+  if (q >= rows) return;
+  float4 st[kRanges];
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j) {
+    st[j] = ML[(size_t)q * kRanges + j];
+    if (st[j].y > 0.0f) M = fmaxf(M, st[j].x);
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  float wsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j) {
+    if (st[j].y > 0.0f) {
+      const float w = st[j].y * fast_exp2(st[j].x - M);
+      wsum += w;
+      const float ws = w * st[j].z;
+      const f16x8 o = *reinterpret_cast<const f16x8*>(Opart + ((size_t)q * kRanges + j) * D + part * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, (float)o[i], acc[i]);
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  bf16x8 out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8*>(O + (size_t)q * D + part * 8) = out;
+  if (lse && part == 0) lse[q] = wsum > 0.0f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -535,26 +959,37 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q, c
 }
 
 static inline int group_cap(const Shape& s) { return (s.N + 7) / 8 + s.nk; }
-// most 64-key tiles one query block can need (every cluster selected)
-static inline int max_tiles_per_block(const Shape& s) { return (group_cap(s) + 7) / 8; }
 
 struct AttnWs {
-  int32_t *gstart, *ntiles, *tbase, *plan;
+  int32_t *gstart, *rng, *ntiles, *tbase, *bsum, *plan;
+  float* vmax;
   bf16 *Kp, *Vp;
+  f16* Opart;
+  float4* ML;
 };
 
 static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
-  const int rows = s.BH * n_qblocks(s.N);
+  const size_t rows = (size_t)s.BH * n_qblocks(s.N);
+  const size_t items = rows * kRanges;
   const size_t kv = (size_t)s.BH * (group_cap(s) + 1) * 8 * s.d * sizeof(bf16);
+  // plan entries of one query block: at most every group of its head, plus the filler of
+  // one partial tile per range
+  const size_t per_row = (size_t)group_cap(s) + 4 * kRanges;
   char* p = static_cast<char*>(base);
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
   AttnWs w;
   w.gstart = reinterpret_cast<int32_t*>(take((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)));
-  w.ntiles = reinterpret_cast<int32_t*>(take((size_t)rows * sizeof(int32_t)));
-  w.tbase = reinterpret_cast<int32_t*>(take((size_t)(rows + 1) * sizeof(int32_t)));
-  w.plan = reinterpret_cast<int32_t*>(take((size_t)rows * max_tiles_per_block(s) * 8 * sizeof(int32_t)));
+  w.rng = reinterpret_cast<int32_t*>(take((size_t)s.BH * s.nk * sizeof(int32_t)));
+  w.vmax = reinterpret_cast<float*>(take((size_t)s.BH * sizeof(float)));
+  w.ntiles = reinterpret_cast<int32_t*>(take(items * sizeof(int32_t)));
+  w.tbase = reinterpret_cast<int32_t*>(take((items + 1) * sizeof(int32_t)));
+  w.bsum = reinterpret_cast<int32_t*>(take(((items + kScanBlock - 1) / kScanBlock) * sizeof(int32_t)));
+  // + slack: the attention kernel copies plan entries up to 80 dwords past an item's end
+  w.plan = reinterpret_cast<int32_t*>(take((rows * per_row + 128) * sizeof(int32_t)));
   w.Kp = reinterpret_cast<bf16*>(take(kv));
   w.Vp = reinterpret_cast<bf16*>(take(kv));
+  w.Opart = reinterpret_cast<f16*>(take((size_t)s.BH * s.N * kRanges * s.d * sizeof(f16)));
+  w.ML = reinterpret_cast<float4*>(take((size_t)s.BH * s.N * kRanges * sizeof(float4)));
   if (total) *total = (size_t)(p - static_cast<char*>(base));
   return w;
 }
@@ -574,34 +1009,50 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
   if (s.dtype == 1) {
     const int Gcap = group_cap(s);
     const int rows = s.BH * NQ;
+    const int items = rows * kRanges;
     AttnWs w = carve_attn(s, ws, nullptr);
     auto k = reinterpret_cast<const bf16*>(K);
     auto v = reinterpret_cast<const bf16*>(V);
+    auto q = reinterpret_cast<const bf16*>(Q);
+    auto o = reinterpret_cast<bf16*>(O);
     hipError_t e;
 #define PARK_CHECK() do { e = hipGetLastError(); if (e != hipSuccess) return e; } while (0)
-    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, w.gstart);
+    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, w.gstart, w.vmax);
+    PARK_CHECK();
+    k_vmax<<<dim3(64, s.BH), 256, 0, st>>>(v, (size_t)s.N * s.d, w.vmax);
     PARK_CHECK();
     dim3 pgrid(s.nk, s.BH);
     if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
     else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
     PARK_CHECK();
-    k_plan_count<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, s.nk, NQ, rows, w.ntiles);
+    k_range_assign<<<s.BH, 1024, 0, st>>>(list, count, offsets, s.nk, NQ, w.rng);
     PARK_CHECK();
-    k_plan_scan<<<1, 1024, 0, st>>>(w.ntiles, rows, w.tbase);
+    k_plan_count<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.rng, s.nk, NQ, rows, w.ntiles);
     PARK_CHECK();
-    k_plan_fill<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.gstart, s.nk, NQ, rows, Gcap, w.tbase, w.plan);
+    const int nb = (items + kScanBlock - 1) / kScanBlock;
+    k_scan_blocks<<<nb, 1024, 0, st>>>(w.ntiles, items, w.bsum);
     PARK_CHECK();
-    dim3 grid((unsigned)(s.BH * 8 * ((NQ + 7) / 8)));
-    auto q = reinterpret_cast<const bf16*>(Q);
-    auto o = reinterpret_cast<bf16*>(O);
+    k_scan_top<<<1, 1024, 0, st>>>(w.bsum, nb);
+    PARK_CHECK();
+    k_scan_final<<<nb, 1024, 0, st>>>(w.ntiles, items, w.bsum, w.tbase);
+    PARK_CHECK();
+    k_plan_fill<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.gstart, w.rng, s.nk, NQ, rows, Gcap,
+                                                 w.tbase, w.plan);
+    PARK_CHECK();
     if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
     if (s.d == 128)
-      k_attn_bf16<128><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
+      k_attn_items<128><<<items, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, w.ML);
     else
-      k_attn_bf16<64><<<grid, 256, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, s.N, NQ, Gcap, scale2, o, lse);
+      k_attn_items<64><<<items, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, w.ML);
+    PARK_CHECK();
+    if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+    const int total_rows = s.BH * s.N;
+    const long long mthreads = (long long)total_rows * (s.d / 8);
+    const unsigned mblocks = (unsigned)((mthreads + 255) / 256);
+    if (s.d == 128) k_attn_merge<128><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, total_rows, o, lse);
+    else k_attn_merge<64><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, total_rows, o, lse);
     PARK_CHECK();
 #undef PARK_CHECK
-    if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
   } else {
     dim3 grid(NQ, s.BH);
     auto q = reinterpret_cast<const float*>(Q);

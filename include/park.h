@@ -149,16 +149,19 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  *   s_ij = scale q_i . k_j,  lse_i = m_i + log sum_{j in J_u} exp(s_ij - m_i);
  * an empty J_u gives O_i = 0 and lse_i = -inf.  O is in the original query order.
  * For bf16 inputs the call first copies every cluster's keys and values, in cluster order, into
- * the workspace as 8-key groups (the last group of a cluster zero-padded; values transposed per
- * group), then lists each query block's 64-key tiles, then runs the attention kernel; float
- * inputs are read in place through perm.
+ * the workspace as 8-key groups in matrix-operand order (the last group of a cluster
+ * zero-padded), deals each head's clusters to 8 key ranges of about equal work (range r is
+ * computed on XCD r, so each XCD's L2 holds one eighth of a head's keys), lists the 32-key
+ * tiles of every (query block, range) pair, computes a partial softmax state per pair and
+ * merges the 8 partial states of every query; float inputs are read in place through perm.
  * Inputs: Q, K, V [B,H,N,d] of `dtype`; perm/offsets from park_cluster_keys; block_list /
  * block_count from park_retrieve_blocks (ids must lie in [0, n_clusters); listing every
  * cluster gives dense attention).  scale <= 0 selects 1/sqrt(d).
  * Outputs: O [B,H,N,d] of `dtype`; lse [B,H,N] float or NULL (natural-log log-sum-exp).
  * Numerics: bf16 inputs use bf16 matrix products with float accumulation and a float
- * online softmax (probabilities rounded to bf16 before the PV product); float inputs are
- * computed in float throughout.
+ * online softmax (probabilities rounded to bf16 before the PV product, O normalised by the
+ * sum of those rounded weights, lse from the float sum; partial outputs of the key ranges in
+ * fp16, scaled by the head's largest |value|); float inputs are computed in float throughout.
  * Workspace: park_workspace_bytes(PARK_OP_BLOCK_SPARSE_ATTN, ...) bytes (sized for any selection,
  * up to every cluster for every query block).
  * Errors: INVALID, UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS),
