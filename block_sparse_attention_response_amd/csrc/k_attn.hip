@@ -108,33 +108,18 @@ __device__ __forceinline__ float value_unit(float vmax) {
   return ldexpf(1.0f, ex);
 }
 
-// vmax[bh] (zeroed by k_group_scan) = largest |value| of head bh.  Grid (blocks, BH).
-__global__ __launch_bounds__(256) void k_vmax(const bf16* __restrict__ V, size_t per_head, float* __restrict__ vmax) {
-  const int bh = blockIdx.y;
-  const bf16* Vh = V + (size_t)bh * per_head;
-  float m = 0.0f;
-  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_head; i += (size_t)gridDim.x * 256 * 8) {
-    const bf16x8 x = load_bf16x8(Vh + i);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)x[j]));
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  // non-negative floats order like their bit patterns
-  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(reinterpret_cast<int*>(vmax) + bh, __float_as_int(m));
-}
-
 // Packed group layouts (8 keys, D columns):
 //   Kp[g] (bf16): D/16 column chunks, each 8 keys x 16 values (chunk c of key slot s at
 //          128 c + 16 s), so the A operand of S^T = K Q^T (16 columns of one key per lane)
 //          is one 16-byte load and the four groups of a tile give 1 KB per chunk;
 //   Vp[g] (bf16): D rows of 8 keys (V^T), the A operand of O^T += V^T P^T.
-// Group Gcap of every head is all zeros: the filler of partial tiles.
+// Group Gcap of every head is all zeros: the filler of partial tiles.  vmax[bh] (zeroed by
+// k_group_scan) becomes the largest |value| of the head.
 template <int D>
 __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                  const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ gstart, int N, int nk, int Gcap,
-                                                 bf16* __restrict__ Kp, bf16* __restrict__ Vp) {
+                                                 bf16* __restrict__ Kp, bf16* __restrict__ Vp, float* __restrict__ vmax) {
   constexpr int NS = D / 8;
   const int v = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
@@ -169,6 +154,7 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
     const int j = slot >> 3, s = slot & 7;
     *reinterpret_cast<bf16x8*>(Kph + (size_t)j * 8 * D + (sg >> 1) * 128 + s * 16 + (sg & 1) * 8) = val;
   }
+  float amax = 0.0f;
   for (int e = tid; e < ng * NS; e += 128) {
     const int j = e / NS, sg = e % NS;
     bf16x8 rows[8];
@@ -186,10 +172,17 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
     for (int dd = 0; dd < 8; ++dd) {
       bf16x8 col;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) col[i] = rows[i][dd];
+      for (int i = 0; i < 8; ++i) {
+        col[i] = rows[i][dd];
+        amax = fmaxf(amax, fabsf((float)col[i]));
+      }
       *reinterpret_cast<bf16x8*>(Vph + (size_t)j * 8 * D + (size_t)(sg * 8 + dd) * 8) = col;
     }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // non-negative floats order like their bit patterns
+  if ((tid & 63) == 0 && amax > 0.0f) atomicMax(reinterpret_cast<int*>(vmax) + bh, __float_as_int(amax));
 }
 
 // Step 2: the range of every cluster.  work(v) = (query blocks selecting v) x (groups of v);
@@ -420,8 +413,8 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
 // the accumulators) when a lane's float sum for a tile leaves [0, 2^60]; the row maximum is
 // then recovered from the probabilities themselves (m + log2 of the largest), and only if
 // one overflowed float are the scores recomputed.  The partial state of the item is
-// O_r = O^T / lb in fp16 (in units of the head's value unit, so |O_r| <= 1), and
-// (m, l, unit) with l the float sum.
+// O_r = O^T / lb in fp16 (in units of the head's value unit, so |O_r| <= 1), and (m, l) with
+// l the float sum.
 __device__ __forceinline__ int sigma16(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 
 // global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
@@ -450,7 +443,7 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
                                                    const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
                                                    const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
                                                    int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
-                                                   float4* __restrict__ ML) {
+                                                   float2* __restrict__ ML) {
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
   static_assert(KC == 2 * DT, "K and V batches have the same size");
@@ -471,7 +464,7 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   const size_t hrow = (size_t)bh * N;
   if (nt <= 0) {
     const int q = 64 * u + lane;
-    if (q < N) ML[(hrow + q) * kRanges + rr] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+    if (q < N) ML[(hrow + q) * kRanges + rr] = make_float2(-INFINITY, 0.0f);
     return;
   }
   const int32_t* pl = plan + (size_t)t0 * 4;
@@ -689,14 +682,22 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   constexpr int kCopyK = KC / 2;           // A1 chunk that refills the key buffer
   constexpr int kCopyV = kNPV / 2 + 2;     // B chunk that refills the value buffer
   bf16x8 pb[2][2];
+  // plan entries of tiles t + 2, t + 3 and the score start of tile t + 1, read for step t at
+  // the end of step t - 1 (their ring slot is complete by then), so a step starts with one
+  // round trip to LDS
+  int4 e2, e3;
+  f32x16 init;
+  auto next_entries = [&](int t) __attribute__((always_inline)) {
+    const int4 e1 = ring_entries((t + 1) & 3, 0);
+    e2 = ring_entries((t + 1) & 3, 1);
+    e3 = ring_entries((t + 1) & 3, 2);
+    init = init_scores(e1);
+  };
   auto step = [&](int t) __attribute__((always_inline)) {
     const bf16x8 (&Vx)[2 * DT][64] = Vs[t & 1];
     const bf16x8 (&Ky)[KC][64] = Ks[(t + 1) & 1];
     copy_plan(t + 4);
     wait_copies<2 * KC + 1>();
-    const int4 e1 = ring_entries((t + 1) & 3, 0), e2 = ring_entries((t + 1) & 3, 1),
-               e3 = ring_entries((t + 1) & 3, 2);
-    const f32x16 init = init_scores(e1);
     bf16x8 kf[KC], vf[2 * DT];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) kf[kc] = Ky[kc][lane];
@@ -768,6 +769,7 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int c = 0; c < 2; ++c) pb[h2][c] = pn[h2][c];
+    if (t + 2 < nt) next_entries(t + 1);
   };
   // the last tile t: P V
   auto last = [&](int t) __attribute__((always_inline)) {
@@ -816,13 +818,14 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   to_bf16(pb);
   weight_sums(pb, lb, 0);
   weight_sums(pb, lb, 1);
+  if (nt > 1) next_entries(0);
   for (int t = 0; t + 1 < nt; ++t) step(t);
   last(nt - 1);
   // no copy may still be writing this workgroup's LDS when the wave ends
   wait_copies<0>();
 
   // partial state: O_r = O^T / lb stored as fp16 in units of the head's value unit (so
-  // |stored| <= 1), and (m, l, unit) in float
+  // |stored| <= 1), and (m, l) in float
   const float unit = value_unit(vmax[bh]);
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
@@ -841,48 +844,54 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
           for (int i = 0; i < 4; ++i) o[i] = (f16)(oacc[h2][dt][4 * g + i] * inv);
           *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
-      if (h == 0) ML[(hrow + qrow) * kRanges + rr] = make_float4(m[h2], l, unit, 0.0f);
+      if (h == 0) ML[(hrow + qrow) * kRanges + rr] = make_float2(m[h2], l);
     }
   }
 }
 
 // Step 5: merge the kRanges partial states of every query:
-//   M = max_r m_r,  w_r = l_r 2^(m_r - M),  O = sum_r w_r O_r / sum_r w_r,
-//   lse = ln 2 (M + log2 sum_r w_r); ranges with l_r = 0 contribute nothing (their O_r is
-// never read).  D / 8 threads per query, 8 columns each.
+//   M = max_r m_r,  w_r = l_r 2^(m_r - M),  O = unit sum_r w_r O_r / sum_r w_r,
+//   lse = ln 2 (M + log2 sum_r w_r).
+// Ranges with l_r = 0 contribute nothing (their O_r is never read), and neither is O_r read
+// when w_r < 2^-20 sum_r w_r: |O_r| <= 1, so skipping it moves O by at most 2^-20 unit, far
+// below the bf16 output's resolution.  D / 8 threads per query, 8 columns each.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_merge(const f16* __restrict__ Opart, const float4* __restrict__ ML,
-                                                    int rows, bf16* __restrict__ O, float* __restrict__ lse) {
+__global__ __launch_bounds__(256) void k_attn_merge(const f16* __restrict__ Opart, const float2* __restrict__ ML,
+                                                    const float* __restrict__ vmax, int rows, int N,
+                                                    bf16* __restrict__ O, float* __restrict__ lse) {
   constexpr int TPQ = D / 8;
   const int gt = blockIdx.x * 256 + threadIdx.x;
   const int q = gt / TPQ, part = gt % TPQ;
   if (q >= rows) return;
-  float4 st[kRanges];
+  float2 st[kRanges];
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kRanges; ++j) {
     st[j] = ML[(size_t)q * kRanges + j];
     if (st[j].y > 0.0f) M = fmaxf(M, st[j].x);
   }
+  float w[kRanges], wsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j) {
+    w[j] = st[j].y > 0.0f ? st[j].y * fast_exp2(st[j].x - M) : 0.0f;
+    wsum += w[j];
+  }
+  const float cut = wsum * 0x1p-20f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  float wsum = 0.0f;
 #pragma unroll
   for (int j = 0; j < kRanges; ++j) {
-    if (st[j].y > 0.0f) {
-      const float w = st[j].y * fast_exp2(st[j].x - M);
-      wsum += w;
-      const float ws = w * st[j].z;
+    if (w[j] > cut) {
       const f16x8 o = *reinterpret_cast<const f16x8*>(Opart + ((size_t)q * kRanges + j) * D + part * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, (float)o[i], acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], (float)o[i], acc[i]);
     }
   }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const float scale = wsum > 0.0f ? value_unit(vmax[q / N]) / wsum : 0.0f;
   bf16x8 out;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = (bf16)(acc[i] * inv);
+  for (int i = 0; i < 8; ++i) out[i] = (bf16)(acc[i] * scale);
   *reinterpret_cast<bf16x8*>(O + (size_t)q * D + part * 8) = out;
   if (lse && part == 0) lse[q] = wsum > 0.0f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
 }
@@ -965,7 +974,7 @@ struct AttnWs {
   float* vmax;
   bf16 *Kp, *Vp;
   f16* Opart;
-  float4* ML;
+  float2* ML;
 };
 
 static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
@@ -989,7 +998,7 @@ static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
   w.Kp = reinterpret_cast<bf16*>(take(kv));
   w.Vp = reinterpret_cast<bf16*>(take(kv));
   w.Opart = reinterpret_cast<f16*>(take((size_t)s.BH * s.N * kRanges * s.d * sizeof(f16)));
-  w.ML = reinterpret_cast<float4*>(take((size_t)s.BH * s.N * kRanges * sizeof(float4)));
+  w.ML = reinterpret_cast<float2*>(take((size_t)s.BH * s.N * kRanges * sizeof(float2)));
   if (total) *total = (size_t)(p - static_cast<char*>(base));
   return w;
 }
@@ -1019,11 +1028,9 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
 #define PARK_CHECK() do { e = hipGetLastError(); if (e != hipSuccess) return e; } while (0)
     k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, w.gstart, w.vmax);
     PARK_CHECK();
-    k_vmax<<<dim3(64, s.BH), 256, 0, st>>>(v, (size_t)s.N * s.d, w.vmax);
-    PARK_CHECK();
     dim3 pgrid(s.nk, s.BH);
-    if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
-    else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp);
+    if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp, w.vmax);
+    else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp, w.vmax);
     PARK_CHECK();
     k_range_assign<<<s.BH, 1024, 0, st>>>(list, count, offsets, s.nk, NQ, w.rng);
     PARK_CHECK();
@@ -1049,8 +1056,8 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     const int total_rows = s.BH * s.N;
     const long long mthreads = (long long)total_rows * (s.d / 8);
     const unsigned mblocks = (unsigned)((mthreads + 255) / 256);
-    if (s.d == 128) k_attn_merge<128><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, total_rows, o, lse);
-    else k_attn_merge<64><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, total_rows, o, lse);
+    if (s.d == 128) k_attn_merge<128><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
+    else k_attn_merge<64><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
     PARK_CHECK();
 #undef PARK_CHECK
   } else {
