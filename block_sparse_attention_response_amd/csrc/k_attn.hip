@@ -1,7 +1,8 @@
 // Block-sparse attention (PARK section 3.1, E1/E2 with the softmax renormalised over the
-// selected keys): every query block walks the concatenation of its selected key clusters,
-// cut into 64-key tiles (only the last tile of a block is partial), gathering keys and
-// values through the cluster permutation.
+// selected keys): every query block attends to the union of its selected key clusters.  The
+// bf16 path packs the clusters' keys and values, splits each head's clusters into key ranges
+// (one per XCD), computes a partial softmax state per (query block, key range) and merges
+// them; the float path walks the selected clusters through the cluster permutation.
 #include "park_device.h"
 #include "park_internal.h"
 #include "../../include/park.h"
