@@ -447,14 +447,18 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   const int bh = blockIdx.y, k0 = blockIdx.x * kAsgKeys;
   const int nT = nkp >> 5;
   const bf16* gA = gneg2 + (size_t)bh * nkp * D + (size_t)lane * 8;  // this lane's piece of fragment 0
-  for (int v = tid; v < nkp; v += kAsgKeys) ccs[v] = ccv[(size_t)bh * nkp + v];
-  lovf[tid] = 0;
-  best[tid] = ~0ull;
+  // The loads that need no key index go first (the slot's key and |c~|^2); the LDS copies are
+  // written once the key-dependent loads are in flight.
   // Slots walk the keys in `order` (the previous step's label order, so that the keys of a
   // tile share their nearest clusters and few tiles produce candidates) or in index order.
-  {
-    const int pos = k0 + tid;
-    kidx[tid] = pos < N ? (order ? order[(size_t)bh * N + pos] : pos) : -1;
+  const int kslot = k0 + tid < N ? (order ? order[(size_t)bh * N + k0 + tid] : k0 + tid) : -1;
+  constexpr int MV = PARK_MAX_CLUSTERS / kAsgKeys;
+  static_assert(MV * kAsgKeys == PARK_MAX_CLUSTERS, "cluster cap");
+  float cvv[MV];
+#pragma unroll
+  for (int i = 0; i < MV; ++i) {
+    const int v = tid + i * kAsgKeys;
+    cvv[i] = v < nkp ? ccv[(size_t)bh * nkp + v] : 0.0f;
   }
   if (tid == 0) npairs = 0;
 
@@ -463,10 +467,12 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   float E[2];
   const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
   const float CC = __uint_as_float(hmax[4 * bh + 2]);
+  // the keys of slots 64 w + l32 and 64 w + 32 + l32 (-1 past N)
+  const int keyi[2] = {__shfl(kslot, l32), __shfl(kslot, 32 + l32)};
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int pos = k0 + 64 * w + 32 * kt + l32;
-    const int key = pos < N ? (order ? order[(size_t)bh * N + pos] : pos) : 0;
+    const int key = pos < N ? keyi[kt] : 0;
 #pragma unroll
     for (int kc = 0; kc < NF; ++kc) {
       if (pos < N) {
@@ -498,8 +504,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     for (int kt = 0; kt < 2; ++kt) {
       const int pos = k0 + 64 * w + 32 * kt + l32;
       if (pos < N) {
-        const int key = order ? order[(size_t)bh * N + pos] : pos;
-        const int vp = labels[(size_t)bh * N + key];
+        const int vp = labels[(size_t)bh * N + keyi[kt]];
         float dot = 0.0f;
 #pragma unroll
         for (int kc = 0; kc < NF; ++kc) {
@@ -514,6 +519,12 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < MV; ++i)
+    if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
+  kidx[tid] = kslot;
+  lovf[tid] = 0;
+  best[tid] = ~0ull;
   __syncthreads();
 
   // stream the 32-cluster tiles straight from memory (fragment-major: 1 KB per fragment);
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
 #pragma unroll
       for (int r = 3; r < 15; r += 2) tm = fminf(fminf(tm, acc[kt][r]), acc[kt][r + 1]);
       tm = fminf(tm, acc[kt][15]);
-      tm = fminf(tm, __shfl_xor(tm, 32));
+      tm = xor32_min(tm);
       mr[kt] = fminf(mr[kt], tm);
       const float th = mr[kt] + E[kt];
       if (__any(tm <= th)) {
@@ -660,9 +671,11 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     if (p < npl && q == 0 && !lovf[pr.x])
       atomicMin(&best[pr.x], ((unsigned long long)__float_as_uint(s) << 32) | (uint32_t)pr.y);
   }
-  for (int kl = w; kl < kAsgKeys; kl += kAsgWaves) {
-    if (k0 + kl >= N) break;
-    if (!lovf[kl]) continue;
+  // slots w + 4 i of this wave that take the exhaustive path (lane i looks at slot w + 4 i)
+  static_assert(kAsgKeys == 64 * kAsgWaves, "one slot per lane and wave");
+  uint64_t todo = __ballot(k0 + w + kAsgWaves * lane < N && lovf[w + kAsgWaves * lane]);
+  for (; todo; todo &= todo - 1) {
+    const int kl = w + kAsgWaves * __builtin_ctzll(todo);
     const f32x4* x = reinterpret_cast<const f32x4*>(Kt + ((size_t)bh * N + kidx[kl]) * D);
     unsigned long long bk = ~0ull;
     for (int v = lane; v < nk; v += 64) {

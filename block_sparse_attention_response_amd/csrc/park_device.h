@@ -52,6 +52,14 @@ __device__ __forceinline__ size_t frag_lane(int t, int kc, int lane, int D) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// min of x over lanes l and l ^ 32 in one VALU exchange (v_permlane32_swap) instead of
+// a round trip through the LDS crossbar: the swap of x with itself leaves lanes l and l ^ 32
+// of the two results holding x_l and x_(l^32) in some order.
+__device__ __forceinline__ float xor32_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
