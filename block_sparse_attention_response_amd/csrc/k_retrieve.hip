@@ -131,15 +131,20 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     crow[vt] = (size_t)bh * nkp * DK + frag_lane(t, 0, lane, DK);
   }
 
-  // B fragments are prefetched one 16-column step ahead when the registers allow it
-  constexpr bool kPrefetch = VT <= 4;
-  bf16x8 nhi[VT], nlo[VT];
-  if constexpr (kPrefetch) {
+  // B fragments stream from L2 PF 16-column steps ahead of their products, through PF + 1
+  // named register buffers (the step loop is unrolled, so every buffer index is a constant);
+  // the scheduling fences keep the compiler from sinking the loads to their first use
+  // (with more than four tiles the registers are short: the loads go just before their use)
+  constexpr int PF = VT <= 4 ? 1 : 0;
+  bf16x8 bhi[PF + 1][VT], blo[PF + 1][VT];   // (used when PF > 0)
+  const auto load_step = [&](int kc, bf16x8 (&hi)[VT], bf16x8 (&lo)[VT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt) { nhi[vt] = load_bf16x8(Chi + crow[vt]); nlo[vt] = load_bf16x8(Clo + crow[vt]); }
-  }
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
+    for (int vt = 0; vt < VT; ++vt) {
+      hi[vt] = load_bf16x8(Chi + crow[vt] + kc * 512);
+      lo[vt] = load_bf16x8(Clo + crow[vt] + kc * 512);
+    }
+  };
+  const auto products = [&](int kc, const bf16x8 (&hi)[VT], const bf16x8 (&lo)[VT]) __attribute__((always_inline)) {
     const int col = kc * 16 + 8 * h;
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qs[l32 * QP + col]);
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qs[(32 + l32) * QP + col]);
@@ -148,33 +153,55 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       a0l = *reinterpret_cast<const bf16x8*>(&qlo[l32 * QP + col]);
       a1l = *reinterpret_cast<const bf16x8*>(&qlo[(32 + l32) * QP + col]);
     }
-    bf16x8 bhi[VT], blo[VT];
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt) { bhi[vt] = nhi[vt]; blo[vt] = nlo[vt]; }
-      if (kc + 1 < KC) {
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-          nhi[vt] = load_bf16x8(Chi + crow[vt] + (kc + 1) * 512);
-          nlo[vt] = load_bf16x8(Clo + crow[vt] + (kc + 1) * 512);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        bhi[vt] = load_bf16x8(Chi + crow[vt] + kc * 512);
-        blo[vt] = load_bf16x8(Clo + crow[vt] + kc * 512);
-      }
-    }
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
-      acc[0][vt] = mfma32(a0, bhi[vt], acc[0][vt]);
-      acc[1][vt] = mfma32(a1, bhi[vt], acc[1][vt]);
-      acc[0][vt] = mfma32(a0, blo[vt], acc[0][vt]);
-      acc[1][vt] = mfma32(a1, blo[vt], acc[1][vt]);
+      acc[0][vt] = mfma32(a0, hi[vt], acc[0][vt]);
+      acc[1][vt] = mfma32(a1, hi[vt], acc[1][vt]);
+      acc[0][vt] = mfma32(a0, lo[vt], acc[0][vt]);
+      acc[1][vt] = mfma32(a1, lo[vt], acc[1][vt]);
       if constexpr (QF32) {
-        acc[0][vt] = mfma32(a0l, bhi[vt], acc[0][vt]);
-        acc[1][vt] = mfma32(a1l, bhi[vt], acc[1][vt]);
+        acc[0][vt] = mfma32(a0l, hi[vt], acc[0][vt]);
+        acc[1][vt] = mfma32(a1l, hi[vt], acc[1][vt]);
+      }
+    }
+  };
+  if constexpr (PF > 0) {
+#pragma unroll
+    for (int kc = 0; kc < PF; ++kc) load_step(kc, bhi[kc], blo[kc]);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (kc + PF < KC) load_step(kc + PF, bhi[(kc + PF) % (PF + 1)], blo[(kc + PF) % (PF + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      products(kc, bhi[kc % (PF + 1)], blo[kc % (PF + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int col = kc * 16 + 8 * h;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&qs[l32 * QP + col]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&qs[(32 + l32) * QP + col]);
+      bf16x8 a0l, a1l;
+      if constexpr (QF32) {
+        a0l = *reinterpret_cast<const bf16x8*>(&qlo[l32 * QP + col]);
+        a1l = *reinterpret_cast<const bf16x8*>(&qlo[(32 + l32) * QP + col]);
+      }
+      bf16x8 hi[VT], lo[VT];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        hi[vt] = load_bf16x8(Chi + crow[vt] + kc * 512);
+        lo[vt] = load_bf16x8(Clo + crow[vt] + kc * 512);
+      }
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        acc[0][vt] = mfma32(a0, hi[vt], acc[0][vt]);
+        acc[1][vt] = mfma32(a1, hi[vt], acc[1][vt]);
+        acc[0][vt] = mfma32(a0, lo[vt], acc[0][vt]);
+        acc[1][vt] = mfma32(a1, lo[vt], acc[1][vt]);
+        if constexpr (QF32) {
+          acc[0][vt] = mfma32(a0l, hi[vt], acc[0][vt]);
+          acc[1][vt] = mfma32(a1l, hi[vt], acc[1][vt]);
+        }
       }
     }
   }
