@@ -3,6 +3,9 @@
 // bf16 path packs the clusters' keys and values, splits each head's clusters into key ranges
 // (one per XCD), computes a partial softmax state per (query block, key range) and merges
 // them; the float path walks the selected clusters through the cluster permutation.
+#include <algorithm>
+#include <atomic>
+
 #include "park_device.h"
 #include "park_internal.h"
 #include "../../include/park.h"
@@ -311,10 +314,11 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const int32_t* __restrict_
   if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
-__global__ __launch_bounds__(1024) void k_scan_top(int32_t* __restrict__ bsum, int nb) {
+__global__ __launch_bounds__(1024) void k_scan_top(int32_t* __restrict__ bsum, int nb, int32_t* __restrict__ ictr) {
   __shared__ int wsum[16];
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
+  if (threadIdx.x < kRanges) ictr[threadIdx.x] = 0;   // the attention kernel's item counters
   __syncthreads();
   for (int c = 0; c < nb; c += 1024) {
     const int i = c + threadIdx.x;
@@ -439,27 +443,34 @@ __device__ __forceinline__ void wait_copies() {
 // all LDS reads issued so far have returned (before a copy overwrites what they read)
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
+// LDS of one wave: two tiles of keys and values in MFMA fragment order (fragment f of lane i
+// at [b][f][i] for buffer b = tile parity), the plan-entry ring (slot s holds the 16 tiles
+// from the one its copy started at) and the score start table
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
-                                                   const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
-                                                   const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
-                                                   int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
-                                                   float2* __restrict__ ML) {
+struct AttnLds {
+  bf16x8 Ks[2][D / 16][64];
+  bf16x8 Vs[2][D / 16][64];
+  __attribute__((aligned(16))) int32_t pring[4][64];
+  __attribute__((aligned(16))) float btab[9][8];
+};
+
+// One item: the partial softmax state of 64 queries over one key range's tiles.
+template <int D>
+__device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const bf16* __restrict__ Q,
+                                          const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
+                                          const int32_t* __restrict__ plan, const int32_t* __restrict__ tbase,
+                                          const float* __restrict__ vmax, int N, int NQ, int Gcap, float scale2,
+                                          f16* __restrict__ Opart, float2* __restrict__ ML) {
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
   static_assert(KC == 2 * DT, "K and V batches have the same size");
-  // Two tiles of keys and values in MFMA fragment order (fragment f of lane i at [b][f][i] for
-  // buffer b = tile parity)
-  __shared__ bf16x8 Ks[2][KC][64];
-  __shared__ bf16x8 Vs[2][2 * DT][64];
-  // plan entries in flight: slot s holds the 16 tiles from the one its copy started at
-  __shared__ __attribute__((aligned(16))) int32_t pring[4][64];
-  __shared__ __attribute__((aligned(16))) float btab[9][8];
-  const int item = blockIdx.x;
+  auto& Ks = sm.Ks;
+  auto& Vs = sm.Vs;
+  auto& pring = sm.pring;
+  auto& btab = sm.btab;
   const int rr = item % kRanges, row = item / kRanges;
   const int bh = row / NQ, u = row - bh * NQ;
   const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
-  for (int i = lane; i < 72; i += 64) btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
   const int t0 = tbase[item];
   const int nt = tbase[item + 1] - t0;
   const size_t hrow = (size_t)bh * N;
@@ -850,6 +861,30 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   }
 }
 
+// Persistent waves, one per workgroup: wave b starts with item b and then takes items of its
+// key range r = b % kRanges (items of range r run on XCD r: workgroups are dealt to the XCDs
+// round robin and the grid size is a multiple of kRanges) from a per-range counter, in item
+// order: items gridDim.x + r + kRanges k for k = 0, 1, ...  The next index is taken as an
+// item starts and used when it ends.  No wave waits for another, so every wave ends once the
+// counter passes the last item, whatever the number of resident waves.
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
+                                                   const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
+                                                   const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
+                                                   int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
+                                                   float2* __restrict__ ML, int items, int32_t* __restrict__ ictr) {
+  __shared__ AttnLds<D> sm;
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
+  const int xr = blockIdx.x % kRanges;
+  for (int item = blockIdx.x; item < items;) {
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&ictr[xr], 1);
+    attn_item<D>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML);
+    item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(nxt);
+  }
+}
+
 // Step 5: merge the kRanges partial states of every query:
 //   M = max_r m_r,  w_r = l_r 2^(m_r - M),  O = unit sum_r w_r O_r / sum_r w_r,
 //   lse = ln 2 (M + log2 sum_r w_r).
@@ -971,7 +1006,7 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q, c
 static inline int group_cap(const Shape& s) { return (s.N + 7) / 8 + s.nk; }
 
 struct AttnWs {
-  int32_t *gstart, *rng, *ntiles, *tbase, *bsum, *plan;
+  int32_t *gstart, *rng, *ntiles, *tbase, *bsum, *plan, *ictr;
   float* vmax;
   bf16 *Kp, *Vp;
   f16* Opart;
@@ -994,6 +1029,7 @@ static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
   w.ntiles = reinterpret_cast<int32_t*>(take(items * sizeof(int32_t)));
   w.tbase = reinterpret_cast<int32_t*>(take((items + 1) * sizeof(int32_t)));
   w.bsum = reinterpret_cast<int32_t*>(take(((items + kScanBlock - 1) / kScanBlock) * sizeof(int32_t)));
+  w.ictr = reinterpret_cast<int32_t*>(take(kRanges * sizeof(int32_t)));
   // + slack: the attention kernel copies plan entries up to 80 dwords past an item's end
   w.plan = reinterpret_cast<int32_t*>(take((rows * per_row + 128) * sizeof(int32_t)));
   w.Kp = reinterpret_cast<bf16*>(take(kv));
@@ -1002,6 +1038,22 @@ static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
   w.ML = reinterpret_cast<float2*>(take((size_t)s.BH * s.N * kRanges * sizeof(float2)));
   if (total) *total = (size_t)(p - static_cast<char*>(base));
   return w;
+}
+
+// compute units of the current device (read once per device)
+static int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 size_t attn_workspace(const Shape& s) {
@@ -1040,7 +1092,7 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     const int nb = (items + kScanBlock - 1) / kScanBlock;
     k_scan_blocks<<<nb, 1024, 0, st>>>(w.ntiles, items, w.bsum);
     PARK_CHECK();
-    k_scan_top<<<1, 1024, 0, st>>>(w.bsum, nb);
+    k_scan_top<<<1, 1024, 0, st>>>(w.bsum, nb, w.ictr);
     PARK_CHECK();
     k_scan_final<<<nb, 1024, 0, st>>>(w.ntiles, items, w.bsum, w.tbase);
     PARK_CHECK();
@@ -1048,10 +1100,15 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
                                                  w.tbase, w.plan);
     PARK_CHECK();
     if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+    // persistent waves: as many as the chip holds (four per CU, bound by LDS), a multiple of
+    // kRanges (items is one)
+    const int waves = std::min(items, 4 * compute_units() / kRanges * kRanges);
     if (s.d == 128)
-      k_attn_items<128><<<items, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, w.ML);
+      k_attn_items<128><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
+                                              w.ML, items, w.ictr);
     else
-      k_attn_items<64><<<items, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, w.ML);
+      k_attn_items<64><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
+                                             w.ML, items, w.ictr);
     PARK_CHECK();
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     const int total_rows = s.BH * s.N;
