@@ -72,6 +72,9 @@ def _declare(L):
     L.orc_select.argtypes = [_P, _L, _I, _P, _D, _I, _P, _P, _P, _P, _P]
     L.orc_block_sparse_attn.argtypes = [_P, _P, _P, _L, _I, _P, _P, _I, _P, _P, _I, _D, _P, _L, _P, _P]
     L.orc_dense_attn.argtypes = [_P, _P, _P, _L, _I, _D, _P, _L, _P, _P]
+    L.orc_pama_blocks.argtypes = [_P, _L, _I, _P, _P, _I, _P, _P, _L, _D, _P]
+    L.orc_block_sparse_attn_blocks.argtypes = [_P, _P, _P, _L, _I, _P, _P, _I, _P, _P, _L, _P, _P, _D, _P, _L,
+                                               _P, _P]
     L.orc_exact_block_importance.argtypes = [_P, _P, _L, _I, _P, _I, _I, _D, _P]
 
 
@@ -212,6 +215,33 @@ def block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, q_block: 
     return O, lse
 
 
+def pama_blocks(Q, cent, counts, qperm, qoffsets, scale: float):
+    """W [N_Q, N_K] over clustered query blocks (block u = queries qperm[qoffsets[u]:qoffsets[u+1]])."""
+    Q = _f32(Q); cent = _f32(cent); counts = _i32(counts); qperm = _i32(qperm); qoffsets = _i32(qoffsets)
+    L_, d = Q.shape
+    nq = qoffsets.shape[0] - 1
+    W = np.empty((nq, cent.shape[0]))
+    lib().orc_pama_blocks(_p(Q), L_, d, _p(cent), _p(counts), cent.shape[0], _p(qperm), _p(qoffsets), nq, scale,
+                          _p(W))
+    return W
+
+
+def block_sparse_attn_blocks(Q, K, V, perm, offsets, qperm, qoffsets, block_list, block_count, scale: float,
+                             ublocks=None):
+    """(O [L,d] float64, lse [L]) over clustered query blocks; rows of blocks not in `ublocks` are NaN."""
+    Q = _f32(Q); K = _f32(K); V = _f32(V)
+    perm = _i32(perm); offsets = _i32(offsets); qperm = _i32(qperm); qoffsets = _i32(qoffsets)
+    block_list = _i32(block_list); block_count = _i32(block_count)
+    L_, d = Q.shape
+    O = np.full((L_, d), np.nan); lse = np.full(L_, np.nan)
+    ub = np.ascontiguousarray(ublocks, dtype=np.int64) if ublocks is not None else None
+    lib().orc_block_sparse_attn_blocks(_p(Q), _p(K), _p(V), L_, d, _p(perm), _p(offsets), offsets.shape[0] - 1,
+                                       _p(qperm), _p(qoffsets), qoffsets.shape[0] - 1, _p(block_list),
+                                       _p(block_count), scale, _p(ub), 0 if ub is None else ub.shape[0], _p(O),
+                                       _p(lse))
+    return O, lse
+
+
 def dense_attn(Q, K, V, scale: float, rows=None):
     """(O [R,d], lse [R]) for the given query rows (all rows if None)."""
     Q = _f32(Q); K = _f32(K); V = _f32(V)
@@ -244,6 +274,25 @@ def cluster_keys(Q, K, nk: int, iters: int, metric: str = "qrkc", alpha: float =
     cent, counts, perm, offsets = finalize(K, km["labels"], nk)
     return dict(G=G, Gs=Gs, R=R, ok=ok, Kt=Kt, km=km, labels=km["labels"], centroids=cent,
                 counts=counts, perm=perm, offsets=offsets)
+
+
+def cluster_queries(Q, nq: int, iters: int, init_idx=None):
+    """Query blocks by plain Euclidean k-means of the queries (Figure 2; N_Q = 128 in section
+    6): the key-clustering routine with R = I applied to the queries."""
+    return cluster_keys(Q, Q, nq, iters, "euclidean", init_idx=init_idx)
+
+
+def run_head_clustered(Q, K, V, nk: int, nq: int, iters: int, top_p: float, top_k: int, scale=None, ublocks=None):
+    """Whole path for one head with clustered query blocks (PARK's own configuration)."""
+    d = Q.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    qc = cluster_queries(Q, nq, iters)
+    cl = cluster_keys(Q, K, nk, iters)
+    W = pama_blocks(Q, cl["centroids"], cl["counts"], qc["perm"], qc["offsets"], scale)
+    mask, lst, cnt, cm, gm = select(W, cl["counts"], top_p, top_k)
+    O, lse = block_sparse_attn_blocks(Q, K, V, cl["perm"], cl["offsets"], qc["perm"], qc["offsets"], lst, cnt,
+                                      scale, ublocks)
+    return dict(qc=qc, cl=cl, W=W, mask=mask, list=lst, count=cnt, cut_margin=cm, gap_margin=gm, O=O, lse=lse)
 
 
 def run_head(Q, K, V, nk: int, iters: int, top_p: float, top_k: int, q_block: int = 64, scale=None,

@@ -406,6 +406,103 @@ ORC_EXPORT void orc_block_sparse_attn(const float* Q, const float* K, const floa
   }
 }
 
+/* ---------------------------------------------------------------------------------
+ * Clustered query blocks (Figure 2 and section 6, "Implementations": the queries are
+ * grouped by plain Euclidean k-means into N_Q = 128 query blocks).  Query block u holds
+ * the queries qperm[qoffsets[u] .. qoffsets[u+1]), the permutation and offsets that the
+ * k-means finalisation above writes when it clusters the queries; n_u = its size.
+ * --------------------------------------------------------------------------------- */
+
+/* PAMA over clustered query blocks, E7 and E8 as printed (the block sum runs over the
+ * block's queries in qperm order):
+ *   W_uv = (1/n_u) sum_{i in Q_u} P_iv,  P_iv = softmax_v(scale q_i . c_v + log n_v);
+ * an empty query block gives a zero row. */
+ORC_EXPORT void orc_pama_blocks(const float* Q, long L, int d, const float* cent, const int* counts, int nk,
+                                const int* qperm, const int* qoffsets, long nq, double scale, double* W) {
+  (void)L;
+#pragma omp parallel for schedule(dynamic)
+  for (long u = 0; u < nq; ++u) {
+    double* S = (double*)malloc(sizeof(double) * (size_t)nk);
+    double* Wu = W + (size_t)u * nk;
+    for (int v = 0; v < nk; ++v) Wu[v] = 0.0;
+    for (long pos = qoffsets[u]; pos < qoffsets[u + 1]; ++pos) {
+      const float* q = Q + (size_t)qperm[pos] * d;
+      double m = -INFINITY;
+      for (int v = 0; v < nk; ++v) {
+        if (counts[v] > 0) {
+          double dot = 0.0;
+          for (int a = 0; a < d; ++a) dot += (double)q[a] * (double)cent[(size_t)v * d + a];
+          S[v] = scale * dot + log((double)counts[v]);
+        } else {
+          S[v] = -INFINITY;
+        }
+        if (S[v] > m) m = S[v];
+      }
+      double z = 0.0;
+      for (int v = 0; v < nk; ++v) z += exp(S[v] - m);
+      for (int v = 0; v < nk; ++v) Wu[v] += exp(S[v] - m) / z;
+    }
+    long n = qoffsets[u + 1] - qoffsets[u];
+    if (n > 0)
+      for (int v = 0; v < nk; ++v) Wu[v] /= (double)n;
+    free(S);
+  }
+}
+
+/* Block-sparse attention over clustered query blocks: for every query i of block u (the
+ * queries qperm[qoffsets[u] .. qoffsets[u+1])), over the keys J_u of the clusters selected
+ * for u, the renormalised softmax of section 3.1:
+ *   s_ij = scale q_i . k_j,  O_i = sum_j exp(s_ij - m) v_j / sum_j exp(s_ij - m),
+ *   lse_i = m + log sum_j exp(s_ij - m).
+ * An empty selection gives O_i = 0 and lse_i = -inf.  Only the blocks in `ublocks` are
+ * computed (all if NULL); O and lse are indexed by the original query index. */
+ORC_EXPORT void orc_block_sparse_attn_blocks(const float* Q, const float* K, const float* V, long L, int d,
+                                             const int* perm, const int* offsets, int nk, const int* qperm,
+                                             const int* qoffsets, long nq, const int* list, const int* count,
+                                             double scale, const long* ublocks, long n_ub, double* O,
+                                             double* lse) {
+  (void)L;
+  long nu = ublocks ? n_ub : nq;
+#pragma omp parallel for schedule(dynamic)
+  for (long t = 0; t < nu; ++t) {
+    long u = ublocks ? ublocks[t] : t;
+    const int* lu = list + (size_t)u * nk;
+    long nsel = 0;
+    for (int r = 0; r < count[u]; ++r) nsel += offsets[lu[r] + 1] - offsets[lu[r]];
+    long* J = (long*)malloc(sizeof(long) * (size_t)(nsel > 0 ? nsel : 1));
+    long n = 0;
+    for (int r = 0; r < count[u]; ++r)
+      for (int p = offsets[lu[r]]; p < offsets[lu[r] + 1]; ++p) J[n++] = perm[p];
+    double* s = (double*)malloc(sizeof(double) * (size_t)(nsel > 0 ? nsel : 1));
+    for (long pos = qoffsets[u]; pos < qoffsets[u + 1]; ++pos) {
+      long i = qperm[pos];
+      double* Oi = O + (size_t)i * d;
+      for (int a = 0; a < d; ++a) Oi[a] = 0.0;
+      if (nsel == 0) {
+        lse[i] = -INFINITY;
+        continue;
+      }
+      double m = -INFINITY;
+      for (long x = 0; x < nsel; ++x) {
+        double dot = 0.0;
+        for (int a = 0; a < d; ++a) dot += (double)Q[(size_t)i * d + a] * (double)K[(size_t)J[x] * d + a];
+        s[x] = scale * dot;
+        if (s[x] > m) m = s[x];
+      }
+      double z = 0.0;
+      for (long x = 0; x < nsel; ++x) {
+        double e = exp(s[x] - m);
+        z += e;
+        for (int a = 0; a < d; ++a) Oi[a] += e * (double)V[(size_t)J[x] * d + a];
+      }
+      for (int a = 0; a < d; ++a) Oi[a] /= z;
+      lse[i] = m + log(z);
+    }
+    free(s);
+    free(J);
+  }
+}
+
 /* Dense attention (section 3.1, E1), textbook form, written independently of the sparse
  * routine above: A_i = softmax_j(scale q_i . k_j) over all L keys, O_i = sum_j A_ij v_j,
  * lse_i = log sum_j exp(scale q_i . k_j).  Rows listed in `rows` (all if NULL); outputs

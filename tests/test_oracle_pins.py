@@ -355,3 +355,113 @@ def test_literal_masked_attention_is_recall_times_output(orc):
     A = np.exp(Z - Z.max(1, keepdims=True)); A /= A.sum(1, keepdims=True)
     lit = (A * sel[None, :]) @ V.astype(np.float64)
     np.testing.assert_allclose(lit, np.exp(lse - lsed)[:, None] * O, rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------- clustered query blocks (next row 1)
+
+def _consecutive_blocks(L, qb):
+    """The 64-token layout written as a query permutation: identity order, blocks of qb."""
+    return np.arange(L, dtype=np.int32), np.minimum(np.arange(0, L + qb, qb), L).astype(np.int32)[: (L + qb - 1) // qb + 1]
+
+
+def test_pama_blocks_reduces_to_consecutive_blocks(orc):
+    """With the identity permutation and 64-token boundaries the clustered-block PAMA is the
+    64-token PAMA (a separately pinned routine), to the last bit: same sums in the same order."""
+    Q, K, _ = _rand_qk(300, 16, 31)
+    cl = orc.cluster_keys(Q, K, 9, 3)
+    qperm, qoff = _consecutive_blocks(300, 64)
+    W = orc.pama_blocks(Q, cl["centroids"], cl["counts"], qperm, qoff, 0.25)
+    np.testing.assert_array_equal(W, orc.pama(Q, cl["centroids"], cl["counts"], 64, 0.25))
+
+
+def test_pama_blocks_rows_sum_to_one_and_order_free(orc):
+    """E8 with clustered blocks: each non-empty row sums to 1, an empty block gives a zero row,
+    and the order of a block's queries in the permutation changes W only by rounding."""
+    Q, K, _ = _rand_qk(240, 12, 32, centres=6)
+    cl = orc.cluster_keys(Q, K, 7, 3)
+    qc = orc.cluster_queries(Q, 5, 4)
+    qoff = np.concatenate([qc["offsets"][:3], qc["offsets"][2:]]).astype(np.int32)  # block 2 empty
+    W = orc.pama_blocks(Q, cl["centroids"], cl["counts"], qc["perm"], qoff, 0.3)
+    sizes = np.diff(qoff)
+    assert sizes[2] == 0 and np.all(W[2] == 0)
+    np.testing.assert_allclose(W[sizes > 0].sum(1), 1.0, rtol=0, atol=1e-12)
+    rng = np.random.default_rng(33)
+    shuf = qc["perm"].copy()
+    for u in range(len(qoff) - 1):
+        seg = shuf[qoff[u]:qoff[u + 1]]
+        shuf[qoff[u]:qoff[u + 1]] = seg[rng.permutation(len(seg))]
+    W2 = orc.pama_blocks(Q, cl["centroids"], cl["counts"], shuf, qoff, 0.3)
+    np.testing.assert_allclose(W2, W, rtol=1e-12, atol=1e-15)
+
+
+def test_pama_blocks_brute_force(orc):
+    """Tiny case against a per-query softmax written out in numpy: block u's row is the mean
+    of its members' distributions, whatever their positions in the sequence."""
+    rng = np.random.default_rng(34)
+    Q = rng.normal(0, 1, (12, 4)).astype(np.float32)
+    C = rng.normal(0, 1, (3, 4)).astype(np.float32)
+    counts = np.array([2, 5, 1], np.int32)
+    qperm = np.array([5, 0, 11, 3, 7, 1, 2, 4, 6, 8, 9, 10], np.int32)
+    qoff = np.array([0, 3, 4, 12], np.int32)
+    W = orc.pama_blocks(Q, C, counts, qperm, qoff, 0.5)
+    S = 0.5 * Q.astype(np.float64) @ C.astype(np.float64).T + np.log(counts)
+    P = np.exp(S - S.max(1, keepdims=True)); P /= P.sum(1, keepdims=True)
+    for u in range(3):
+        np.testing.assert_allclose(W[u], P[qperm[qoff[u]:qoff[u + 1]]].mean(0), rtol=1e-13)
+
+
+def test_attention_blocks_reduces_to_consecutive_blocks(orc):
+    """Identity permutation with 64-token boundaries: the clustered-block attention is the
+    64-token routine exactly (same keys, same order, same arithmetic per query)."""
+    Q, K, V = _rand_qk(200, 16, 35)
+    cl = orc.cluster_keys(Q, K, 6, 2)
+    W = orc.pama(Q, cl["centroids"], cl["counts"], 64, 0.25)
+    _, lst, cnt, _, _ = orc.select(W, cl["counts"], 0.8, 2)
+    qperm, qoff = _consecutive_blocks(200, 64)
+    O, lse = orc.block_sparse_attn_blocks(Q, K, V, cl["perm"], cl["offsets"], qperm, qoff, lst, cnt, 0.25)
+    O2, lse2 = orc.block_sparse_attn(Q, K, V, cl["perm"], cl["offsets"], lst, cnt, 64, 0.25)
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_attention_blocks_density_one_equals_dense(orc):
+    """Every key cluster selected for every clustered query block: dense attention (the
+    independent textbook routine), for queries scattered across the blocks."""
+    Q, K, V = _rand_qk(180, 8, 36, centres=5)
+    cl = orc.cluster_keys(Q, K, 5, 2)
+    qc = orc.cluster_queries(Q, 4, 3)
+    lst = np.tile(np.arange(5, dtype=np.int32), (4, 1)); cnt = np.full(4, 5, np.int32)
+    O, lse = orc.block_sparse_attn_blocks(Q, K, V, cl["perm"], cl["offsets"], qc["perm"], qc["offsets"], lst,
+                                          cnt, 0.4)
+    Od, lsed = orc.dense_attn(Q, K, V, 0.4)
+    np.testing.assert_allclose(O, Od, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lsed, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_blocks_follow_each_query_block(orc):
+    """Each query gets its own block's selection: with one cluster selected per block, query i
+    of block u attends exactly to the keys of that cluster (checked against the 64-token routine
+    run on that query alone as a one-query block)."""
+    Q, K, V = _rand_qk(90, 6, 37, centres=3)
+    cl = orc.cluster_keys(Q, K, 3, 2)
+    qc = orc.cluster_queries(Q, 3, 3)
+    lst = np.array([[2, -1, -1], [0, -1, -1], [1, -1, -1]], np.int32); cnt = np.ones(3, np.int32)
+    O, lse = orc.block_sparse_attn_blocks(Q, K, V, cl["perm"], cl["offsets"], qc["perm"], qc["offsets"], lst,
+                                          cnt, 0.5)
+    for u in range(3):
+        for i in qc["perm"][qc["offsets"][u]:qc["offsets"][u + 1]][:4]:
+            o1, l1 = orc.block_sparse_attn(Q[i:i + 1], K, V, cl["perm"], cl["offsets"], lst[u:u + 1],
+                                           cnt[u:u + 1], 1, 0.5)
+            np.testing.assert_array_equal(O[i], o1[0])
+            assert lse[i] == l1[0]
+
+
+def test_query_clustering_blocks_hold_their_members(orc):
+    """Query blocks from Euclidean k-means of the queries: block u's queries all carry label u,
+    the permutation covers every query once, and the blocks partition the sequence."""
+    Q, _, _ = _rand_qk(256, 16, 38, centres=6)
+    qc = orc.cluster_queries(Q, 8, 4)
+    assert np.array_equal(np.sort(qc["perm"]), np.arange(256))
+    assert qc["offsets"][0] == 0 and qc["offsets"][-1] == 256
+    for u in range(8):
+        assert np.all(qc["labels"][qc["perm"][qc["offsets"][u]:qc["offsets"][u + 1]]] == u)
