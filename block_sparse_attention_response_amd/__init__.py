@@ -9,6 +9,13 @@ declared in include/park.h:
   park_retrieve_blocks_pooled  the pooled-query baseline (section 4.1)
   park_block_sparse_attn   attention over the selected blocks (section 3.1)
 
+and, for query blocks formed by Euclidean k-means of the queries (PARK's own setting,
+Figure 2 and section 6):
+
+  park_cluster_queries             the query blocks
+  park_retrieve_blocks_clustered   PAMA + selection over them
+  park_block_sparse_attn_clustered attention over them
+
 There is no fallback: if libpark.so is missing or was built for another GPU the calls
 raise.
 """
@@ -21,6 +28,8 @@ import os
 __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
     "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
+    "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
+    "park_block_sparse_attn_clustered",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
     "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
@@ -67,6 +76,16 @@ def lib():
         L.park_block_sparse_attn.restype = _I
         L.park_block_sparse_attn_timed.argtypes = L.park_block_sparse_attn.argtypes + [_P, _P]
         L.park_block_sparse_attn_timed.restype = _I
+        L.park_workspace_bytes_clustered.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+        L.park_workspace_bytes_clustered.restype = _S
+        L.park_cluster_queries.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+        L.park_cluster_queries.restype = _I
+        L.park_retrieve_blocks_clustered.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _I, _F,
+                                                     _P, _P, _P, _P, _P, _S, _P]
+        L.park_retrieve_blocks_clustered.restype = _I
+        L.park_block_sparse_attn_clustered.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P,
+                                                       _P, _F, _P, _P, _P, _S, _P]
+        L.park_block_sparse_attn_clustered.restype = _I
         _lib = L
     return _lib
 
@@ -84,6 +103,10 @@ def park_abi_version() -> int:
 
 def workspace_bytes(op: int, B: int, H: int, N: int, d: int, n_clusters: int) -> int:
     return int(lib().park_workspace_bytes(op, B, H, N, d, n_clusters))
+
+
+def workspace_bytes_clustered(op: int, B: int, H: int, N: int, d: int, n_clusters: int, n_qblocks: int) -> int:
+    return int(lib().park_workspace_bytes_clustered(op, B, H, N, d, n_clusters, n_qblocks))
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -242,6 +265,98 @@ def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scal
         _check(lib().park_block_sparse_attn(*args), "park_block_sparse_attn")
     else:
         _check(lib().park_block_sparse_attn_timed(*args, events[0], events[1]), "park_block_sparse_attn_timed")
+    return O, (lse if want_lse else None)
+
+
+def park_cluster_queries(Q, n_qblocks: int, iters: int, init_idx=None, workspace=None):
+    """Query blocks by Euclidean k-means of the queries.  Returns a dict of GPU tensors:
+    centroids [B,H,n_qblocks,d] float32, counts [B,H,n_qblocks], labels [B,H,N],
+    perm [B,H,N] (the q_perm of the clustered calls), offsets [B,H,n_qblocks+1] (q_offsets)."""
+    torch = _torch()
+    _dev(Q, "Q")
+    B, H, N, d = _bhnd(Q, "Q")
+    dev = Q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(centroids=torch.empty(B, H, n_qblocks, d, dtype=torch.float32, device=dev),
+               counts=torch.empty(B, H, n_qblocks, **i32), labels=torch.empty(B, H, N, **i32),
+               perm=torch.empty(B, H, N, **i32), offsets=torch.empty(B, H, n_qblocks + 1, **i32))
+    if init_idx is not None:
+        _dev(init_idx, "init_idx")
+        if init_idx.dtype != torch.int32 or init_idx.numel() != n_qblocks:
+            raise ValueError("init_idx must be int32 [n_qblocks]")
+    ws, wsb = _workspace(workspace_bytes(OP_CLUSTER_KEYS, B, H, N, d, n_qblocks), dev, workspace)
+    st = lib().park_cluster_queries(_ptr(Q), _dtype_code(Q), B, H, N, d, n_qblocks, iters, _ptr(init_idx),
+                                    _ptr(out["centroids"]), _ptr(out["counts"]), _ptr(out["labels"]),
+                                    _ptr(out["perm"]), _ptr(out["offsets"]), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_cluster_queries")
+    return out
+
+
+def _qblocks(q_perm, q_offsets, B, H, N):
+    _dev(q_perm, "q_perm"); _dev(q_offsets, "q_offsets")
+    nq = q_offsets.shape[-1] - 1
+    if q_perm.shape != (B, H, N) or q_offsets.shape != (B, H, nq + 1):
+        raise ValueError("q_perm must be [B, H, N] and q_offsets [B, H, n_qblocks + 1]")
+    return nq
+
+
+def park_retrieve_blocks_clustered(Q, centroids, counts, q_perm, q_offsets, top_p: float, top_k: int, scale=None,
+                                   scores: bool = True, workspace=None):
+    """PAMA and the top-p / top-k selection over clustered query blocks (q_perm / q_offsets as
+    park_cluster_queries returns them).  Returns dict(scores?, mask, block_list, block_count)
+    with n_qblocks rows per head."""
+    torch = _torch()
+    _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
+    B, H, N, d = _bhnd(Q, "Q")
+    nk = centroids.shape[2]
+    if centroids.shape != (B, H, nk, d) or centroids.dtype != torch.float32:
+        raise ValueError("centroids must be float32 [B, H, n_clusters, d]")
+    if counts.shape != (B, H, nk) or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [B, H, n_clusters]")
+    nq = _qblocks(q_perm, q_offsets, B, H, N)
+    dev = Q.device
+    out = dict(mask=torch.empty(B, H, nq, nk, dtype=torch.uint8, device=dev),
+               block_list=torch.empty(B, H, nq, nk, dtype=torch.int32, device=dev),
+               block_count=torch.empty(B, H, nq, dtype=torch.int32, device=dev))
+    if scores:
+        out["scores"] = torch.empty(B, H, nq, nk, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(workspace_bytes_clustered(OP_RETRIEVE_BLOCKS, B, H, N, d, nk, nq), dev, workspace)
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_retrieve_blocks_clustered(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts),
+                                              nk, _ptr(q_perm), _ptr(q_offsets), nq, float(top_p), int(top_k), sc,
+                                              _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
+                                              _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_retrieve_blocks_clustered")
+    return out
+
+
+def park_block_sparse_attn_clustered(Q, K, V, perm, offsets, q_perm, q_offsets, block_list, block_count, scale=None,
+                                     want_lse: bool = True, out=None, lse=None, workspace=None):
+    """Attention over the clusters selected for each clustered query block.  Returns
+    (O [B,H,N,d] in Q's dtype, lse [B,H,N] float32 or None), in the original query order."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (perm, "perm"), (offsets, "offsets"),
+                 (block_list, "block_list"), (block_count, "block_count")):
+        _dev(t, n)
+    B, H, N, d = _bhnd(Q, "Q")
+    if K.shape != Q.shape or V.shape != Q.shape or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("K and V must match Q in shape and dtype")
+    nk = offsets.shape[-1] - 1
+    nq = _qblocks(q_perm, q_offsets, B, H, N)
+    if block_list.shape != (B, H, nq, nk) or block_count.shape != (B, H, nq):
+        raise ValueError("block_list must be [B, H, n_qblocks, n_clusters] and block_count [B, H, n_qblocks]")
+    if perm.shape != (B, H, N) or offsets.shape != (B, H, nk + 1):
+        raise ValueError("perm must be [B, H, N] and offsets [B, H, n_clusters + 1]")
+    O = torch.empty_like(Q) if out is None else out
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
+    sc = -1.0 if scale is None else float(scale)
+    ws, wsb = _workspace(workspace_bytes_clustered(OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk, nq), Q.device, workspace)
+    st = lib().park_block_sparse_attn_clustered(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), B, H, N, d, _ptr(perm),
+                                                _ptr(offsets), nk, _ptr(q_perm), _ptr(q_offsets), nq,
+                                                _ptr(block_list), _ptr(block_count), sc, _ptr(O),
+                                                _ptr(lse if want_lse else None), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_block_sparse_attn_clustered")
     return O, (lse if want_lse else None)
 
 

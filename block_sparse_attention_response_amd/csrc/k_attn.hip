@@ -303,6 +303,53 @@ __device__ __forceinline__ int block_excl_scan(int x, int* wsum, int* total) {
   return ex;
 }
 
+// Chunk tables of clustered query blocks (one workgroup per head, two blocks per thread):
+// block u of n_u queries is split into ceil(n_u / 64) chunks of consecutive positions.
+constexpr int kQcPer = 2;
+__global__ __launch_bounds__(1024) void k_qchunks(const int32_t* __restrict__ qoffsets, int N, int NQ, int maxc,
+                                                  int4* __restrict__ chunks, int32_t* __restrict__ cbase,
+                                                  int32_t* __restrict__ ctotal) {
+  __shared__ int wsum[16];
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int32_t* off = qoffsets + (size_t)bh * (NQ + 1);
+  int st[kQcPer], n[kQcPer], s = 0;
+#pragma unroll
+  for (int j = 0; j < kQcPer; ++j) {
+    const int u = kQcPer * t + j;
+    st[j] = 0;
+    n[j] = 0;
+    if (u < NQ) {
+      const int a = min(max(off[u], 0), N), b = min(max(off[u + 1], a), N);
+      st[j] = a;
+      n[j] = b - a;
+    }
+    s += (n[j] + 63) >> 6;
+  }
+  int tot;
+  int c = block_excl_scan(s, wsum, &tot);
+  int32_t* cb = cbase + (size_t)bh * (NQ + 1);
+#pragma unroll
+  for (int j = 0; j < kQcPer; ++j) {
+    const int u = kQcPer * t + j;
+    if (u < NQ) {
+      cb[u] = min(c, maxc);
+      for (int k = 0; k < n[j]; k += 64, ++c)
+        if (c < maxc) chunks[(size_t)bh * maxc + c] = make_int4(u, st[j] + k, min(64, n[j] - k), 0);
+    }
+  }
+  if (t == 0) {
+    cb[NQ] = min(tot, maxc);
+    ctotal[bh] = min(tot, maxc);
+  }
+}
+
+hipError_t launch_qchunks(const int32_t* qoffsets, int BH, int N, int NQ, int maxc, int4* chunks,
+                          int32_t* cbase, int32_t* ctotal, hipStream_t st) {
+  if (NQ > kQcPer * 1024) return hipErrorInvalidValue;
+  k_qchunks<<<BH, 1024, 0, st>>>(qoffsets, N, NQ, maxc, chunks, cbase, ctotal);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(1024) void k_scan_blocks(const int32_t* __restrict__ x, int n, int32_t* __restrict__ bsum) {
   __shared__ int wsum[16];
   const int b0 = blockIdx.x * kScanBlock + threadIdx.x * 4;
@@ -460,7 +507,9 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
                                           const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
                                           const int32_t* __restrict__ plan, const int32_t* __restrict__ tbase,
                                           const float* __restrict__ vmax, int N, int NQ, int Gcap, float scale2,
-                                          f16* __restrict__ Opart, float2* __restrict__ ML) {
+                                          f16* __restrict__ Opart, float2* __restrict__ ML,
+                                          const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
+                                          const int32_t* __restrict__ qperm, int maxc) {
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
   static_assert(KC == 2 * DT, "K and V batches have the same size");
@@ -468,15 +517,37 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   auto& Vs = sm.Vs;
   auto& pring = sm.pring;
   auto& btab = sm.btab;
-  const int rr = item % kRanges, row = item / kRanges;
-  const int bh = row / NQ, u = row - bh * NQ;
+  const int rr = item % kRanges;
   const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
-  const int t0 = tbase[item];
-  const int nt = tbase[item + 1] - t0;
+  // The item's queries: 64-token blocks (chunks == NULL): block u = item / kRanges of the
+  // plan rows, tokens 64u + i.  Clustered query blocks: item / kRanges = (head, chunk slot);
+  // chunk (u, p0, n) of block u holds positions p0 .. p0 + n - 1 of qperm, and the plan row
+  // is block u's.
+  int bh, prow, p0, nq;
+  if (chunks) {
+    const int cr = item / kRanges;
+    bh = cr / maxc;
+    const int c = cr - bh * maxc;
+    if (c >= ctotal[bh]) return;
+    const int4 ch = chunks[(size_t)bh * maxc + c];
+    prow = bh * NQ + ch.x;
+    p0 = ch.y;
+    nq = ch.z;
+  } else {
+    prow = item / kRanges;
+    bh = prow / NQ;
+    p0 = 64 * (prow - bh * NQ);
+    nq = min(64, N - p0);
+  }
   const size_t hrow = (size_t)bh * N;
+  // query index of position i < nq of the item
+  auto query = [&](int i) __attribute__((always_inline)) {
+    return qperm ? min(max(qperm[hrow + p0 + i], 0), N - 1) : p0 + i;
+  };
+  const int t0 = tbase[(size_t)prow * kRanges + rr];
+  const int nt = tbase[(size_t)prow * kRanges + rr + 1] - t0;
   if (nt <= 0) {
-    const int q = 64 * u + lane;
-    if (q < N) ML[(hrow + q) * kRanges + rr] = make_float2(-INFINITY, 0.0f);
+    if (lane < nq) ML[(hrow + query(lane)) * kRanges + rr] = make_float2(-INFINITY, 0.0f);
     return;
   }
   const int32_t* pl = plan + (size_t)t0 * 4;
@@ -530,15 +601,18 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     return *reinterpret_cast<const int4*>(&pring[slot][4 * j]);
   };
 
-  // Q^T fragments of query halves 0 and 1 in registers
+  // Q^T fragments of query halves 0 and 1 in registers (qrow: this lane's query of each
+  // half, -1 past the item's queries)
   bf16x8 qf[2][KC];
+  int qrow[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) qrow[h2] = 32 * h2 + l32 < nq ? query(32 * h2 + l32) : -1;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    const int qrow = 64 * u + 32 * h2 + l32;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      if (qrow < N) {
-        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow) * D + kc * 16 + 8 * h);
+      if (qrow[h2] >= 0) {
+        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow[h2]) * D + kc * 16 + 8 * h);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) qf[h2][kc][i] = (bf16)0.0f;
@@ -843,10 +917,9 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   for (int h2 = 0; h2 < 2; ++h2) {
     const float l = lsum[h2] + __shfl_xor(lsum[h2], 32);
     const float lbs = lb[h2] + __shfl_xor(lb[h2], 32);
-    const int qrow = 64 * u + 32 * h2 + l32;
-    if (qrow < N) {
+    if (qrow[h2] >= 0) {
       const float inv = lbs > 0.0f ? 1.0f / (lbs * unit) : 0.0f;
-      f16* orow = Opart + ((hrow + qrow) * kRanges + rr) * D;
+      f16* orow = Opart + ((hrow + qrow[h2]) * kRanges + rr) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -856,7 +929,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
           for (int i = 0; i < 4; ++i) o[i] = (f16)(oacc[h2][dt][4 * g + i] * inv);
           *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
-      if (h == 0) ML[(hrow + qrow) * kRanges + rr] = make_float2(m[h2], l);
+      if (h == 0) ML[(hrow + qrow[h2]) * kRanges + rr] = make_float2(m[h2], l);
     }
   }
 }
@@ -872,7 +945,9 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
                                                    const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
                                                    const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
                                                    int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
-                                                   float2* __restrict__ ML, int items, int32_t* __restrict__ ictr) {
+                                                   float2* __restrict__ ML, int items, int32_t* __restrict__ ictr,
+                                                   const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
+                                                   const int32_t* __restrict__ qperm, int maxc) {
   __shared__ AttnLds<D> sm;
   const int lane = threadIdx.x;
   for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
@@ -880,7 +955,7 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   for (int item = blockIdx.x; item < items;) {
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&ictr[xr], 1);
-    attn_item<D>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML);
+    attn_item<D>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal, qperm, maxc);
     item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(nxt);
   }
 }
@@ -941,21 +1016,37 @@ __global__ __launch_bounds__(128) void k_attn_f32(const float* __restrict__ Q, c
                                                   const int32_t* __restrict__ offsets,
                                                   const int32_t* __restrict__ list,
                                                   const int32_t* __restrict__ count, int N, int nk, int NQ,
-                                                  float scale2, float* __restrict__ O, float* __restrict__ lse) {
+                                                  float scale2, float* __restrict__ O, float* __restrict__ lse,
+                                                  const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
+                                                  const int32_t* __restrict__ qperm, int maxc) {
   __shared__ float Ks[64][D + 1];
   __shared__ float Vs[64][D + 1];
   __shared__ int pre[PARK_MAX_CLUSTERS + 1];
   __shared__ int kidx[64];
   __shared__ int wsum[2];
-  const int bh = blockIdx.y, u = blockIdx.x, tid = threadIdx.x;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  // workgroup blockIdx.x: 64-token block u (chunks == NULL), or chunk (u, p0, n) of a
+  // clustered query block (positions p0 .. p0 + n - 1 of qperm)
+  int u, p0, nq;
+  if (chunks) {
+    if ((int)blockIdx.x >= ctotal[bh]) return;
+    const int4 ch = chunks[(size_t)bh * maxc + blockIdx.x];
+    u = ch.x;
+    p0 = ch.y;
+    nq = ch.z;
+  } else {
+    u = blockIdx.x;
+    p0 = 64 * u;
+    nq = min(64, N - p0);
+  }
   const size_t row = (size_t)bh * NQ + u;
   const int cnt = min(max(count[row], 0), nk);
   const int32_t* lst = list + row * nk;
   const int32_t* off = offsets + (size_t)bh * (nk + 1);
   const int32_t* pm = perm + (size_t)bh * N;
   const int T = selected_prefix(lst, off, cnt, nk, pre, wsum);
-  const int qrow = 64 * u + tid;
-  const bool active = tid < 64 && qrow < N;
+  const bool active = tid < nq;
+  const int qrow = !active ? 0 : qperm ? min(max(qperm[(size_t)bh * N + p0 + tid], 0), N - 1) : p0 + tid;
   float q[D], o[D];
 #pragma unroll
   for (int a = 0; a < D; ++a) {
@@ -1011,18 +1102,32 @@ struct AttnWs {
   bf16 *Kp, *Vp;
   f16* Opart;
   float2* ML;
+  int4* chunks;               // clustered query blocks only
+  int32_t *cbase, *ctotal;
 };
 
-static AttnWs carve_attn(const Shape& s, void* base, size_t* total) {
-  const size_t rows = (size_t)s.BH * n_qblocks(s.N);
+// Workspace layout; the float path needs only the chunk tables of clustered query blocks.
+static AttnWs carve_attn(const Shape& s, const QueryBlocks* qb, void* base, size_t* total) {
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  AttnWs w{};
+  if (qb) {
+    const int maxc = chunk_slots(s.N, qb->NQ);
+    w.chunks = reinterpret_cast<int4*>(take((size_t)s.BH * maxc * sizeof(int4)));
+    w.cbase = reinterpret_cast<int32_t*>(take((size_t)s.BH * (qb->NQ + 1) * sizeof(int32_t)));
+    w.ctotal = reinterpret_cast<int32_t*>(take((size_t)s.BH * sizeof(int32_t)));
+  }
+  if (s.dtype != 1) {
+    if (total) *total = (size_t)(p - static_cast<char*>(base));
+    return w;
+  }
+  // plan rows: one per query block
+  const size_t rows = (size_t)s.BH * (qb ? qb->NQ : n_qblocks(s.N));
   const size_t items = rows * kRanges;
   const size_t kv = (size_t)s.BH * (group_cap(s) + 1) * 8 * s.d * sizeof(bf16);
   // plan entries of one query block: at most every group of its head, plus the filler of
   // one partial tile per range
   const size_t per_row = (size_t)group_cap(s) + 4 * kRanges;
-  char* p = static_cast<char*>(base);
-  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
-  AttnWs w;
   w.gstart = reinterpret_cast<int32_t*>(take((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)));
   w.rng = reinterpret_cast<int32_t*>(take((size_t)s.BH * s.nk * sizeof(int32_t)));
   w.vmax = reinterpret_cast<float*>(take((size_t)s.BH * sizeof(float)));
@@ -1056,23 +1161,33 @@ static int compute_units() {
   return n;
 }
 
-size_t attn_workspace(const Shape& s) {
-  if (s.dtype != 1) return 0;
+size_t attn_workspace(const Shape& s, const QueryBlocks* qb) {
   size_t total = 0;
-  carve_attn(s, nullptr, &total);
+  carve_attn(s, qb, nullptr, &total);
   return total;
 }
 
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
-                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  const int NQ = n_qblocks(s.N);
+                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
+                       const QueryBlocks* qb) {
+  // query blocks per head (plan rows) and chunk slots per head (clustered blocks)
+  const int NQ = qb ? qb->NQ : n_qblocks(s.N);
+  const int maxc = qb ? chunk_slots(s.N, qb->NQ) : 0;
   const float scale2 = scale * kLog2e;
+  AttnWs w = carve_attn(s, qb, ws, nullptr);
+  const int32_t* qperm = qb ? qb->qperm : nullptr;
+  if (qb) {
+    hipError_t e = launch_qchunks(qb->qoffsets, s.BH, s.N, NQ, maxc, w.chunks, w.cbase, w.ctotal, st);
+    if (e != hipSuccess) return e;
+  }
   if (s.dtype == 1) {
     const int Gcap = group_cap(s);
     const int rows = s.BH * NQ;
     const int items = rows * kRanges;
-    AttnWs w = carve_attn(s, ws, nullptr);
+    // attention items: (plan row, range), or (head, chunk slot, range) for clustered blocks
+    const long long aitems = qb ? (long long)s.BH * maxc * kRanges : (long long)items;
+    if (aitems >= (1LL << 31)) return hipErrorInvalidValue;
     auto k = reinterpret_cast<const bf16*>(K);
     auto v = reinterpret_cast<const bf16*>(V);
     auto q = reinterpret_cast<const bf16*>(Q);
@@ -1102,13 +1217,13 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
     // persistent waves: as many as the chip holds (four per CU, bound by LDS), a multiple of
     // kRanges (items is one)
-    const int waves = std::min(items, 4 * compute_units() / kRanges * kRanges);
+    const int waves = (int)std::min<long long>(aitems, 4 * compute_units() / kRanges * kRanges);
     if (s.d == 128)
       k_attn_items<128><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
-                                              w.ML, items, w.ictr);
+                                              w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc);
     else
       k_attn_items<64><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
-                                             w.ML, items, w.ictr);
+                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc);
     PARK_CHECK();
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     const int total_rows = s.BH * s.N;
@@ -1119,15 +1234,17 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     PARK_CHECK();
 #undef PARK_CHECK
   } else {
-    dim3 grid(NQ, s.BH);
+    dim3 grid(qb ? maxc : NQ, s.BH);
     auto q = reinterpret_cast<const float*>(Q);
     auto k = reinterpret_cast<const float*>(K);
     auto v = reinterpret_cast<const float*>(V);
     auto o = reinterpret_cast<float*>(O);
     if (s.d == 128)
-      k_attn_f32<128><<<grid, 128, 0, st>>>(q, k, v, perm, offsets, list, count, s.N, s.nk, NQ, scale2, o, lse);
+      k_attn_f32<128><<<grid, 128, 0, st>>>(q, k, v, perm, offsets, list, count, s.N, s.nk, NQ, scale2, o, lse,
+                                            w.chunks, w.ctotal, qperm, maxc);
     else
-      k_attn_f32<64><<<grid, 128, 0, st>>>(q, k, v, perm, offsets, list, count, s.N, s.nk, NQ, scale2, o, lse);
+      k_attn_f32<64><<<grid, 128, 0, st>>>(q, k, v, perm, offsets, list, count, s.N, s.nk, NQ, scale2, o, lse,
+                                           w.chunks, w.ctotal, qperm, maxc);
   }
   return hipGetLastError();
 }

@@ -72,7 +72,9 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int l32) {
 template <int D, int VT, bool QF32>
 __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const bf16* __restrict__ Chi,
                                               const bf16* __restrict__ Clo, int N, int nk, int nkp, int NQ,
-                                              float* __restrict__ W) {
+                                              float* __restrict__ W, const int4* __restrict__ chunks,
+                                              const int32_t* __restrict__ ctotal,
+                                              const int32_t* __restrict__ qperm, int maxc) {
   constexpr int DK = D + 16;       // columns of the extended product
   constexpr int KC = DK / 16;
   constexpr int QP = DK + 8;       // padded LDS row
@@ -84,8 +86,20 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int u = blockIdx.x, bh = blockIdx.y;
-  const int q0 = u * 64;
-  const int nu = min(64, N - q0);
+  // 64-token blocks: block u is tokens [64u, 64u + 64) and W row u gets the mean.  Clustered
+  // query blocks (chunks != NULL): workgroup u is chunk u of the head, positions
+  // [q0, q0 + nu) of qperm, and its W row gets the chunk's column sums (k_pama_reduce then
+  // adds the chunks of each block and divides by n_u).
+  int q0, nu;
+  if (chunks) {
+    if (u >= ctotal[bh]) return;
+    const int4 ch = chunks[(size_t)bh * maxc + u];
+    q0 = ch.y;
+    nu = ch.z;
+  } else {
+    q0 = u * 64;
+    nu = min(64, N - q0);
+  }
 
   for (int e = tid; e < 64 * (DK / 8); e += blockDim.x) {
     const int row = e / (DK / 8), seg = e % (DK / 8);
@@ -94,7 +108,8 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     for (int i = 0; i < 8; ++i) { hi[i] = (bf16)0.0f; lo[i] = (bf16)0.0f; }
     if (seg * 8 < D) {
       if (row < nu) {
-        const size_t off = ((size_t)bh * N + q0 + row) * D + seg * 8;
+        const int qi = qperm ? min(max(qperm[(size_t)bh * N + q0 + row], 0), N - 1) : q0 + row;
+        const size_t off = ((size_t)bh * N + qi) * D + seg * 8;
         if constexpr (QF32) {
           const float* q = reinterpret_cast<const float*>(Qv) + off;
 #pragma unroll
@@ -274,7 +289,8 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
       for (int i = 0; i < 4; ++i) ri[qt][4 * g + i] = x[i];
     }
-  const float inv_nu = 1.0f / (float)nu;
+  const float inv_nu = chunks ? 1.0f : 1.0f / (float)nu;
+  const size_t wrow = (size_t)bh * (chunks ? maxc : NQ) + u;
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt) {
     float cs = 0.0f;
@@ -284,8 +300,26 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       for (int r = 0; r < 16; ++r) cs = fmaf(acc[qt][vt][r], ri[qt][r], cs);
     cs += __shfl_xor(cs, 32);
     const int v = v0 + 32 * vt + l32;
-    if (h == 0 && v < nk) W[((size_t)bh * NQ + u) * nk + v] = cs * inv_nu;
+    if (h == 0 && v < nk) W[wrow * nk + v] = cs * inv_nu;
   }
+}
+
+// Clustered query blocks: W_uv = (1/n_u) sum over the chunks of block u of their column sums
+// (chunks in order, float).  grid (ceil(nk / 256), NQ, BH).
+__global__ __launch_bounds__(256) void k_pama_reduce(const float* __restrict__ Wp, const int4* __restrict__ chunks,
+                                                     const int32_t* __restrict__ cbase, int nk, int NQ, int maxc,
+                                                     float* __restrict__ W) {
+  const int v = blockIdx.x * 256 + threadIdx.x, u = blockIdx.y, bh = blockIdx.z;
+  if (v >= nk) return;
+  const int32_t* cb = cbase + (size_t)bh * (NQ + 1);
+  const int c0 = cb[u], c1 = cb[u + 1];
+  float acc = 0.0f;
+  int n = 0;
+  for (int c = c0; c < c1; ++c) {
+    acc += Wp[((size_t)bh * maxc + c) * nk + v];
+    n += chunks[(size_t)bh * maxc + c].z;
+  }
+  W[((size_t)bh * NQ + u) * nk + v] = n > 0 ? acc / (float)n : 0.0f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -492,18 +526,52 @@ size_t retrieve_workspace(const Shape& s, bool need_scores) {
   return b;
 }
 
+// chunks == nullptr: 64-token blocks, W [BH][NQ][nk] means; otherwise one workgroup per chunk
+// slot, W [BH][maxc][nk] column sums
 template <int D, bool QF32>
 static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo,
-                                float* W, hipStream_t st) {
+                                float* W, hipStream_t st, const int4* chunks = nullptr,
+                                const int32_t* ctotal = nullptr, const int32_t* qperm = nullptr, int maxc = 0) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   const int vt = (nkp + 255) / 256;
   const int nw = (nkp + 32 * vt - 1) / (32 * vt);
-  dim3 grid(NQ, s.BH), block(64 * nw);
+  dim3 grid(chunks ? maxc : NQ, s.BH), block(64 * nw);
   switch (vt) {
 #define PARK_PAMA_CASE(V) \
-  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W); break;
+  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W, chunks, ctotal, qperm, maxc); \
+    break;
     PARK_PAMA_CASE(1) PARK_PAMA_CASE(2) PARK_PAMA_CASE(3) PARK_PAMA_CASE(4) PARK_PAMA_CASE(5) PARK_PAMA_CASE(6)
 #undef PARK_PAMA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// workspace of the clustered-block retrieval: Chi, Clo, lg, W (when not returned), per-chunk
+// column sums and the chunk tables
+size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores) {
+  const int nkp = nk_pad32(s.nk), maxc = chunk_slots(s.N, NQ);
+  size_t b = 0;
+  b += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)) * 2;  // Chi, Clo
+  b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
+  if (need_scores) b += align256((size_t)s.BH * NQ * s.nk * sizeof(float));
+  b += align256((size_t)s.BH * maxc * s.nk * sizeof(float));   // chunk column sums
+  b += align256((size_t)s.BH * maxc * sizeof(int4));           // chunks
+  b += align256((size_t)s.BH * (NQ + 1) * sizeof(int32_t));     // cbase
+  b += align256((size_t)s.BH * sizeof(int32_t));                // ctotal
+  return b;
+}
+
+// top-p / top-k selection of `rows` score rows (NQ per head)
+static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int NQ, int rows, float top_p,
+                              int top_k, uint8_t* mask, int32_t* list, int32_t* count, hipStream_t st) {
+  const int sgrid = (rows + 3) / 4;
+  const int epl = (nk + 63) / 64;
+  switch (epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : epl <= 16 ? 16 : 32) {
+#define PARK_SEL_CASE(E) \
+  case E: k_select<E><<<sgrid, 256, 0, st>>>(W, counts, nk, NQ, rows, top_p, top_k, mask, list, count); break;
+    PARK_SEL_CASE(1) PARK_SEL_CASE(2) PARK_SEL_CASE(4) PARK_SEL_CASE(8) PARK_SEL_CASE(16) PARK_SEL_CASE(32)
+#undef PARK_SEL_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -542,17 +610,42 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
                      : launch_pama_d<64, true>(s, Q, Chi, Clo, W, st);
   }
   if (e != hipSuccess) return e;
-  const int rows = s.BH * NQ;
-  const int sgrid = (rows + 3) / 4;
-  const int epl = (s.nk + 63) / 64;
-  switch (epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : epl <= 16 ? 16 : 32) {
-#define PARK_SEL_CASE(E) \
-  case E: k_select<E><<<sgrid, 256, 0, st>>>(W, counts, s.nk, NQ, rows, top_p, top_k, mask, list, count); break;
-    PARK_SEL_CASE(1) PARK_SEL_CASE(2) PARK_SEL_CASE(4) PARK_SEL_CASE(8) PARK_SEL_CASE(16) PARK_SEL_CASE(32)
-#undef PARK_SEL_CASE
-    default: return hipErrorInvalidValue;
+  return select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st);
+}
+
+hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
+                                     const QueryBlocks& qb, float scale, float top_p, int top_k, float* scores,
+                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st) {
+  const int nkp = nk_pad32(s.nk), NQ = qb.NQ, maxc = chunk_slots(s.N, NQ);
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  bf16* Chi = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)));
+  bf16* Clo = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)));
+  float* lg = reinterpret_cast<float*>(take((size_t)s.BH * nkp * sizeof(float)));
+  float* W = scores ? scores : reinterpret_cast<float*>(take((size_t)s.BH * NQ * s.nk * sizeof(float)));
+  float* Wp = reinterpret_cast<float*>(take((size_t)s.BH * maxc * s.nk * sizeof(float)));
+  int4* chunks = reinterpret_cast<int4*>(take((size_t)s.BH * maxc * sizeof(int4)));
+  int32_t* cbase = reinterpret_cast<int32_t*>(take((size_t)s.BH * (NQ + 1) * sizeof(int32_t)));
+  int32_t* ctotal = reinterpret_cast<int32_t*>(take((size_t)s.BH * sizeof(int32_t)));
+  const float scale2 = scale * kLog2e;
+  {
+    dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
+    k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, scale2, Chi, Clo, lg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  hipError_t e = launch_qchunks(qb.qoffsets, s.BH, s.N, NQ, maxc, chunks, cbase, ctotal, st);
+  if (e != hipSuccess) return e;
+  if (s.d == 128)
+    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc)
+                     : launch_pama_d<128, true>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc);
+  else
+    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc)
+                     : launch_pama_d<64, true>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc);
+  if (e != hipSuccess) return e;
+  k_pama_reduce<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(Wp, chunks, cbase, s.nk, NQ, maxc, W);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st);
 }
 
 }  // namespace park

@@ -51,6 +51,13 @@ int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, in
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
+// clustered query blocks: n_qblocks in [1, min(N, PARK_MAX_QUERY_BLOCKS)], both tables given
+int check_qblocks(int N, const int32_t* q_perm, const int32_t* q_offsets, int n_qblocks) {
+  if (!q_perm || !q_offsets || n_qblocks < 1 || n_qblocks > N) return PARK_ERR_INVALID;
+  if (n_qblocks > PARK_MAX_QUERY_BLOCKS) return PARK_ERR_UNSUPPORTED;
+  return PARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +86,35 @@ size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_clusters) 
     case PARK_OP_BLOCK_SPARSE_ATTN: return park::attn_workspace(s);
     default: return 0;
   }
+}
+
+size_t park_workspace_bytes_clustered(int op, int B, int H, int N, int d, int n_clusters, int n_qblocks) {
+  bool uns;
+  if (check_common(PARK_BF16, B, H, N, d, n_clusters, &uns) != PARK_OK) return 0;
+  if (n_qblocks < 1 || n_qblocks > N || n_qblocks > PARK_MAX_QUERY_BLOCKS) return 0;
+  const Shape s = make_shape(PARK_BF16, B, H, N, d, n_clusters);
+  const park::QueryBlocks qb{nullptr, nullptr, n_qblocks};
+  switch (op) {
+    case PARK_OP_CLUSTER_KEYS: return park::cluster_workspace(s);
+    case PARK_OP_RETRIEVE_BLOCKS: return park::retrieve_clustered_workspace(s, n_qblocks, true);
+    case PARK_OP_BLOCK_SPARSE_ATTN: return park::attn_workspace(s, &qb);
+    default: return 0;
+  }
+}
+
+int park_cluster_queries(const void* Q, int dtype, int B, int H, int N, int d, int n_qblocks, int iters,
+                         const int32_t* init_idx, float* centroids, int32_t* counts, int32_t* labels, int32_t* perm,
+                         int32_t* offsets, void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_qblocks, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !centroids || !counts || !labels || !perm || !offsets || iters < 1) return PARK_ERR_INVALID;
+  const Shape s = make_shape(dtype, B, H, N, d, n_qblocks);
+  st = check_ws(workspace, workspace_bytes, park::cluster_workspace(s));
+  if (st != PARK_OK) return st;
+  hipError_t e = park::launch_cluster(s, Q, Q, iters, PARK_METRIC_EUCLIDEAN, 0.0f, init_idx, centroids, counts, labels,
+                                      perm, offsets, nullptr, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
 int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int N, int d, int n_clusters,
@@ -113,6 +149,49 @@ int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, i
                                 int32_t* block_count, void* workspace, size_t workspace_bytes, void* stream) {
   return retrieve_impl(true, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
                        scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
+}
+
+int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                                   const int32_t* counts, int n_clusters, const int32_t* q_perm,
+                                   const int32_t* q_offsets, int n_qblocks, float top_p, int top_k, float scale,
+                                   float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !centroids || !counts || !mask || !block_list || !block_count) return PARK_ERR_INVALID;
+  if (!finite_f(top_p) || top_p < 0.0f || top_p > 1.0f || top_k < 0 || !finite_f(scale)) return PARK_ERR_INVALID;
+  if ((st = check_qblocks(N, q_perm, q_offsets, n_qblocks)) != PARK_OK) return st;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::retrieve_clustered_workspace(s, n_qblocks, scores == nullptr));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  const park::QueryBlocks qb{q_perm, q_offsets, n_qblocks};
+  hipError_t e = park::launch_retrieve_clustered(s, Q, centroids, counts, qb, scale, top_p, top_k, scores, mask,
+                                                 block_list, block_count, workspace,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+int park_block_sparse_attn_clustered(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N,
+                                     int d, const int32_t* perm, const int32_t* offsets, int n_clusters,
+                                     const int32_t* q_perm, const int32_t* q_offsets, int n_qblocks,
+                                     const int32_t* block_list, const int32_t* block_count, float scale, void* O,
+                                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !K || !V || !perm || !offsets || !block_list || !block_count || !O) return PARK_ERR_INVALID;
+  if (!finite_f(scale)) return PARK_ERR_INVALID;
+  if ((st = check_qblocks(N, q_perm, q_offsets, n_qblocks)) != PARK_OK) return st;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  const park::QueryBlocks qb{q_perm, q_offsets, n_qblocks};
+  st = check_ws(workspace, workspace_bytes, park::attn_workspace(s, &qb));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  hipError_t e = park::launch_attn(s, Q, K, V, perm, offsets, block_list, block_count, scale, O, lse, workspace,
+                                   static_cast<hipStream_t>(stream), nullptr, nullptr, &qb);
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
 static int attn_impl(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,

@@ -16,18 +16,41 @@ inline int nk_pad32(int nk) { return (nk + 31) / 32 * 32; }
 inline int n_qblocks(int N) { return (N + 63) / 64; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Clustered query blocks: block u of head bh holds the queries
+// qperm[bh][qoffsets[bh][u] .. qoffsets[bh][u+1]) (n_u of them).  Kernels walk a block as
+// chunks of at most 64 consecutive positions; a head has at most chunk_slots() chunks.
+struct QueryBlocks {
+  const int32_t* qperm;     // [BH][N]
+  const int32_t* qoffsets;  // [BH][NQ+1]
+  int NQ;                   // query blocks per head
+};
+inline int chunk_slots(int N, int NQ) { return n_qblocks(N) + NQ; }
+
+// Chunk tables of clustered query blocks, per head: chunks[c] = (block u, first position,
+// count, 0) for c < ctotal, blocks in order; cbase[u] = first chunk of block u
+// (cbase[NQ] = ctotal).  Offsets are clamped to [0, N], so inconsistent ones cannot lead to
+// an access out of range.
+hipError_t launch_qchunks(const int32_t* qoffsets, int BH, int N, int NQ, int maxc, int4* chunks,
+                          int32_t* cbase, int32_t* ctotal, hipStream_t st);
+
 // ----- retrieval (PAMA, pooled baseline, selection)
 size_t retrieve_workspace(const Shape& s, bool need_scores);
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
                            uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st);
+// PAMA and the same selection over clustered query blocks
+size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores);
+hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
+                                     const QueryBlocks& qb, float scale, float top_p, int top_k, float* scores,
+                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st);
 
 // ----- block-sparse attention
-size_t attn_workspace(const Shape& s);
+// qb == nullptr: 64-token query blocks; otherwise clustered query blocks
+size_t attn_workspace(const Shape& s, const QueryBlocks* qb = nullptr);
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
                        void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin = nullptr,
-                       hipEvent_t ev_end = nullptr);
+                       hipEvent_t ev_end = nullptr, const QueryBlocks* qb = nullptr);
 
 // ----- key clustering
 size_t cluster_workspace(const Shape& s);

@@ -19,8 +19,10 @@
  *   - Arguments are validated on the host before anything is launched; a failing check
  *     returns its status and launches nothing.  No C++ exception crosses the ABI.
  *   - dtype: PARK_F32 (inputs are float) or PARK_BF16 (inputs are bfloat16).
- *   - Head dimension d must be 64 or 128; the query block is 64 tokens; the number of
- *     key clusters is at most PARK_MAX_CLUSTERS.
+ *   - Head dimension d must be 64 or 128; the number of key clusters is at most
+ *     PARK_MAX_CLUSTERS.  Query blocks are either 64 consecutive tokens (the entry points
+ *     without a suffix) or clustered (the *_clustered entry points, PARK's own setting:
+ *     Euclidean k-means of the queries, Figure 2 and section 6 "Implementations").
  */
 #ifndef PARK_H
 #define PARK_H
@@ -41,6 +43,7 @@ extern "C" {
 #define PARK_ABI_VERSION 1
 #define PARK_MAX_CLUSTERS 1536
 #define PARK_QUERY_BLOCK 64
+#define PARK_MAX_QUERY_BLOCKS 1536   /* clustered query blocks per head */
 
 typedef enum park_status {
   PARK_OK = 0,
@@ -186,6 +189,82 @@ PARK_API int park_block_sparse_attn_timed(const void* Q, const void* K, const vo
                                  int n_clusters, const int32_t* block_list, const int32_t* block_count,
                                  int q_block, float scale, void* O, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end);
+
+/* ---------------------------------------------------------------------------------
+ * Clustered query blocks.  PARK groups the queries by plain Euclidean k-means (Figure 2;
+ * N_Q = 128 in section 6, "Implementations") instead of taking runs of 64 tokens.  Query
+ * block u of head (b, h) is then the set of queries
+ *   q_perm[b,h][q_offsets[b,h][u] .. q_offsets[b,h][u+1])        (n_u of them),
+ * which is what park_cluster_queries (or park_cluster_keys with metric EUCLIDEAN and K = Q)
+ * writes as perm / offsets.  q_perm must hold each query index once and q_offsets must rise
+ * from 0 to N; other contents give undefined results but never an access out of range
+ * (offsets are clamped to [0, N] and indices to [0, N - 1]).  Internally every block is
+ * walked as chunks of at most 64 consecutive positions of q_perm.
+ * --------------------------------------------------------------------------------- */
+
+/* Bytes of workspace the *_clustered entry points (op PARK_OP_RETRIEVE_BLOCKS or
+ * PARK_OP_BLOCK_SPARSE_ATTN) or park_cluster_queries (op PARK_OP_CLUSTER_KEYS with
+ * n_clusters = n_qblocks) need; 0 for invalid sizes. */
+PARK_API size_t park_workspace_bytes_clustered(int op, int B, int H, int N, int d, int n_clusters, int n_qblocks);
+
+/*
+ * park_cluster_queries - the query blocks of PARK (Figure 2: the queries are clustered by
+ * standard Euclidean k-means): park_cluster_keys with K = Q and metric EUCLIDEAN, i.e. Lloyd
+ * k-means of the raw queries from the anchors q_{floor(u N / n_qblocks)} (or init_idx), ties
+ * to the lowest block, empty blocks keeping their centroid.  Outputs as park_cluster_keys
+ * with n_clusters = n_qblocks: centroids [B,H,n_qblocks,d] float (block means), counts
+ * [B,H,n_qblocks] (n_u), labels [B,H,N], perm [B,H,N] (queries in (block, index) order) and
+ * offsets [B,H,n_qblocks+1] - perm and offsets are the q_perm / q_offsets below.
+ * Workspace: park_workspace_bytes(PARK_OP_CLUSTER_KEYS, B, H, N, d, n_qblocks).
+ * Errors: INVALID (NULL required pointers, sizes, n_qblocks outside [1, N], iters < 1),
+ * UNSUPPORTED (d, n_qblocks > PARK_MAX_CLUSTERS), WORKSPACE, HIP.
+ */
+PARK_API int park_cluster_queries(const void* Q, int dtype, int B, int H, int N, int d, int n_qblocks, int iters,
+                                  const int32_t* init_idx, float* centroids, int32_t* counts, int32_t* labels,
+                                  int32_t* perm, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * park_retrieve_blocks_clustered - PAMA (section 5.1, E7/E8) and the top-p / top-k selection
+ * of park_retrieve_blocks over clustered query blocks:
+ *   W_uv = (1/n_u) sum_{i in block u} P_iv  (a zero row for an empty block).
+ * The fused kernel computes, per chunk of a block, the column sums of the chunk's 64 x
+ * n_clusters softmax in registers; a second kernel adds the chunks of each block in order
+ * and divides by n_u.
+ * Inputs: Q, centroids, counts as for park_retrieve_blocks; q_perm [B,H,N], q_offsets
+ * [B,H,n_qblocks+1] int32 (device).
+ * Outputs: scores [B,H,n_qblocks,n_clusters] float or NULL, mask [B,H,n_qblocks,n_clusters]
+ * uint8, block_list [B,H,n_qblocks,n_clusters] int32, block_count [B,H,n_qblocks] int32, with
+ * the meanings of park_retrieve_blocks.
+ * Workspace: park_workspace_bytes_clustered(PARK_OP_RETRIEVE_BLOCKS, ...).
+ * Errors: as park_retrieve_blocks; INVALID also for NULL q_perm / q_offsets or n_qblocks
+ * outside [1, N]; UNSUPPORTED for n_qblocks > PARK_MAX_QUERY_BLOCKS.
+ */
+PARK_API int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int H, int N, int d,
+                                            const float* centroids, const int32_t* counts, int n_clusters,
+                                            const int32_t* q_perm, const int32_t* q_offsets, int n_qblocks,
+                                            float top_p, int top_k, float scale, float* scores, uint8_t* mask,
+                                            int32_t* block_list, int32_t* block_count, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
+ * park_block_sparse_attn_clustered - park_block_sparse_attn with clustered query blocks:
+ * query i of block u attends to J_u, the keys of the clusters block_list[u][0 ..
+ * block_count[u]), with the same formulas, numerics and output layout (O [B,H,N,d] and lse
+ * [B,H,N] in the original query order).  block_list / block_count [B,H,n_qblocks,...] come
+ * from park_retrieve_blocks_clustered.  The bf16 path computes a partial state per (chunk,
+ * key range) with the kernel of park_block_sparse_attn (the tile plan of a block serves all
+ * its chunks); queries are read and results written through q_perm.
+ * Workspace: park_workspace_bytes_clustered(PARK_OP_BLOCK_SPARSE_ATTN, ...).
+ * Errors: as park_block_sparse_attn; INVALID also for NULL q_perm / q_offsets or n_qblocks
+ * outside [1, N]; UNSUPPORTED for n_qblocks > PARK_MAX_QUERY_BLOCKS.
+ */
+PARK_API int park_block_sparse_attn_clustered(const void* Q, const void* K, const void* V, int dtype, int B,
+                                              int H, int N, int d, const int32_t* perm, const int32_t* offsets,
+                                              int n_clusters, const int32_t* q_perm, const int32_t* q_offsets,
+                                              int n_qblocks, const int32_t* block_list,
+                                              const int32_t* block_count, float scale, void* O, float* lse,
+                                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }
