@@ -32,15 +32,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def effective_pairs(torch, counts, block_list, block_count, N):
-    """Sum over (b, h, query block u) of n_u * sum_{v selected} n_v."""
+def effective_pairs(torch, counts, block_list, block_count, N, qcounts=None):
+    """Sum over (b, h, query block u) of n_u * sum_{v selected} n_v; n_u = 64 (the last
+    block ragged) or the clustered blocks' sizes qcounts [B, H, NQ]."""
     B, H, NQ, nk = block_list.shape
     valid = block_list >= 0
     idx = block_list.clamp(min=0).long()
     sizes = torch.gather(counts.long().unsqueeze(2).expand(B, H, NQ, nk), 3, idx) * valid
     keys_per_block = sizes.sum(-1)                               # [B, H, NQ]
-    nu = torch.full((NQ,), 64, dtype=torch.long, device=counts.device)
-    nu[-1] = N - 64 * (NQ - 1)
+    if qcounts is None:
+        nu = torch.full((NQ,), 64, dtype=torch.long, device=counts.device)
+        nu[-1] = N - 64 * (NQ - 1)
+    else:
+        nu = qcounts.long()
     return int((keys_per_block * nu).sum().item()), keys_per_block
 
 
@@ -118,6 +122,96 @@ def copy_calibration(gib):
                       "GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream, lse_dense):
+    """PARK's own configuration: query blocks by Euclidean k-means of the queries (NQ blocks,
+    the same k-means steps as the keys), timed like the main leg on the same inputs."""
+    B, H, N, d = q.shape
+    nk, nq = cfg.n_clusters, args.query_blocks
+    ws_q = torch.empty(park.workspace_bytes_clustered(park.OP_CLUSTER_KEYS, B, H, N, d, nq, nq), dtype=torch.uint8,
+                       device="cuda")
+    ws_c = torch.empty(park.workspace_bytes(park.OP_CLUSTER_KEYS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(park.workspace_bytes_clustered(park.OP_RETRIEVE_BLOCKS, B, H, N, d, nk, nq),
+                       dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(park.workspace_bytes_clustered(park.OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk, nq),
+                       dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        qc = park.park_cluster_queries(q, nq, cfg.iters, workspace=ws_q)
+        if ev: ev[1].record(stream)
+        cl = park.park_cluster_keys(q, k, nk, cfg.iters, workspace=ws_c)
+        if ev: ev[2].record(stream)
+        rb = park.park_retrieve_blocks_clustered(q, cl["centroids"], cl["counts"], qc["perm"], qc["offsets"], top_p,
+                                                 top_k, workspace=ws_r)
+        if ev: ev[3].record(stream)
+        O, lse = park.park_block_sparse_attn_clustered(q, k, v, cl["perm"], cl["offsets"], qc["perm"], qc["offsets"],
+                                                       rb["block_list"], rb["block_count"], workspace=ws_a)
+        if ev: ev[4].record(stream)
+        return qc, cl, rb, O, lse
+
+    log(f"clustered query blocks ({nq}): warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    qc, cl, rb, O, lse = out
+    ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)]).mean(0)
+    ms_per_step = wall * 1e3 / args.steps
+    pairs, _ = effective_pairs(torch, cl["counts"], rb["block_list"], rb["block_count"], N, qc["counts"])
+    flops = 4.0 * d * pairs
+    log(f"clustered step {ms_per_step:.2f} ms: query clusters {ms[0]:.2f} key clusters {ms[1]:.2f} "
+        f"retrieve {ms[2]:.2f} attention {ms[3]:.2f}")
+    res = {"query_blocks": nq, "ms_per_step": round(ms_per_step, 3),
+           "effective_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+           "query_cluster_ms_per_layer": round(float(ms[0]), 3), "cluster_ms_per_layer": round(float(ms[1]), 3),
+           "retrieval_ms_per_layer": round(float(ms[2]), 3), "attn_ms_per_layer": round(float(ms[3]), 3),
+           "attn_effective_tflops": round(flops / (ms[3] * 1e-3) / 1e12, 2),
+           "block_density": round(float(rb["block_count"].float().mean().item()) / nk, 4),
+           "pair_density": round(pairs / (B * H * float(N) * N), 4)}
+    if lse_dense is not None:
+        rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
+        res["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
+                         "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+    return res
+
+
+def schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k):
+    """PARK's step schedule (section 6: 50 steps, dense for the first 20%, clustering and
+    masks recomputed every R = 10 steps): the three kinds of step timed on the same inputs
+    and combined into the mean time per layer-step over the schedule."""
+    from block_sparse_attention_response_amd.schedule import ParkSchedule
+    s = ParkSchedule(cfg.n_clusters, cfg.iters, top_p, top_k, query_blocks=args.query_blocks or None)
+    kinds = [s.kind(t) for t in range(s.total_steps)]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    log("schedule: dense, recompute and reuse steps")
+    t = {"dense": timed(lambda: s.dense(q, k, v)),
+         "recompute": timed(lambda: (s.refresh(q, k), s.sparse(q, k, v))),
+         "reuse": timed(lambda: s.sparse(q, k, v))}
+    mean = sum(t[x] for x in kinds) / len(kinds)
+    return {"total_steps": s.total_steps, "dense_steps": kinds.count("dense"),
+            "recompute_steps": kinds.count("recompute"), "reuse_steps": kinds.count("reuse"),
+            "recompute_every": s.recompute_every, "query_blocks": args.query_blocks or 64,
+            "dense_step_ms": round(t["dense"], 3), "recompute_step_ms": round(t["recompute"], 3),
+            "reuse_step_ms": round(t["reuse"], 3), "mean_step_ms": round(mean, 3),
+            "speedup_vs_dense": round(t["dense"] / mean, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +220,10 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload index of park_synth.CONFIGS")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--recall", choices=["on", "off"], default="on")
+    ap.add_argument("--query-blocks", type=int, default=128, metavar="NQ",
+                    help="also time the clustered-query-block path with NQ query clusters (0: skip)")
+    ap.add_argument("--schedule", choices=["on", "off"], default="on",
+                    help="also time the 50-step schedule (dense prefix, recompute every 10 steps)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -231,10 +329,18 @@ def main():
         allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()
         allc = torch.full_like(rb["block_count"], nk)
         _, lse_dense = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], allb, allc, workspace=ws_a)
+        del allb, allc
         torch.cuda.synchronize()
         rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
         result["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
                             "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+
+    if args.query_blocks > 0:
+        result["query_clustered"] = clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream,
+                                                  lse_dense if args.recall == "on" else None)
+
+    if args.schedule == "on":
+        result["schedule"] = schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k)
 
     if args.cpu_baseline == "on":
         log("CPU oracle baseline on a bounded sample")
