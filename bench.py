@@ -180,6 +180,26 @@ def clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream, lse
     return res
 
 
+def diagnostics_leg(park, torch, cfg, q, k, cl, W_pama):
+    """Retrieval accuracy (PARK appendix A, M1): the total-variation error, weighted by block
+    size and averaged over heads, of the PAMA map and of the pooled-query map (same key
+    clusters) against the exact block importance of Eq. (3), computed on the GPU."""
+    B, H, N, d = q.shape
+    t0 = time.perf_counter()
+    Wx = park.park_block_importance_exact(q, k, cl["perm"], cl["offsets"])
+    Wc = park.park_retrieve_blocks_pooled(q, cl["centroids"], cl["counts"], cfg.top_p, cfg.top_k)["scores"]
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t0
+    nq = Wx.shape[2]
+    nu = torch.clamp(N - 64 * torch.arange(nq, device=Wx.device), max=64).double()
+
+    def tv(We):
+        return float(((We.double() - Wx.double()).abs().sum(-1) * 0.5 * nu / N).sum(-1).mean().item())
+    return {"tv_pama": round(tv(W_pama), 4), "tv_pooled": round(tv(Wc), 4),
+            "over": "heads (block-size weighted TV per head against the exact Eq. (3) map)",
+            "exact_map_s": round(secs, 2)}
+
+
 def schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k):
     """PARK's step schedule (section 6: 50 steps, dense for the first 20%, clustering and
     masks recomputed every R = 10 steps): the three kinds of step timed on the same inputs
@@ -224,6 +244,8 @@ def main():
                     help="also time the clustered-query-block path with NQ query clusters (0: skip)")
     ap.add_argument("--schedule", choices=["on", "off"], default="on",
                     help="also time the 50-step schedule (dense prefix, recompute every 10 steps)")
+    ap.add_argument("--diagnostics", choices=["on", "off"], default="on",
+                    help="also measure the retrieval TV error against the exact block importance")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -341,6 +363,11 @@ def main():
 
     if args.schedule == "on":
         result["schedule"] = schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k)
+
+    if args.diagnostics == "on":
+        log("diagnostics: exact block importance and TV errors")
+        W_pama = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)["scores"]
+        result["retrieval_tv"] = diagnostics_leg(park, torch, cfg, q, k, cl, W_pama)
 
     if args.cpu_baseline == "on":
         log("CPU oracle baseline on a bounded sample")

@@ -29,7 +29,7 @@ __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
     "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
-    "park_block_sparse_attn_clustered",
+    "park_block_sparse_attn_clustered", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
     "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
@@ -37,7 +37,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpark.so")
 
 PARK_OK, PARK_ERR_INVALID, PARK_ERR_UNSUPPORTED, PARK_ERR_WORKSPACE, PARK_ERR_HIP, PARK_ERR_NUMERIC = range(6)
-OP_CLUSTER_KEYS, OP_RETRIEVE_BLOCKS, OP_BLOCK_SPARSE_ATTN = range(3)
+OP_CLUSTER_KEYS, OP_RETRIEVE_BLOCKS, OP_BLOCK_SPARSE_ATTN, OP_BLOCK_IMPORTANCE = range(4)
 _METRIC = {"qrkc": 0, "euclidean": 1}
 
 
@@ -86,6 +86,8 @@ def lib():
         L.park_block_sparse_attn_clustered.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P,
                                                        _P, _F, _P, _P, _P, _S, _P]
         L.park_block_sparse_attn_clustered.restype = _I
+        L.park_block_importance_exact.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _P, _P, _S, _P]
+        L.park_block_importance_exact.restype = _I
         _lib = L
     return _lib
 
@@ -358,6 +360,27 @@ def park_block_sparse_attn_clustered(Q, K, V, perm, offsets, q_perm, q_offsets, 
                                                 _ptr(lse if want_lse else None), _ptr(ws), wsb, _stream(Q))
     _check(st, "park_block_sparse_attn_clustered")
     return O, (lse if want_lse else None)
+
+
+def park_block_importance_exact(Q, K, perm, offsets, scale=None, workspace=None):
+    """Exact block importance (section 3.2, Eq. (3)) of every 64-token query block over the
+    key clusters: W [B,H,NQ,n_clusters] float32 (a retrieval-accuracy diagnostic)."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (perm, "perm"), (offsets, "offsets")):
+        _dev(t, n)
+    B, H, N, d = _bhnd(Q, "Q")
+    if K.shape != Q.shape or K.dtype != Q.dtype:
+        raise ValueError("K must match Q in shape and dtype")
+    nk = offsets.shape[-1] - 1
+    if perm.shape != (B, H, N) or offsets.shape != (B, H, nk + 1):
+        raise ValueError("perm must be [B, H, N] and offsets [B, H, n_clusters + 1]")
+    W = torch.empty(B, H, (N + 63) // 64, nk, dtype=torch.float32, device=Q.device)
+    ws, wsb = _workspace(workspace_bytes(OP_BLOCK_IMPORTANCE, B, H, N, d, nk), Q.device, workspace)
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_block_importance_exact(_ptr(Q), _ptr(K), _dtype_code(Q), B, H, N, d, _ptr(perm), _ptr(offsets),
+                                           nk, sc, _ptr(W), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_block_importance_exact")
+    return W
 
 
 class HipEvents:

@@ -1249,4 +1249,116 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Exact block importance (section 3.2, Eq. (3)), a retrieval-accuracy diagnostic:
+//   W_uv = (1/n_u) sum_{i in block u} sum_{j in cluster v} softmax_j(scale q_i . k_j),
+// softmax over all N keys.  The attention kernel computes it: with values V_j = the one-hot
+// vector of key j's cluster (restricted to a chunk of d clusters) and every key selected, O_i
+// is query i's attention mass on each cluster of the chunk.  Dense attention is the selection
+// of nk_dense runs of consecutive keys (identity permutation), so every key range has work.
+constexpr int kDenseRuns = 64;
+
+// lab[bh][perm[p]] = v for the positions p of cluster v
+__global__ __launch_bounds__(256) void k_key_labels(const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+                                                    int N, int nk, int32_t* __restrict__ lab) {
+  const int v = blockIdx.x, bh = blockIdx.y;
+  const int32_t* off = offsets + (size_t)bh * (nk + 1);
+  const int a = min(max(off[v], 0), N), b = min(max(off[v + 1], a), N);
+  for (int p = a + (int)threadIdx.x; p < b; p += 256) {
+    const int j = perm[(size_t)bh * N + p];
+    if (j >= 0 && j < N) lab[(size_t)bh * N + j] = v;
+  }
+}
+
+// identity permutation, kDenseRuns runs of consecutive keys, every run listed for every block
+__global__ __launch_bounds__(256) void k_dense_lists(int N, int NQ, int runs, int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ list,
+                                                     int32_t* __restrict__ count) {
+  const int bh = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < N) perm[(size_t)bh * N + t] = t;
+  if (t <= runs) offsets[(size_t)bh * (runs + 1) + t] = (int)(((long long)t * N) / runs);
+  if (t < NQ * runs) list[(size_t)bh * NQ * runs + t] = t % runs;
+  if (t < NQ) count[(size_t)bh * NQ + t] = runs;
+}
+
+// V[bh][j][a] = 1 if key j is in cluster c0 + a, else 0
+template <typename T>
+__global__ __launch_bounds__(256) void k_onehot(const int32_t* __restrict__ lab, int N, int d, int c0,
+                                                T* __restrict__ V) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)N * d) return;
+  const size_t bhj = (size_t)blockIdx.y * N + e / d;
+  const int a = (int)(e % d);
+  V[bhj * d + a] = (T)(lab[bhj] == c0 + a ? 1.0f : 0.0f);
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ x, size_t n, int v) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) x[e] = v;
+}
+
+// W[bh][u][c0 + a] = mean over block u's rows of O[bh][i][a], for a < min(d, nk - c0)
+template <typename T>
+__global__ __launch_bounds__(128) void k_block_mean(const T* __restrict__ O, int N, int d, int nk, int c0, int NQ,
+                                                    float* __restrict__ W) {
+  const int u = blockIdx.x, bh = blockIdx.y, a = threadIdx.x;
+  if (a >= d || c0 + a >= nk) return;
+  const int i0 = 64 * u, i1 = min(N, i0 + 64);
+  float acc = 0.0f;
+  for (int i = i0; i < i1; ++i) acc += to_f32(O[((size_t)bh * N + i) * d + a]);
+  W[((size_t)bh * NQ + u) * nk + c0 + a] = acc / (float)(i1 - i0);
+}
+
+size_t importance_workspace(const Shape& s) {
+  const size_t BH = s.BH, N = s.N, NQ = n_qblocks(s.N), esz = s.dtype == 1 ? 2 : 4;
+  Shape sd = s;
+  sd.nk = kDenseRuns < s.N ? kDenseRuns : s.N;
+  size_t b = 0;
+  b += align256(BH * N * 4) * 2;                            // labels, identity permutation
+  b += align256(BH * (sd.nk + 1) * 4);                      // run offsets
+  b += align256(BH * NQ * sd.nk * 4) + align256(BH * NQ * 4);  // lists, counts
+  b += align256(BH * N * s.d * esz) * 2;                    // one-hot values, outputs
+  b += attn_workspace(sd);
+  return b;
+}
+
+hipError_t launch_importance(const Shape& s, const void* Q, const void* K, const int32_t* perm,
+                             const int32_t* offsets, float scale, float* W, void* ws, hipStream_t st) {
+  const int N = s.N, NQ = n_qblocks(N), d = s.d;
+  const size_t BH = s.BH, esz = s.dtype == 1 ? 2 : 4;
+  Shape sd = s;
+  sd.nk = kDenseRuns < N ? kDenseRuns : N;
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
+  int32_t* lab = reinterpret_cast<int32_t*>(take(BH * N * 4));
+  int32_t* pid = reinterpret_cast<int32_t*>(take(BH * N * 4));
+  int32_t* offd = reinterpret_cast<int32_t*>(take(BH * (sd.nk + 1) * 4));
+  int32_t* lst = reinterpret_cast<int32_t*>(take(BH * NQ * sd.nk * 4));
+  int32_t* cnt = reinterpret_cast<int32_t*>(take(BH * NQ * 4));
+  void* V = take(BH * N * d * esz);
+  void* O = take(BH * N * d * esz);
+  void* aws = p;
+  hipError_t e;
+  k_dense_lists<<<dim3((unsigned)((std::max<long long>((long long)N, (long long)NQ * sd.nk) + 256) / 256), s.BH),
+                  256, 0, st>>>(N, NQ, sd.nk, pid, offd, lst, cnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // keys of no cluster (inconsistent perm) keep label -1
+  k_fill_i32<<<dim3((unsigned)((BH * N + 255) / 256)), 256, 0, st>>>(lab, BH * N, -1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_key_labels<<<dim3(s.nk, s.BH), 256, 0, st>>>(perm, offsets, N, s.nk, lab);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int c0 = 0; c0 < s.nk; c0 += d) {
+    const dim3 og((unsigned)(((size_t)N * d + 255) / 256), s.BH);
+    if (s.dtype == 1) k_onehot<bf16><<<og, 256, 0, st>>>(lab, N, d, c0, static_cast<bf16*>(V));
+    else k_onehot<float><<<og, 256, 0, st>>>(lab, N, d, c0, static_cast<float*>(V));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_attn(sd, Q, K, V, pid, offd, lst, cnt, scale, O, nullptr, aws, st)) != hipSuccess) return e;
+    if (s.dtype == 1) k_block_mean<bf16><<<dim3(NQ, s.BH), 128, 0, st>>>(static_cast<const bf16*>(O), N, d, s.nk, c0, NQ, W);
+    else k_block_mean<float><<<dim3(NQ, s.BH), 128, 0, st>>>(static_cast<const float*>(O), N, d, s.nk, c0, NQ, W);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace park

@@ -84,8 +84,25 @@ size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_clusters) 
     case PARK_OP_CLUSTER_KEYS: return park::cluster_workspace(s);
     case PARK_OP_RETRIEVE_BLOCKS: return park::retrieve_workspace(s, true);
     case PARK_OP_BLOCK_SPARSE_ATTN: return park::attn_workspace(s);
+    case PARK_OP_BLOCK_IMPORTANCE: return park::importance_workspace(s);
     default: return 0;
   }
+}
+
+int park_block_importance_exact(const void* Q, const void* K, int dtype, int B, int H, int N, int d,
+                                const int32_t* perm, const int32_t* offsets, int n_clusters, float scale,
+                                float* W, void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !K || !perm || !offsets || !W || !finite_f(scale)) return PARK_ERR_INVALID;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::importance_workspace(s));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  hipError_t e = park::launch_importance(s, Q, K, perm, offsets, scale, W, workspace,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
 size_t park_workspace_bytes_clustered(int op, int B, int H, int N, int d, int n_clusters, int n_qblocks) {

@@ -52,6 +52,11 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
                        void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin = nullptr,
                        hipEvent_t ev_end = nullptr, const QueryBlocks* qb = nullptr);
 
+// ----- exact block importance (section 3.2, Eq. (3)) for 64-token blocks, a diagnostic
+size_t importance_workspace(const Shape& s);
+hipError_t launch_importance(const Shape& s, const void* Q, const void* K, const int32_t* perm,
+                             const int32_t* offsets, float scale, float* W, void* ws, hipStream_t st);
+
 // ----- key clustering
 size_t cluster_workspace(const Shape& s);
 hipError_t launch_cluster(const Shape& s, const void* Q, const void* K, int iters, int metric,

@@ -64,7 +64,8 @@ typedef enum park_metric {
 typedef enum park_op {
   PARK_OP_CLUSTER_KEYS = 0,
   PARK_OP_RETRIEVE_BLOCKS = 1,
-  PARK_OP_BLOCK_SPARSE_ATTN = 2
+  PARK_OP_BLOCK_SPARSE_ATTN = 2,
+  PARK_OP_BLOCK_IMPORTANCE = 3
 } park_op;
 
 /* PARK_ABI_VERSION of the loaded library. */
@@ -189,6 +190,24 @@ PARK_API int park_block_sparse_attn_timed(const void* Q, const void* K, const vo
                                  int n_clusters, const int32_t* block_list, const int32_t* block_count,
                                  int q_block, float scale, void* O, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end);
+
+/*
+ * park_block_importance_exact - a retrieval-accuracy diagnostic: the exact block importance
+ * of section 3.2, Eq. (3), for 64-token query blocks,
+ *   W_uv = (1/n_u) sum_{i in block u} sum_{j in cluster v} softmax_j(scale q_i . k_j)
+ * (softmax over all N keys), the reference against which PARK's appendix A measures the
+ * total-variation error of an estimated map (M1).  Computed with the block-sparse attention
+ * kernel: every key selected (dense attention) and values equal to the one-hot vector of each
+ * key's cluster, d clusters per pass (ceil(n_clusters / d) passes), then the mean over each
+ * block's queries.  Numerics: as park_block_sparse_attn (for bf16 inputs the probabilities are
+ * rounded to bf16 and the per-query masses are bf16 outputs, so |W error| stays near 1e-3).
+ * Inputs: Q, K [B,H,N,d]; perm / offsets from park_cluster_keys.  scale <= 0 selects 1/sqrt(d).
+ * Output: W [B,H,NQ,n_clusters] float.  Workspace: park_workspace_bytes(PARK_OP_BLOCK_IMPORTANCE,
+ * ...).  Errors: INVALID, UNSUPPORTED (d, n_clusters > PARK_MAX_CLUSTERS), WORKSPACE, HIP.
+ */
+PARK_API int park_block_importance_exact(const void* Q, const void* K, int dtype, int B, int H, int N, int d,
+                                         const int32_t* perm, const int32_t* offsets, int n_clusters, float scale,
+                                         float* W, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Clustered query blocks.  PARK groups the queries by plain Euclidean k-means (Figure 2;

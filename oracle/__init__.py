@@ -73,6 +73,8 @@ def _declare(L):
     L.orc_block_sparse_attn.argtypes = [_P, _P, _P, _L, _I, _P, _P, _I, _P, _P, _I, _D, _P, _L, _P, _P]
     L.orc_dense_attn.argtypes = [_P, _P, _P, _L, _I, _D, _P, _L, _P, _P]
     L.orc_pama_blocks.argtypes = [_P, _L, _I, _P, _P, _I, _P, _P, _L, _D, _P]
+    L.orc_tv.argtypes = [_P, _P, _P, _L, _I, _L]
+    L.orc_tv.restype = _D
     L.orc_block_sparse_attn_blocks.argtypes = [_P, _P, _P, _L, _I, _P, _P, _I, _P, _P, _L, _P, _P, _D, _P, _L,
                                                _P, _P]
     L.orc_exact_block_importance.argtypes = [_P, _P, _L, _I, _P, _I, _I, _D, _P]
@@ -240,6 +242,19 @@ def block_sparse_attn_blocks(Q, K, V, perm, offsets, qperm, qoffsets, block_list
                                        _p(block_count), scale, _p(ub), 0 if ub is None else ub.shape[0], _p(O),
                                        _p(lse))
     return O, lse
+
+
+def tv(W_est, W_exact, block_sizes):
+    """M1 total-variation error of an estimated map against the exact one (block-size weighted)."""
+    W_est = _f64(W_est); W_exact = _f64(W_exact)
+    nu = np.ascontiguousarray(block_sizes, dtype=np.int64)
+    nq, nk = W_est.shape
+    return lib().orc_tv(_p(W_est), _p(W_exact), _p(nu), nq, nk, int(nu.sum()))
+
+
+def block_sizes(L: int, q_block: int = 64):
+    """n_u of the q_block-token query blocks (the last one ragged)."""
+    return np.minimum(q_block, L - q_block * np.arange((L + q_block - 1) // q_block))
 
 
 def dense_attn(Q, K, V, scale: float, rows=None):

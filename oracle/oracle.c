@@ -503,6 +503,21 @@ ORC_EXPORT void orc_block_sparse_attn_blocks(const float* Q, const float* K, con
   }
 }
 
+/* M1 (Appendix A, "Attention-weight approximation error"): the total-variation distance of an
+ * estimated block-importance map W^m from the exact one (Eq. (3)), weighted by the query-block
+ * sizes:
+ *   E_TV = sum_u (n_u / L) (1/2) sum_v |W^m_uv - W_uv|
+ * (the printed formula lost its absolute-value bars; the TV distance is half the L1 distance). */
+ORC_EXPORT double orc_tv(const double* West, const double* Wex, const long* nu, long nq, int nk, long L) {
+  double e = 0.0;
+  for (long u = 0; u < nq; ++u) {
+    double t = 0.0;
+    for (int v = 0; v < nk; ++v) t += fabs(West[(size_t)u * nk + v] - Wex[(size_t)u * nk + v]);
+    e += (double)nu[u] / (double)L * 0.5 * t;
+  }
+  return e;
+}
+
 /* Dense attention (section 3.1, E1), textbook form, written independently of the sparse
  * routine above: A_i = softmax_j(scale q_i . k_j) over all L keys, O_i = sum_j A_ij v_j,
  * lse_i = log sum_j exp(scale q_i . k_j).  Rows listed in `rows` (all if NULL); outputs

@@ -262,3 +262,32 @@ def test_empty_and_partial_selection(dev, orc):
         z = np.isneginf(lo)
         assert np.all(np.isneginf(lseg[0, h][z])) and np.all(Og[0, h][z] == 0)
         assert np.abs(Og[0, h][~z] - Oo[~z]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["cfg0-f32-d64", "ragged-bf16-d128", "ragged-bf16-d64-text", "ragged-f32-d128"])
+def test_exact_block_importance(dev, orc, name):
+    """Retrieval-accuracy diagnostic (section 3.2, Eq. (3); appendix A, M1): the GPU's exact
+    block importance against the oracle's, and the M1 error of the GPU's PAMA map measured
+    with either one."""
+    import torch
+    cfg, Q, K, V = _data(name)
+    ocl = _oracle_clusters(orc, name)
+    B, H, N, d = Q.shape
+    perm = np.stack([np.stack([o["perm"] for o in row]) for row in ocl]).astype(np.int32)
+    off = np.stack([np.stack([o["offsets"] for o in row]) for row in ocl]).astype(np.int32)
+    cent = np.stack([np.stack([o["centroids"] for o in row]) for row in ocl])
+    counts = np.stack([np.stack([o["counts"] for o in row]) for row in ocl]).astype(np.int32)
+    Wg = dev.park_block_importance_exact(to_dev(Q, cfg.dtype), to_dev(K, cfg.dtype), to_dev(perm, "f32"),
+                                         to_dev(off, "f32"))
+    rb = dev.park_retrieve_blocks(to_dev(Q, cfg.dtype), to_dev(cent, "f32"), to_dev(counts, "f32"), cfg.top_p,
+                                  cfg.top_k)
+    torch.cuda.synchronize()
+    Wg, Wp = host(Wg), host(rb["scores"])
+    tol = 2e-3 if cfg.dtype == "bf16" else 1e-5
+    sizes = orc.block_sizes(N)
+    for b in range(B):
+        for h in range(H):
+            Wx = orc.exact_block_importance(Q[b, h], K[b, h], ocl[b][h]["labels"], cfg.n_clusters, 64,
+                                            1.0 / np.sqrt(d))
+            assert np.abs(Wg[b, h] - Wx).max() <= tol
+            assert abs(orc.tv(Wp[b, h], Wg[b, h], sizes) - orc.tv(Wp[b, h], Wx, sizes)) <= tol

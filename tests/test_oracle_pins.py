@@ -465,3 +465,30 @@ def test_query_clustering_blocks_hold_their_members(orc):
     assert qc["offsets"][0] == 0 and qc["offsets"][-1] == 256
     for u in range(8):
         assert np.all(qc["labels"][qc["perm"][qc["offsets"][u]:qc["offsets"][u + 1]]] == u)
+
+
+# ------------------------------------------------- retrieval-accuracy diagnostics (next row 3)
+
+def test_tv_hand_example_and_limits(orc):
+    """Appendix A, M1: block-size weighted half-L1 distance.  Hand example: blocks of 64 and 36
+    queries, TV 0.5 each -> 0.5; identical maps -> 0; disjoint one-hot rows -> 1; symmetric."""
+    We = np.array([[0.5, 0.5], [1.0, 0.0]]); Wx = np.array([[1.0, 0.0], [0.5, 0.5]])
+    assert abs(orc.tv(We, Wx, [64, 36]) - 0.5) < 1e-15
+    assert orc.tv(We, We, [64, 36]) == 0.0
+    assert orc.tv(np.eye(3), np.roll(np.eye(3), 1, 1), [10, 10, 5]) == 1.0
+    assert orc.tv(We, Wx, [64, 36]) == orc.tv(Wx, We, [64, 36])
+    assert list(orc.block_sizes(130)) == [64, 64, 2]
+
+
+def test_tv_of_pama_on_singleton_clusters_is_zero(orc):
+    """With one key per cluster PAMA is the exact importance (pinned above), so its M1 error
+    against the independent exact routine vanishes; pooled queries do not (App. D.1)."""
+    Q, K, _ = _rand_qk(96, 8, 39)
+    labels = np.arange(96, dtype=np.int32)
+    cent, counts, _, _ = orc.finalize(K, labels, 96)
+    Wx = orc.exact_block_importance(Q, K, labels, 96, 32, 0.3)
+    Wp = orc.pama(Q, cent, counts, 32, 0.3)
+    Wc = orc.pooled_scores(Q, cent, counts, 32, 0.3)
+    sizes = orc.block_sizes(96, 32)
+    assert orc.tv(Wp, Wx, sizes) < 1e-12
+    assert orc.tv(Wc, Wx, sizes) > 1e-3
