@@ -195,9 +195,19 @@ def diagnostics_leg(park, torch, cfg, q, k, cl, W_pama):
 
     def tv(We):
         return float(((We.double() - Wx.double()).abs().sum(-1) * 0.5 * nu / N).sum(-1).mean().item())
-    return {"tv_pama": round(tv(W_pama), 4), "tv_pooled": round(tv(Wc), 4),
-            "over": "heads (block-size weighted TV per head against the exact Eq. (3) map)",
-            "exact_map_s": round(secs, 2)}
+    res = {"tv_pama": round(tv(W_pama), 4), "tv_pooled": round(tv(Wc), 4),
+           "over": "heads (block-size weighted TV per head against the exact Eq. (3) map)",
+           "exact_map_s": round(secs, 2)}
+    if q.dtype == torch.bfloat16:
+        # M2 (appendix B): centred log-mass RMSE of the QRKC key centroids and of Euclidean ones
+        t0 = time.perf_counter()
+        ce = park.park_cluster_keys(q, k, cfg.n_clusters, cfg.iters, metric="euclidean")
+        r_q = park.park_logmass_rmse(q, k, cl["perm"], cl["offsets"], cl["centroids"], cl["counts"])
+        r_e = park.park_logmass_rmse(q, k, ce["perm"], ce["offsets"], ce["centroids"], ce["counts"])
+        torch.cuda.synchronize()
+        res["logmass_rmse"] = {"qrkc": round(float(r_q.mean().item()), 4), "euclidean": round(float(r_e.mean().item()), 4),
+                               "over": "heads", "s": round(time.perf_counter() - t0, 2)}
+    return res
 
 
 def schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k):

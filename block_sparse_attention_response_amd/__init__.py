@@ -29,7 +29,7 @@ __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
     "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
-    "park_block_sparse_attn_clustered", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE",
+    "park_block_sparse_attn_clustered", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
     "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
@@ -88,6 +88,10 @@ def lib():
         L.park_block_sparse_attn_clustered.restype = _I
         L.park_block_importance_exact.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _F, _P, _P, _S, _P]
         L.park_block_importance_exact.restype = _I
+        L.park_logmass_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.park_logmass_workspace_bytes.restype = _S
+        L.park_logmass_rmse.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _P, _P, _S, _P]
+        L.park_logmass_rmse.restype = _I
         _lib = L
     return _lib
 
@@ -381,6 +385,27 @@ def park_block_importance_exact(Q, K, perm, offsets, scale=None, workspace=None)
                                            nk, sc, _ptr(W), _ptr(ws), wsb, _stream(Q))
     _check(st, "park_block_importance_exact")
     return W
+
+
+def park_logmass_rmse(Q, K, perm, offsets, centroids, counts, scale=None, workspace=None):
+    """Centred log-mass RMSE of the key centroids (PARK appendix B, M2) per head: [B, H] float32."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (perm, "perm"), (offsets, "offsets"), (centroids, "centroids"),
+                 (counts, "counts")):
+        _dev(t, n)
+    B, H, N, d = _bhnd(Q, "Q")
+    nk = offsets.shape[-1] - 1
+    if K.shape != Q.shape or K.dtype != Q.dtype:
+        raise ValueError("K must match Q in shape and dtype")
+    if centroids.shape != (B, H, nk, d) or counts.shape != (B, H, nk):
+        raise ValueError("centroids must be [B, H, n_clusters, d] and counts [B, H, n_clusters]")
+    out = torch.empty(B, H, dtype=torch.float32, device=Q.device)
+    ws, wsb = _workspace(int(lib().park_logmass_workspace_bytes(B, H, N, d, nk)), Q.device, workspace)
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_logmass_rmse(_ptr(Q), _ptr(K), _dtype_code(Q), B, H, N, d, _ptr(perm), _ptr(offsets), nk,
+                                 _ptr(centroids), _ptr(counts), sc, _ptr(out), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_logmass_rmse")
+    return out
 
 
 class HipEvents:

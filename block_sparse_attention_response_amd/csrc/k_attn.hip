@@ -1361,4 +1361,148 @@ hipError_t launch_importance(const Shape& s, const void* Q, const void* K, const
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------------------
+// Centred log-mass error (appendix B, M2; section 4.2), a retrieval-accuracy diagnostic:
+//   S*_iv = log sum_{j in cluster v} exp(scale q_i . k_j),   S_iv = log n_v + scale q_i . c_v,
+//   D_iv = S*_iv - S_iv over the non-empty clusters, centred per query (minus its mean over v);
+//   RMSE over all (i, v) of the centred D.
+// One wave per (64-query block, head) walks every cluster's keys through perm in 32-key tiles:
+// S^T = K Q^T by MFMA (bf16 products exact, float sums), a lane holds 16 of a tile's keys for
+// its query and the swap with lane l ^ 32 completes the tile's log-sum-exp, which is folded
+// into the cluster's.  q . c_v in float (each lane half takes 64 of the d columns).  Per block:
+// (sum over queries of the centred sum of squares, number of (i, v) pairs) in double.
+template <int D>
+__global__ __launch_bounds__(64) void k_logmass(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+                                                const float* __restrict__ cent, const int32_t* __restrict__ counts,
+                                                int N, int nk, float scale, double2* __restrict__ stats) {
+  constexpr int KC = D / 16;
+  const int u = blockIdx.x, bh = blockIdx.y, NQ = gridDim.x;
+  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
+  const size_t hrow = (size_t)bh * N;
+  const int32_t* off = offsets + (size_t)bh * (nk + 1);
+  const int32_t* pm = perm + hrow;
+  bf16x8 qf[2][KC];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int qrow = 64 * u + 32 * h2 + l32;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (qrow < N) {
+        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow) * D + kc * 16 + 8 * h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[h2][kc][i] = (bf16)0.0f;
+      }
+    }
+  }
+  double sd[2] = {0.0, 0.0}, sd2[2] = {0.0, 0.0};
+  int pairs = 0;
+  for (int v = 0; v < nk; ++v) {
+    const int a = min(max(off[v], 0), N), b = min(max(off[v + 1], a), N);
+    const int n = counts[(size_t)bh * nk + v];
+    if (b <= a || n <= 0) continue;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};   // running log-sum-exp of cluster v
+    for (int p0 = a; p0 < b; p0 += 32) {
+      const int p = p0 + l32;
+      bf16x8 kf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (p < b) {
+          kf[kc] = load_bf16x8(K + (hrow + min(max(pm[p], 0), N - 1)) * D + kc * 16 + 8 * h);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kf[kc][i] = (bf16)0.0f;
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) acc = mfma32(kf[kc], qf[h2][kc], acc);
+        // this lane's keys of the tile: rows c_row(r, lane)
+        float tm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (p0 + c_row(r, lane) < b) tm = fmaxf(tm, acc[r] * scale);
+        float ts = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (p0 + c_row(r, lane) < b) ts += __expf(acc[r] * scale - tm);
+        // the other 16 keys sit in lane l ^ 32
+        const float om = __shfl_xor(tm, 32), os = __shfl_xor(ts, 32);
+        const float mm = fmaxf(fmaxf(tm, om), m[h2]);
+        l[h2] = (m[h2] == -INFINITY ? 0.0f : l[h2] * __expf(m[h2] - mm)) +
+                (tm == -INFINITY ? 0.0f : ts * __expf(tm - mm)) + (om == -INFINITY ? 0.0f : os * __expf(om - mm));
+        m[h2] = mm;
+      }
+    }
+    // S_iv = log n_v + scale q_i . c_v (this lane half's 64 columns, then the swap)
+    const float* c = cent + ((size_t)bh * nk + v) * D;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf((float)qf[h2][kc][i], c[kc * 16 + 8 * h + i], dot);
+      dot += __shfl_xor(dot, 32);
+      const double dlt = ((double)m[h2] + log((double)l[h2])) - (log((double)n) + (double)scale * (double)dot);
+      sd[h2] += dlt;
+      sd2[h2] += dlt * dlt;
+    }
+    ++pairs;
+  }
+  // per query: sum over v of (D - mean D)^2 = sum D^2 - (sum D)^2 / pairs; lanes of half h = 0
+  // hold each query once
+  double ss = 0.0;
+  int np = 0;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int qrow = 64 * u + 32 * h2 + l32;
+    if (h == 0 && qrow < N && pairs > 0) {
+      ss += fmax(sd2[h2] - sd[h2] * sd[h2] / pairs, 0.0);
+      np += pairs;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    ss += __shfl_xor(ss, o);
+    np += __shfl_xor(np, o);
+  }
+  if (lane == 0) stats[(size_t)bh * NQ + u] = make_double2(ss, (double)np);
+}
+
+// rmse[bh] = sqrt(sum of the blocks' centred squares / their pairs)
+__global__ void k_logmass_rmse(const double2* __restrict__ stats, int BH, int NQ, float* __restrict__ rmse) {
+  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  double s = 0.0, n = 0.0;
+  for (int u = 0; u < NQ; ++u) {
+    s += stats[(size_t)bh * NQ + u].x;
+    n += stats[(size_t)bh * NQ + u].y;
+  }
+  rmse[bh] = n > 0.0 ? (float)sqrt(s / n) : 0.0f;
+}
+
+size_t logmass_workspace(const Shape& s) { return align256((size_t)s.BH * n_qblocks(s.N) * sizeof(double2)); }
+
+hipError_t launch_logmass(const Shape& s, const void* Q, const void* K, const int32_t* perm, const int32_t* offsets,
+                          const float* cent, const int32_t* counts, float scale, float* rmse, void* ws,
+                          hipStream_t st) {
+  if (s.dtype != 1) return hipErrorInvalidValue;
+  const int NQ = n_qblocks(s.N);
+  double2* stats = static_cast<double2*>(ws);
+  auto q = static_cast<const bf16*>(Q);
+  auto k = static_cast<const bf16*>(K);
+  if (s.d == 128) k_logmass<128><<<dim3(NQ, s.BH), 64, 0, st>>>(q, k, perm, offsets, cent, counts, s.N, s.nk, scale, stats);
+  else k_logmass<64><<<dim3(NQ, s.BH), 64, 0, st>>>(q, k, perm, offsets, cent, counts, s.N, s.nk, scale, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_logmass_rmse<<<(s.BH + 63) / 64, 64, 0, st>>>(stats, s.BH, NQ, rmse);
+  return hipGetLastError();
+}
+
 }  // namespace park

@@ -105,6 +105,29 @@ int park_block_importance_exact(const void* Q, const void* K, int dtype, int B, 
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
+size_t park_logmass_workspace_bytes(int B, int H, int N, int d, int n_clusters) {
+  bool uns;
+  if (check_common(PARK_BF16, B, H, N, d, n_clusters, &uns) != PARK_OK) return 0;
+  return park::logmass_workspace(make_shape(PARK_BF16, B, H, N, d, n_clusters));
+}
+
+int park_logmass_rmse(const void* Q, const void* K, int dtype, int B, int H, int N, int d, const int32_t* perm,
+                      const int32_t* offsets, int n_clusters, const float* centroids, const int32_t* counts,
+                      float scale, float* rmse, void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !K || !perm || !offsets || !centroids || !counts || !rmse || !finite_f(scale)) return PARK_ERR_INVALID;
+  if (dtype != PARK_BF16) return PARK_ERR_UNSUPPORTED;
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  st = check_ws(workspace, workspace_bytes, park::logmass_workspace(s));
+  if (st != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  hipError_t e = park::launch_logmass(s, Q, K, perm, offsets, centroids, counts, scale, rmse, workspace,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
 size_t park_workspace_bytes_clustered(int op, int B, int H, int N, int d, int n_clusters, int n_qblocks) {
   bool uns;
   if (check_common(PARK_BF16, B, H, N, d, n_clusters, &uns) != PARK_OK) return 0;

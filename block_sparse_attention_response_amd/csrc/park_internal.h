@@ -57,6 +57,12 @@ size_t importance_workspace(const Shape& s);
 hipError_t launch_importance(const Shape& s, const void* Q, const void* K, const int32_t* perm,
                              const int32_t* offsets, float scale, float* W, void* ws, hipStream_t st);
 
+// ----- centred log-mass RMSE (appendix B, M2) per head, a diagnostic (bf16 inputs)
+size_t logmass_workspace(const Shape& s);
+hipError_t launch_logmass(const Shape& s, const void* Q, const void* K, const int32_t* perm, const int32_t* offsets,
+                          const float* cent, const int32_t* counts, float scale, float* rmse, void* ws,
+                          hipStream_t st);
+
 // ----- key clustering
 size_t cluster_workspace(const Shape& s);
 hipError_t launch_cluster(const Shape& s, const void* Q, const void* K, int iters, int metric,

@@ -209,6 +209,25 @@ PARK_API int park_block_importance_exact(const void* Q, const void* K, int dtype
                                          const int32_t* perm, const int32_t* offsets, int n_clusters, float scale,
                                          float* W, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * park_logmass_rmse - a retrieval-accuracy diagnostic: the centred log-mass error of the key
+ * centroids (PARK appendix B, M2, with the quantities of section 4.2), per head:
+ *   S*_iv = log sum_{j in cluster v} exp(scale q_i . k_j),  S_iv = log n_v + scale q_i . c_v,
+ *   D_iv = S*_iv - S_iv for every query i and non-empty cluster v, centred per query (the
+ *   mean over v subtracted: a softmax over clusters does not see a per-query constant);
+ *   rmse = sqrt(mean over all (i, v) of the centred D^2).
+ * One wave per 64-query block computes every (query, cluster) log-sum-exp from the keys
+ * (bf16 products, float sums) - L^2 d work per head, a diagnostic rather than a step.
+ * Inputs: Q, K [B,H,N,d] bf16; perm / offsets / centroids / counts from park_cluster_keys.
+ * Output: rmse [B,H] float.  Workspace: park_logmass_workspace_bytes(...).
+ * Errors: INVALID, UNSUPPORTED (float inputs, d, n_clusters > PARK_MAX_CLUSTERS), WORKSPACE, HIP.
+ */
+PARK_API size_t park_logmass_workspace_bytes(int B, int H, int N, int d, int n_clusters);
+PARK_API int park_logmass_rmse(const void* Q, const void* K, int dtype, int B, int H, int N, int d,
+                               const int32_t* perm, const int32_t* offsets, int n_clusters, const float* centroids,
+                               const int32_t* counts, float scale, float* rmse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * Clustered query blocks.  PARK groups the queries by plain Euclidean k-means (Figure 2;
  * N_Q = 128 in section 6, "Implementations") instead of taking runs of 64 tokens.  Query

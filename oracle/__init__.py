@@ -75,6 +75,8 @@ def _declare(L):
     L.orc_pama_blocks.argtypes = [_P, _L, _I, _P, _P, _I, _P, _P, _L, _D, _P]
     L.orc_tv.argtypes = [_P, _P, _P, _L, _I, _L]
     L.orc_tv.restype = _D
+    L.orc_logmass_rmse.argtypes = [_P, _P, _L, _I, _P, _P, _P, _I, _D, _P, _L]
+    L.orc_logmass_rmse.restype = _D
     L.orc_block_sparse_attn_blocks.argtypes = [_P, _P, _P, _L, _I, _P, _P, _I, _P, _P, _L, _P, _P, _D, _P, _L,
                                                _P, _P]
     L.orc_exact_block_importance.argtypes = [_P, _P, _L, _I, _P, _I, _I, _D, _P]
@@ -250,6 +252,15 @@ def tv(W_est, W_exact, block_sizes):
     nu = np.ascontiguousarray(block_sizes, dtype=np.int64)
     nq, nk = W_est.shape
     return lib().orc_tv(_p(W_est), _p(W_exact), _p(nu), nq, nk, int(nu.sum()))
+
+
+def logmass_rmse(Q, K, labels, cent, counts, scale: float, rows=None):
+    """M2 centred log-mass RMSE of the key centroids over the given query rows (all if None)."""
+    Q = _f32(Q); K = _f32(K); labels = _i32(labels); cent = _f32(cent); counts = _i32(counts)
+    L_, d = Q.shape
+    r = np.ascontiguousarray(rows, dtype=np.int64) if rows is not None else None
+    return lib().orc_logmass_rmse(_p(Q), _p(K), L_, d, _p(labels), _p(cent), _p(counts), cent.shape[0], scale,
+                                  _p(r), 0 if r is None else r.shape[0])
 
 
 def block_sizes(L: int, q_block: int = 64):

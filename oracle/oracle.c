@@ -518,6 +518,57 @@ ORC_EXPORT double orc_tv(const double* West, const double* Wex, const long* nu, 
   return e;
 }
 
+/* M2 (appendix B, "Centered log-mass approximation error"; section 4.2):
+ *   S*_iv = log sum_{j in K_v} exp(scale q_i . k_j),   S_iv = log n_v + scale q_i . c_v,
+ *   Delta_iv = S*_iv - S_iv over the non-empty blocks v, centred per query (minus its mean
+ *   over v; the centring is not printed - a softmax over blocks ignores a per-query constant),
+ *   RMSE = sqrt(mean over (i, v) of the centred Delta^2).
+ * Queries `rows` (all if NULL).  Returns the RMSE. */
+ORC_EXPORT double orc_logmass_rmse(const float* Q, const float* K, long L, int d, const int* labels,
+                                   const float* cent, const int* counts, int nk, double scale,
+                                   const long* rows, long nrows) {
+  long nr = rows ? nrows : L;
+  double ss = 0.0, np = 0.0;
+#pragma omp parallel for schedule(dynamic) reduction(+ : ss, np)
+  for (long r = 0; r < nr; ++r) {
+    long i = rows ? rows[r] : r;
+    double* mx = (double*)malloc(sizeof(double) * (size_t)nk);
+    double* sm = (double*)malloc(sizeof(double) * (size_t)nk);
+    double* dl = (double*)malloc(sizeof(double) * (size_t)nk);
+    for (int v = 0; v < nk; ++v) { mx[v] = -INFINITY; sm[v] = 0.0; }
+    for (long j = 0; j < L; ++j) {
+      double dot = 0.0;
+      for (int a = 0; a < d; ++a) dot += (double)Q[(size_t)i * d + a] * (double)K[(size_t)j * d + a];
+      double sc = scale * dot;
+      int v = labels[j];
+      if (sc > mx[v]) {
+        sm[v] = sm[v] * exp(mx[v] - sc) + 1.0;
+        mx[v] = sc;
+      } else {
+        sm[v] += exp(sc - mx[v]);
+      }
+    }
+    double mean = 0.0;
+    int n = 0;
+    for (int v = 0; v < nk; ++v) {
+      if (counts[v] <= 0) continue;
+      double dot = 0.0;
+      for (int a = 0; a < d; ++a) dot += (double)Q[(size_t)i * d + a] * (double)cent[(size_t)v * d + a];
+      dl[v] = (mx[v] + log(sm[v])) - (log((double)counts[v]) + scale * dot);
+      mean += dl[v];
+      ++n;
+    }
+    if (n > 0) {
+      mean /= n;
+      for (int v = 0; v < nk; ++v)
+        if (counts[v] > 0) ss += (dl[v] - mean) * (dl[v] - mean);
+      np += n;
+    }
+    free(mx); free(sm); free(dl);
+  }
+  return np > 0 ? sqrt(ss / np) : 0.0;
+}
+
 /* Dense attention (section 3.1, E1), textbook form, written independently of the sparse
  * routine above: A_i = softmax_j(scale q_i . k_j) over all L keys, O_i = sum_j A_ij v_j,
  * lse_i = log sum_j exp(scale q_i . k_j).  Rows listed in `rows` (all if NULL); outputs

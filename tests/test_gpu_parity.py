@@ -291,3 +291,27 @@ def test_exact_block_importance(dev, orc, name):
                                             1.0 / np.sqrt(d))
             assert np.abs(Wg[b, h] - Wx).max() <= tol
             assert abs(orc.tv(Wp[b, h], Wg[b, h], sizes) - orc.tv(Wp[b, h], Wx, sizes)) <= tol
+
+
+@pytest.mark.parametrize("name", ["ragged-bf16-d128", "ragged-bf16-d64-text"])
+def test_logmass_rmse(dev, orc, name):
+    """Retrieval-accuracy diagnostic M2 (appendix B): the GPU's centred log-mass RMSE per head
+    against the oracle's, for the oracle's QRKC clusters and for Euclidean ones."""
+    import torch
+    cfg, Q, K, V = _data(name)
+    B, H, N, d = Q.shape
+    for metric in ("qrkc", "euclidean"):
+        cl = [[orc.cluster_keys(Q[b, h], K[b, h], cfg.n_clusters, cfg.iters, metric) for h in range(H)]
+              for b in range(B)]
+        st = {k: np.stack([np.stack([c[k] for c in row]) for row in cl]) for k in
+              ("perm", "offsets", "centroids", "counts", "labels")}
+        r = dev.park_logmass_rmse(to_dev(Q, cfg.dtype), to_dev(K, cfg.dtype), to_dev(st["perm"].astype(np.int32), "f32"),
+                                  to_dev(st["offsets"].astype(np.int32), "f32"), to_dev(st["centroids"], "f32"),
+                                  to_dev(st["counts"].astype(np.int32), "f32"))
+        torch.cuda.synchronize()
+        r = host(r)
+        for b in range(B):
+            for h in range(H):
+                ref = orc.logmass_rmse(Q[b, h], K[b, h], st["labels"][b, h], st["centroids"][b, h],
+                                       st["counts"][b, h], 1.0 / np.sqrt(d))
+                assert abs(r[b, h] - ref) <= 1e-3 * ref, (metric, b, h, r[b, h], ref)

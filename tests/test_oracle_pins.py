@@ -492,3 +492,39 @@ def test_tv_of_pama_on_singleton_clusters_is_zero(orc):
     sizes = orc.block_sizes(96, 32)
     assert orc.tv(Wp, Wx, sizes) < 1e-12
     assert orc.tv(Wc, Wx, sizes) > 1e-3
+
+
+def test_logmass_rmse_exact_cases(orc):
+    """M2 (section 4.2 quantities): one key per cluster, or identical keys within a cluster,
+    make the centroid log-mass exact (App. D.2 exact decomposition), so the RMSE vanishes."""
+    Q, K, _ = _rand_qk(80, 8, 40)
+    labels = np.arange(80, dtype=np.int32)
+    cent, counts, _, _ = orc.finalize(K, labels, 80)
+    assert orc.logmass_rmse(Q, K, labels, cent, counts, 0.4) < 1e-12
+    rng = np.random.default_rng(41)
+    base = rng.normal(0, 1, (5, 8)).astype(np.float32)
+    lab = rng.integers(0, 5, 120).astype(np.int32); lab[:5] = np.arange(5)
+    cent, counts, _, _ = orc.finalize(base[lab], lab, 5)
+    assert orc.logmass_rmse(Q[:60].repeat(2, 0), base[lab], lab, cent, counts, 0.4) < 1e-12
+
+
+def test_logmass_rmse_closed_form_and_translation(orc):
+    """Two keys c_v +- e_v per cluster: S* - S = log cosh(scale q.e_v) exactly, so the centred
+    RMSE has a closed form; moving every key by one vector leaves it unchanged."""
+    rng = np.random.default_rng(42)
+    nk, d, s = 6, 4, 0.7
+    c = rng.normal(0, 1, (nk, d)); e = rng.normal(0, 0.6, (nk, d))
+    K = np.concatenate([c + e, c - e]).astype(np.float32)
+    lab = np.concatenate([np.arange(nk), np.arange(nk)]).astype(np.int32)
+    Q = rng.normal(0, 1, (2 * nk, d)).astype(np.float32)
+    cent, counts, _, _ = orc.finalize(K, lab, nk)
+    Kd = K.astype(np.float64)
+    ed = (Kd[:nk] - Kd[nk:]) / 2
+    D = np.log(np.cosh(s * Q.astype(np.float64) @ ed.T))
+    Dc = D - D.mean(1, keepdims=True)
+    ref = np.sqrt((Dc ** 2).mean())
+    got = orc.logmass_rmse(Q, K, lab, cent, counts, s)
+    assert abs(got - ref) < 1e-6 * max(ref, 1e-3), (got, ref)
+    K2 = (K + np.float32(0.5)).astype(np.float32)
+    cent2, _, _, _ = orc.finalize(K2, lab, nk)
+    assert abs(orc.logmass_rmse(Q, K2, lab, cent2, counts, s) - got) < 1e-6
