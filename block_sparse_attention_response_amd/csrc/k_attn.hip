@@ -938,8 +938,10 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
 // key range r = b % kRanges (items of range r run on XCD r: workgroups are dealt to the XCDs
 // round robin and the grid size is a multiple of kRanges) from a per-range counter, in item
 // order: items gridDim.x + r + kRanges k for k = 0, 1, ...  The next index is taken as an
-// item starts and used when it ends.  No wave waits for another, so every wave ends once the
-// counter passes the last item, whatever the number of resident waves.
+// item starts and used when it ends.  A wave whose range is exhausted moves on to the next
+// ranges' counters (the ranges' total work differs a little).  No wave waits for another, so
+// every wave ends once it has found every counter past its last item, whatever the number of
+// resident waves.
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
                                                    const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
@@ -951,8 +953,19 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
   __shared__ AttnLds<D> sm;
   const int lane = threadIdx.x;
   for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
-  const int xr = blockIdx.x % kRanges;
-  for (int item = blockIdx.x; item < items;) {
+  int xr = blockIdx.x % kRanges;
+  int item = blockIdx.x;
+  for (int moved = 0;;) {
+    if (item >= items) {
+      // this range is done: help the next ones (their keys are not in this XCD's L2, but only
+      // the last items of the launch run this way)
+      if (++moved >= kRanges) break;
+      xr = (xr + 1) % kRanges;
+      int k = 0;
+      if (lane == 0) k = atomicAdd(&ictr[xr], 1);
+      item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(k);
+      continue;
+    }
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&ictr[xr], 1);
     attn_item<D>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal, qperm, maxc);
