@@ -770,20 +770,31 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__
                                                      int N, int nk, int nch, int32_t* __restrict__ perm) {
   extern __shared__ int cur[];
   const int lane = threadIdx.x, bh = blockIdx.y, ch = blockIdx.x;
+  const int nbits = nk > 1 ? 32 - __builtin_clz((unsigned)(nk - 1)) : 0;   // bits of a label
+  // every label of the chunk is loaded before the first is ranked
+  constexpr int kSteps = kSortChunk / 64;
+  int labs[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const int j = ch * kSortChunk + 64 * st + lane;
+    labs[st] = j < N ? labels[(size_t)bh * N + j] : -1;
+  }
   for (int v = lane; v < nk; v += 64) cur[v] = hist[((size_t)bh * nch + ch) * nk + v];
   __syncthreads();
-  for (int st = 0; st < kSortChunk / 64; ++st) {
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
     const int j = ch * kSortChunk + 64 * st + lane;
-    const int lab = j < N ? labels[(size_t)bh * N + j] : -1;
-    int rank = 0;
-    bool last = true;
-    for (int i = 0; i < 64; ++i) {
-      const int li = __shfl(lab, i);
-      if (li == lab) {
-        if (i < lane) ++rank;
-        if (i > lane) last = false;
-      }
+    const int lab = labs[st];
+    // lanes holding the same label: one ballot per label bit (and one for validity)
+    uint64_t same = __ballot(lab >= 0);
+    if (lab < 0) same = ~same;
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t bl = __ballot((lab >> b) & 1);
+      same &= ((lab >> b) & 1) ? bl : ~bl;
     }
+    const uint64_t below = (1ull << lane) - 1;
+    const int rank = __builtin_popcountll(same & below);
+    const bool last = (same & ~below & ~(1ull << lane)) == 0;
     if (lab >= 0) {
       const int pos = cur[lab] + rank;
       perm[(size_t)bh * N + pos] = j;
