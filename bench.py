@@ -180,6 +180,46 @@ def clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream, lse
     return res
 
 
+def online_leg(args, park, torch, np, cfg, q, k, v, cl, top_p, top_k, stream, lse_dense, ws_r, ws_a):
+    """SCOPE's online per-head top-k floor (its section 3, "Online Per-Head Top-k Estimation")
+    on 64-token query blocks, timed on the main leg's key clustering: the two-pass selection
+    and the attention over its larger selections, with the densities and recall beside the
+    fixed-floor selection's."""
+    B, H, N, d = q.shape
+    nk = cfg.n_clusters
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        rb = park.park_retrieve_blocks_online(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)
+        if ev: ev[1].record(stream)
+        O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
+                                             workspace=ws_a)
+        if ev: ev[2].record(stream)
+        return rb, O, lse
+
+    log("online per-head top-k: warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        rb, O, lse = step(evs[i])
+    torch.cuda.synchronize()
+    ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(2)] for i in range(args.steps)]).mean(0)
+    pairs, _ = effective_pairs(torch, cl["counts"], rb["block_list"], rb["block_count"], N)
+    flops = 4.0 * d * pairs
+    log(f"online: retrieve {ms[0]:.2f} ms, attention {ms[1]:.2f} ms")
+    res = {"retrieval_ms_per_layer": round(float(ms[0]), 3), "attn_ms_per_layer": round(float(ms[1]), 3),
+           "attn_effective_tflops": round(flops / (ms[1] * 1e-3) / 1e12, 2),
+           "block_density": round(float(rb["block_count"].float().mean().item()) / nk, 4),
+           "pair_density": round(pairs / (B * H * float(N) * N), 4)}
+    if lse_dense is not None:
+        rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
+        res["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
+                         "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+    return res
+
+
 def diagnostics_leg(park, torch, cfg, q, k, cl, W_pama):
     """Retrieval accuracy (PARK appendix A, M1): the total-variation error, weighted by block
     size and averaged over heads, of the PAMA map and of the pooled-query map (same key
@@ -254,6 +294,8 @@ def main():
                     help="also time the clustered-query-block path with NQ query clusters (0: skip)")
     ap.add_argument("--schedule", choices=["on", "off"], default="on",
                     help="also time the 50-step schedule (dense prefix, recompute every 10 steps)")
+    ap.add_argument("--online", choices=["on", "off"], default="on",
+                    help="also time SCOPE's online per-head top-k selection on 64-token blocks")
     ap.add_argument("--diagnostics", choices=["on", "off"], default="on",
                     help="also measure the retrieval TV error against the exact block importance")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -366,6 +408,10 @@ def main():
         rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
         result["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
                             "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+
+    if args.online == "on":
+        result["online_topk"] = online_leg(args, park, torch, np, cfg, q, k, v, cl, top_p, top_k, stream,
+                                           lse_dense if args.recall == "on" else None, ws_r, ws_a)
 
     if args.query_blocks > 0:
         result["query_clustered"] = clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream,

@@ -16,6 +16,10 @@ Figure 2 and section 6):
   park_retrieve_blocks_clustered   PAMA + selection over them
   park_block_sparse_attn_clustered attention over them
 
+and SCOPE's online per-head top-k floor over either kind of query block:
+
+  park_retrieve_blocks_online      PAMA + the two-pass selection
+
 There is no fallback: if libpark.so is missing or was built for another GPU the calls
 raise.
 """
@@ -29,7 +33,7 @@ __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
     "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
-    "park_block_sparse_attn_clustered", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
+    "park_block_sparse_attn_clustered", "park_retrieve_blocks_online", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
     "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
@@ -83,6 +87,8 @@ def lib():
         L.park_retrieve_blocks_clustered.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _I, _F,
                                                      _P, _P, _P, _P, _P, _S, _P]
         L.park_retrieve_blocks_clustered.restype = _I
+        L.park_retrieve_blocks_online.argtypes = L.park_retrieve_blocks_clustered.argtypes
+        L.park_retrieve_blocks_online.restype = _I
         L.park_block_sparse_attn_clustered.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P,
                                                        _P, _F, _P, _P, _P, _S, _P]
         L.park_block_sparse_attn_clustered.restype = _I
@@ -333,6 +339,42 @@ def park_retrieve_blocks_clustered(Q, centroids, counts, q_perm, q_offsets, top_
                                               _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
                                               _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
     _check(st, "park_retrieve_blocks_clustered")
+    return out
+
+
+def park_retrieve_blocks_online(Q, centroids, counts, top_p: float, top_k: int, q_perm=None, q_offsets=None,
+                                scale=None, scores: bool = True, workspace=None):
+    """PAMA scores and SCOPE's online per-head top-k selection: 64-token query blocks when
+    q_perm / q_offsets are None, else the clustered blocks they describe.  Returns
+    dict(scores?, mask, block_list, block_count)."""
+    torch = _torch()
+    _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
+    B, H, N, d = _bhnd(Q, "Q")
+    nk = centroids.shape[2]
+    if centroids.shape != (B, H, nk, d) or centroids.dtype != torch.float32:
+        raise ValueError("centroids must be float32 [B, H, n_clusters, d]")
+    if counts.shape != (B, H, nk) or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [B, H, n_clusters]")
+    clustered = q_perm is not None or q_offsets is not None
+    if clustered:
+        nq = _qblocks(q_perm, q_offsets, B, H, N)
+        need = workspace_bytes_clustered(OP_RETRIEVE_BLOCKS, B, H, N, d, nk, nq)
+    else:
+        nq = (N + 63) // 64
+        need = workspace_bytes(OP_RETRIEVE_BLOCKS, B, H, N, d, nk)
+    dev = Q.device
+    out = dict(mask=torch.empty(B, H, nq, nk, dtype=torch.uint8, device=dev),
+               block_list=torch.empty(B, H, nq, nk, dtype=torch.int32, device=dev),
+               block_count=torch.empty(B, H, nq, dtype=torch.int32, device=dev))
+    if scores:
+        out["scores"] = torch.empty(B, H, nq, nk, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(need, dev, workspace)
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_retrieve_blocks_online(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts), nk,
+                                           _ptr(q_perm), _ptr(q_offsets), nq, float(top_p), int(top_k), sc,
+                                           _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
+                                           _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
+    _check(st, "park_retrieve_blocks_online")
     return out
 
 

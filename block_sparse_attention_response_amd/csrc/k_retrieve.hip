@@ -393,7 +393,7 @@ template <int EPL>
 __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, const int32_t* __restrict__ counts,
                                                 int nk, int NQ, int rows, float top_p, int top_k,
                                                 uint8_t* __restrict__ mask, int32_t* __restrict__ list,
-                                                int32_t* __restrict__ count) {
+                                                int32_t* __restrict__ count, const int32_t* __restrict__ floors) {
   __shared__ uint32_t hcnt[4][64];
   __shared__ uint64_t hmass[4][64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -491,9 +491,19 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, con
 
   int tp = 0;
   uint64_t kp = 0;
-  if (top_p > 0.0f && ne > 0) descend(true, (double)top_p * total, &kp, &tp);
-  int cnt = tp > top_k ? tp : top_k;
-  cnt = min(cnt, ne);
+  int cnt;
+  if (floors) {
+    // second pass of the online per-head top-k: `count` holds this row's first selection
+    // b = min(max(t_p, top_k), ne).  A row at or above the head's floor keeps it; a row below
+    // is extended to the floor, which exceeds t_p, so only the count descent is needed.
+    const int b = count[row], kf = max(top_k, floors[bh]);
+    if (b >= kf) return;
+    cnt = min(kf, ne);
+    if (cnt == b) return;
+  } else {
+    if (top_p > 0.0f && ne > 0) descend(true, (double)top_p * total, &kp, &tp);
+    cnt = min(tp > top_k ? tp : top_k, ne);
+  }
   uint64_t kc = kp;
   if (cnt > 0 && cnt != tp) {
     int rk;
@@ -523,6 +533,7 @@ size_t retrieve_workspace(const Shape& s, bool need_scores) {
   b += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)) * 2;  // Chi, Clo
   b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
   if (need_scores) b += align256((size_t)s.BH * n_qblocks(s.N) * s.nk * sizeof(float));
+  b += align256((size_t)s.BH * sizeof(int32_t));                // online per-head floors
   return b;
 }
 
@@ -556,20 +567,71 @@ size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores) {
   b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
   if (need_scores) b += align256((size_t)s.BH * NQ * s.nk * sizeof(float));
   b += align256((size_t)s.BH * maxc * s.nk * sizeof(float));   // chunk column sums
+  b += align256((size_t)s.BH * sizeof(int32_t));                // online per-head floors
   b += align256((size_t)s.BH * maxc * sizeof(int4));           // chunks
   b += align256((size_t)s.BH * (NQ + 1) * sizeof(int32_t));     // cbase
   b += align256((size_t)s.BH * sizeof(int32_t));                // ctotal
   return b;
 }
 
-// top-p / top-k selection of `rows` score rows (NQ per head)
+// Online per-head top-k (SCOPE, appendix "Online Per-Head Top-k Selection"): from the base
+// counts b_u of a first selection, floor[bh] = ceil(sum_u n_u b_u / sum_u n_u), the
+// query-size-weighted mean; n_u = 64-token block sizes, or the clustered blocks' sizes.
+__global__ __launch_bounds__(256) void k_online_floor(const int32_t* __restrict__ count, int NQ, int N,
+                                                      const int32_t* __restrict__ qoffsets,
+                                                      int32_t* __restrict__ floors) {
+  __shared__ long long sw[4], sn[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  long long w = 0, n = 0;
+  for (int u = tid; u < NQ; u += 256) {
+    long long nu;
+    if (qoffsets) {
+      const int32_t* off = qoffsets + (size_t)bh * (NQ + 1);
+      const int a = min(max(off[u], 0), N), b = min(max(off[u + 1], a), N);
+      nu = b - a;
+    } else {
+      nu = min(64, N - 64 * u);
+    }
+    w += nu * (long long)count[(size_t)bh * NQ + u];
+    n += nu;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    w += __shfl_xor(w, o);
+    n += __shfl_xor(n, o);
+  }
+  if ((tid & 63) == 0) { sw[tid >> 6] = w; sn[tid >> 6] = n; }
+  __syncthreads();
+  if (tid == 0) {
+    const long long W = sw[0] + sw[1] + sw[2] + sw[3], Nn = sn[0] + sn[1] + sn[2] + sn[3];
+    floors[bh] = Nn > 0 ? (int)((W + Nn - 1) / Nn) : 0;
+  }
+}
+
+// top-p / top-k selection of `rows` score rows (NQ per head); floors (per head) or NULL
 static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int NQ, int rows, float top_p,
-                              int top_k, uint8_t* mask, int32_t* list, int32_t* count, hipStream_t st) {
+                              int top_k, uint8_t* mask, int32_t* list, int32_t* count, hipStream_t st,
+                              const int32_t* floors = nullptr);
+
+// the selection, then (online) the per-head floors from its counts and the selection again
+static hipError_t select_all(const Shape& s, const float* W, const int32_t* counts, int NQ, float top_p, int top_k,
+                             uint8_t* mask, int32_t* list, int32_t* count, bool online, const int32_t* qoffsets,
+                             int32_t* floors, hipStream_t st) {
+  hipError_t e = select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st);
+  if (e != hipSuccess || !online) return e;
+  k_online_floor<<<s.BH, 256, 0, st>>>(count, NQ, s.N, qoffsets, floors);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st, floors);
+}
+
+static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int NQ, int rows, float top_p,
+                              int top_k, uint8_t* mask, int32_t* list, int32_t* count, hipStream_t st,
+                              const int32_t* floors) {
   const int sgrid = (rows + 3) / 4;
   const int epl = (nk + 63) / 64;
   switch (epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : epl <= 16 ? 16 : 32) {
 #define PARK_SEL_CASE(E) \
-  case E: k_select<E><<<sgrid, 256, 0, st>>>(W, counts, nk, NQ, rows, top_p, top_k, mask, list, count); break;
+  case E: k_select<E><<<sgrid, 256, 0, st>>>(W, counts, nk, NQ, rows, top_p, top_k, mask, list, count, floors); break;
     PARK_SEL_CASE(1) PARK_SEL_CASE(2) PARK_SEL_CASE(4) PARK_SEL_CASE(8) PARK_SEL_CASE(16) PARK_SEL_CASE(32)
 #undef PARK_SEL_CASE
     default: return hipErrorInvalidValue;
@@ -579,13 +641,15 @@ static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int
 
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
-                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st) {
+                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st, bool online) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   char* p = static_cast<char*>(ws);
   bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
   bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
   float* lg = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * nkp * sizeof(float));
-  float* W = scores ? scores : reinterpret_cast<float*>(p);
+  float* W = scores;
+  if (!W) { W = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * NQ * s.nk * sizeof(float)); }
+  int32_t* floors = reinterpret_cast<int32_t*>(p);
   const float scale2 = scale * kLog2e;
   {
     dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
@@ -610,12 +674,13 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
                      : launch_pama_d<64, true>(s, Q, Chi, Clo, W, st);
   }
   if (e != hipSuccess) return e;
-  return select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st);
+  return select_all(s, W, counts, NQ, top_p, top_k, mask, list, count, online, nullptr, floors, st);
 }
 
 hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                                      const QueryBlocks& qb, float scale, float top_p, int top_k, float* scores,
-                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st) {
+                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st,
+                                     bool online) {
   const int nkp = nk_pad32(s.nk), NQ = qb.NQ, maxc = chunk_slots(s.N, NQ);
   char* p = static_cast<char*>(ws);
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
@@ -627,6 +692,7 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
   int4* chunks = reinterpret_cast<int4*>(take((size_t)s.BH * maxc * sizeof(int4)));
   int32_t* cbase = reinterpret_cast<int32_t*>(take((size_t)s.BH * (NQ + 1) * sizeof(int32_t)));
   int32_t* ctotal = reinterpret_cast<int32_t*>(take((size_t)s.BH * sizeof(int32_t)));
+  int32_t* floors = reinterpret_cast<int32_t*>(take((size_t)s.BH * sizeof(int32_t)));
   const float scale2 = scale * kLog2e;
   {
     dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
@@ -645,7 +711,7 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
   if (e != hipSuccess) return e;
   k_pama_reduce<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(Wp, chunks, cbase, s.nk, NQ, maxc, W);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return select_rows(W, counts, s.nk, NQ, s.BH * NQ, top_p, top_k, mask, list, count, st);
+  return select_all(s, W, counts, NQ, top_p, top_k, mask, list, count, online, qb.qoffsets, floors, st);
 }
 
 }  // namespace park

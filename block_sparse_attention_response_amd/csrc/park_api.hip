@@ -213,6 +213,40 @@ int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int H, int N
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
+int park_retrieve_blocks_online(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                                const int32_t* counts, int n_clusters, const int32_t* q_perm,
+                                const int32_t* q_offsets, int n_qblocks, float top_p, int top_k, float scale,
+                                float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  bool uns;
+  int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
+  if (st != PARK_OK) return st;
+  if (!Q || !centroids || !counts || !mask || !block_list || !block_count) return PARK_ERR_INVALID;
+  if (!finite_f(top_p) || top_p < 0.0f || top_p > 1.0f || top_k < 0 || !finite_f(scale)) return PARK_ERR_INVALID;
+  const bool clustered = q_perm || q_offsets;
+  if (clustered) {
+    if ((st = check_qblocks(N, q_perm, q_offsets, n_qblocks)) != PARK_OK) return st;
+  } else if (n_qblocks != 0 && n_qblocks != (N + PARK_QUERY_BLOCK - 1) / PARK_QUERY_BLOCK) {
+    return PARK_ERR_INVALID;
+  }
+  const Shape s = make_shape(dtype, B, H, N, d, n_clusters);
+  const size_t need = clustered ? park::retrieve_clustered_workspace(s, n_qblocks, scores == nullptr)
+                                : park::retrieve_workspace(s, scores == nullptr);
+  if ((st = check_ws(workspace, workspace_bytes, need)) != PARK_OK) return st;
+  if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (clustered) {
+    const park::QueryBlocks qb{q_perm, q_offsets, n_qblocks};
+    e = park::launch_retrieve_clustered(s, Q, centroids, counts, qb, scale, top_p, top_k, scores, mask, block_list,
+                                        block_count, workspace, hs, true);
+  } else {
+    e = park::launch_retrieve(s, Q, centroids, counts, scale, top_p, top_k, false, scores, mask, block_list,
+                              block_count, workspace, hs, true);
+  }
+  return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
 int park_block_sparse_attn_clustered(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N,
                                      int d, const int32_t* perm, const int32_t* offsets, int n_clusters,
                                      const int32_t* q_perm, const int32_t* q_offsets, int n_qblocks,

@@ -35,14 +35,17 @@ hipError_t launch_qchunks(const int32_t* qoffsets, int BH, int N, int NQ, int ma
 
 // ----- retrieval (PAMA, pooled baseline, selection)
 size_t retrieve_workspace(const Shape& s, bool need_scores);
+// online: SCOPE's online per-head top-k floor on top of the fixed one
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
-                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st);
+                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st,
+                           bool online = false);
 // PAMA and the same selection over clustered query blocks
 size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores);
 hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                                      const QueryBlocks& qb, float scale, float top_p, int top_k, float* scores,
-                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st);
+                                     uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st,
+                                     bool online = false);
 
 // ----- block-sparse attention
 // qb == nullptr: 64-token query blocks; otherwise clustered query blocks

@@ -286,6 +286,28 @@ PARK_API int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int
                                             size_t workspace_bytes, void* stream);
 
 /*
+ * park_retrieve_blocks_online - the PAMA scores of park_retrieve_blocks (q_perm and q_offsets
+ * NULL: 64-token query blocks, n_qblocks 0 or ceil(N/64)) or of park_retrieve_blocks_clustered
+ * (both given), selected with SCOPE's online per-head top-k (SCOPE, section 3 "Online Per-Head
+ * Top-k Estimation" and the appendix "Online Per-Head Top-k Selection"):
+ *   1. b_u = the count of the top-p / fixed top-k selection of park_retrieve_blocks;
+ *   2. per head, k_on = ceil(sum_u n_u b_u / sum_u n_u), n_u the size of query block u
+ *      (64, the last block N - 64 (NQ - 1); or q_offsets[u+1] - q_offsets[u]);
+ *   3. block u keeps max(b_u, min(k_on, non-empty clusters)) clusters: blocks below k_on are
+ *      extended along the same ranking, the others keep their selection.
+ * The counted unit is a key cluster (the unit PARK selects), where SCOPE counts keys.
+ * Inputs, outputs, workspace (park_workspace_bytes or park_workspace_bytes_clustered with op
+ * PARK_OP_RETRIEVE_BLOCKS) and errors as the two entry points above; INVALID also for a
+ * non-zero n_qblocks other than ceil(N/64) without q_perm / q_offsets.
+ */
+PARK_API int park_retrieve_blocks_online(const void* Q, int dtype, int B, int H, int N, int d,
+                                         const float* centroids, const int32_t* counts, int n_clusters,
+                                         const int32_t* q_perm, const int32_t* q_offsets, int n_qblocks,
+                                         float top_p, int top_k, float scale, float* scores, uint8_t* mask,
+                                         int32_t* block_list, int32_t* block_count, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * park_block_sparse_attn_clustered - park_block_sparse_attn with clustered query blocks:
  * query i of block u attends to J_u, the keys of the clusters block_list[u][0 ..
  * block_count[u]), with the same formulas, numerics and output layout (O [B,H,N,d] and lse

@@ -205,6 +205,28 @@ def select(W, counts, top_p: float, top_k: int):
     return mask, lst, cnt, cm, gm
 
 
+def select_online(W, counts, top_p: float, top_k: int, sizes):
+    """SCOPE's online per-head top-k (SCOPE, paperpeel.com/paper/2608.12780, section 3 "Online
+    Per-Head Top-k Estimation" and the appendix "Online Per-Head Top-k Selection"), over the
+    rows of one head:
+      1. base counts b_u of the hybrid top-p / fixed top-k selection (`select`);
+      2. the head's online minimum k_on, the query-size-weighted average of the b_u, rounded
+         up to a whole count: ceil(sum_u n_u b_u / sum_u n_u), in exact integer arithmetic;
+      3. each row below k_on is extended along its own ranking to k_on keys (at most the
+         non-empty clusters); the other rows keep their selection.
+    Returns (mask, list, count, base_count, k_on)."""
+    mask, lst, cnt, _, _ = select(W, counts, top_p, top_k)
+    base = cnt.copy()
+    n = np.asarray(sizes, dtype=np.int64)
+    tot = int(n.sum())
+    k_on = -(-int((n * base.astype(np.int64)).sum()) // tot) if tot > 0 else 0
+    W = _f64(W)
+    for u in np.nonzero(base < k_on)[0]:
+        m1, l1, c1, _, _ = select(W[u:u + 1], counts, top_p, k_on)
+        mask[u], lst[u], cnt[u] = m1[0], l1[0], c1[0]
+    return mask, lst, cnt, base, k_on
+
+
 def block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, q_block: int, scale: float,
                       ublocks=None):
     """(O [L,d] float64, lse [L]); rows of blocks not in `ublocks` are NaN."""

@@ -57,7 +57,7 @@ def test_degenerate_sizes(dev, orc, N, d, dtype, nk, nq):
     g = {kk: host(vv) for kk, vv in rb.items()}
     W = orc.pama(Q[0, 0], cent, counts, 64, scale)
     check_scores(g["scores"][0, 0], W)
-    compare_selection(g["scores"][0, 0], counts, top_p, top_k, g["mask"][0, 0], g["block_list"][0, 0],
+    compare_selection(g["scores"][0, 0], W, counts, top_p, top_k, g["mask"][0, 0], g["block_list"][0, 0],
                       g["block_count"][0, 0], orc)
     O, lse = dev.park_block_sparse_attn(q, k, v, to_dev(perm[None, None], "f32"), to_dev(offsets[None, None], "f32"),
                                         rb["block_list"], rb["block_count"])
@@ -76,7 +76,7 @@ def test_degenerate_sizes(dev, orc, N, d, dtype, nk, nq):
     gc = {kk: host(vv) for kk, vv in rc.items()}
     Wc = orc.pama_blocks(Q[0, 0], cent, counts, qc["perm"], qc["offsets"], scale)
     check_scores(gc["scores"][0, 0], Wc)
-    compare_selection(gc["scores"][0, 0], counts, top_p, top_k, gc["mask"][0, 0], gc["block_list"][0, 0],
+    compare_selection(gc["scores"][0, 0], Wc, counts, top_p, top_k, gc["mask"][0, 0], gc["block_list"][0, 0],
                       gc["block_count"][0, 0], orc)
     O2, lse2 = dev.park_block_sparse_attn_clustered(q, k, v, to_dev(perm[None, None], "f32"),
                                                     to_dev(offsets[None, None], "f32"), qp, qo, rc["block_list"],

@@ -5,8 +5,9 @@ CPU oracle can afford:
     previous labels (margin < 1e-5 exempt);
   * clustering outputs (counts, offsets, perm, centroids) against the oracle's finalisation
     of the GPU labels, for every head;
-  * PAMA scores (rel 1e-3) and the selection (bit-exact except margin < 1e-5), teacher-forced
-    on the GPU's own clustering;
+  * PAMA scores (rel 1e-3) and the selection (the oracle's on its own scores, bit-exact
+    except where a cut or gap margin lies within the score error), teacher-forced on the
+    GPU's own clustering;
   * attention on sampled query blocks (max abs 2e-2 against the double oracle).
 """
 import numpy as np
@@ -71,7 +72,7 @@ def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc
     ref = orc.pooled_scores if pooled else orc.pama
     W = ref(q, cent, counts, 64, scale)
     check_scores(gT["scores"][b, h], W)
-    _, ex = compare_selection(gT["scores"][b, h], counts, top_p, top_k, gT["mask"][b, h], gT["block_list"][b, h],
+    _, ex = compare_selection(gT["scores"][b, h], W, counts, top_p, top_k, gT["mask"][b, h], gT["block_list"][b, h],
                               gT["block_count"][b, h], orc)
     # attention on sampled query blocks
     NQ = W.shape[0]
@@ -113,13 +114,20 @@ def test_density_sweep_config4(dev, orc, pooled):
     Q, K, V = park_synth.generate(cfg, seed=0, heads=[0, 1, 2, 3], workers=4)
     metric = "euclidean" if pooled else "qrkc"
     import torch
+    ref = orc.pooled_scores if pooled else orc.pama
+    W_ref = cl_ref = None
     for kk in cfg.forced_k:
         g = _run(dev, cfg, Q, K, V, cfg.iters, 0.0, kk, metric=metric, pooled=pooled)
         h = 1
         counts = g["counts"][0, h]
         nne = int((counts > 0).sum())
         assert np.all(g["block_count"][0, h] == min(kk, nne))
-        compare_selection(g["scores"][0, h], counts, 0.0, kk, g["mask"][0, h], g["block_list"][0, h],
+        # the clustering does not depend on k: the oracle's scores on it are computed once
+        if W_ref is None:
+            cl_ref = (g["centroids"][0, h].copy(), counts.copy())
+            W_ref = ref(Q[0, h], cl_ref[0], cl_ref[1], 64, 1.0 / np.sqrt(cfg.d))
+        assert np.array_equal(counts, cl_ref[1]) and np.array_equal(g["centroids"][0, h], cl_ref[0])
+        compare_selection(g["scores"][0, h], W_ref, counts, 0.0, kk, g["mask"][0, h], g["block_list"][0, h],
                           g["block_count"][0, h], orc)
         if kk == 1024:
             rows = np.r_[np.arange(0, cfg.N, 997), cfg.N - 1]

@@ -528,3 +528,58 @@ def test_logmass_rmse_closed_form_and_translation(orc):
     K2 = (K + np.float32(0.5)).astype(np.float32)
     cent2, _, _, _ = orc.finalize(K2, lab, nk)
     assert abs(orc.logmass_rmse(Q, K2, lab, cent2, counts, s) - got) < 1e-6
+
+
+# ---------------------------------------------------------------- SCOPE online per-head top-k
+
+def test_select_online_hand_example(orc):
+    """SCOPE, section 3 "Online Per-Head Top-k Estimation": base counts b = (1, 6, 1) of
+    query blocks of sizes (64, 64, 1) give the weighted minimum ceil(449 / 129) = 4 (the
+    unweighted mean, its floor or its rounding would give 3); blocks 0 and 2 are extended
+    along their rankings to 4 clusters, block 1 keeps its 6.  Cluster 7 is empty."""
+    W = np.array([[0.9, 0.012, 0.05, 0.004, 0.02, 0.008, 0.006, 0.0],
+                  [0.16, 0.155, 0.15, 0.145, 0.14, 0.135, 0.115, 0.0],
+                  [0.002, 0.003, 0.005, 0.87, 0.05, 0.04, 0.03, 0.0]])
+    counts = np.array([5, 5, 5, 5, 5, 5, 5, 0], np.int32)
+    mask, lst, cnt, base, k_on = orc.select_online(W, counts, 0.8, 1, orc.block_sizes(129))
+    assert base.tolist() == [1, 6, 1] and k_on == 4
+    assert cnt.tolist() == [4, 6, 4]
+    assert lst[0, :4].tolist() == [0, 1, 2, 4]
+    assert lst[1, :6].tolist() == [0, 1, 2, 3, 4, 5]
+    assert lst[2, :4].tolist() == [3, 4, 5, 6]
+    for u in range(3):
+        assert np.all(lst[u, cnt[u]:] == -1) and mask[u].nonzero()[0].tolist() == lst[u, :cnt[u]].tolist()
+
+
+def test_select_online_invariants(orc):
+    """On random rows: counts never drop, rows at or above the minimum are untouched, the
+    others hold exactly min(k_on, non-empty) clusters, and every selection is a prefix of its
+    row's ranking (W descending, index ascending)."""
+    rng = np.random.default_rng(41)
+    nq, nk = 37, 50
+    counts = rng.integers(0, 4, nk).astype(np.int32)
+    ne = int((counts > 0).sum())
+    W = rng.dirichlet(np.full(nk, 0.3), nq) * (counts > 0)
+    sizes = rng.integers(1, 65, nq)
+    m0, l0, c0, _, _ = orc.select(W, counts, 0.7, 2)
+    mask, lst, cnt, base, k_on = orc.select_online(W, counts, 0.7, 2, sizes)
+    assert np.array_equal(base, c0)
+    assert k_on >= (sizes * base).sum() / sizes.sum() > k_on - 1
+    assert np.all(cnt >= base)
+    keep = base >= k_on
+    assert np.array_equal(cnt[keep], c0[keep]) and np.array_equal(lst[keep], l0[keep])
+    assert np.all(cnt[~keep] == min(k_on, ne)) and (~keep).any() and keep.any()
+    for u in range(nq):
+        order = sorted((v for v in range(nk) if counts[v] > 0), key=lambda v: (-W[u, v], v))
+        assert sorted(order[:cnt[u]]) == lst[u, :cnt[u]].tolist()
+
+
+def test_select_online_fixed_k_is_unchanged(orc):
+    """Pure top-k (p = 0): every base count is k, so the minimum is k and nothing changes;
+    equal base counts with any block sizes leave the selection as it was."""
+    rng = np.random.default_rng(42)
+    W = rng.dirichlet(np.ones(20), 9)
+    counts = np.ones(20, np.int32)
+    m0, l0, c0, _, _ = orc.select(W, counts, 0.0, 6)
+    mask, lst, cnt, base, k_on = orc.select_online(W, counts, 0.0, 6, rng.integers(1, 65, 9))
+    assert k_on == 6 and np.array_equal(cnt, c0) and np.array_equal(lst, l0) and np.array_equal(mask, m0)
