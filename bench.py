@@ -220,6 +220,36 @@ def online_leg(args, park, torch, np, cfg, q, k, v, cl, top_p, top_k, stream, ls
     return res
 
 
+def unfused_ablation(args, park, torch, np, cfg, q, cl, top_p, top_k, ws_r):
+    """The ablation of PARK's fused retrieval kernel (section 5.1): the same retrieval with the
+    per-query probabilities P [B,H,N,N_K] float32 written to HBM and averaged by a second
+    kernel, timed against the fused call on the same clustering."""
+    B, H, N, d = q.shape
+    nk = cfg.n_clusters
+    probs = torch.empty(B, H, N, nk, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    fused = timed(lambda: park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r))
+    unfused = timed(lambda: park.park_retrieve_blocks_unfused(q, cl["centroids"], cl["counts"], top_p, top_k,
+                                                              probs=probs, workspace=ws_r))
+    nbytes = probs.numel() * 4
+    del probs
+    return {"fused_ms": round(fused, 3), "unfused_ms": round(unfused, 3),
+            "probs_bytes": nbytes, "extra_ms": round(unfused - fused, 3),
+            "extra_hbm_GBps": round(2 * nbytes / ((unfused - fused) * 1e-3) / 1e9, 1) if unfused > fused else None,
+            "note": "P written once and read once: 2 x probs_bytes of extra HBM traffic"}
+
+
 def diagnostics_leg(park, torch, cfg, q, k, cl, W_pama):
     """Retrieval accuracy (PARK appendix A, M1): the total-variation error, weighted by block
     size and averaged over heads, of the PAMA map and of the pooled-query map (same key
@@ -297,7 +327,7 @@ def main():
     ap.add_argument("--online", choices=["on", "off"], default="on",
                     help="also time SCOPE's online per-head top-k selection on 64-token blocks")
     ap.add_argument("--diagnostics", choices=["on", "off"], default="on",
-                    help="also measure the retrieval TV error against the exact block importance")
+                    help="also measure the retrieval TV and log-mass errors and time the unfused retrieval")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -424,6 +454,8 @@ def main():
         log("diagnostics: exact block importance and TV errors")
         W_pama = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)["scores"]
         result["retrieval_tv"] = diagnostics_leg(park, torch, cfg, q, k, cl, W_pama)
+        log("diagnostics: unfused retrieval ablation")
+        result["pama_unfused"] = unfused_ablation(args, park, torch, np, cfg, q, cl, top_p, top_k, ws_r)
 
     if args.cpu_baseline == "on":
         log("CPU oracle baseline on a bounded sample")

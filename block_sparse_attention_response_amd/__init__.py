@@ -7,6 +7,8 @@ declared in include/park.h:
   park_cluster_keys        query-response key clustering (PARK, section 5.2)
   park_retrieve_blocks     PAMA block scores + top-p / top-k selection (section 5.1, 6.1)
   park_retrieve_blocks_pooled  the pooled-query baseline (section 4.1)
+  park_retrieve_blocks_unfused the same retrieval with P materialised in HBM (the ablation of
+                               the fused kernel, section 5.1)
   park_block_sparse_attn   attention over the selected blocks (section 3.1)
 
 and, for query blocks formed by Euclidean k-means of the queries (PARK's own setting,
@@ -31,7 +33,7 @@ import os
 
 __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
-    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_block_sparse_attn", "HipEvents",
+    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_retrieve_blocks_unfused", "park_block_sparse_attn", "HipEvents",
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
     "park_block_sparse_attn_clustered", "park_retrieve_blocks_online", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
@@ -75,6 +77,9 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P, _P, _P, _S, _P]
             f.restype = _I
+        L.park_retrieve_blocks_unfused.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P,
+                                                   _P, _P, _P, _S, _P]
+        L.park_retrieve_blocks_unfused.restype = _I
         L.park_block_sparse_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _P, _P,
                                              _P, _S, _P]
         L.park_block_sparse_attn.restype = _I
@@ -207,7 +212,7 @@ def park_cluster_keys(Q, K, n_clusters: int, iters: int, metric: str = "qrkc", a
     return out
 
 
-def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace):
+def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace, probs=None):
     torch = _torch()
     _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
     B, H, N, d = _bhnd(Q, "Q")
@@ -226,8 +231,16 @@ def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, work
     need = workspace_bytes(OP_RETRIEVE_BLOCKS, B, H, N, d, nk)
     ws, wsb = _workspace(need, dev, workspace)
     sc = -1.0 if scale is None else float(scale)
+    extra = ()
+    if probs is not None:
+        if probs is True:
+            probs = torch.empty(B, H, N, nk, dtype=torch.float32, device=dev)
+        elif probs.shape != (B, H, N, nk) or probs.dtype != torch.float32 or not probs.is_contiguous():
+            raise ValueError("probs must be contiguous float32 [B, H, N, n_clusters]")
+        out["probs"] = probs
+        extra = (_ptr(probs),)
     st = fn(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts), nk, 64, float(top_p),
-            int(top_k), sc, _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
+            int(top_k), sc, *extra, _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
             _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
     _check(st, where)
     return out
@@ -239,6 +252,15 @@ def park_retrieve_blocks(Q, centroids, counts, top_p: float, top_k: int, scale=N
     block_count)."""
     return _retrieve(lib().park_retrieve_blocks, "park_retrieve_blocks", Q, centroids, counts, top_p, top_k,
                      scale, scores, workspace)
+
+
+def park_retrieve_blocks_unfused(Q, centroids, counts, top_p: float, top_k: int, scale=None, scores: bool = True,
+                                 probs=None, workspace=None):
+    """park_retrieve_blocks without the fusion: the probabilities P [B,H,N,n_clusters] float32
+    go to HBM (`probs`, allocated when None) and a second kernel averages them into W.
+    Returns dict(probs, scores?, mask, block_list, block_count)."""
+    return _retrieve(lib().park_retrieve_blocks_unfused, "park_retrieve_blocks_unfused", Q, centroids, counts,
+                     top_p, top_k, scale, scores, workspace, probs=True if probs is None else probs)
 
 
 def park_retrieve_blocks_pooled(Q, centroids, counts, top_p: float, top_k: int, scale=None,

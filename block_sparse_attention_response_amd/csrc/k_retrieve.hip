@@ -69,7 +69,10 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int l32) {
 //   W_uv = (1/n_u) sum_i P_iv
 // Row maxima and sums: in-lane over the wave's tiles, a 32-lane reduce-scatter (one query
 // row per lane), then across the waves through LDS.
-template <int D, int VT, bool QF32>
+// PROBS (the unfused ablation, 64-token blocks only): instead of the block's column sums, every
+// query row's normalised probabilities P_i. go to W, laid out [BH][N][nk]; k_rows_mean then
+// forms the block means from them in a second pass over HBM.
+template <int D, int VT, bool QF32, bool PROBS = false>
 __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const bf16* __restrict__ Chi,
                                               const bf16* __restrict__ Clo, int N, int nk, int nkp, int NQ,
                                               float* __restrict__ W, const int4* __restrict__ chunks,
@@ -289,6 +292,23 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
       for (int i = 0; i < 4; ++i) ri[qt][4 * g + i] = x[i];
     }
+  if constexpr (PROBS) {
+    // element r of tile (qt, vt) is query row 32 qt + 8 (r / 4) + 4 h + r % 4, cluster column
+    // v0 + 32 vt + l32: each store instruction writes two 128-byte row segments
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      const int v = v0 + 32 * vt + l32;
+      if (v >= nk) continue;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * qt + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row < nu) W[((size_t)bh * N + q0 + row) * nk + v] = acc[qt][vt][r] * ri[qt][r];
+        }
+    }
+    return;
+  }
   const float inv_nu = chunks ? 1.0f : 1.0f / (float)nu;
   const size_t wrow = (size_t)bh * (chunks ? maxc : NQ) + u;
 #pragma unroll
@@ -302,6 +322,19 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     const int v = v0 + 32 * vt + l32;
     if (h == 0 && v < nk) W[wrow * nk + v] = cs * inv_nu;
   }
+}
+
+// Unfused ablation, second pass: W_uv = (1/n_u) sum_{i in block u} P_iv over the materialised
+// probabilities P [BH][N][nk] (rows in order, float).  grid (ceil(nk / 256), NQ, BH).
+__global__ __launch_bounds__(256) void k_rows_mean(const float* __restrict__ P, int N, int nk, int NQ,
+                                                   float* __restrict__ W) {
+  const int v = blockIdx.x * 256 + threadIdx.x, u = blockIdx.y, bh = blockIdx.z;
+  if (v >= nk) return;
+  const int i0 = 64 * u, nu = min(64, N - i0);
+  const float* p = P + ((size_t)bh * N + i0) * nk + v;
+  float acc = 0.0f;
+  for (int i = 0; i < nu; ++i) acc += p[(size_t)i * nk];
+  W[((size_t)bh * NQ + u) * nk + v] = acc / (float)nu;
 }
 
 // Clustered query blocks: W_uv = (1/n_u) sum over the chunks of block u of their column sums
@@ -539,7 +572,7 @@ size_t retrieve_workspace(const Shape& s, bool need_scores) {
 
 // chunks == nullptr: 64-token blocks, W [BH][NQ][nk] means; otherwise one workgroup per chunk
 // slot, W [BH][maxc][nk] column sums
-template <int D, bool QF32>
+template <int D, bool QF32, bool PROBS = false>
 static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo,
                                 float* W, hipStream_t st, const int4* chunks = nullptr,
                                 const int32_t* ctotal = nullptr, const int32_t* qperm = nullptr, int maxc = 0) {
@@ -549,7 +582,7 @@ static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, 
   dim3 grid(chunks ? maxc : NQ, s.BH), block(64 * nw);
   switch (vt) {
 #define PARK_PAMA_CASE(V) \
-  case V: k_pama<D, V, QF32><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W, chunks, ctotal, qperm, maxc); \
+  case V: k_pama<D, V, QF32, PROBS><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W, chunks, ctotal, qperm, maxc); \
     break;
     PARK_PAMA_CASE(1) PARK_PAMA_CASE(2) PARK_PAMA_CASE(3) PARK_PAMA_CASE(4) PARK_PAMA_CASE(5) PARK_PAMA_CASE(6)
 #undef PARK_PAMA_CASE
@@ -641,7 +674,8 @@ static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int
 
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
-                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st, bool online) {
+                           uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st, bool online,
+                           float* probs) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   char* p = static_cast<char*>(ws);
   bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
@@ -666,6 +700,18 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
     else
       k_pooled<float><<<grid, 256, shm, st>>>(reinterpret_cast<const float*>(Q), cent, lg, s.N, s.d, s.nk, nkp, NQ, scale2, W);
     e = hipGetLastError();
+  } else if (probs) {
+    // unfused ablation: probabilities to HBM, then the block means in a second kernel
+    if (s.d == 128)
+      e = s.dtype == 1 ? launch_pama_d<128, false, true>(s, Q, Chi, Clo, probs, st)
+                       : launch_pama_d<128, true, true>(s, Q, Chi, Clo, probs, st);
+    else
+      e = s.dtype == 1 ? launch_pama_d<64, false, true>(s, Q, Chi, Clo, probs, st)
+                       : launch_pama_d<64, true, true>(s, Q, Chi, Clo, probs, st);
+    if (e == hipSuccess) {
+      k_rows_mean<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(probs, s.N, s.nk, NQ, W);
+      e = hipGetLastError();
+    }
   } else if (s.d == 128) {
     e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, W, st)
                      : launch_pama_d<128, true>(s, Q, Chi, Clo, W, st);

@@ -35,7 +35,7 @@ Shape make_shape(int dtype, int B, int H, int N, int d, int nk) {
 int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
                   const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k, float scale,
                   float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream, float* probs = nullptr) {
   bool uns;
   int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
   if (st != PARK_OK) return st;
@@ -47,7 +47,8 @@ int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, in
   if (st != PARK_OK) return st;
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   hipError_t e = park::launch_retrieve(s, Q, centroids, counts, scale, top_p, top_k, pooled, scores, mask,
-                                       block_list, block_count, workspace, static_cast<hipStream_t>(stream));
+                                       block_list, block_count, workspace, static_cast<hipStream_t>(stream), false,
+                                       probs);
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
@@ -189,6 +190,15 @@ int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, i
                                 int32_t* block_count, void* workspace, size_t workspace_bytes, void* stream) {
   return retrieve_impl(true, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
                        scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
+}
+
+int park_retrieve_blocks_unfused(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                                 const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k,
+                                 float scale, float* probs, float* scores, uint8_t* mask, int32_t* block_list,
+                                 int32_t* block_count, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!probs) return PARK_ERR_INVALID;
+  return retrieve_impl(false, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
+                       scores, mask, block_list, block_count, workspace, workspace_bytes, stream, probs);
 }
 
 int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,

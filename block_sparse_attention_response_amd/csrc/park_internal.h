@@ -35,11 +35,13 @@ hipError_t launch_qchunks(const int32_t* qoffsets, int BH, int N, int NQ, int ma
 
 // ----- retrieval (PAMA, pooled baseline, selection)
 size_t retrieve_workspace(const Shape& s, bool need_scores);
-// online: SCOPE's online per-head top-k floor on top of the fixed one
+// online: SCOPE's online per-head top-k floor on top of the fixed one; probs [BH][N][nk] (or
+// NULL): the unfused ablation, which materialises the probabilities there and averages them in
+// a second kernel
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
                            uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st,
-                           bool online = false);
+                           bool online = false, float* probs = nullptr);
 // PAMA and the same selection over clustered query blocks
 size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores);
 hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,

@@ -228,6 +228,21 @@ PARK_API int park_logmass_rmse(const void* Q, const void* K, int dtype, int B, i
                                const int32_t* counts, float scale, float* rmse, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * park_retrieve_blocks_unfused - park_retrieve_blocks without the fusion of PARK section 5.1
+ * ("Efficient Kernel Implementation"): the per-query probabilities P_iv of E7 are written to
+ * HBM (probs, [B,H,N,n_clusters] float, caller-allocated device memory, 4 N n_clusters bytes
+ * per head) and a second kernel averages each 64-token block's rows into W.  Scores and
+ * selection equal park_retrieve_blocks up to the order of the block sums; the call exists to
+ * measure what the fusion saves.  Inputs, outputs, workspace and errors as
+ * park_retrieve_blocks; INVALID also for a NULL probs.
+ */
+PARK_API int park_retrieve_blocks_unfused(const void* Q, int dtype, int B, int H, int N, int d,
+                                          const float* centroids, const int32_t* counts, int n_clusters,
+                                          int q_block, float top_p, int top_k, float scale, float* probs,
+                                          float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * Clustered query blocks.  PARK groups the queries by plain Euclidean k-means (Figure 2;
  * N_Q = 128 in section 6, "Implementations") instead of taking runs of 64 tokens.  Query

@@ -168,6 +168,34 @@ def test_retrieve(dev, orc, name, pooled):
     print(f"{name} pooled={pooled}: {ex} of {rows} rows exempt by margin")
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_retrieve_unfused(dev, orc, name):
+    """The unfused ablation (PARK section 5.1): the materialised probabilities P equal the
+    oracle's per-query softmax (PAMA over one-query blocks), and its W and selection meet the
+    same bars as the fused call's."""
+    import torch
+    cfg, Q, K, V = _data(name)
+    ocl = _oracle_clusters(orc, name)
+    B, H = Q.shape[:2]
+    cent = np.stack([np.stack([ocl[b][h]["centroids"] for h in range(H)]) for b in range(B)])
+    counts = np.stack([np.stack([ocl[b][h]["counts"] for h in range(H)]) for b in range(B)]).astype(np.int32)
+    scale = 1.0 / np.sqrt(cfg.d)
+    out = dev.park_retrieve_blocks_unfused(to_dev(Q, cfg.dtype), to_dev(cent, "f32"), to_dev(counts, "f32"),
+                                           cfg.top_p, cfg.top_k)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    assert g["probs"].shape == Q.shape[:3] + (cfg.n_clusters,)
+    for b in range(B):
+        for h in range(H):
+            P_ref = orc.pama(Q[b, h], cent[b, h], counts[b, h], 1, scale)
+            check_scores(g["probs"][b, h], P_ref)
+            assert np.all(g["probs"][b, h][:, counts[b, h] == 0] == 0.0)
+            W_ref = orc.pama(Q[b, h], cent[b, h], counts[b, h], 64, scale)
+            check_scores(g["scores"][b, h], W_ref)
+            compare_selection(g["scores"][b, h], W_ref, counts[b, h], cfg.top_p, cfg.top_k, g["mask"][b, h],
+                              g["block_list"][b, h], g["block_count"][b, h], orc)
+
+
 @pytest.mark.parametrize("p,k", [(0.0, 5), (1.0, 0), (0.5, 10 ** 6), (0.0, 0)])
 def test_retrieve_edge_parameters(dev, orc, p, k):
     import torch
