@@ -109,6 +109,41 @@ def test_retrieve_rejects(lib, fn):
     assert _retrieve(lib, fn, wsb=16) == WORKSPACE
 
 
+def test_unfused_retrieve_rejects(lib):
+    def call(**kw):
+        a = dict(Q=FAKE, dtype=1, B=1, H=1, N=256, d=128, cent=FAKE, counts=FAKE, nk=8, qb=64, p=0.9, k=2,
+                 scale=-1.0, probs=FAKE, scores=FAKE, mask=FAKE, lst=FAKE, cnt=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.park_retrieve_blocks_unfused(a["Q"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["cent"],
+                                                a["counts"], a["nk"], a["qb"], a["p"], a["k"], a["scale"], a["probs"],
+                                                a["scores"], a["mask"], a["lst"], a["cnt"], a["ws"], a["wsb"], None)
+    assert call(probs=None) == INVALID
+    assert call(mask=None) == INVALID
+    assert call(p=2.0) == INVALID
+    assert call(qb=16) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+
+
+def test_online_retrieve_rejects(lib):
+    def call(**kw):
+        a = dict(Q=FAKE, dtype=1, B=1, H=1, N=256, d=128, cent=FAKE, counts=FAKE, nk=8, qperm=None, qoff=None, nq=0,
+                 p=0.9, k=2, scale=-1.0, scores=FAKE, mask=FAKE, lst=FAKE, cnt=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.park_retrieve_blocks_online(a["Q"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["cent"],
+                                               a["counts"], a["nk"], a["qperm"], a["qoff"], a["nq"], a["p"], a["k"],
+                                               a["scale"], a["scores"], a["mask"], a["lst"], a["cnt"], a["ws"],
+                                               a["wsb"], None)
+    assert call(nq=3) == INVALID                       # 64-token blocks: 0 or ceil(N / 64) = 4
+    assert call(qperm=FAKE) == INVALID                 # one table without the other
+    assert call(qperm=FAKE, qoff=FAKE, nq=0) == INVALID
+    assert call(qperm=FAKE, qoff=FAKE, nq=257) == INVALID
+    assert call(k=-1) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(nq=4, ws=None) == WORKSPACE            # valid sizes reach the workspace check
+    assert call(qperm=FAKE, qoff=FAKE, nq=8, wsb=64) == WORKSPACE
+
+
 def _attn(lib, **kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=1, B=1, H=1, N=256, d=128, perm=FAKE, off=FAKE, nk=8, lst=FAKE, cnt=FAKE,
              qb=64, scale=-1.0, O=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
