@@ -258,42 +258,50 @@ __global__ __launch_bounds__(256) void k_chol(const double* G, int metric, doubl
 
 // ---------------------------------------------------------------------------------------
 // a3: k~ = R^T k for bf16 keys, as K . Rt^T with Rt split into three bf16 matrices (so the
-// float accumulation sees R to ~24 bits).  64 keys per workgroup, 4 waves.
+// float accumulation sees R to ~24 bits).  kTfKeys keys per workgroup of 4 waves.
 template <int D>
 __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__ K, const bf16* __restrict__ Rsp,
                                                         int N, float* __restrict__ Kt, float4* __restrict__ knorm) {
   // k~ = R^T k for kTfKeys keys per workgroup, and the key norms (|k|, 0, |k~|) on the way.
-  // Wave w computes output columns [32 ct, 32 ct + 32) (ct = w % NT) of the key tiles with
-  // parity w / NT; its B fragments (three bf16 splits of R^T for those columns) stay in
-  // registers while the keys stream through.
+  // The workgroup's keys are copied to LDS once (rows padded by 16 bytes: the 16 rows one
+  // 16-lane pass of a fragment read touches start in distinct banks); wave w computes output
+  // columns [32 ct, 32 ct + 32) (ct = w % NT) of the key tiles with parity w / NT, with its B
+  // fragments (three bf16 splits of R^T for those columns) in registers.
   constexpr int NT = D / 32;            // 32-column output tiles
   constexpr int KC = D / 16;
   constexpr int PAR = 4 / NT;           // waves per output tile
   constexpr int KTILES = kTfKeys / 32;
+  constexpr int KP = D + 8;             // padded LDS row (bf16)
+  __shared__ bf16 ks[kTfKeys * KP];
   __shared__ float tpart[NT][kTfKeys];  // |k~|^2 partial sums per output tile
   __shared__ float ksq[kTfKeys];        // |k|^2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int ct = w % NT, par = w / NT;
   const int bh = blockIdx.y, k0 = blockIdx.x * kTfKeys;
+  // the keys: 16-byte pieces, consecutive threads on consecutive pieces of a row
+  for (int e = tid; e < kTfKeys * (D / 8); e += 256) {
+    const int r = e / (D / 8), c = e % (D / 8);
+    bf16x8 x;
+    if (k0 + r < N) {
+      x = load_bf16x8(K + ((size_t)bh * N + k0 + r) * D + 8 * c);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (bf16)0.0f;
+    }
+    *reinterpret_cast<bf16x8*>(&ks[r * KP + 8 * c]) = x;
+  }
   const bf16* rs = Rsp + (size_t)bh * 3 * D * D + (size_t)(32 * ct + l32) * D + 8 * h;
   bf16x8 bfr[3][KC];
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) bfr[sp][kc] = load_bf16x8(rs + (size_t)sp * D * D + 16 * kc);
+  __syncthreads();
   const int my_row = c_row(l32 >> 1, lane);   // tile row of this lane after the reduce-scatter
   for (int kt = par; kt < KTILES; kt += PAR) {
-    const int key = k0 + 32 * kt + l32;
     bf16x8 a[KC];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (key < N) {
-        a[kc] = load_bf16x8(K + ((size_t)bh * N + key) * D + 16 * kc + 8 * h);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[kc][i] = (bf16)0.0f;
-      }
-    }
+    for (int kc = 0; kc < KC; ++kc) a[kc] = *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + l32) * KP + 16 * kc + 8 * h]);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
