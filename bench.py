@@ -423,7 +423,7 @@ def main():
         "attn_effective_tflops": round(attn_tflops, 2),
         "block_density": round(block_density, 4),
         "pair_density": round(pair_density, 4),
-        "roofline": {"bound": "mfma", "kernel": "k_attn_items<128>", "achieved": round(kernel_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_attn_items<128, false>", "achieved": round(kernel_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(cfg.name), "kernel_ms": round(kernel_ms, 3),
                      "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch" % (attn_flops / 1e12)},

@@ -502,7 +502,7 @@ struct AttnLds {
 };
 
 // One item: the partial softmax state of 64 queries over one key range's tiles.
-template <int D>
+template <int D, bool FUSED>
 __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const bf16* __restrict__ Q,
                                           const bf16* __restrict__ Kp, const bf16* __restrict__ Vp,
                                           const int32_t* __restrict__ plan, const int32_t* __restrict__ tbase,
@@ -510,6 +510,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
                                           f16* __restrict__ Opart, float2* __restrict__ ML,
                                           const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
                                           const int32_t* __restrict__ qperm, int maxc) {
+  constexpr bool fused = FUSED;
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
   static_assert(KC == 2 * DT, "K and V batches have the same size");
@@ -517,7 +518,10 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   auto& Vs = sm.Vs;
   auto& pring = sm.pring;
   auto& btab = sm.btab;
-  const int rr = item % kRanges;
+  // fused: the item is a whole row (all its ranges' tiles, which are contiguous in the plan),
+  // its state goes to range slot 0 and the other slots are marked empty
+  const int rr = fused ? 0 : item % kRanges;
+  const int row = fused ? item : item / kRanges;
   const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
   // The item's queries: 64-token blocks (chunks == NULL): block u = item / kRanges of the
   // plan rows, tokens 64u + i.  Clustered query blocks: item / kRanges = (head, chunk slot);
@@ -525,7 +529,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   // is block u's.
   int bh, prow, p0, nq;
   if (chunks) {
-    const int cr = item / kRanges;
+    const int cr = row;
     bh = cr / maxc;
     const int c = cr - bh * maxc;
     if (c >= ctotal[bh]) return;
@@ -534,7 +538,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     p0 = ch.y;
     nq = ch.z;
   } else {
-    prow = item / kRanges;
+    prow = row;
     bh = prow / NQ;
     p0 = 64 * (prow - bh * NQ);
     nq = min(64, N - p0);
@@ -545,9 +549,17 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     return qperm ? min(max(qperm[hrow + p0 + i], 0), N - 1) : p0 + i;
   };
   const int t0 = tbase[(size_t)prow * kRanges + rr];
-  const int nt = tbase[(size_t)prow * kRanges + rr + 1] - t0;
+  const int nt = tbase[(size_t)prow * kRanges + (fused ? kRanges : rr + 1)] - t0;
   if (nt <= 0) {
-    if (lane < nq) ML[(hrow + query(lane)) * kRanges + rr] = make_float2(-INFINITY, 0.0f);
+    if (lane < nq) {
+      float2* ml = ML + (hrow + query(lane)) * kRanges;
+      if (fused) {
+#pragma unroll
+        for (int r = 0; r < kRanges; ++r) ml[r] = make_float2(-INFINITY, 0.0f);
+      } else {
+        ml[rr] = make_float2(-INFINITY, 0.0f);
+      }
+    }
     return;
   }
   const int32_t* pl = plan + (size_t)t0 * 4;
@@ -930,6 +942,10 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
           *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
       if (h == 0) ML[(hrow + qrow[h2]) * kRanges + rr] = make_float2(m[h2], l);
+      if (fused && h == 1) {
+#pragma unroll
+        for (int r = 1; r < kRanges; ++r) ML[(hrow + qrow[h2]) * kRanges + r] = make_float2(-INFINITY, 0.0f);
+      }
     }
   }
 }
@@ -941,15 +957,17 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
 // item starts and used when it ends.  A wave whose range is exhausted moves on to the next
 // ranges' counters (the ranges' total work differs a little).  No wave waits for another, so
 // every wave ends once it has found every counter past its last item, whatever the number of
-// resident waves.
-template <int D>
+// resident waves.  FUSED (clustered query blocks): the items are whole rows (all ranges),
+// counter r hands out rows r per .. (r + 1) per - 1 (per = items / kRanges; indices past frows
+// are skipped).
+template <int D, bool FUSED>
 __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, const bf16* __restrict__ Kp,
                                                    const bf16* __restrict__ Vp, const int32_t* __restrict__ plan,
                                                    const int32_t* __restrict__ tbase, const float* __restrict__ vmax,
                                                    int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
                                                    float2* __restrict__ ML, int items, int32_t* __restrict__ ictr,
                                                    const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
-                                                   const int32_t* __restrict__ qperm, int maxc) {
+                                                   const int32_t* __restrict__ qperm, int maxc, int frows) {
   __shared__ AttnLds<D> sm;
   const int lane = threadIdx.x;
   for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
@@ -968,7 +986,18 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
     }
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&ictr[xr], 1);
-    attn_item<D>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal, qperm, maxc);
+    if constexpr (FUSED) {
+      // fused rows: counter r walks rows [r per, (r + 1) per), so the rows of a head (and
+      // the tiles they share) stay on one XCD
+      const int per = items / kRanges;
+      const int row = (item % kRanges) * per + item / kRanges;
+      if (row < frows)
+        attn_item<D, true>(row, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
+                           qperm, maxc);
+    } else {
+      attn_item<D, false>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
+                          qperm, maxc);
+    }
     item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(nxt);
   }
 }
@@ -1198,8 +1227,11 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     const int Gcap = group_cap(s);
     const int rows = s.BH * NQ;
     const int items = rows * kRanges;
-    // attention items: (plan row, range), or (head, chunk slot, range) for clustered blocks
-    const long long aitems = qb ? (long long)s.BH * maxc * kRanges : (long long)items;
+    // attention items: (plan row, range); for clustered blocks whole (head, chunk slot) rows
+    // over all ranges (their selections are small: split into ranges, items would hold a
+    // few tiles each), kRanges ceil(rows / kRanges) of them
+    const long long frows = qb ? (long long)s.BH * maxc : 0;
+    const long long aitems = qb ? (frows + kRanges - 1) / kRanges * kRanges : (long long)items;
     if (aitems >= (1LL << 31)) return hipErrorInvalidValue;
     auto k = reinterpret_cast<const bf16*>(K);
     auto v = reinterpret_cast<const bf16*>(V);
@@ -1231,12 +1263,15 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     // persistent waves: as many as the chip holds (four per CU, bound by LDS), a multiple of
     // kRanges (items is one)
     const int waves = (int)std::min<long long>(aitems, 4 * compute_units() / kRanges * kRanges);
-    if (s.d == 128)
-      k_attn_items<128><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
-                                              w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc);
-    else
-      k_attn_items<64><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart,
-                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc);
+#define PARK_ITEMS(DD, FF)                                                                                  \
+  k_attn_items<DD, FF><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, \
+                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc, (int)frows)
+    if (s.d == 128) {
+      if (qb) PARK_ITEMS(128, true); else PARK_ITEMS(128, false);
+    } else {
+      if (qb) PARK_ITEMS(64, true); else PARK_ITEMS(64, false);
+    }
+#undef PARK_ITEMS
     PARK_CHECK();
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     const int total_rows = s.BH * s.N;

@@ -220,8 +220,10 @@ def test_ragged_and_empty_query_blocks(dev, orc):
 
 def test_consecutive_blocks_match_64_token_path(dev, orc):
     """The identity permutation with 64-token offsets makes the clustered entry points compute
-    the 64-token ones: the attention items are the same (same queries, tiles and order), so O
-    and lse are bit-identical; W differs at most by the final division's rounding."""
+    the 64-token ones: W differs at most by the final division's rounding; attention sees the
+    same queries and tiles, but the clustered call takes a block's tiles in one pass where the
+    64-token call splits them into key ranges and merges the partial states, so O agrees to two
+    bf16 units in the last place and lse to float rounding."""
     import torch
     name = "ragged-bf16-d128-q8"
     cfg, nq, Q, K, V, qc, kc = _case(orc, name)
@@ -242,5 +244,7 @@ def test_consecutive_blocks_match_64_token_path(dev, orc):
     O2, l2 = dev.park_block_sparse_attn_clustered(*dv, to_dev(perm, "f32"), to_dev(off, "f32"), to_dev(qperm, "f32"),
                                                   to_dev(qoff, "f32"), lst, cnt)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(O2), host(O1))
-    np.testing.assert_array_equal(host(l2), host(l1))
+    o1, o2 = host(O1).astype(np.float64), host(O2).astype(np.float64)
+    assert np.all(np.abs(o2 - o1) <= 2.0 ** -6 * np.maximum(1.0, np.abs(o1)))
+    lse1, lse2 = host(l1).astype(np.float64), host(l2).astype(np.float64)
+    assert np.all(np.abs(lse2 - lse1) <= 1e-5 * np.maximum(1.0, np.abs(lse1)))
