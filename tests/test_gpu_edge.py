@@ -1,6 +1,7 @@
-"""Degenerate sizes through the whole path, GPU against the oracle: a single token, one
-cluster, every key its own cluster, sizes just below, at and above one query block, for
-both dtypes and head sizes, with 64-token and clustered query blocks."""
+"""Degenerate and maximum sizes through the whole path, GPU against the oracle: a single
+token, one cluster, every key its own cluster, sizes just below, at and above one query block,
+and the largest cluster and query-block counts the library takes, for both dtypes and head
+sizes, with 64-token and clustered query blocks."""
 import numpy as np
 import pytest
 
@@ -10,7 +11,9 @@ pytestmark = pytest.mark.gpu
 
 # (N, d, dtype, key clusters, query blocks for the clustered path)
 SHAPES = [(1, 64, "f32", 1, 1), (1, 128, "bf16", 1, 1), (5, 64, "bf16", 5, 2), (63, 128, "f32", 1, 3),
-          (64, 64, "bf16", 3, 1), (65, 128, "bf16", 65, 4), (129, 64, "f32", 7, 5), (200, 128, "bf16", 200, 8)]
+          (64, 64, "bf16", 3, 1), (65, 128, "bf16", 65, 4), (129, 64, "f32", 7, 5), (200, 128, "bf16", 200, 8),
+          # the library's maxima: PARK_MAX_CLUSTERS key clusters and PARK_MAX_QUERY_BLOCKS query blocks
+          (4000, 128, "bf16", 1536, 1536), (3001, 64, "f32", 1536, 1536)]
 
 
 @pytest.fixture(scope="module")
