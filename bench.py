@@ -328,6 +328,8 @@ def main():
                     help="also time SCOPE's online per-head top-k selection on 64-token blocks")
     ap.add_argument("--diagnostics", choices=["on", "off"], default="on",
                     help="also measure the retrieval TV and log-mass errors and time the unfused retrieval")
+    ap.add_argument("--leg", choices=["all", "clustered"], default="all",
+                    help="clustered: time only the clustered-query-block step (for kernel traces of it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -357,10 +359,18 @@ def main():
     B, H, N, d = q.shape
     nk = cfg.n_clusters
     top_p, top_k = cfg.top_p, (cfg.top_k if not cfg.forced_k else cfg.forced_k[1])
+    stream = torch.cuda.current_stream()
+    if args.leg == "clustered":
+        if args.query_blocks <= 0:
+            print("--leg clustered needs --query-blocks > 0", file=sys.stderr)
+            sys.exit(2)
+        res = clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream, None)
+        print(json.dumps({"leg": "query_clustered", "workload": cfg.name, "steps": args.steps,
+                          "warmup": args.warmup, **res}), flush=True)
+        return
     ws_c = torch.empty(park.workspace_bytes(park.OP_CLUSTER_KEYS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     ws_r = torch.empty(park.workspace_bytes(park.OP_RETRIEVE_BLOCKS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     ws_a = torch.empty(park.workspace_bytes(park.OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def step(ev=None, kev=None):
         if ev: ev[0].record(stream)
