@@ -64,9 +64,17 @@ def test_online_topk(dev, orc, name):
     else:
         base = dev.park_retrieve_blocks(q, c_d, n_d, cfg.top_p, cfg.top_k)
         out = dev.park_retrieve_blocks_online(q, c_d, n_d, cfg.top_p, cfg.top_k)
+    # without returned scores (W then lives in the workspace) the selection is the same
+    if nq:
+        out2 = dev.park_retrieve_blocks_online(q, c_d, n_d, cfg.top_p, cfg.top_k, qp, qo, scores=False)
+    else:
+        out2 = dev.park_retrieve_blocks_online(q, c_d, n_d, cfg.top_p, cfg.top_k, scores=False)
     torch.cuda.synchronize()
     gb = {k: host(v) for k, v in base.items()}
     g = {k: host(v) for k, v in out.items()}
+    assert "scores" not in out2
+    for key in ("mask", "block_list", "block_count"):
+        assert np.array_equal(host(out2[key]), g[key])
     assert np.array_equal(g["scores"], gb["scores"])
     scale = 1.0 / np.sqrt(d)
     extended = moved = 0
