@@ -220,6 +220,52 @@ def online_leg(args, park, torch, np, cfg, q, k, v, cl, top_p, top_k, stream, ls
     return res
 
 
+def sweep_leg(args, park, torch, np, cfg, q, k, v, cl, lse_dense, ws_c, ws_r, ws_a):
+    """The density sweep (forced top-k with top-p = 0, the k values of the density-sweep
+    workload) for PARK (QRKC clusters, PAMA scores) and for the baseline (Euclidean clusters,
+    pooled-query scores), on the main leg's inputs: retrieval and attention times, densities
+    and recall against dense attention for every k."""
+    import park_synth
+    B, H, N, d = q.shape
+    nk = cfg.n_clusters
+    ks = park_synth.CONFIGS[4].forced_k
+    ce = park.park_cluster_keys(q, k, nk, cfg.iters, metric="euclidean", workspace=ws_c)
+
+    def timed(fn):
+        out = fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1) / args.steps
+
+    res = {"k": list(ks), "top_p": 0.0}
+    for name, c, f in (("park", cl, park.park_retrieve_blocks),
+                       ("pooled_euclidean", ce, park.park_retrieve_blocks_pooled)):
+        rows = []
+        for kk in ks:
+            log(f"sweep {name} k={kk}")
+            rb, t_r = timed(lambda: f(q, c["centroids"], c["counts"], 0.0, kk, scores=False, workspace=ws_r))
+            (O, lse), t_a = timed(lambda: park.park_block_sparse_attn(q, k, v, c["perm"], c["offsets"], rb["block_list"],
+                                                                     rb["block_count"], workspace=ws_a))
+            pairs, _ = effective_pairs(torch, c["counts"], rb["block_list"], rb["block_count"], N)
+            row = {"k": kk, "retrieval_ms": round(t_r, 3), "attn_ms": round(t_a, 3),
+                   "attn_effective_tflops": round(4.0 * d * pairs / (t_a * 1e-3) / 1e12, 2),
+                   "block_density": round(float(rb["block_count"].float().mean().item()) / nk, 4),
+                   "pair_density": round(pairs / (B * H * float(N) * N), 4)}
+            if lse_dense is not None:
+                rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
+                row["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
+                                 "worst": round(float(rec.min()), 4)}
+            rows.append(row)
+            del rb, O, lse
+        res[name] = rows
+    return res
+
+
 def unfused_ablation(args, park, torch, np, cfg, q, cl, top_p, top_k, ws_r):
     """The ablation of PARK's fused retrieval kernel (section 5.1): the same retrieval with the
     per-query probabilities P [B,H,N,N_K] float32 written to HBM and averaged by a second
@@ -328,6 +374,8 @@ def main():
                     help="also time SCOPE's online per-head top-k selection on 64-token blocks")
     ap.add_argument("--diagnostics", choices=["on", "off"], default="on",
                     help="also measure the retrieval TV and log-mass errors and time the unfused retrieval")
+    ap.add_argument("--sweep", choices=["on", "off"], default="on",
+                    help="also time the forced top-k density sweep for PARK and the pooled/Euclidean baseline")
     ap.add_argument("--leg", choices=["all", "clustered"], default="all",
                     help="clustered: time only the clustered-query-block step (for kernel traces of it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -448,6 +496,10 @@ def main():
         rec = torch.exp((lse - lse_dense).double()).mean(-1).flatten().cpu().numpy()
         result["recall"] = {"mean": round(float(rec.mean()), 4), "p05": round(float(np.percentile(rec, 5)), 4),
                             "worst": round(float(rec.min()), 4), "over": "heads (mean over queries)"}
+
+    if args.sweep == "on":
+        result["density_sweep"] = sweep_leg(args, park, torch, np, cfg, q, k, v, cl,
+                                            lse_dense if args.recall == "on" else None, ws_c, ws_r, ws_a)
 
     if args.online == "on":
         result["online_topk"] = online_leg(args, park, torch, np, cfg, q, k, v, cl, top_p, top_k, stream,
