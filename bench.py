@@ -361,8 +361,8 @@ def schedule_leg(args, torch, np, cfg, q, k, v, top_p, top_k):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload index of park_synth.CONFIGS")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--recall", choices=["on", "off"], default="on")
@@ -476,6 +476,10 @@ def main():
                    "key_clusters": nk, "kmeans_iters": cfg.iters, "top_p": top_p, "top_k_floor": top_k,
                    "query_block": 64, "parallelism": "single GPU"},
         "retrieval_ms_per_layer": round(float(retrieve_ms), 3),
+        "median_ms": {"cluster": round(float(np.median(ms[:, 0])), 3), "retrieval": round(float(np.median(ms[:, 1])), 3),
+                      "attention": round(float(np.median(ms[:, 2])), 3),
+                      "attention_kernel": round(float(np.median([e.elapsed_ms() for e in kevs])), 3),
+                      "over": "timed steps"},
         "cluster_ms_per_layer": round(float(cluster_ms), 3),
         "attn_ms_per_layer": round(float(attn_ms), 3),
         "attn_effective_tflops": round(attn_tflops, 2),
