@@ -228,7 +228,7 @@ def sweep_leg(args, park, torch, np, cfg, q, k, v, cl, lse_dense, ws_c, ws_r, ws
     import park_synth
     B, H, N, d = q.shape
     nk = cfg.n_clusters
-    ks = park_synth.CONFIGS[4].forced_k
+    ks = park_synth.DENSITY_SWEEP.forced_k
     ce = park.park_cluster_keys(q, k, nk, cfg.iters, metric="euclidean", workspace=ws_c)
 
     def timed(fn):
@@ -363,7 +363,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload index of park_synth.CONFIGS")
+    ap.add_argument("--workload", default="wan2.1-14b-720p-21x45x80",
+                    help="synthetic workload by name (park_synth.WORKLOADS)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--recall", choices=["on", "off"], default="on")
     ap.add_argument("--query-blocks", type=int, default=128, metavar="NQ",
@@ -391,7 +392,7 @@ def main():
 
     import numpy as np
     import park_synth
-    cfg = park_synth.CONFIGS[args.config]
+    cfg = park_synth.WORKLOADS[args.workload]
     log(f"generating {cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} {cfg.dtype}")
     t = time.perf_counter()
     Q, K, V = park_synth.generate(cfg, seed=0, workers=16)

@@ -18,7 +18,8 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "generate", "round_bf16", "rope_3d"]
+__all__ = ["Config", "WORKLOADS", "TINY", "WAN13B_480P", "WAN14B_720P", "HUNYUAN_720P", "DENSITY_SWEEP", "generate",
+           "round_bf16", "rope_3d"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,14 +50,16 @@ class Config:
         return (self.N + self.q_block - 1) // self.q_block
 
 
-CONFIGS = {
-    0: Config("tiny-fp32-2x32x32", 1, 1, (2, 32, 32), 0, 64, "f32", 16, (22, 21, 21), 32, 5, 0.9, 2),
-    1: Config("wan1.3b-480p-21x30x52", 1, 12, (21, 30, 52), 0, 128, "bf16", 64, (44, 42, 42), 512, 10, 0.9, 8),
-    2: Config("wan2.1-14b-720p-21x45x80", 1, 40, (21, 45, 80), 0, 128, "bf16", 128, (44, 42, 42), 1024, 10, 0.9, 8),
-    3: Config("hunyuan-720p-33x45x80+256text", 1, 24, (33, 45, 80), 256, 128, "bf16", 128, (16, 56, 56), 1536, 10, 0.9, 8),
-    4: Config("density-sweep-wan2.1-14b-720p", 1, 40, (21, 45, 80), 0, 128, "bf16", 128, (44, 42, 42), 1024, 10, 0.0, 0,
-              forced_k=(51, 102, 205, 410, 1024)),
-}
+TINY = Config("tiny-fp32-2x32x32", 1, 1, (2, 32, 32), 0, 64, "f32", 16, (22, 21, 21), 32, 5, 0.9, 2)
+WAN13B_480P = Config("wan1.3b-480p-21x30x52", 1, 12, (21, 30, 52), 0, 128, "bf16", 64, (44, 42, 42), 512, 10, 0.9, 8)
+WAN14B_720P = Config("wan2.1-14b-720p-21x45x80", 1, 40, (21, 45, 80), 0, 128, "bf16", 128, (44, 42, 42), 1024, 10,
+                     0.9, 8)
+HUNYUAN_720P = Config("hunyuan-720p-33x45x80+256text", 1, 24, (33, 45, 80), 256, 128, "bf16", 128, (16, 56, 56), 1536,
+                      10, 0.9, 8)
+DENSITY_SWEEP = Config("density-sweep-wan2.1-14b-720p", 1, 40, (21, 45, 80), 0, 128, "bf16", 128, (44, 42, 42), 1024,
+                       10, 0.0, 0, forced_k=(51, 102, 205, 410, 1024))
+# every workload by its name
+WORKLOADS = {c.name: c for c in (TINY, WAN13B_480P, WAN14B_720P, HUNYUAN_720P, DENSITY_SWEEP)}
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

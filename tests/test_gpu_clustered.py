@@ -19,12 +19,12 @@ pytestmark = pytest.mark.gpu
 
 # (config, heads, query blocks)
 CASES = {
-    "cfg0-f32-d64-q16": (park_synth.CONFIGS[0], None, 16),
+    "cfg0-f32-d64-q16": (park_synth.TINY, None, 16),
     "ragged-bf16-d128-q8": (Config("ragged-bf16-d128", 1, 2, (3, 10, 33), 0, 128, "bf16", 8, (44, 42, 42), 24, 4,
                                    0.9, 3), None, 8),
     "ragged-bf16-d64-text-q5": (Config("ragged-bf16-d64", 1, 2, (2, 17, 29), 37, 64, "bf16", 6, (22, 21, 21), 20, 3,
                                        0.8, 2), None, 5),
-    "cfg1-2heads-q128": (park_synth.CONFIGS[1], [0, 7], 128),
+    "cfg1-2heads-q128": (park_synth.WAN13B_480P, [0, 7], 128),
 }
 
 

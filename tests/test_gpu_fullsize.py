@@ -89,9 +89,10 @@ def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc
     return ex, err
 
 
-@pytest.mark.parametrize("cid,heads", [(1, (0, 11)), (2, (0, 39)), (3, (5, 23))])
-def test_fullsize_config(dev, orc, cid, heads):
-    cfg = park_synth.CONFIGS[cid]
+@pytest.mark.parametrize("cid,heads", [("wan1.3b-480p-21x30x52", (0, 11)), ("wan2.1-14b-720p-21x45x80", (0, 39)),
+                                       ("hunyuan-720p-33x45x80+256text", (5, 23))])
+def test_fullsize_workload(dev, orc, cid, heads):
+    cfg = park_synth.WORKLOADS[cid]
     Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
     g1 = _run(dev, cfg, Q, K, V, 1, cfg.top_p, cfg.top_k)
     gT1 = _run(dev, cfg, Q, K, V, cfg.iters - 1, cfg.top_p, cfg.top_k)
@@ -106,14 +107,14 @@ def test_fullsize_config(dev, orc, cid, heads):
             assert np.all(gT["block_count"][b, h] >= np.minimum(cfg.top_k, (gT["counts"][b, h] > 0).sum()))
     for h in heads:
         ex, err = _check_head(orc, cfg, Q, K, V, g1, gT1, gT, 0, h, cfg.top_p, cfg.top_k)
-        print(f"config {cid} head {h}: {ex} selection rows exempt by margin, attention err {err:.2e}")
+        print(f"{cid} head {h}: {ex} selection rows exempt by margin, attention err {err:.2e}")
 
 
 @pytest.mark.parametrize("pooled", [False, True])
 def test_density_sweep_config4(dev, orc, pooled):
-    """Config 4: forced top-k (top_p = 0) at the config-2 shape; PARK and the pooled-query /
+    """The density sweep: forced top-k (top_p = 0) at the 75.6k-token shape; PARK and the pooled-query /
     Euclidean-key baseline.  k = 1024 (every cluster) must reproduce dense attention."""
-    cfg = park_synth.CONFIGS[4]
+    cfg = park_synth.DENSITY_SWEEP
     Q, K, V = park_synth.generate(cfg, seed=0, heads=[0, 1, 2, 3], workers=4)
     metric = "euclidean" if pooled else "qrkc"
     import torch
@@ -140,7 +141,7 @@ def test_density_sweep_config4(dev, orc, pooled):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cid,h", [(2, 17), (3, 9)])
+@pytest.mark.parametrize("cid,h", [("wan2.1-14b-720p-21x45x80", 17), ("hunyuan-720p-33x45x80+256text", 9)])
 def test_fullsize_from_oracle_clustering(dev, orc, cid, h):
     """A full-size head with no oracle input taken from the GPU.  The oracle clusters head h
     from scratch: the GPU's own full run must agree on >= 99% of the labels with an objective
@@ -149,7 +150,7 @@ def test_fullsize_from_oracle_clustering(dev, orc, cid, h):
     attention, the oracle's selection) for head h, and head h's scores, selection and sampled
     query blocks meet the usual bars against the oracle on those same inputs."""
     import torch
-    cfg = park_synth.CONFIGS[cid]
+    cfg = park_synth.WORKLOADS[cid]
     Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
     g = _run(dev, cfg, Q, K, V, cfg.iters, cfg.top_p, cfg.top_k)
     nk, scale = cfg.n_clusters, 1.0 / np.sqrt(cfg.d)
@@ -157,7 +158,7 @@ def test_fullsize_from_oracle_clustering(dev, orc, cid, h):
     agree = float(np.mean(o["labels"] == g["labels"][0, h]))
     Jo = orc.objective(o["Kt"], orc.update(o["Kt"], o["labels"], o["km"]["centroids"]), o["labels"])
     Jg = orc.objective(o["Kt"], orc.update(o["Kt"], g["labels"][0, h], o["km"]["centroids"]), g["labels"][0, h])
-    print(f"config {cid} head {h}: label agreement {agree:.5f}, objective ratio {Jg / Jo:.6f}")
+    print(f"{cid} head {h}: label agreement {agree:.5f}, objective ratio {Jg / Jo:.6f}")
     assert agree >= 0.99 and Jg <= Jo * 1.01
     # retrieval on the oracle's clustering of head h
     cent, counts = g["centroids"].copy(), g["counts"].copy()
@@ -183,7 +184,7 @@ def test_fullsize_from_oracle_clustering(dev, orc, cid, h):
     Oo, lo = orc.block_sparse_attn(Q[0, h], K[0, h], V[0, h], o["perm"], o["offsets"], lst_o, cnt_o, 64, scale, ub)
     rows = np.concatenate([np.arange(64 * u, min(64 * u + 64, cfg.N)) for u in ub])
     err = np.abs(host(O[0, h])[rows] - Oo[rows]).max()
-    print(f"config {cid} head {h}: {ex} selection rows exempt, attention err {err:.2e}")
+    print(f"{cid} head {h}: {ex} selection rows exempt, attention err {err:.2e}")
     assert err <= 2e-2
     assert np.abs(host(lse[0, h])[rows] - lo[rows]).max() <= 1e-3
     del q, k, v, O, lse

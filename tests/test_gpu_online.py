@@ -25,8 +25,8 @@ CASES = {
                                       0.9, 3), None, 0),
     "ragged-f32-d64-text-q5": (Config("ragged-f32-d64", 1, 2, (2, 17, 29), 37, 64, "f32", 6, (22, 21, 21), 20, 3,
                                       0.8, 2), None, 5),
-    "cfg1-2heads-64tok": (park_synth.CONFIGS[1], [0, 7], 0),
-    "cfg1-2heads-q128": (park_synth.CONFIGS[1], [0, 7], 128),
+    "cfg1-2heads-64tok": (park_synth.WAN13B_480P, [0, 7], 0),
+    "cfg1-2heads-q128": (park_synth.WAN13B_480P, [0, 7], 128),
 }
 
 

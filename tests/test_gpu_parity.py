@@ -21,14 +21,14 @@ from parity_util import check_scores, compare_selection, host, to_dev
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    "cfg0-f32-d64": (park_synth.CONFIGS[0], None),
+    "cfg0-f32-d64": (park_synth.TINY, None),
     "ragged-bf16-d128": (Config("ragged-bf16-d128", 1, 2, (3, 10, 33), 0, 128, "bf16", 8, (44, 42, 42), 24, 4,
                                 0.9, 3), None),
     "ragged-bf16-d64-text": (Config("ragged-bf16-d64", 1, 2, (2, 17, 29), 37, 64, "bf16", 6, (22, 21, 21), 20, 3,
                                     0.8, 2), None),
     "ragged-f32-d128": (Config("ragged-f32-d128", 2, 1, (1, 20, 35), 0, 128, "f32", 5, (44, 42, 42), 16, 3,
                                0.9, 4), None),
-    "cfg1-2heads": (park_synth.CONFIGS[1], [0, 7]),
+    "cfg1-2heads": (park_synth.WAN13B_480P, [0, 7]),
 }
 
 

@@ -128,7 +128,7 @@ def test_kmeans_objective_non_increasing(orc):
     """Lloyd steps never increase the objective (k-means, App. D.2 'K-means optimizes the
     specified objective iteratively')."""
     import park_synth
-    Q, K, _ = park_synth.generate(park_synth.CONFIGS[0])
+    Q, K, _ = park_synth.generate(park_synth.TINY)
     cl = orc.cluster_keys(Q[0, 0], K[0, 0], 32, 10)
     ja, ju = cl["km"]["J_assign"], cl["km"]["J_update"]
     for t in range(len(ja)):
