@@ -509,7 +509,8 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
                                           const float* __restrict__ vmax, int N, int NQ, int Gcap, float scale2,
                                           f16* __restrict__ Opart, float2* __restrict__ ML,
                                           const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
-                                          const int32_t* __restrict__ qperm, int maxc) {
+                                          const int32_t* __restrict__ qperm, int maxc, bf16* __restrict__ Ofin,
+                                          float* __restrict__ lse) {
   constexpr bool fused = FUSED;
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
@@ -519,7 +520,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   auto& pring = sm.pring;
   auto& btab = sm.btab;
   // fused: the item is a whole row (all its ranges' tiles, which are contiguous in the plan),
-  // its state goes to range slot 0 and the other slots are marked empty
+  // so it writes the final output and log-sum-exp itself (no partial states, no merge)
   const int rr = fused ? 0 : item % kRanges;
   const int row = fused ? item : item / kRanges;
   const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
@@ -552,12 +553,17 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   const int nt = tbase[(size_t)prow * kRanges + (fused ? kRanges : rr + 1)] - t0;
   if (nt <= 0) {
     if (lane < nq) {
-      float2* ml = ML + (hrow + query(lane)) * kRanges;
-      if (fused) {
+      if constexpr (FUSED) {
+        // no key selected: O = 0, lse = -inf
+        bf16x8 z;
 #pragma unroll
-        for (int r = 0; r < kRanges; ++r) ml[r] = make_float2(-INFINITY, 0.0f);
+        for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+        bf16* orow = Ofin + (hrow + query(lane)) * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) *reinterpret_cast<bf16x8*>(orow + 8 * c) = z;
+        if (lse) lse[hrow + query(lane)] = -INFINITY;
       } else {
-        ml[rr] = make_float2(-INFINITY, 0.0f);
+        ML[(hrow + query(lane)) * kRanges + rr] = make_float2(-INFINITY, 0.0f);
       }
     }
     return;
@@ -922,6 +928,30 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   // no copy may still be writing this workgroup's LDS when the wave ends
   wait_copies<0>();
 
+  if constexpr (FUSED) {
+    // the whole row: O = O^T / lb in bf16, lse = ln 2 (m + log2 l) (what the merge gives for
+    // a single live state)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float l = lsum[h2] + __shfl_xor(lsum[h2], 32);
+      const float lbs = lb[h2] + __shfl_xor(lb[h2], 32);
+      if (qrow[h2] >= 0) {
+        const float inv = lbs > 0.0f ? 1.0f / lbs : 0.0f;
+        bf16* orow = Ofin + (hrow + qrow[h2]) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (bf16)(oacc[h2][dt][4 * g + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
+          }
+        if (lse && h == 0) lse[hrow + qrow[h2]] = l > 0.0f ? (m[h2] + __log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+    return;
+  }
   // partial state: O_r = O^T / lb stored as fp16 in units of the head's value unit (so
   // |stored| <= 1), and (m, l) in float
   const float unit = value_unit(vmax[bh]);
@@ -942,10 +972,6 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
           *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * g + 4 * h) = o;
         }
       if (h == 0) ML[(hrow + qrow[h2]) * kRanges + rr] = make_float2(m[h2], l);
-      if (fused && h == 1) {
-#pragma unroll
-        for (int r = 1; r < kRanges; ++r) ML[(hrow + qrow[h2]) * kRanges + r] = make_float2(-INFINITY, 0.0f);
-      }
     }
   }
 }
@@ -967,7 +993,8 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
                                                    int N, int NQ, int Gcap, float scale2, f16* __restrict__ Opart,
                                                    float2* __restrict__ ML, int items, int32_t* __restrict__ ictr,
                                                    const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
-                                                   const int32_t* __restrict__ qperm, int maxc, int frows) {
+                                                   const int32_t* __restrict__ qperm, int maxc, int frows,
+                                                   bf16* __restrict__ Ofin, float* __restrict__ lse) {
   __shared__ AttnLds<D> sm;
   const int lane = threadIdx.x;
   for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
@@ -993,10 +1020,10 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
       const int row = (item % kRanges) * per + item / kRanges;
       if (row < frows)
         attn_item<D, true>(row, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
-                           qperm, maxc);
+                           qperm, maxc, Ofin, lse);
     } else {
       attn_item<D, false>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
-                          qperm, maxc);
+                          qperm, maxc, Ofin, lse);
     }
     item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(nxt);
   }
@@ -1265,7 +1292,7 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     const int waves = (int)std::min<long long>(aitems, 4 * compute_units() / kRanges * kRanges);
 #define PARK_ITEMS(DD, FF)                                                                                  \
   k_attn_items<DD, FF><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, \
-                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc, (int)frows)
+                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc, (int)frows, o, lse)
     if (s.d == 128) {
       if (qb) PARK_ITEMS(128, true); else PARK_ITEMS(128, false);
     } else {
@@ -1274,12 +1301,14 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
 #undef PARK_ITEMS
     PARK_CHECK();
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
-    const int total_rows = s.BH * s.N;
-    const long long mthreads = (long long)total_rows * (s.d / 8);
-    const unsigned mblocks = (unsigned)((mthreads + 255) / 256);
-    if (s.d == 128) k_attn_merge<128><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
-    else k_attn_merge<64><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
-    PARK_CHECK();
+    if (!qb) {   // clustered blocks: the fused rows wrote O and lse themselves
+      const int total_rows = s.BH * s.N;
+      const long long mthreads = (long long)total_rows * (s.d / 8);
+      const unsigned mblocks = (unsigned)((mthreads + 255) / 256);
+      if (s.d == 128) k_attn_merge<128><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
+      else k_attn_merge<64><<<mblocks, 256, 0, st>>>(w.Opart, w.ML, w.vmax, total_rows, s.N, o, lse);
+      PARK_CHECK();
+    }
 #undef PARK_CHECK
   } else {
     dim3 grid(qb ? maxc : NQ, s.BH);
