@@ -341,6 +341,38 @@ __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__
   }
 }
 
+// a3 for the Euclidean metric with bf16 keys: R = I, so k~ = k exactly (a widening copy) and
+// |k~| = |k|.  D / 8 threads per key, 64 keys per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void k_copy_keys_bf16(const bf16* __restrict__ K, int N, float* __restrict__ Kt,
+                                                        float4* __restrict__ knorm) {
+  constexpr int TPK = D / 8;             // threads per key
+  constexpr int KPS = 256 / TPK;         // keys per pass
+  const int tid = threadIdx.x, bh = blockIdx.y;
+  const int sub = tid / TPK, c = tid % TPK;
+  for (int r = sub; r < 64; r += KPS) {
+    const int j = blockIdx.x * 64 + r;
+    float s2 = 0.0f;
+    if (j < N) {
+      const size_t off = ((size_t)bh * N + j) * D + 8 * c;
+      const bf16x8 x = load_bf16x8(K + off);
+      f32x4 lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { lo[i] = (float)x[i]; hi[i] = (float)x[4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s2 = fmaf((float)x[i], (float)x[i], s2);
+      *reinterpret_cast<f32x4*>(Kt + off) = lo;
+      *reinterpret_cast<f32x4*>(Kt + off + 4) = hi;
+    }
+#pragma unroll
+    for (int o = 1; o < TPK; o <<= 1) s2 += __shfl_xor(s2, o);
+    if (j < N && c == 0) {
+      const float n = sqrtf(s2);
+      knorm[(size_t)bh * N + j] = make_float4(n, 0.0f, n, 0.0f);
+    }
+  }
+}
+
 // a3 for float keys: one thread per output, double sums.
 template <int D>
 __global__ __launch_bounds__(256) void k_transform_f32(const float* __restrict__ K, const double* __restrict__ R64,
@@ -1027,6 +1059,9 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     PARK_CHECK();
     dim3 ngrid((s.N + 63) / 64, s.BH);
     k_key_norms<float, D><<<ngrid, 256, 0, st>>>(reinterpret_cast<const float*>(K), w.Kt, s.N, w.knorm);
+  } else if (metric != 0) {
+    k_copy_keys_bf16<D><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), s.N, w.Kt,
+                                                                     w.knorm);
   } else {
     dim3 grid((s.N + kTfKeys - 1) / kTfKeys, s.BH);
     k_transform_bf16<D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(K), w.Rsp, s.N, w.Kt, w.knorm);
