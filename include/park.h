@@ -313,7 +313,8 @@ PARK_API int park_retrieve_blocks_clustered(const void* Q, int dtype, int B, int
  * The counted unit is a key cluster (the unit PARK selects), where SCOPE counts keys.
  * Inputs, outputs, workspace (park_workspace_bytes or park_workspace_bytes_clustered with op
  * PARK_OP_RETRIEVE_BLOCKS) and errors as the two entry points above; INVALID also for a
- * non-zero n_qblocks other than ceil(N/64) without q_perm / q_offsets.
+ * non-zero n_qblocks other than ceil(N/64) without q_perm / q_offsets, and for only one of
+ * q_perm / q_offsets given.
  */
 PARK_API int park_retrieve_blocks_online(const void* Q, int dtype, int B, int H, int N, int d,
                                          const float* centroids, const int32_t* counts, int n_clusters,
