@@ -37,7 +37,7 @@ __all__ = [
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
     "park_block_sparse_attn_clustered", "park_retrieve_blocks_online", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
-    "PARK_ERR_NUMERIC", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
+    "PARK_ERR_NUMERIC", "numeric_status", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpark.so")
@@ -210,6 +210,13 @@ def park_cluster_keys(Q, K, n_clusters: int, iters: int, metric: str = "qrkc", a
                                  _ptr(out["offsets"]), _ptr(out["status"]), _ptr(ws), wsb, _stream(Q))
     _check(st, "park_cluster_keys")
     return out
+
+
+def numeric_status(status) -> int:
+    """PARK_ERR_NUMERIC if any head of a park_cluster_keys `status` tensor is flagged (its
+    query metric could not be factored and the head was clustered with R = I), else PARK_OK.
+    Reads the tensor on the host, so it waits for the clustering to finish."""
+    return PARK_ERR_NUMERIC if bool((status != 0).any().item()) else PARK_OK
 
 
 def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace, probs=None):

@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
 // holding all 64 queries of the block, so every K or V fragment it reads feeds two MFMAs:
 //   S^T = K Q^T      (A: 32 keys x 16 columns in bf16; B: Q^T fragments of query halves 0 and
 //                     1 in registers; the accumulators start at 0 / -inf, which masks padding)
-//   O^T += V^T P^T   (A: V^T in fp16; B: P^T straight from the S^T accumulators, as fp16)
+//   O^T += V^T P^T   (A: V^T in bf16; B: P^T from the S^T accumulators, rounded to bf16)
 // Keys and values are copied memory -> LDS (global_load_lds, two tiles deep per wave) in MFMA
 // fragment order and read back one fragment per lane per MFMA.
 // Row swap inside each 16-row chunk of a tile (rows 4..7 <-> 8..11): with it, the 8 rows of
@@ -767,13 +767,13 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     lb[1] += wb[1];
   };
 
-  // One pipeline step (tile t + 1 exists): tile t's fp16 weights are in pb (settled) and its
+  // One pipeline step (tile t + 1 exists): tile t's bf16 weights are in pb (settled) and its
   // values in LDS buffer t & 1, tile t + 1's keys in buffer (t + 1) & 1.  In the order written
   // (scheduling fences keep it; with one wave per SIMD the matrix and vector units overlap
   // only through this interleave):
   //   A1: S^T MFMAs of tile t + 1, query half 0;
   //   A2: S^T MFMAs of tile t + 1, query half 1, with the exponentials of half 0;
-  //   B:  P V MFMAs of tile t (O^T += V^T P^T) with the exponentials of half 1 and the fp16
+  //   B:  P V MFMAs of tile t (O^T += V^T P^T) with the exponentials of half 1 and the bf16
   //       conversion and weight sums of half 0;
   //   then the conversion and sums of half 1 and the check of tile t + 1's weights (the rare
   //   rescale), leaving them settled in pb.
@@ -1208,8 +1208,10 @@ static AttnWs carve_attn(const Shape& s, const QueryBlocks* qb, void* base, size
   w.plan = reinterpret_cast<int32_t*>(take((rows * per_row + 128) * sizeof(int32_t)));
   w.Kp = reinterpret_cast<bf16*>(take(kv));
   w.Vp = reinterpret_cast<bf16*>(take(kv));
-  w.Opart = reinterpret_cast<f16*>(take((size_t)s.BH * s.N * kRanges * s.d * sizeof(f16)));
-  w.ML = reinterpret_cast<float2*>(take((size_t)s.BH * s.N * kRanges * sizeof(float2)));
+  if (!qb) {   // clustered query blocks: whole-row items write O and lse themselves
+    w.Opart = reinterpret_cast<f16*>(take((size_t)s.BH * s.N * kRanges * s.d * sizeof(f16)));
+    w.ML = reinterpret_cast<float2*>(take((size_t)s.BH * s.N * kRanges * sizeof(float2)));
+  }
   if (total) *total = (size_t)(p - static_cast<char*>(base));
   return w;
 }

@@ -13,7 +13,13 @@ int check_common(int dtype, int B, int H, int N, int d, int n_clusters, bool* un
   *unsupported = false;
   if (dtype != PARK_F32 && dtype != PARK_BF16) return PARK_ERR_INVALID;
   if (B < 1 || H < 1 || N < 1 || d < 1 || n_clusters < 1 || n_clusters > N) return PARK_ERR_INVALID;
-  if ((long long)B * H * N * d >= (1LL << 31)) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
+  // B H N d < 2^31, multiplied one factor at a time: every partial product stays below
+  // 2^31 before the next factor (< 2^31), so none overflows
+  long long elems = B;
+  for (const int f : {H, N, d}) {
+    elems *= f;
+    if (elems >= (1LL << 31)) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
+  }
   if (d != 64 && d != 128) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
   if (n_clusters > PARK_MAX_CLUSTERS) { *unsupported = true; return PARK_ERR_UNSUPPORTED; }
   return PARK_OK;

@@ -51,7 +51,9 @@ typedef enum park_status {
   PARK_ERR_UNSUPPORTED = 2,  /* valid, but not built: d not in {64,128}, q_block != 64, ... */
   PARK_ERR_WORKSPACE = 3,    /* workspace NULL, misaligned or smaller than required */
   PARK_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError after the launch) */
-  PARK_ERR_NUMERIC = 5       /* reserved for the host-side check of per-head status flags */
+  PARK_ERR_NUMERIC = 5       /* a per-head status flag is set (see park_cluster_keys); the
+                                entry points themselves never return it, because the flag is
+                                written on the device after they return */
 } park_status;
 
 typedef enum park_dtype { PARK_F32 = 0, PARK_BF16 = 1 } park_dtype;
@@ -93,8 +95,13 @@ PARK_API size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_c
  *   perm      [B,H,N]            int32: key indices in (label, index) order, so cluster v
  *             is perm[offsets[v] .. offsets[v+1]);
  *   offsets   [B,H,n_clusters+1] int32: exclusive prefix sum of counts, offsets[n] = N;
- *   status    [B,H] int32 or NULL: 0, or 1 when the Cholesky factorisation failed (the
- *             head is then clustered with R = I); written asynchronously on `stream`.
+ *   status    [B,H] int32 or NULL: 0, or 1 when the Cholesky factorisation failed (App. D.2
+ *             "Numerically stable Cholesky factorization"); the head is then clustered with
+ *             R = I, i.e. with the Euclidean metric.  For finite queries the (alpha + 1e-6) s_Q I
+ *             term keeps Gs positive definite, so only non-finite input (or overflow) sets
+ *             it.  It is written on `stream` after the call has returned PARK_OK: a caller
+ *             that needs the outcome synchronises and reports PARK_ERR_NUMERIC for a non-zero
+ *             flag (the Python binding's numeric_status does so).
  * init_idx: NULL or device int32 [n_clusters] of key indices in [0, N), shared by all heads.
  * Errors: INVALID for NULL required pointers, B,H < 1, N < 1, n_clusters outside [1, N],
  * iters < 1, alpha outside [0, 1] or not finite, unknown dtype/metric; UNSUPPORTED for d
@@ -164,8 +171,9 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  * Outputs: O [B,H,N,d] of `dtype`; lse [B,H,N] float or NULL (natural-log log-sum-exp).
  * Numerics: bf16 inputs use bf16 matrix products with float accumulation and a float
  * online softmax (probabilities rounded to bf16 before the PV product, O normalised by the
- * sum of those rounded weights, lse from the float sum; partial outputs of the key ranges in
- * fp16, scaled by the head's largest |value|); float inputs are computed in float throughout.
+ * sum of those rounded weights, lse from the float sum); here (64-token blocks) the partial
+ * outputs of the key ranges are kept in fp16, scaled by the head's largest |value|, and
+ * merged in range order; float inputs are computed in float throughout.
  * Workspace: park_workspace_bytes(PARK_OP_BLOCK_SPARSE_ATTN, ...) bytes (sized for any selection,
  * up to every cluster for every query block).
  * Errors: INVALID, UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS),
@@ -328,9 +336,11 @@ PARK_API int park_retrieve_blocks_online(const void* Q, int dtype, int B, int H,
  * query i of block u attends to J_u, the keys of the clusters block_list[u][0 ..
  * block_count[u]), with the same formulas, numerics and output layout (O [B,H,N,d] and lse
  * [B,H,N] in the original query order).  block_list / block_count [B,H,n_qblocks,...] come
- * from park_retrieve_blocks_clustered.  The bf16 path computes a partial state per (chunk,
- * key range) with the kernel of park_block_sparse_attn (the tile plan of a block serves all
- * its chunks); queries are read and results written through q_perm.
+ * from park_retrieve_blocks_clustered.  The bf16 path packs keys and values and plans the
+ * tiles of every block as park_block_sparse_attn does (the tile plan of a block serves all its
+ * chunks); one wave computes a whole chunk over all its selected tiles in one pass and writes
+ * the final O (bf16) and lse itself, so there are no partial states and no merge.  Queries are
+ * read and results written through q_perm.
  * Workspace: park_workspace_bytes_clustered(PARK_OP_BLOCK_SPARSE_ATTN, ...).
  * Errors: as park_block_sparse_attn; INVALID also for NULL q_perm / q_offsets or n_qblocks
  * outside [1, N]; UNSUPPORTED for n_qblocks > PARK_MAX_QUERY_BLOCKS.

@@ -51,7 +51,11 @@
  *   s_Q = max(tr(G_Q)/d, s_min)
  *   Gs  = (1 - alpha) G_Q + (alpha + eps) s_Q I
  *   Gs  = R R^T, R lower triangular (Cholesky)
- * metric 1 (Euclidean) sets R = I.  Returns 0, or 1 if the factorisation fails.
+ * metric 1 (Euclidean) sets R = I.  Returns 0, or 1 if the factorisation fails (a pivot
+ * that is not a finite positive number, which for finite queries the (alpha + eps) s_Q I
+ * term rules out); the head then falls back to R = I, the Euclidean metric, so that it is
+ * still clustered (App. D.2 "Numerically stable Cholesky factorization" asks for a
+ * per-head flag; the fallback is the reading the GPU path follows too).
  * G, Gs, R: d*d row-major doubles (may be NULL except R).
  * --------------------------------------------------------------------------------- */
 ORC_EXPORT int orc_query_metric(const float* Q, long L, int d, int metric, double alpha,
@@ -90,6 +94,10 @@ ORC_EXPORT int orc_query_metric(const float* Q, long L, int d, int metric, doubl
         }
       }
     }
+  }
+  if (fail) {
+    memset(R, 0, sizeof(double) * (size_t)d * d);
+    for (int a = 0; a < d; ++a) R[a * d + a] = 1.0;
   }
   if (G_out) memcpy(G_out, G, sizeof(double) * (size_t)d * d);
   if (Gs_out) memcpy(Gs_out, Gs, sizeof(double) * (size_t)d * d);

@@ -60,6 +60,21 @@ def test_workspace_sizes(lib):
     assert b > a > 0
 
 
+def test_clustered_attention_workspace_has_no_partial_states(lib):
+    """Clustered query blocks: whole-row attention items write O and lse themselves, so the
+    workspace holds no per-range partial states (fp16 O and float (m, l) per query and key
+    range), only the chunk tables that the 64-token path does not need."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    B, H, N, d, nk = 1, 40, 75600, 128, 1024
+    NQ = (N + 63) // 64          # as many clustered blocks as 64-token blocks: same plan size
+    BH, maxc = B * H, (N + 63) // 64 + NQ
+    w64 = lib.park_workspace_bytes(2, B, H, N, d, nk)
+    wcl = lib.park_workspace_bytes_clustered(2, B, H, N, d, nk, NQ)
+    partial = a256(BH * N * 8 * d * 2) + a256(BH * N * 8 * 8)
+    tables = a256(BH * maxc * 16) + a256(BH * (NQ + 1) * 4) + a256(BH * 4)
+    assert w64 - wcl == partial - tables
+
+
 def _cluster(lib, **kw):
     a = dict(Q=FAKE, K=FAKE, dtype=1, B=1, H=1, N=256, d=128, nk=8, iters=2, metric=0, alpha=0.05, init=None,
              cent=FAKE, counts=FAKE, labels=FAKE, perm=FAKE, offsets=FAKE, status=None, ws=FAKE, wsb=1 << 40)

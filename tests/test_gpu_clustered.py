@@ -109,7 +109,7 @@ def test_retrieve_clustered(dev, orc, name):
         for h in range(H):
             W = orc.pama_blocks(Q[b, h], cent[b, h], counts[b, h], qperm[b, h], qoff[b, h], scale)
             check_scores(g["scores"][b, h], W)
-            n, e = compare_selection(g["scores"][b, h], W, counts[b, h], cfg.top_p, cfg.top_k, g["mask"][b, h],
+            n, e, _ = compare_selection(g["scores"][b, h], W, counts[b, h], cfg.top_p, cfg.top_k, g["mask"][b, h],
                                      g["block_list"][b, h], g["block_count"][b, h], orc)
             rows += n; ex += e
     print(f"{name}: {ex} of {rows} rows exempt by margin")

@@ -5,7 +5,7 @@ sizes, with 64-token and clustered query blocks."""
 import numpy as np
 import pytest
 
-from parity_util import check_scores, compare_selection, host, to_dev
+from parity_util import check_scores, compare_selection, host, teacher_forced_chain, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +48,13 @@ def test_degenerate_sizes(dev, orc, N, d, dtype, nk, nq):
     q, k, v = (to_dev(x, dtype) for x in (Q, K, V))
     # clustering: from the GPU's labels the oracle's finalisation must match bit for bit, and
     # the labels must be the oracle's assignment from the GPU's previous step (teacher forced)
-    cl = {kk: host(vv) for kk, vv in dev.park_cluster_keys(q, k, nk, iters).items()}
+    runs = [{kk: host(vv) for kk, vv in dev.park_cluster_keys(q, k, nk, t).items()} for t in range(1, iters + 1)]
+    cl = runs[-1]
     lab = cl["labels"][0, 0]
     assert lab.min() >= 0 and lab.max() < nk
+    assert all(r["status"][0, 0] == 0 for r in runs)
+    n_diff, n_keys, n_empty = teacher_forced_chain(orc, Q[0, 0], K[0, 0], nk, [r["labels"][0, 0] for r in runs])
+    print(f"N={N} nk={nk}: {n_diff} near-tie label differences over {n_keys} keys, {n_empty} empty clusters")
     cent, counts, perm, offsets = orc.finalize(K[0, 0], lab, nk)
     assert np.array_equal(cl["counts"][0, 0], counts) and np.array_equal(cl["perm"][0, 0], perm)
     assert np.array_equal(cl["offsets"][0, 0], offsets)

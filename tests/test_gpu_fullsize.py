@@ -1,8 +1,8 @@
 """Full-size parity at the benchmark shapes (all heads on the GPU, in the launch
 configuration bench.py times), checked on sampled heads and sampled query blocks that the
 CPU oracle can afford:
-  * k-means: the first step from the anchors, and the last step teacher-forced from the GPU's
-    previous labels (margin < 1e-5 exempt);
+  * k-means: the first step from the anchors, and the last step teacher-forced (the oracle's
+    centroids rebuilt from the GPU's labels of every earlier step; margin < 1e-5 exempt);
   * clustering outputs (counts, offsets, perm, centroids) against the oracle's finalisation
     of the GPU labels, for every head;
   * PAMA scores (rel 1e-3) and the selection (the oracle's on its own scores, bit-exact
@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import park_synth
-from parity_util import check_scores, compare_selection, host, to_dev
+from parity_util import check_scores, compare_selection, host, teacher_forced_chain, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,23 +47,34 @@ def _run(park, cfg, Q, K, V, iters, top_p, top_k, metric="qrkc", pooled=False):
     return out
 
 
-def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc", pooled=False, ub_step=37):
+def _cluster_labels(park, cfg, Q, K, iters):
+    """The GPU's labels after 1 .. iters - 1 Lloyd steps (clustering only, every head)."""
+    import torch
+    q, k = (to_dev(x, cfg.dtype) for x in (Q, K))
+    out = []
+    for t in range(1, iters):
+        cl = park.park_cluster_keys(q, k, cfg.n_clusters, t)
+        torch.cuda.synchronize()
+        out.append(host(cl["labels"]))
+        assert np.all(host(cl["status"]) == 0)
+        del cl
+    del q, k
+    torch.cuda.empty_cache()
+    return out
+
+
+def _check_head(orc, cfg, Q, K, V, labels_hist, gT, b, h, top_p, top_k, metric="qrkc", pooled=False, ub_step=37):
     q, k, v = Q[b, h], K[b, h], V[b, h]
     nk = cfg.n_clusters
     _, _, R, ok = orc.query_metric(q, metric=metric)
     assert ok
-    Kt = orc.transform(k, R)
-    # first step from the strided anchors
-    lab_o, mar, _, _ = orc.assign(Kt, orc.init_centroids(Kt, nk))
-    d = lab_o != g1["labels"][b, h]
-    assert np.all(mar[d] < 1e-5), f"step 1: {d.sum()} labels differ"
-    # last step, teacher-forced from the GPU's previous labels (needs no empty cluster there)
-    prev = gT1["labels"][b, h]
-    if np.all(np.bincount(prev, minlength=nk) > 0):
-        C = orc.update(Kt, prev, np.zeros((nk, q.shape[1]), np.float32))
-        lab_o, mar, _, _ = orc.assign(Kt, C)
-        d = lab_o != gT["labels"][b, h]
-        assert np.all(mar[d] < 1e-5), f"last step: {d.sum()} labels differ"
+    # the first and the last step, teacher-forced: the oracle's centroid chain follows the
+    # GPU's labels of every step (empty clusters keep their centroid), and its assignment
+    # must give the GPU's labels after step 1 and after step T
+    chain = [lh[b, h] for lh in labels_hist] + [gT["labels"][b, h]]
+    n_diff, n_keys, n_empty = teacher_forced_chain(orc, q, k, nk, chain, metric=metric, steps=(1, len(chain)))
+    print(f"head {h}: {n_diff} near-tie label differences over {n_keys} keys (steps 1 and {len(chain)}), "
+          f"{n_empty} empty clusters along the chain")
     # outputs of the final clustering
     cent, counts, perm, offsets = orc.finalize(k, gT["labels"][b, h], nk)
     assert np.array_equal(gT["counts"][b, h], counts)
@@ -75,7 +86,7 @@ def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc
     ref = orc.pooled_scores if pooled else orc.pama
     W = ref(q, cent, counts, 64, scale)
     check_scores(gT["scores"][b, h], W)
-    _, ex = compare_selection(gT["scores"][b, h], W, counts, top_p, top_k, gT["mask"][b, h], gT["block_list"][b, h],
+    _, ex, _ = compare_selection(gT["scores"][b, h], W, counts, top_p, top_k, gT["mask"][b, h], gT["block_list"][b, h],
                               gT["block_count"][b, h], orc)
     # attention on sampled query blocks
     NQ = W.shape[0]
@@ -94,8 +105,7 @@ def _check_head(orc, cfg, Q, K, V, g1, gT1, gT, b, h, top_p, top_k, metric="qrkc
 def test_fullsize_workload(dev, orc, cid, heads):
     cfg = park_synth.WORKLOADS[cid]
     Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
-    g1 = _run(dev, cfg, Q, K, V, 1, cfg.top_p, cfg.top_k)
-    gT1 = _run(dev, cfg, Q, K, V, cfg.iters - 1, cfg.top_p, cfg.top_k)
+    labels_hist = _cluster_labels(dev, cfg, Q, K, cfg.iters)
     gT = _run(dev, cfg, Q, K, V, cfg.iters, cfg.top_p, cfg.top_k)
     B, H = Q.shape[:2]
     for b in range(B):
@@ -106,7 +116,7 @@ def test_fullsize_workload(dev, orc, cid, heads):
             assert np.array_equal(np.diff(off), gT["counts"][b, h])
             assert np.all(gT["block_count"][b, h] >= np.minimum(cfg.top_k, (gT["counts"][b, h] > 0).sum()))
     for h in heads:
-        ex, err = _check_head(orc, cfg, Q, K, V, g1, gT1, gT, 0, h, cfg.top_p, cfg.top_k)
+        ex, err = _check_head(orc, cfg, Q, K, V, labels_hist, gT, 0, h, cfg.top_p, cfg.top_k)
         print(f"{cid} head {h}: {ex} selection rows exempt by margin, attention err {err:.2e}")
 
 
@@ -170,7 +180,7 @@ def test_fullsize_from_oracle_clustering(dev, orc, cid, h):
     W = orc.pama(Q[0, h], o["centroids"], o["counts"], 64, scale)
     sc = host(rb["scores"][0, h])
     check_scores(sc, W)
-    _, ex = compare_selection(sc, W, o["counts"], cfg.top_p, cfg.top_k, host(rb["mask"][0, h]),
+    _, ex, _ = compare_selection(sc, W, o["counts"], cfg.top_p, cfg.top_k, host(rb["mask"][0, h]),
                               host(rb["block_list"][0, h]), host(rb["block_count"][0, h]), orc)
     # attention with the oracle's selection for head h
     _, lst_o, cnt_o, _, _ = orc.select(W, o["counts"], cfg.top_p, cfg.top_k)

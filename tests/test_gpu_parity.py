@@ -162,7 +162,7 @@ def test_retrieve(dev, orc, name, pooled):
         for h in range(H):
             W_ref = ref(Q[b, h], cent[b, h], counts[b, h], 64, scale)
             check_scores(g["scores"][b, h], W_ref)
-            n, e = compare_selection(g["scores"][b, h], W_ref, counts[b, h], cfg.top_p, cfg.top_k, g["mask"][b, h],
+            n, e, _ = compare_selection(g["scores"][b, h], W_ref, counts[b, h], cfg.top_p, cfg.top_k, g["mask"][b, h],
                                      g["block_list"][b, h], g["block_count"][b, h], orc)
             rows += n; ex += e
     print(f"{name} pooled={pooled}: {ex} of {rows} rows exempt by margin")

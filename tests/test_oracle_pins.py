@@ -78,11 +78,23 @@ def test_euclidean_metric_is_identity(orc):
 
 
 def test_metric_failure_reported(orc):
-    """A factorisation that cannot succeed (non-finite queries) is reported, not hidden."""
-    Q, _, _ = _rand_qk(40, 8, 5)
+    """A factorisation that cannot succeed (non-finite queries) is reported, not hidden
+    (App. D.2 "Numerically stable Cholesky factorization" plans a per-head flag), and the
+    head falls back to R = I, so its keys are clustered with the Euclidean metric: the
+    transform is then the identity and the clustering equals the Euclidean one."""
+    Q, K, _ = _rand_qk(40, 8, 5)
     Q[3, 2] = np.nan
-    *_, ok = orc.query_metric(Q)
+    *_, R, ok = orc.query_metric(Q)
     assert not ok
+    assert np.array_equal(R, np.eye(8))
+    assert np.array_equal(orc.transform(K, R), K)
+    a = orc.cluster_keys(Q, K, 5, 3)
+    b = orc.cluster_keys(Q, K, 5, 3, metric="euclidean")
+    assert not a["ok"] and b["ok"]
+    assert np.array_equal(a["labels"], b["labels"])
+    # the flag needs a non-finite input: an all-zero head still factors (s_Q = s_min)
+    *_, R0, ok0 = orc.query_metric(np.zeros((10, 8), np.float32))
+    assert ok0 and np.all(np.diag(R0) > 0)
 
 
 def test_qrkc_objective_identity(orc):
@@ -122,6 +134,43 @@ def test_kmeans_golden_line(orc):
     assert km["J_assign"][0] == g["J_assign_1"]
     assert km["J_update"][0] == g["J_update_1"]
     assert abs(km["margins"][0][1] - g["margin_key1_step1"]) < 1e-15
+
+
+def test_kmeans_tie_rule_golden(orc):
+    """Reading of the silent argmin tie rule: exact ties go to the lowest cluster index
+    (hand-worked in golden/kmeans_ties_empty.json)."""
+    g = _gold("kmeans_ties_empty.json")["ties"]
+    Kt = np.array(g["Kt"], np.float32)
+    C = np.array(g["C"], np.float32)
+    lab, _, dist, J = orc.assign(Kt, C)
+    assert lab.tolist() == g["labels"]
+    assert dist.tolist() == g["dist"]
+    # the same keys against the centroids in reverse order: still the lowest index of a tie
+    lab_r, *_ = orc.assign(Kt, C[::-1].copy())
+    assert lab_r.tolist() == [0, 1, 0]
+
+
+def test_kmeans_empty_cluster_keeps_centroid(orc):
+    """Reading of the silent empty-cluster rule: a cluster without keys keeps its centroid
+    through the update (hand-worked in golden/kmeans_ties_empty.json); the final outputs
+    give it count 0 and a zero centroid."""
+    g = _gold("kmeans_ties_empty.json")["empty"]
+    Kt = np.array(g["Kt"], np.float32)
+    C0 = np.array(g["C0"], np.float32)
+    lab1, *_ = orc.assign(Kt, C0)
+    assert lab1.tolist() == g["labels_1"]
+    C1 = orc.update(Kt, lab1, C0)
+    np.testing.assert_array_equal(C1, np.array(g["C1"], np.float32))
+    lab2, *_ = orc.assign(Kt, C1)
+    assert lab2.tolist() == g["labels_2"]
+    km = orc.kmeans(Kt, 3, 2, init_idx=[0, 2, 2])
+    # init (0,0), (10,0), (10,0): cluster 2 ties with cluster 1 for key 2 and loses, so it
+    # is empty after every step and keeps its anchor
+    assert km["labels"].tolist() == [0, 0, 1]
+    np.testing.assert_array_equal(km["centroids"][2], np.array([10.0, 0.0], np.float32))
+    cent, counts, perm, offsets = orc.finalize(Kt, km["labels"], 3)
+    assert counts.tolist() == [2, 1, 0] and offsets.tolist() == [0, 2, 3, 3]
+    assert np.array_equal(cent[2], np.zeros(2, np.float32))
 
 
 def test_kmeans_objective_non_increasing(orc):
