@@ -37,7 +37,7 @@ __all__ = [
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
     "park_block_sparse_attn_clustered", "park_retrieve_blocks_online", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
-    "PARK_ERR_NUMERIC", "numeric_status", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
+    "PARK_ERR_NUMERIC", "numeric_status", "park_retrieve_blocks_noalloc", "OP_CLUSTER_KEYS", "OP_RETRIEVE_BLOCKS", "OP_BLOCK_SPARSE_ATTN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpark.so")
@@ -103,6 +103,11 @@ def lib():
         L.park_logmass_workspace_bytes.restype = _S
         L.park_logmass_rmse.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _F, _P, _P, _S, _P]
         L.park_logmass_rmse.restype = _I
+        L.park_noalloc_scratch_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.park_noalloc_scratch_bytes.restype = _S
+        L.park_retrieve_blocks_noalloc.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P,
+                                                   _P, _P]
+        L.park_retrieve_blocks_noalloc.restype = _I
         _lib = L
     return _lib
 
@@ -250,6 +255,37 @@ def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, work
             int(top_k), sc, *extra, _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
             _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
     _check(st, where)
+    return out
+
+
+def park_retrieve_blocks_noalloc(Q, centroids, counts, top_p: float, top_k: int, scale=None, out=None):
+    """park_retrieve_blocks through the entry point that allocates nothing (its scratch is the
+    library's static per-GPU array).  `out` may hold preallocated outputs (scores, mask,
+    block_list, block_count); missing ones are allocated here, by the caller's side, before
+    the call.  Calls on one GPU share the scratch: overlapping calls race."""
+    torch = _torch()
+    _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
+    B, H, N, d = _bhnd(Q, "Q")
+    nk = centroids.shape[2]
+    if centroids.shape != (B, H, nk, d) or centroids.dtype != torch.float32:
+        raise ValueError("centroids must be float32 [B, H, n_clusters, d]")
+    if counts.shape != (B, H, nk) or counts.dtype != torch.int32:
+        raise ValueError("counts must be int32 [B, H, n_clusters]")
+    NQ = (N + 63) // 64
+    dev = Q.device
+    want = dict(scores=((B, H, NQ, nk), torch.float32), mask=((B, H, NQ, nk), torch.uint8),
+                block_list=((B, H, NQ, nk), torch.int32), block_count=((B, H, NQ), torch.int32))
+    out = dict(out or {})
+    for k, (shape, dt) in want.items():
+        if k not in out:
+            out[k] = torch.empty(shape, dtype=dt, device=dev)
+        elif tuple(out[k].shape) != shape or out[k].dtype != dt or not out[k].is_contiguous():
+            raise ValueError(f"out[{k!r}] must be contiguous {dt} {list(shape)}")
+    sc = -1.0 if scale is None else float(scale)
+    st = lib().park_retrieve_blocks_noalloc(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts), nk, 64,
+                                            float(top_p), int(top_k), sc, _ptr(out["scores"]), _ptr(out["mask"]),
+                                            _ptr(out["block_list"]), _ptr(out["block_count"]), _stream(Q))
+    _check(st, "park_retrieve_blocks_noalloc")
     return out
 
 

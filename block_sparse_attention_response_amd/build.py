@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpark.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build", "libpark")
-SOURCES = ["park_api.hip", "k_retrieve.hip", "k_attn.hip", "k_cluster.hip"]
+SOURCES = ["park_api.hip", "park_noalloc.hip", "k_retrieve.hip", "k_attn.hip", "k_cluster.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions are kept out of the generated code

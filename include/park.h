@@ -352,6 +352,40 @@ PARK_API int park_block_sparse_attn_clustered(const void* Q, const void* K, cons
                                               const int32_t* block_count, float scale, void* O, float* lse,
                                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ * --------------------------------------------------------------------------------- */
+
+/* Size of the library's fixed per-GPU scratch array used by park_retrieve_blocks_noalloc:
+ * 32 MiB, held on every GPU the library runs on until the process ends (enough for the
+ * 75,600-token / 40-head / 1024-cluster and the 119,056-token / 24-head / 1536-cluster
+ * shapes at d = 128). */
+#define PARK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* Bytes of that scratch park_retrieve_blocks_noalloc needs for these sizes (0 for invalid
+ * sizes); the call works when this is at most PARK_NOALLOC_SCRATCH_BYTES. */
+PARK_API size_t park_noalloc_scratch_bytes(int B, int H, int N, int d, int n_clusters);
+
+/*
+ * park_retrieve_blocks_noalloc - park_retrieve_blocks (same computation, same kernels,
+ * same outputs) that allocates nothing and takes no workspace: its scratch (the centroid
+ * operands of the fused PAMA kernel) is the library's static per-GPU array of
+ * PARK_NOALLOC_SCRATCH_BYTES.  `scores` is required here (W is an output in caller memory,
+ * not scratch).  The device address of the array is looked up once per device, on the first
+ * call with that device current.  Every call on one GPU uses the same array and overwrites
+ * all of it that it reads, so calls that overlap on one GPU (several host threads, or
+ * several streams running at once) race and must be serialised by the caller.
+ * Errors: as park_retrieve_blocks; INVALID also for a NULL scores; WORKSPACE when the sizes
+ * need more than PARK_NOALLOC_SCRATCH_BYTES (park_noalloc_scratch_bytes); HIP also when the
+ * scratch address cannot be obtained.
+ */
+PARK_API int park_retrieve_blocks_noalloc(const void* Q, int dtype, int B, int H, int N, int d,
+                                          const float* centroids, const int32_t* counts, int n_clusters,
+                                          int q_block, float top_p, int top_k, float scale, float* scores,
+                                          uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

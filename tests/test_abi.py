@@ -75,6 +75,31 @@ def test_clustered_attention_workspace_has_no_partial_states(lib):
     assert w64 - wcl == partial - tables
 
 
+def test_noalloc_retrieve_rejects(lib):
+    """The no-allocation retrieval: host-side rejections, including sizes whose scratch would
+    exceed the library's fixed per-GPU array (nothing is launched or looked up for them)."""
+    limit = 32 << 20
+    def call(**kw):
+        a = dict(Q=FAKE, dtype=1, B=1, H=2, N=256, d=128, cent=FAKE, counts=FAKE, nk=8, qb=64, p=0.9, k=2,
+                 scale=-1.0, scores=FAKE, mask=FAKE, lst=FAKE, cnt=FAKE)
+        a.update(kw)
+        return lib.park_retrieve_blocks_noalloc(a["Q"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["cent"],
+                                                a["counts"], a["nk"], a["qb"], a["p"], a["k"], a["scale"],
+                                                a["scores"], a["mask"], a["lst"], a["cnt"], None)
+    assert call(scores=None) == INVALID            # W is an output here, never scratch
+    assert call(mask=None) == INVALID
+    assert call(p=1.5) == INVALID
+    assert call(k=-1) == INVALID
+    assert call(nk=300) == INVALID
+    assert call(qb=32) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert lib.park_noalloc_scratch_bytes(1, 40, 75600, 128, 1024) <= limit
+    assert lib.park_noalloc_scratch_bytes(1, 24, 119056, 128, 1536) <= limit
+    assert lib.park_noalloc_scratch_bytes(1, 40, 75600, 96, 1024) == 0
+    assert lib.park_noalloc_scratch_bytes(1, 160, 75600, 128, 1536) > limit
+    assert call(H=160, N=75600, nk=1536) == WORKSPACE
+
+
 def _cluster(lib, **kw):
     a = dict(Q=FAKE, K=FAKE, dtype=1, B=1, H=1, N=256, d=128, nk=8, iters=2, metric=0, alpha=0.05, init=None,
              cent=FAKE, counts=FAKE, labels=FAKE, perm=FAKE, offsets=FAKE, status=None, ws=FAKE, wsb=1 << 40)

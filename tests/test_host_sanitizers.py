@@ -13,7 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_sparse_attention_response_amd", "csrc")
-KERNELS = ["k_retrieve.hip", "k_attn.hip", "k_cluster.hip"]
+KERNELS = ["park_noalloc.hip", "k_retrieve.hip", "k_attn.hip", "k_cluster.hip"]
 ARCH = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all"]
