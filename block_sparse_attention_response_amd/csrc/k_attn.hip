@@ -5,6 +5,7 @@
 // them; the float path walks the selected clusters through the cluster permutation.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "park_device.h"
 #include "park_internal.h"
@@ -453,8 +454,10 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
 //   S^T = K Q^T      (A: 32 keys x 16 columns in bf16; B: Q^T fragments of query halves 0 and
 //                     1 in registers; the accumulators start at 0 / -inf, which masks padding)
 //   O^T += V^T P^T   (A: V^T in bf16; B: P^T from the S^T accumulators, rounded to bf16)
-// Keys and values are copied memory -> LDS (global_load_lds, two tiles deep per wave) in MFMA
-// fragment order and read back one fragment per lane per MFMA.
+// Keys and values are loaded from the packed groups straight into the MFMA operand registers
+// (every lane loads exactly the 16 bytes it feeds to the matrix unit, one coalesced 1 KB piece
+// per instruction), about one and a half tiles ahead of their use; no operand passes through
+// LDS, which holds only a small table of score starts.
 // Row swap inside each 16-row chunk of a tile (rows 4..7 <-> 8..11): with it, the 8 rows of
 // S^T an MFMA lane holds for one 16-key chunk are 8 consecutive keys of one group, which is
 // the P^T operand layout.
@@ -469,35 +472,10 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
 // l the float sum.
 __device__ __forceinline__ int sigma16(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 
-// global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
-// Written as inline assembly so that the compiler does not guard every later LDS read with
-// a wait for all outstanding copies: the kernel waits for exactly the copies it needs
-// (s_waitcnt vmcnt; copies complete in issue order).  The instruction has no register
-// results; the scalar base carries the per-instruction displacement, so a batch of copies
-// needs one lane offset and no vector address arithmetic.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
-}
-// the same with 4 bytes per lane (lane i writes lds + 4 i)
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-// all LDS reads issued so far have returned (before a copy overwrites what they read)
-__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
-
-// LDS of one wave: two tiles of keys and values in MFMA fragment order (fragment f of lane i
-// at [b][f][i] for buffer b = tile parity), the plan-entry ring (slot s holds the 16 tiles
-// from the one its copy started at) and the score start table
+// LDS of one wave: the score start table (row n: 0 for the first n slots of a group, -inf
+// for its padding)
 template <int D>
 struct AttnLds {
-  bf16x8 Ks[2][D / 16][64];
-  bf16x8 Vs[2][D / 16][64];
-  __attribute__((aligned(16))) int32_t pring[4][64];
   __attribute__((aligned(16))) float btab[9][8];
 };
 
@@ -515,9 +493,6 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
   static_assert(KC == 2 * DT, "K and V batches have the same size");
-  auto& Ks = sm.Ks;
-  auto& Vs = sm.Vs;
-  auto& pring = sm.pring;
   auto& btab = sm.btab;
   // fused: the item is a whole row (all its ranges' tiles, which are contiguous in the plan),
   // so it writes the final output and log-sum-exp itself (no partial states, no merge)
@@ -577,46 +552,39 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   const uint32_t koff = (uint32_t)((kk & 7) * 32 + h * 16);
   const uint32_t voff = (uint32_t)(l32 * 16);
 
-  // plan entries of tile t (clamped to the item, so copies past its last tile read that tile
-  // again; they are never used)
-  auto entries = [&](int t) __attribute__((always_inline)) {
-    const int4 e = *reinterpret_cast<const int4*>(pl + 4 * min(t, nt - 1));
+  // plan entries of tile t (clamped to the item, so loads past its last tile read that tile
+  // again; they are never used): one 16-byte load with a uniform address, made uniform
+  auto load_entries = [&](int t) __attribute__((always_inline)) {
+    return *reinterpret_cast<const int4*>(pl + 4 * min(t, nt - 1));
+  };
+  auto uniform = [](const int4& e) __attribute__((always_inline)) {
     return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
                      __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
   };
-  // group ids are clamped to the head's packed groups: entries copied from past an item's
-  // plan (only ever used for unused copies) may hold anything
+  auto entries = [&](int t) __attribute__((always_inline)) { return uniform(load_entries(t)); };
+  // group ids are clamped to the head's packed groups: entries read from past an item's
+  // plan (only ever used for unused loads) may hold anything
   auto key_offset = [&](const int4& e) __attribute__((always_inline)) {
     const int g01 = (kj & 1) ? e.y : e.x, g23 = (kj & 1) ? e.w : e.z;
     return (uint32_t)min((uint32_t)((kj & 2) ? g23 : g01) >> 4, (uint32_t)Gcap) * GB + koff;
   };
-  auto lds_addr = [](const void* p) __attribute__((always_inline)) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-  };
-  // copies of a tile's keys (A operands of S^T) and values (A operands of O^T)
-  auto copy_k = [&](int t, const int4& e) __attribute__((always_inline)) {
-    const uint32_t off = key_offset(e);
-    const uint32_t dst = lds_addr(&Ks[t & 1][0][0]);
+  // A operands of a tile straight from the packed groups into registers: the keys of S^T
+  // (KC fragments) and the values of O^T (2 DT fragments).  Every lane loads exactly the 16
+  // bytes of each fragment it feeds to the MFMA (one coalesced 1 KB piece per instruction),
+  // so no operand passes through LDS.
+  auto load_k = [&](const int4& e, bf16x8 (&kf)[KC]) __attribute__((always_inline)) {
+    const char* src = Kb + key_offset(e);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) dma16(Kb + kc * 256, off, dst + kc * 1024);
+    for (int kc = 0; kc < KC; ++kc) kf[kc] = *reinterpret_cast<const bf16x8*>(src + kc * 256);
   };
-  auto copy_v = [&](int t, const int4& e) __attribute__((always_inline)) {
+  auto load_v = [&](const int4& e, bf16x8 (&vf)[2 * DT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int g = c ? (h ? e.w : e.z) : (h ? e.y : e.x);
-      const uint32_t off = min((uint32_t)g >> 4, (uint32_t)Gcap) * GB + voff;
-      const uint32_t dst = lds_addr(&Vs[t & 1][c * DT][0]);
+      const char* src = Vb + min((uint32_t)g >> 4, (uint32_t)Gcap) * GB + voff;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dma16(Vb + dt * 512, off, dst + dt * 1024);
+      for (int dt = 0; dt < DT; ++dt) vf[c * DT + dt] = *reinterpret_cast<const bf16x8*>(src + dt * 512);
     }
-  };
-
-  // copy of the plan entries of tiles t .. t + 15 into ring slot t & 3 (one dword per lane)
-  auto copy_plan = [&](int t) __attribute__((always_inline)) {
-    dma4(pl, (uint32_t)(4 * t + lane) * 4u, lds_addr(&pring[t & 3][0]));
-  };
-  auto ring_entries = [&](int slot, int j) __attribute__((always_inline)) {
-    return *reinterpret_cast<const int4*>(&pring[slot][4 * j]);
   };
 
   // Q^T fragments of query halves 0 and 1 in registers (qrow: this lane's query of each
@@ -666,19 +634,22 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     for (int i = 0; i < 4; ++i) { init[i] = x0[i]; init[4 + i] = x1[i]; init[8 + i] = x2[i]; init[12 + i] = x3[i]; }
     return init;
   };
-  // scores of tile t into out; from_lds: keys from the tile's LDS buffer, otherwise straight
-  // from the packed groups (the rare rescale path, when the buffer may be refilled already)
-  auto scores = [&](int t, bool from_lds, f32x16 (&out)[2]) __attribute__((always_inline)) {
-    const int4 e = entries(t);
+  // scores of tile t into out, from its key fragments kf
+  auto scores_of = [&](const int4& e, const bf16x8 (&kf)[KC], f32x16 (&out)[2]) __attribute__((always_inline)) {
     out[0] = init_scores(e);
     out[1] = out[0];
-    const char* src = Kb + key_offset(e);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const bf16x8 a = from_lds ? Ks[t & 1][kc][lane] : *reinterpret_cast<const bf16x8*>(src + kc * 256);
-      out[0] = mfma32(a, qf[0][kc], out[0]);
-      out[1] = mfma32(a, qf[1][kc], out[1]);
+      out[0] = mfma32(kf[kc], qf[0][kc], out[0]);
+      out[1] = mfma32(kf[kc], qf[1][kc], out[1]);
     }
+  };
+  // scores of tile t read afresh from the packed groups (the rare rescale path)
+  auto scores = [&](int t, f32x16 (&out)[2]) __attribute__((always_inline)) {
+    const int4 e = entries(t);
+    bf16x8 kf[KC];
+    load_k(e, kf);
+    scores_of(e, kf, out);
   };
   auto prob = [&](float x, int h2) __attribute__((always_inline)) { return fast_exp2(fmaf(x, scale2, -m[h2])); };
   // bf16 weights of the probabilities in sc
@@ -723,7 +694,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
         for (int h2 = 0; h2 < 2; ++h2) mx[h2] = m[h2] + __log2f(pmax[h2]);
       } else {
         f32x16 st[2];
-        scores(t, false, st);
+        scores(t, st);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           float x = st[h2][0];
@@ -767,55 +738,39 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     lb[1] += wb[1];
   };
 
-  // One pipeline step (tile t + 1 exists): tile t's bf16 weights are in pb (settled) and its
-  // values in LDS buffer t & 1, tile t + 1's keys in buffer (t + 1) & 1.  In the order written
-  // (scheduling fences keep it; with one wave per SIMD the matrix and vector units overlap
-  // only through this interleave):
+  // Operand registers: the keys of tile t live in kbuf[t & 1], its values in vbuf[t & 1].
+  // One pipeline step t (tile t + 1 exists) finds the keys of tiles t + 1 and t + 2 and the
+  // values of tiles t and t + 1 loaded or in flight, tile t's bf16 weights settled in pb, and
+  // in the order written (scheduling fences keep it; with one wave per SIMD the matrix and
+  // vector units overlap only through this interleave):
   //   A1: S^T MFMAs of tile t + 1, query half 0;
   //   A2: S^T MFMAs of tile t + 1, query half 1, with the exponentials of half 0;
+  //   then the loads of tile t + 3's keys into the buffer A just freed, and of the plan
+  //   entries of tile t + 4;
   //   B:  P V MFMAs of tile t (O^T += V^T P^T) with the exponentials of half 1 and the bf16
   //       conversion and weight sums of half 0;
-  //   then the conversion and sums of half 1 and the check of tile t + 1's weights (the rare
-  //   rescale), leaving them settled in pb.
-  // Each buffer is refilled as soon as its reads have returned: the keys of t + 3 in A1, the
-  // values of t + 2 in B.  Copies are issued in the order P1 P2 P3 K0 V0 K1 V1 K2 | P4 K3 V2 |
-  // P5 K4 V3 | ... (K, V: batches of KC instructions; P: one plan copy), so at the start of
-  // step t, after its plan copy, leaving 2 KC + 1 copies in flight completes K(t + 1), V(t) and
-  // the plan copy of tile t + 1 (issued three steps before).
+  //   then the loads of tile t + 2's values into the buffer B just freed, the conversion and
+  //   sums of half 1 and the check of tile t + 1's weights (the rare rescale), leaving them
+  //   settled in pb.
+  // A key buffer is refilled about 1.4 steps before its use, a value buffer about 1.5 (the
+  // compiler's memory counter waits cover exactly the loads each use needs).
   constexpr int kNPV = 4 * DT;             // P V MFMAs: 2 key chunks x DT x 2 query halves
-  constexpr int kCopyK = KC / 2;           // A1 chunk that refills the key buffer
-  constexpr int kCopyV = kNPV / 2 + 2;     // B chunk that refills the value buffer
+  bf16x8 kbuf[2][KC], vbuf[2][2 * DT];
   bf16x8 pb[2][2];
-  // plan entries of tiles t + 2, t + 3 and the score start of tile t + 1, read for step t at
-  // the end of step t - 1 (their ring slot is complete by then), so a step starts with one
-  // round trip to LDS
-  int4 e2, e3;
+  // uniform plan entries of tile t + 2 (values loaded in step t), the plan entries of tile
+  // t + 3 in flight (made uniform in step t, for its keys) and the score start of tile t + 1
+  int4 e2, pe3;
   f32x16 init;
-  auto next_entries = [&](int t) __attribute__((always_inline)) {
-    const int4 e1 = ring_entries((t + 1) & 3, 0);
-    e2 = ring_entries((t + 1) & 3, 1);
-    e3 = ring_entries((t + 1) & 3, 2);
-    init = init_scores(e1);
-  };
-  auto step = [&](int t) __attribute__((always_inline)) {
-    const bf16x8 (&Vx)[2 * DT][64] = Vs[t & 1];
-    const bf16x8 (&Ky)[KC][64] = Ks[(t + 1) & 1];
-    copy_plan(t + 4);
-    wait_copies<2 * KC + 1>();
-    bf16x8 kf[KC], vf[2 * DT];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kf[kc] = Ky[kc][lane];
+  auto step = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;   // t & 1
+    bf16x8 (&Kx)[KC] = kbuf[P ^ 1];           // tile t + 1
+    bf16x8 (&Vx)[2 * DT] = vbuf[P];           // tile t
     __builtin_amdgcn_sched_barrier(0);
     // A1
     sc[0] = init;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      if (kc == kCopyK) {
-        wait_lds_reads();
-        copy_k(t + 3, e3);
-      }
-      sc[0] = mfma32(kf[kc], qf[0][kc], sc[0]);
-      if (kc < 2) vf[kc] = Vx[kc][lane];
+      sc[0] = mfma32(Kx[kc], qf[0][kc], sc[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // A2: the 16 exponentials (and float sums) of half 0
@@ -823,15 +778,19 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     sc[1] = init;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      sc[1] = mfma32(kf[kc], qf[1][kc], sc[1]);
+      sc[1] = mfma32(Kx[kc], qf[1][kc], sc[1]);
 #pragma unroll
       for (int r = kc * 16 / KC; r < (kc + 1) * 16 / KC; ++r) {
         sc[0][r] = prob(sc[0][r], 0);
         acc[0][r & 1] += sc[0][r];
       }
-      if (kc + 2 < 2 * DT && kc < 2) vf[kc + 2] = Vx[kc + 2][lane];
       __builtin_amdgcn_sched_barrier(0);
     }
+    // keys of tile t + 3 into the buffer of tile t + 1, plan entries of tile t + 4
+    const int4 e3 = uniform(pe3);
+    load_k(e3, Kx);
+    pe3 = load_entries(t + 4);
+    __builtin_amdgcn_sched_barrier(0);
     // B: 16 exponentials (and sums) of half 1, then 8 conversions (pairs) and 8 weight sums of
     // half 0
     bf16x8 pn[2][2];
@@ -839,12 +798,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
 #pragma unroll
     for (int j = 0; j < kNPV; ++j) {
       const int c = j / (2 * DT), dt = (j / 2) % DT, h2 = j & 1;
-      if ((j & 1) == 0 && j / 2 + 4 < 2 * DT) vf[j / 2 + 4] = Vx[j / 2 + 4][lane];
-      if (j == kCopyV) {
-        wait_lds_reads();
-        copy_v(t + 2, e2);
-      }
-      oacc[h2][dt] = mfma32(vf[c * DT + dt], pb[h2][c], oacc[h2][dt]);
+      oacc[h2][dt] = mfma32(Vx[c * DT + dt], pb[h2][c], oacc[h2][dt]);
 #pragma unroll
       for (int w = j * 32 / kNPV; w < (j + 1) * 32 / kNPV; ++w) {
         if (w < 16) {
@@ -862,6 +816,9 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // values of tile t + 2 into the buffer of tile t
+    load_v(e2, Vx);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -873,38 +830,38 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int c = 0; c < 2; ++c) pb[h2][c] = pn[h2][c];
-    if (t + 2 < nt) next_entries(t + 1);
+    init = init_scores(e2);   // tile t + 2, the next step's score tile
+    e2 = e3;
   };
   // the last tile t: P V
-  auto last = [&](int t) __attribute__((always_inline)) {
-    const bf16x8 (&Vx)[2 * DT][64] = Vs[t & 1];
-    wait_copies<2 * KC>();
+  auto last = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    const bf16x8 (&Vx)[2 * DT] = vbuf[P];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a = Vx[c * DT + dt][lane];
-        oacc[0][dt] = mfma32(a, pb[0][c], oacc[0][dt]);
-        oacc[1][dt] = mfma32(a, pb[1][c], oacc[1][dt]);
+        oacc[0][dt] = mfma32(Vx[c * DT + dt], pb[0][c], oacc[0][dt]);
+        oacc[1][dt] = mfma32(Vx[c * DT + dt], pb[1][c], oacc[1][dt]);
       }
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
   {
     const int4 e0 = entries(0), e1 = entries(1);
-    copy_plan(1);
-    copy_plan(2);
-    copy_plan(3);
-    copy_k(0, e0);
-    copy_v(0, e0);
-    copy_k(1, e1);
-    copy_v(1, e1);
+    e2 = entries(2);
+    load_k(e0, kbuf[0]);
+    load_v(e0, vbuf[0]);
+    load_k(e1, kbuf[1]);
+    load_v(e1, vbuf[1]);
+    pe3 = load_entries(3);
+    // tile 0: m starts at the row maximum of its scores (every tile holds a real key), so its
+    // probabilities are at most 1 and need no check
+    scores_of(e0, kbuf[0], sc);
+    load_k(e2, kbuf[0]);
+    init = init_scores(e1);
   }
-  wait_copies<3 * KC>();
-  // tile 0: m starts at the row maximum of its scores (every tile holds a real key), so its
-  // probabilities are at most 1 and need no check
-  scores(0, true, sc);
-  wait_lds_reads();
-  copy_k(2, entries(2));
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     float mx = sc[h2][0];
@@ -922,11 +879,17 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   to_bf16(pb);
   weight_sums(pb, lb, 0);
   weight_sums(pb, lb, 1);
-  if (nt > 1) next_entries(0);
-  for (int t = 0; t + 1 < nt; ++t) step(t);
-  last(nt - 1);
-  // no copy may still be writing this workgroup's LDS when the wave ends
-  wait_copies<0>();
+  int t = 0;
+  for (; t + 2 < nt; t += 2) {
+    step(P0{}, t);
+    step(P1{}, t + 1);
+  }
+  if (t + 1 < nt) {
+    step(P0{}, t);
+    last(P1{}, t + 1);
+  } else {
+    last(P0{}, t);
+  }
 
   if constexpr (FUSED) {
     // the whole row: O = O^T / lb in bf16, lse = ln 2 (m + log2 l) (what the merge gives for
@@ -1204,7 +1167,7 @@ static AttnWs carve_attn(const Shape& s, const QueryBlocks* qb, void* base, size
   w.tbase = reinterpret_cast<int32_t*>(take((items + 1) * sizeof(int32_t)));
   w.bsum = reinterpret_cast<int32_t*>(take(((items + kScanBlock - 1) / kScanBlock) * sizeof(int32_t)));
   w.ictr = reinterpret_cast<int32_t*>(take(kRanges * sizeof(int32_t)));
-  // + slack: the attention kernel copies plan entries up to 80 dwords past an item's end
+  // (+ slack; the attention kernel reads plan entries clamped to each item's own tiles)
   w.plan = reinterpret_cast<int32_t*>(take((rows * per_row + 128) * sizeof(int32_t)));
   w.Kp = reinterpret_cast<bf16*>(take(kv));
   w.Vp = reinterpret_cast<bf16*>(take(kv));
@@ -1289,8 +1252,8 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
                                                  w.tbase, w.plan);
     PARK_CHECK();
     if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-    // persistent waves: as many as the chip holds (four per CU, bound by LDS), a multiple of
-    // kRanges (items is one)
+    // persistent waves: as many as the chip holds (one per SIMD, bound by the registers), a
+    // multiple of kRanges (items is one)
     const int waves = (int)std::min<long long>(aitems, 4 * compute_units() / kRanges * kRanges);
 #define PARK_ITEMS(DD, FF)                                                                                  \
   k_attn_items<DD, FF><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, \
