@@ -31,6 +31,7 @@ struct ClusterWs {
   double* cmean;  // [BH][nkp][D] original-space member means
   uint32_t* hmax; // [BH][4] float bits of max |R c~|, max bf16 error of R c~, max |c~|^2
   int32_t* hist;  // [BH][nch_s][nk] counting-sort histograms, then bases
+  int32_t* plab;  // [BH][N] label of each position of the key permutation (labels in sorted order)
   int nch_g, nch_s, nkp;
 };
 
@@ -55,6 +56,7 @@ static ClusterWs carve(const Shape& s, void* base) {
   w.cmean = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
   w.hmax = reinterpret_cast<uint32_t*>(take(BH * 4 * sizeof(uint32_t)));
   w.hist = reinterpret_cast<int32_t*>(take(BH * (size_t)w.nch_s * s.nk * sizeof(int32_t)));
+  w.plab = reinterpret_cast<int32_t*>(take(BH * (size_t)s.N * sizeof(int32_t)));
   if (base == nullptr) w.gpart = reinterpret_cast<double*>(p);  // total size in the pointer
   return w;
 }
@@ -453,32 +455,54 @@ __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ ci
 // (a_j = |k_j|, e_j = |k_j - bf16(k_j)|, t_j = |k~_j|, G = max |R c~|, F = max bf16 error of
 // R c~, CC = max |c~|^2).  Every cluster whose score is within 2 E_j of the key's minimum is
 // a candidate; the true argmin always is one.
-// One workgroup: 4 waves x 64 keys.  The cluster operand streams through LDS in 32-cluster
-// tiles (LDS DMA, double-buffered, shared by the 4 waves); each wave keeps its keys' B
-// fragments in registers and a running minimum per key, and records every score within 2 E_j
-// of the running minimum in a small per-key list (a value that ends within 2 E_j of the final
-// minimum was within 2 E_j of the running minimum when it was seen).  A single surviving
-// candidate is the answer; otherwise the candidates are compared with exact float distances
-// (k~ and c~ as stored, summed in dimension order), then by id; a key whose list overflowed
-// compares every cluster.
+// One workgroup: 4 waves x 64 keys.  The cluster operand streams through a three-slot LDS ring
+// in 32-cluster tiles (LDS DMA, each wave copying a quarter of every tile, one barrier per
+// tile), shared by the 4 waves; each wave keeps its keys' B fragments in registers and a
+// running minimum per key, and records every score within 2 E_j of the running minimum in a
+// small per-key list (a value that ends within 2 E_j of the final minimum was within 2 E_j of
+// the running minimum when it was seen).  From the second step on, keys are visited in the
+// previous step's label order and the screen starts at the tile of the workgroup's first
+// previous cluster, so the running minimum is tight from the first tile on.  A single
+// surviving candidate is the answer; otherwise the candidates are compared with exact float
+// distances (k~ and c~ as stored, summed in dimension order), then by id; a key whose list
+// overflowed compares every cluster.
 constexpr int kAsgWaves = 4;
 constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
-constexpr int kAsgCap = 12;                // list entries per key and lane half (compacted when half full)
+constexpr int kAsgCap = 10;                // list entries per key and lane half (compacted when half full)
+
+// global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
+// Inline assembly, so that the compiler does not guard later LDS reads with a wait for all
+// outstanding copies; the kernel waits for exactly the copies it needs (copies complete in
+// issue order).  The instruction has no register results.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// every LDS read this wave has issued has returned
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int D, bool KF32>
 __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ Kv, const float* __restrict__ Kt,
                                                       const float4* __restrict__ knorm, const float* __restrict__ ctil,
                                                       const bf16* __restrict__ gneg2, const float* __restrict__ ccv,
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
-                                                      int have_prev, const int32_t* __restrict__ order,
-                                                      int32_t* __restrict__ labels) {
+                                                      const int32_t* __restrict__ order,
+                                                      const int32_t* __restrict__ plab, int32_t* __restrict__ labels) {
   constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
   __shared__ int lcnt[kAsgKeys][2];
   __shared__ int lovf[kAsgKeys];
   __shared__ int2 lst[kAsgKeys][2][kAsgCap];   // one list per key and lane half (one writer each)
   __shared__ float ths[kAsgKeys];
   __shared__ unsigned long long best[kAsgKeys];
-  __shared__ int2 pairs[kAsgKeys * 4];
+  // the three-slot ring of screen tiles; after the screen it holds the refine pairs
+  constexpr int kRingBytes = 3 * NF * 1024;
+  static_assert(kRingBytes >= kAsgKeys * 4 * (int)sizeof(int2), "pairs fit the ring");
+  __shared__ __attribute__((aligned(16))) char ring[kRingBytes];
+  int2* const pairs = reinterpret_cast<int2*>(ring);
   __shared__ int npairs;
   __shared__ __attribute__((aligned(16))) float ccs[PARK_MAX_CLUSTERS];
   __shared__ int kidx[kAsgKeys];   // key index of each slot (-1 past N)
@@ -486,7 +510,6 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, k0 = blockIdx.x * kAsgKeys;
   const int nT = nkp >> 5;
-  const bf16* gA = gneg2 + (size_t)bh * nkp * D + (size_t)lane * 8;  // this lane's piece of fragment 0
   // The loads that need no key index go first (the slot's key and |c~|^2); the LDS copies are
   // written once the key-dependent loads are in flight.
   // Slots walk the keys in `order` (the previous step's label order, so that the keys of a
@@ -533,32 +556,17 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       E[kt] *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
     }
   }
-  // Running minimum.  From the second step on it starts at the screen score of the key's
-  // previous cluster (plus half the window, which covers the different summation order), an
-  // upper bound of the final minimum: far fewer scores then fall inside the window.
+  // Running minimum and candidate lists.  From the second step on the keys are visited in the
+  // previous step's label order, so the workgroup's keys share a few consecutive previous
+  // clusters; the screen starts at the 32-cluster tile holding the previous cluster of the
+  // workgroup's first key (plab), which makes the running minimum tight from the first tile
+  // on.  The candidate set does not depend on the tile order: every score within the final
+  // window is recorded whatever its turn (the window only shrinks).
   float mr[2] = {INFINITY, INFINITY};
   int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
   bool ovf[2] = {false, false};
-  if (have_prev) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int pos = k0 + 64 * w + 32 * kt + l32;
-      if (pos < N) {
-        const int vp = labels[(size_t)bh * N + keyi[kt]];
-        float dot = 0.0f;
-#pragma unroll
-        for (int kc = 0; kc < NF; ++kc) {
-          const bf16x8 g = load_bf16x8(gneg2 + (size_t)bh * nkp * D + frag_offset(vp, 16 * kc + 8 * h, D));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dot = fmaf((float)bfr[kt][kc][i], (float)g[i], dot);
-        }
-        dot += __shfl_xor(dot, 32);
-        mr[kt] = ccv[(size_t)bh * nkp + vp] + dot + 0.5f * E[kt];
-      } else {
-        mr[kt] = INFINITY;
-      }
-    }
-  }
+  int t0 = 0;
+  if (plab) t0 = __builtin_amdgcn_readfirstlane(min(max(plab[(size_t)bh * N + k0], 0), nkp - 1) >> 5);
 #pragma unroll
   for (int i = 0; i < MV; ++i)
     if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
@@ -567,23 +575,36 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   best[tid] = ~0ull;
   __syncthreads();
 
-  // stream the 32-cluster tiles straight from memory (fragment-major: 1 KB per fragment);
-  // three named fragment buffers rotate (the loop is unrolled by 3), so tile t + 3 is loaded
-  // into the buffer of tile t as soon as its products are issued, with no register copies
-  auto load_tile = [&](int t, bf16x8 (&buf)[NF]) {
-    const int tt = min(t, nT - 1);
+  // The 32-cluster tiles of the screen operand (fragment-major: 1 KB per fragment) pass through
+  // a three-slot LDS ring shared by the workgroup's waves: the tile of turn i sits in slot
+  // i % 3, each wave copies NF / 4 of its fragments two turns ahead, and one barrier per turn
+  // both publishes a tile and frees the slot the next copy refills.  Every fragment crosses
+  // the memory path once per workgroup instead of once per wave.
+  // tile of turn i (rotated start)
+  auto tile_of = [&](int i) { const int j = t0 + i; return j >= nT ? j - nT : j; };
+  constexpr int FPW = NF / kAsgWaves;   // fragments each wave copies per turn
+  static_assert(FPW * kAsgWaves == NF, "fragments per wave");
+  const char* gtiles = reinterpret_cast<const char*>(gneg2 + (size_t)bh * nkp * D);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
+  auto copy_turn = [&](int i) {
+    const char* src = gtiles + (size_t)tile_of(i) * NF * 1024;
+    const uint32_t dst = ring0 + (uint32_t)((i % 3) * NF * 1024);
 #pragma unroll
-    for (int kc = 0; kc < NF; ++kc) buf[kc] = load_bf16x8(gA + ((size_t)tt * NF + kc) * 512);
+    for (int f = 0; f < FPW; ++f) {
+      const int kc = w * FPW + f;
+      dma16(src + kc * 1024, (uint32_t)lane * 16u, dst + (uint32_t)kc * 1024u);
+    }
   };
-  auto tile = [&](int t, bf16x8 (&a)[NF]) {
+  // the screen products of turn i's tile into acc
+  auto products = [&](int i, const bf16x8 (&a)[NF], f32x16 (&acc)[2]) {
+    const int t = tile_of(i);
     f32x16 init;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {  // rows 8g + 4h + 0..3 of the tile
       const f32x4 c = *reinterpret_cast<const f32x4*>(&ccs[32 * t + 8 * g + 4 * h]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) init[4 * g + i] = c[i];
+      for (int i2 = 0; i2 < 4; ++i2) init[4 * g + i2] = c[i2];
     }
-    f32x16 acc[2];
     acc[0] = mfma32(a[0], bfr[0][0], init);
     acc[1] = mfma32(a[0], bfr[1][0], init);
 #pragma unroll
@@ -591,17 +612,25 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       acc[0] = mfma32(a[kc], bfr[0][kc], acc[0]);
       acc[1] = mfma32(a[kc], bfr[1][kc], acc[1]);
     }
-    load_tile(t + 3, a);
+  };
+  // minima of turn i's products per key (lane halves combined), into tm
+  auto minima = [&](const f32x16 (&acc)[2], float (&tm)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      float tm = fminf(fminf(acc[kt][0], acc[kt][1]), acc[kt][2]);
+      float x = fminf(fminf(acc[kt][0], acc[kt][1]), acc[kt][2]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) tm = fminf(fminf(tm, acc[kt][r]), acc[kt][r + 1]);
-      tm = fminf(tm, acc[kt][15]);
-      tm = xor32_min(tm);
-      mr[kt] = fminf(mr[kt], tm);
+      for (int r = 3; r < 15; r += 2) x = fminf(fminf(x, acc[kt][r]), acc[kt][r + 1]);
+      tm[kt] = xor32_min(fminf(x, acc[kt][15]));
+    }
+  };
+  // running minimum and candidate lists from turn i's products and minima
+  auto candidates = [&](int i, const f32x16 (&acc)[2], const float (&tm)[2]) {
+    const int t = tile_of(i);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      mr[kt] = fminf(mr[kt], tm[kt]);
       const float th = mr[kt] + E[kt];
-      if (__any(tm <= th)) {
+      if (__any(tm[kt] <= th)) {
         const int slot = 64 * w + 32 * kt + l32;
         int c = cnt[kt];
 #pragma unroll
@@ -626,18 +655,64 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       }
     }
   };
-  bf16x8 fa[NF], fb[NF], fc[NF];
-  load_tile(0, fa);
-  load_tile(1, fb);
-  load_tile(2, fc);
-  int t = 0;
-  for (; t + 2 < nT; t += 3) {
-    tile(t, fa);
-    tile(t + 1, fb);
-    tile(t + 2, fc);
+  // fragments of turn i from its slot
+  auto read_turn = [&](int i, bf16x8 (&a)[NF]) {
+    const bf16x8* tl = reinterpret_cast<const bf16x8*>(ring + (i % 3) * NF * 1024);
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) a[kc] = tl[kc * 64 + lane];
+  };
+  // Software pipeline over the turns (two named sets of fragment and product registers, the
+  // loop unrolled by two).  Iteration i: a barrier (before it every wave has its LDS reads
+  // returned and its copies of turn i + 2 landed; after it turn i + 2 is whole and the slot of
+  // turn i + 1, read an iteration earlier, is free for the copy of turn i + 4); then, as one
+  // block whose instructions are interleaved (scheduling group barriers), the products of turn
+  // i + 1, the LDS reads of turn i + 2 and the minima of turn i's products, so the matrix
+  // unit works on the next tile while the vector unit reduces this one; last the candidate
+  // lists of turn i (a branch taken only when a score falls inside a key's window).
+  bf16x8 fa[NF], fb[NF];
+  f32x16 pa[2], pb[2];
+  auto iteration = [&](int i, bf16x8 (&fi)[NF], bf16x8 (&fn)[NF], f32x16 (&pi)[2], f32x16 (&pn)[2]) {
+    float tm[2];
+    if (i + 2 < nT) {
+      wait_lds();
+      if (i + 3 < nT) wait_copies<FPW>(); else wait_copies<0>();
+      __syncthreads();
+      if (i + 4 < nT) copy_turn(i + 4);
+      products(i + 1, fn, pn);
+      read_turn(i + 2, fi);
+      minima(pi, tm);
+#pragma unroll
+      for (int k = 0; k < 2 * NF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+        if (k < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+    } else {
+      if (i + 1 < nT) products(i + 1, fn, pn);
+      minima(pi, tm);
+    }
+    candidates(i, pi, tm);
+  };
+  copy_turn(0);
+  if (nT > 1) copy_turn(1);
+  if (nT > 2) copy_turn(2);
+  if (nT > 2) wait_copies<FPW>(); else wait_copies<0>();
+  __syncthreads();
+  read_turn(0, fa);
+  if (nT > 1) read_turn(1, fb);
+  products(0, fa, pa);
+  if (nT > 3) {   // turn 3 goes to the slot of turn 0, once every wave has read it
+    wait_lds();
+    __syncthreads();
+    copy_turn(3);
   }
-  if (t < nT) tile(t, fa);
-  if (t + 1 < nT) tile(t + 1, fb);
+  int i = 0;
+  for (; i + 1 < nT; i += 2) {
+    iteration(i, fa, fb, pa, pb);
+    iteration(i + 1, fb, fa, pb, pa);
+  }
+  if (i < nT) iteration(i, fa, fb, pa, pb);
+  wait_copies<0>();
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int slot = 64 * w + 32 * kt + l32;
@@ -807,7 +882,8 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
 }
 
 __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__ labels, const int32_t* __restrict__ hist,
-                                                     int N, int nk, int nch, int32_t* __restrict__ perm) {
+                                                     int N, int nk, int nch, int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ plab) {
   extern __shared__ int cur[];
   const int lane = threadIdx.x, bh = blockIdx.y, ch = blockIdx.x;
   const int nbits = nk > 1 ? 32 - __builtin_clz((unsigned)(nk - 1)) : 0;   // bits of a label
@@ -838,6 +914,7 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__
     if (lab >= 0) {
       const int pos = cur[lab] + rank;
       perm[(size_t)bh * N + pos] = j;
+      plab[(size_t)bh * N + pos] = lab;
       if (last) cur[lab] = pos + 1;
     }
     __syncthreads();
@@ -1021,15 +1098,15 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
 
 // ---------------------------------------------------------------------------------------
 template <int D>
-static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, int have_prev,
-                                const int32_t* order, int32_t* labels, hipStream_t st) {
+static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, const int32_t* order,
+                                const int32_t* plab, int32_t* labels, hipStream_t st) {
   dim3 grid((s.N + kAsgKeys - 1) / kAsgKeys, s.BH);
   if (s.dtype == 0)
     k_km_assign<D, true><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk,
-                                                         w.nkp, have_prev, order, labels);
+                                                         w.nkp, order, plab, labels);
   else
     k_km_assign<D, false><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N,
-                                                          s.nk, w.nkp, have_prev, order, labels);
+                                                          s.nk, w.nkp, order, plab, labels);
   return hipGetLastError();
 }
 
@@ -1077,13 +1154,13 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   const size_t shm_nk = (size_t)s.nk * sizeof(int);
   for (int it = 0; it < iters; ++it) {
     // from the second step on, the keys are visited in the previous step's label order (perm)
-    e = launch_assign<D>(s, w, K, it > 0 ? 1 : 0, it > 0 ? perm : nullptr, labels, st);
+    e = launch_assign<D>(s, w, K, it > 0 ? perm : nullptr, it > 0 ? w.plab : nullptr, labels, st);
     if (e != hipSuccess) return e;
     k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
     k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets);
     PARK_CHECK();
-    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64, shm_nk, st>>>(labels, w.hist, s.N, s.nk, w.nch_s, perm);
+    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64, shm_nk, st>>>(labels, w.hist, s.N, s.nk, w.nch_s, perm, w.plab);
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
     if (f32)
