@@ -7,29 +7,24 @@
 namespace park {
 
 // ---------------------------------------------------------------------------------------
-// Centroids for the PAMA product, pre-multiplied by scale2 = scale log2(e) and extended by one
-// 16-column chunk whose first column holds log2 n_v (-1e30 for an empty cluster), so that
-// one matrix product with the queries (extended by a column of ones) gives the logits
+// Centroids for the PAMA product, pre-multiplied by scale2 = scale log2(e), so that the matrix
+// product with the queries gives scale log2(e) q_i . c_v; the fused kernel starts each cluster's
+// accumulators at log2 n_v (lg, -inf for an empty cluster), so the logits come out as
 //   S_iv (log2 units) = scale log2(e) q_i . c_v + log2 n_v.
 // Each value is stored as an unevaluated sum of two bf16 numbers (hi + lo), so a bf16 product
 // with the exact-bf16 queries carries about 16 mantissa bits of it.  Layout: fragment-major
-// over DK = d + 16 columns; rows nk..nkp-1 are empty clusters.  lg keeps log2 n_v (-inf if
-// empty) for the pooled baseline.
+// over the d columns; rows nk..nkp-1 are empty clusters.
 __global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __restrict__ counts,
                                  int nk, int nkp, int d, float scale2, bf16* __restrict__ Chi,
                                  bf16* __restrict__ Clo, float* __restrict__ lg) {
   const int bh = blockIdx.y;
-  const int DK = d + 16;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < nkp * DK) {
-    const int v = e / DK, c = e % DK;
-    const int n = v < nk ? counts[(size_t)bh * nk + v] : 0;
-    float x = 0.0f;
-    if (c < d) x = v < nk ? C[((size_t)bh * nk + v) * d + c] * scale2 : 0.0f;
-    else if (c == d) x = n > 0 ? __log2f((float)n) : -1e30f;
+  if (e < nkp * d) {
+    const int v = e / d, c = e % d;
+    const float x = v < nk ? C[((size_t)bh * nk + v) * d + c] * scale2 : 0.0f;
     const bf16 hi = (bf16)x;
-    const bf16 lo = (c == d && n <= 0) ? (bf16)0.0f : (bf16)(x - (float)hi);
-    const size_t o = (size_t)bh * nkp * DK + frag_offset(v, c, DK);
+    const bf16 lo = (bf16)(x - (float)hi);
+    const size_t o = (size_t)bh * nkp * d + frag_offset(v, c, d);
     Chi[o] = hi;
     Clo[o] = lo;
   }
@@ -74,11 +69,12 @@ __device__ __forceinline__ float reduce_scatter32(float (&v)[32], int l32) {
 // forms the block means from them in a second pass over HBM.
 template <int D, int VT, bool QF32, bool PROBS = false>
 __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const bf16* __restrict__ Chi,
-                                              const bf16* __restrict__ Clo, int N, int nk, int nkp, int NQ,
+                                              const bf16* __restrict__ Clo, const float* __restrict__ lg,
+                                              int N, int nk, int nkp, int NQ,
                                               float* __restrict__ W, const int4* __restrict__ chunks,
                                               const int32_t* __restrict__ ctotal,
                                               const int32_t* __restrict__ qperm, int maxc) {
-  constexpr int DK = D + 16;       // columns of the extended product
+  constexpr int DK = D;            // columns of the product
   constexpr int KC = DK / 16;
   constexpr int QP = DK + 8;       // padded LDS row
   __shared__ bf16 qs[64 * QP];
@@ -109,7 +105,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
     bf16x8 hi, lo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { hi[i] = (bf16)0.0f; lo[i] = (bf16)0.0f; }
-    if (seg * 8 < D) {
+    {
       if (row < nu) {
         const int qi = qperm ? min(max(qperm[(size_t)bh * N + q0 + row], 0), N - 1) : q0 + row;
         const size_t off = ((size_t)bh * N + qi) * D + seg * 8;
@@ -124,8 +120,6 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
           hi = load_bf16x8(reinterpret_cast<const bf16*>(Qv) + off);
         }
       }
-    } else if (seg * 8 == D) {
-      hi[0] = (bf16)1.0f;   // multiplies the log2 n_v column
     }
     *reinterpret_cast<bf16x8*>(&qs[row * QP + seg * 8]) = hi;
     if constexpr (QF32) *reinterpret_cast<bf16x8*>(&qlo[row * QP + seg * 8]) = lo;
@@ -133,13 +127,17 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
   __syncthreads();
 
   const int v0 = w * VT * 32;
+  // every accumulator of a lane belongs to one cluster column: it starts at log2 n_v
   f32x16 acc[2][VT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int vt = 0; vt < VT; ++vt) {
+    const int v = v0 + 32 * vt + l32;
+    const float l2n = v < nkp ? lg[(size_t)bh * nkp + v] : -INFINITY;
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[qt][vt][r] = l2n;
+  }
   // B operand fragments (fragment-major Chi / Clo); spare tiles past nkp re-read tile 0
   // and are masked to -inf below
   size_t crow[VT];
@@ -563,7 +561,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, con
 size_t retrieve_workspace(const Shape& s, bool need_scores) {
   const int nkp = nk_pad32(s.nk);
   size_t b = 0;
-  b += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)) * 2;  // Chi, Clo
+  b += align256((size_t)s.BH * nkp * s.d * sizeof(bf16)) * 2;  // Chi, Clo
   b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
   if (need_scores) b += align256((size_t)s.BH * n_qblocks(s.N) * s.nk * sizeof(float));
   b += align256((size_t)s.BH * sizeof(int32_t));                // online per-head floors
@@ -573,7 +571,7 @@ size_t retrieve_workspace(const Shape& s, bool need_scores) {
 // chunks == nullptr: 64-token blocks, W [BH][NQ][nk] means; otherwise one workgroup per chunk
 // slot, W [BH][maxc][nk] column sums
 template <int D, bool QF32, bool PROBS = false>
-static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo,
+static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, const bf16* Clo, const float* lg,
                                 float* W, hipStream_t st, const int4* chunks = nullptr,
                                 const int32_t* ctotal = nullptr, const int32_t* qperm = nullptr, int maxc = 0) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
@@ -582,7 +580,7 @@ static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, 
   dim3 grid(chunks ? maxc : NQ, s.BH), block(64 * nw);
   switch (vt) {
 #define PARK_PAMA_CASE(V) \
-  case V: k_pama<D, V, QF32, PROBS><<<grid, block, 0, st>>>(Q, Chi, Clo, s.N, s.nk, nkp, NQ, W, chunks, ctotal, qperm, maxc); \
+  case V: k_pama<D, V, QF32, PROBS><<<grid, block, 0, st>>>(Q, Chi, Clo, lg, s.N, s.nk, nkp, NQ, W, chunks, ctotal, qperm, maxc); \
     break;
     PARK_PAMA_CASE(1) PARK_PAMA_CASE(2) PARK_PAMA_CASE(3) PARK_PAMA_CASE(4) PARK_PAMA_CASE(5) PARK_PAMA_CASE(6)
 #undef PARK_PAMA_CASE
@@ -596,7 +594,7 @@ static hipError_t launch_pama_d(const Shape& s, const void* Q, const bf16* Chi, 
 size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores) {
   const int nkp = nk_pad32(s.nk), maxc = chunk_slots(s.N, NQ);
   size_t b = 0;
-  b += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)) * 2;  // Chi, Clo
+  b += align256((size_t)s.BH * nkp * s.d * sizeof(bf16)) * 2;  // Chi, Clo
   b += align256((size_t)s.BH * nkp * sizeof(float));           // lg
   if (need_scores) b += align256((size_t)s.BH * NQ * s.nk * sizeof(float));
   b += align256((size_t)s.BH * maxc * s.nk * sizeof(float));   // chunk column sums
@@ -678,15 +676,15 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
                            float* probs) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   char* p = static_cast<char*>(ws);
-  bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
-  bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16));
+  bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
+  bf16* Clo = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
   float* lg = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * nkp * sizeof(float));
   float* W = scores;
   if (!W) { W = reinterpret_cast<float*>(p); p += align256((size_t)s.BH * NQ * s.nk * sizeof(float)); }
   int32_t* floors = reinterpret_cast<int32_t*>(p);
   const float scale2 = scale * kLog2e;
   {
-    dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
+    dim3 grid((nkp * s.d + 255) / 256, s.BH);
     k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, scale2, Chi, Clo, lg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -703,21 +701,21 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
   } else if (probs) {
     // unfused ablation: probabilities to HBM, then the block means in a second kernel
     if (s.d == 128)
-      e = s.dtype == 1 ? launch_pama_d<128, false, true>(s, Q, Chi, Clo, probs, st)
-                       : launch_pama_d<128, true, true>(s, Q, Chi, Clo, probs, st);
+      e = s.dtype == 1 ? launch_pama_d<128, false, true>(s, Q, Chi, Clo, lg, probs, st)
+                       : launch_pama_d<128, true, true>(s, Q, Chi, Clo, lg, probs, st);
     else
-      e = s.dtype == 1 ? launch_pama_d<64, false, true>(s, Q, Chi, Clo, probs, st)
-                       : launch_pama_d<64, true, true>(s, Q, Chi, Clo, probs, st);
+      e = s.dtype == 1 ? launch_pama_d<64, false, true>(s, Q, Chi, Clo, lg, probs, st)
+                       : launch_pama_d<64, true, true>(s, Q, Chi, Clo, lg, probs, st);
     if (e == hipSuccess) {
       k_rows_mean<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(probs, s.N, s.nk, NQ, W);
       e = hipGetLastError();
     }
   } else if (s.d == 128) {
-    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, W, st)
-                     : launch_pama_d<128, true>(s, Q, Chi, Clo, W, st);
+    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, W, st)
+                     : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, W, st);
   } else {
-    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, W, st)
-                     : launch_pama_d<64, true>(s, Q, Chi, Clo, W, st);
+    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, W, st)
+                     : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, W, st);
   }
   if (e != hipSuccess) return e;
   return select_all(s, W, counts, NQ, top_p, top_k, mask, list, count, online, nullptr, floors, st);
@@ -730,8 +728,8 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
   const int nkp = nk_pad32(s.nk), NQ = qb.NQ, maxc = chunk_slots(s.N, NQ);
   char* p = static_cast<char*>(ws);
   auto take = [&](size_t bytes) { char* q = p; p += align256(bytes); return q; };
-  bf16* Chi = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)));
-  bf16* Clo = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * (s.d + 16) * sizeof(bf16)));
+  bf16* Chi = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * s.d * sizeof(bf16)));
+  bf16* Clo = reinterpret_cast<bf16*>(take((size_t)s.BH * nkp * s.d * sizeof(bf16)));
   float* lg = reinterpret_cast<float*>(take((size_t)s.BH * nkp * sizeof(float)));
   float* W = scores ? scores : reinterpret_cast<float*>(take((size_t)s.BH * NQ * s.nk * sizeof(float)));
   float* Wp = reinterpret_cast<float*>(take((size_t)s.BH * maxc * s.nk * sizeof(float)));
@@ -741,7 +739,7 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
   int32_t* floors = reinterpret_cast<int32_t*>(take((size_t)s.BH * sizeof(int32_t)));
   const float scale2 = scale * kLog2e;
   {
-    dim3 grid((nkp * (s.d + 16) + 255) / 256, s.BH);
+    dim3 grid((nkp * s.d + 255) / 256, s.BH);
     k_centroid_split<<<grid, 256, 0, st>>>(cent, counts, s.nk, nkp, s.d, scale2, Chi, Clo, lg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -749,11 +747,11 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
   hipError_t e = launch_qchunks(qb.qoffsets, s.BH, s.N, NQ, maxc, chunks, cbase, ctotal, st);
   if (e != hipSuccess) return e;
   if (s.d == 128)
-    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc)
-                     : launch_pama_d<128, true>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc);
+    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, Wp, st, chunks, ctotal, qb.qperm, maxc)
+                     : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, Wp, st, chunks, ctotal, qb.qperm, maxc);
   else
-    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc)
-                     : launch_pama_d<64, true>(s, Q, Chi, Clo, Wp, st, chunks, ctotal, qb.qperm, maxc);
+    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, Wp, st, chunks, ctotal, qb.qperm, maxc)
+                     : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, Wp, st, chunks, ctotal, qb.qperm, maxc);
   if (e != hipSuccess) return e;
   k_pama_reduce<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(Wp, chunks, cbase, s.nk, NQ, maxc, W);
   if ((e = hipGetLastError()) != hipSuccess) return e;
