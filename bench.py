@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+EXP_PER_S = 9.8e12          # v_exp_f32 throughput of the chip (256 CUs), estimated
 
 
 def log(msg):
@@ -46,6 +47,25 @@ def effective_pairs(torch, counts, block_list, block_count, N, qcounts=None):
     else:
         nu = qcounts.long()
     return int((keys_per_block * nu).sum().item()), keys_per_block
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(cfg, Q, K, V, budget_heads=1):
@@ -76,6 +96,7 @@ def cpu_baseline(cfg, Q, K, V, budget_heads=1):
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
         "value": flops / layer_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(), "nproc": os.cpu_count(),
         "sample": (f"batch 0 head 0 of {heads}: full clustering ({cfg.iters} k-means steps) and retrieval, "
                    f"attention on {len(ub)} of {NQ} query blocks; per-layer time extrapolated x{heads} heads "
                    f"(attention x{NQ / len(ub):.1f})"),
@@ -86,23 +107,44 @@ def cpu_baseline(cfg, Q, K, V, budget_heads=1):
     }
 
 
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_response_amd", "csrc", "k_attn.hip")
+CSRC = os.path.join(ROOT, "block_sparse_attention_response_amd", "csrc")
 
 
-def traffic_bytes(workload):
-    """HBM bytes per launch of the attention kernel, from the committed rocprofv3 counter
-    summary for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
-    size); None when there is none or the kernel source changed since it was taken."""
+def traffic_bytes(tag, source, workload):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary
+    profiles/<tag>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size); None when there is none or the kernel's source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"k_attn_items_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{tag}_{workload}_traffic.txt")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(os.path.join(CSRC, source), "rb").read()).hexdigest()
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_roofline(name, bound, flops, kernel_ms, algorithmic, alg_bytes, traffic, extra=None):
+    """One kernel's roofline entry from its launch's algorithmic work and live duration."""
+    sec = kernel_ms * 1e-3
+    r = {"kernel": name, "bound": bound, "kernel_ms": round(kernel_ms, 3)}
+    if bound == "mfma":
+        ach = flops / sec / 1e12
+        r.update({"achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(ach / PEAK_BF16_TFLOPS, 4)})
+    r["algorithmic"] = algorithmic
+    gbs = alg_bytes / sec / 1e9
+    r["hbm_algorithmic"] = {"bytes": int(alg_bytes), "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    r["traffic"] = traffic
+    if traffic:
+        tg = traffic / sec / 1e9
+        r["hbm_measured"] = {"GBps": round(tg, 1), "frac": round(tg / PEAK_HBM_GBS, 4),
+                             "over": "FETCH_SIZE + WRITE_SIZE per launch (profiles/) / live duration"}
+    if extra:
+        r.update(extra)
+    return r
 
 
 def copy_calibration(gib):
@@ -421,11 +463,12 @@ def main():
     ws_r = torch.empty(park.workspace_bytes(park.OP_RETRIEVE_BLOCKS, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
     ws_a = torch.empty(park.workspace_bytes(park.OP_BLOCK_SPARSE_ATTN, B, H, N, d, nk), dtype=torch.uint8, device="cuda")
 
-    def step(ev=None, kev=None):
+    def step(ev=None, kev=None, cev=None, rev=None):
         if ev: ev[0].record(stream)
-        cl = park.park_cluster_keys(q, k, nk, cfg.iters, workspace=ws_c)
+        cl = park.park_cluster_keys(q, k, nk, cfg.iters, workspace=ws_c, events=cev.handles if cev else None)
         if ev: ev[1].record(stream)
-        rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r)
+        rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], top_p, top_k, workspace=ws_r,
+                                       events=rev.handles if rev else None)
         if ev: ev[2].record(stream)
         O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
                                              workspace=ws_a, events=kev.handles if kev else None)
@@ -438,19 +481,24 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     kevs = [park.HipEvents() for _ in range(args.steps)]   # around the attention kernel itself
+    cevs = [park.HipEvents() for _ in range(args.steps)]   # around the last k-means assignment kernel
+    revs = [park.HipEvents() for _ in range(args.steps)]   # around the fused PAMA kernel
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        out = step(evs[i], kevs[i])
+        out = step(evs[i], kevs[i], cevs[i], revs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cl, rb, O, lse = out
     ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(args.steps)])
     cluster_ms, retrieve_ms, attn_ms = ms.mean(0)
     kernel_ms = float(np.mean([e.elapsed_ms() for e in kevs]))
+    assign_ms = float(np.mean([e.elapsed_ms() for e in cevs]))
+    pama_ms = float(np.mean([e.elapsed_ms() for e in revs]))
     ms_per_step = wall * 1e3 / args.steps
     log(f"step {ms_per_step:.2f} ms: cluster {cluster_ms:.2f} retrieve {retrieve_ms:.2f} attention {attn_ms:.2f}")
+    log(f"kernels: attention {kernel_ms:.3f} ms, PAMA {pama_ms:.3f} ms, last k-means assignment {assign_ms:.3f} ms")
 
     pairs, keys_per_block = effective_pairs(torch, cl["counts"], rb["block_list"], rb["block_count"], N)
     attn_flops = 4.0 * d * pairs
@@ -488,9 +536,33 @@ def main():
         "pair_density": round(pair_density, 4),
         "roofline": {"bound": "mfma", "kernel": "k_attn_items<128, false>", "achieved": round(kernel_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes(cfg.name), "kernel_ms": round(kernel_ms, 3),
+                     "traffic": traffic_bytes("k_attn_items", "k_attn.hip", cfg.name), "kernel_ms": round(kernel_ms, 3),
                      "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch" % (attn_flops / 1e12)},
     }
+    # the three heavy kernels of the step, each timed live (HIP events around one launch)
+    BH, NQ = B * H, (N + 63) // 64
+    esz = 2 if cfg.dtype == "bf16" else 4
+    kv_bytes = 4.0 * d * float(keys_per_block.sum().item())      # K and V of every selected key, once per block
+    pama_flops = 2.0 * BH * N * nk * d
+    assign_flops = 2.0 * BH * N * nk * d
+    result["kernels"] = [
+        kernel_roofline("k_attn_items<128, false>", "mfma", attn_flops, kernel_ms,
+                        "4 d FLOP per selected (query, key) pair; bytes: Q and O once, K and V once per "
+                        "(query block, selected key)", BH * N * d * esz * 2 + kv_bytes,
+                        traffic_bytes("k_attn_items", "k_attn.hip", cfg.name)),
+        kernel_roofline("k_pama<128, 4, false, false>", "mfma", pama_flops, pama_ms,
+                        "2 N_K d FLOP per query (the score product; the kernel runs it twice on the matrix unit, "
+                        "hi and lo halves of the centroids) and N_K exponentials; bytes: Q once, the centroids once "
+                        "per head, W once", BH * N * d * esz + BH * nk * d * 4 + BH * NQ * nk * 4,
+                        traffic_bytes("k_pama", "k_retrieve.hip", cfg.name),
+                        {"mfma_issued_frac": round(2 * pama_flops / (pama_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "exp_floor_ms": round(BH * N * nk / EXP_PER_S * 1e3, 3)}),
+        kernel_roofline("k_km_assign<128, false>", "mfma", assign_flops, assign_ms,
+                        "2 N_K d FLOP per key (the bf16 distance screen of one k-means step; the last step's "
+                        "launch); bytes: the keys once, the screen operand once per head, the labels once",
+                        BH * N * d * esz + BH * nk * d * 2 + BH * N * 4,
+                        traffic_bytes("k_km_assign", "k_cluster.hip", cfg.name)),
+    ]
 
     if args.recall == "on":
         allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()

@@ -73,6 +73,11 @@ def lib():
         L.park_cluster_keys.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _S, _P]
         L.park_cluster_keys.restype = _I
+        L.park_cluster_keys_timed.argtypes = L.park_cluster_keys.argtypes + [_P, _P]
+        L.park_cluster_keys_timed.restype = _I
+        L.park_retrieve_blocks_timed.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P, _P,
+                                                 _P, _S, _P, _P, _P]
+        L.park_retrieve_blocks_timed.restype = _I
         for name in ("park_retrieve_blocks", "park_retrieve_blocks_pooled"):
             f = getattr(L, name)
             f.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _F, _I, _F, _P, _P, _P, _P, _P, _S, _P]
@@ -189,10 +194,11 @@ def _check(st: int, where: str):
 # ------------------------------------------------------------------------- entry points
 
 def park_cluster_keys(Q, K, n_clusters: int, iters: int, metric: str = "qrkc", alpha: float = 0.05,
-                      init_idx=None, workspace=None):
+                      init_idx=None, workspace=None, events=None):
     """Cluster the keys of every (b, h).  Returns a dict of GPU tensors:
     centroids [B,H,nk,d] float32, counts [B,H,nk], labels [B,H,N], perm [B,H,N],
-    offsets [B,H,nk+1], status [B,H] (int32)."""
+    offsets [B,H,nk+1], status [B,H] (int32).  `events` = (begin, end) raw hipEvent_t
+    handles selects park_cluster_keys_timed (events around the last step's assignment kernel)."""
     torch = _torch()
     _dev(Q, "Q"); _dev(K, "K")
     B, H, N, d = _bhnd(Q, "Q")
@@ -209,11 +215,13 @@ def park_cluster_keys(Q, K, n_clusters: int, iters: int, metric: str = "qrkc", a
         if init_idx.dtype != torch.int32 or init_idx.numel() != n_clusters:
             raise ValueError("init_idx must be int32 [n_clusters]")
     ws, wsb = _workspace(workspace_bytes(OP_CLUSTER_KEYS, B, H, N, d, n_clusters), dev, workspace)
-    st = lib().park_cluster_keys(_ptr(Q), _ptr(K), _dtype_code(Q), B, H, N, d, n_clusters, iters,
-                                 _METRIC[metric], alpha, _ptr(init_idx), _ptr(out["centroids"]),
-                                 _ptr(out["counts"]), _ptr(out["labels"]), _ptr(out["perm"]),
-                                 _ptr(out["offsets"]), _ptr(out["status"]), _ptr(ws), wsb, _stream(Q))
-    _check(st, "park_cluster_keys")
+    args = (_ptr(Q), _ptr(K), _dtype_code(Q), B, H, N, d, n_clusters, iters, _METRIC[metric], alpha, _ptr(init_idx),
+            _ptr(out["centroids"]), _ptr(out["counts"]), _ptr(out["labels"]), _ptr(out["perm"]), _ptr(out["offsets"]),
+            _ptr(out["status"]), _ptr(ws), wsb, _stream(Q))
+    if events is None:
+        _check(lib().park_cluster_keys(*args), "park_cluster_keys")
+    else:
+        _check(lib().park_cluster_keys_timed(*args, events[0], events[1]), "park_cluster_keys_timed")
     return out
 
 
@@ -224,7 +232,7 @@ def numeric_status(status) -> int:
     return PARK_ERR_NUMERIC if bool((status != 0).any().item()) else PARK_OK
 
 
-def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace, probs=None):
+def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, workspace, probs=None, events=None):
     torch = _torch()
     _dev(Q, "Q"); _dev(centroids, "centroids"); _dev(counts, "counts")
     B, H, N, d = _bhnd(Q, "Q")
@@ -253,7 +261,7 @@ def _retrieve(fn, where, Q, centroids, counts, top_p, top_k, scale, scores, work
         extra = (_ptr(probs),)
     st = fn(_ptr(Q), _dtype_code(Q), B, H, N, d, _ptr(centroids), _ptr(counts), nk, 64, float(top_p),
             int(top_k), sc, *extra, _ptr(out.get("scores")), _ptr(out["mask"]), _ptr(out["block_list"]),
-            _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q))
+            _ptr(out["block_count"]), _ptr(ws), wsb, _stream(Q), *(events or ()))
     _check(st, where)
     return out
 
@@ -290,9 +298,13 @@ def park_retrieve_blocks_noalloc(Q, centroids, counts, top_p: float, top_k: int,
 
 
 def park_retrieve_blocks(Q, centroids, counts, top_p: float, top_k: int, scale=None, scores: bool = True,
-                         workspace=None):
+                         workspace=None, events=None):
     """PAMA scores and top-p / top-k selection.  Returns dict(scores?, mask, block_list,
-    block_count)."""
+    block_count).  `events` = (begin, end) raw hipEvent_t handles selects
+    park_retrieve_blocks_timed (events around the fused PAMA kernel)."""
+    if events is not None:
+        return _retrieve(lib().park_retrieve_blocks_timed, "park_retrieve_blocks_timed", Q, centroids, counts, top_p,
+                         top_k, scale, scores, workspace, events=events)
     return _retrieve(lib().park_retrieve_blocks, "park_retrieve_blocks", Q, centroids, counts, top_p, top_k,
                      scale, scores, workspace)
 

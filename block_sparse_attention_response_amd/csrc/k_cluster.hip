@@ -1114,7 +1114,7 @@ template <int D>
 static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K, int iters, int metric, float alpha,
                                    const int32_t* init_idx, float* cent, int32_t* counts, int32_t* labels,
                                    int32_t* perm, int32_t* offsets, int32_t* status, const ClusterWs& w,
-                                   hipStream_t st) {
+                                   hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const bool f32 = s.dtype == 0;
   hipError_t e;
 #define PARK_CHECK() do { e = hipGetLastError(); if (e != hipSuccess) return e; } while (0)
@@ -1154,8 +1154,11 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   const size_t shm_nk = (size_t)s.nk * sizeof(int);
   for (int it = 0; it < iters; ++it) {
     // from the second step on, the keys are visited in the previous step's label order (perm)
+    const bool timed = it == iters - 1;
+    if (timed && ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
     e = launch_assign<D>(s, w, K, it > 0 ? perm : nullptr, it > 0 ? w.plab : nullptr, labels, st);
     if (e != hipSuccess) return e;
+    if (timed && ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
     k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets);
@@ -1183,11 +1186,14 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
 
 hipError_t launch_cluster(const Shape& s, const void* Q, const void* K, int iters, int metric, float alpha,
                           const int32_t* init_idx, float* cent, int32_t* counts, int32_t* labels, int32_t* perm,
-                          int32_t* offsets, int32_t* status, void* ws, hipStream_t st) {
+                          int32_t* offsets, int32_t* status, void* ws, hipStream_t st, hipEvent_t ev_begin,
+                          hipEvent_t ev_end) {
   const ClusterWs w = carve(s, ws);
   if (s.d == 128)
-    return launch_cluster_d<128>(s, Q, K, iters, metric, alpha, init_idx, cent, counts, labels, perm, offsets, status, w, st);
-  return launch_cluster_d<64>(s, Q, K, iters, metric, alpha, init_idx, cent, counts, labels, perm, offsets, status, w, st);
+    return launch_cluster_d<128>(s, Q, K, iters, metric, alpha, init_idx, cent, counts, labels, perm, offsets, status, w,
+                                 st, ev_begin, ev_end);
+  return launch_cluster_d<64>(s, Q, K, iters, metric, alpha, init_idx, cent, counts, labels, perm, offsets, status, w,
+                              st, ev_begin, ev_end);
 }
 
 }  // namespace park

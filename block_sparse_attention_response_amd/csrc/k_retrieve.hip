@@ -673,7 +673,7 @@ static hipError_t select_rows(const float* W, const int32_t* counts, int nk, int
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
                            uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st, bool online,
-                           float* probs) {
+                           float* probs, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int nkp = nk_pad32(s.nk), NQ = n_qblocks(s.N);
   char* p = static_cast<char*>(ws);
   bf16* Chi = reinterpret_cast<bf16*>(p); p += align256((size_t)s.BH * nkp * s.d * sizeof(bf16));
@@ -710,12 +710,15 @@ hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, con
       k_rows_mean<<<dim3((s.nk + 255) / 256, NQ, s.BH), 256, 0, st>>>(probs, s.N, s.nk, NQ, W);
       e = hipGetLastError();
     }
-  } else if (s.d == 128) {
-    e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, W, st)
-                     : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, W, st);
   } else {
-    e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, W, st)
-                     : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, W, st);
+    if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+    if (s.d == 128)
+      e = s.dtype == 1 ? launch_pama_d<128, false>(s, Q, Chi, Clo, lg, W, st)
+                       : launch_pama_d<128, true>(s, Q, Chi, Clo, lg, W, st);
+    else
+      e = s.dtype == 1 ? launch_pama_d<64, false>(s, Q, Chi, Clo, lg, W, st)
+                       : launch_pama_d<64, true>(s, Q, Chi, Clo, lg, W, st);
+    if (e == hipSuccess && ev_end) e = hipEventRecord(ev_end, st);
   }
   if (e != hipSuccess) return e;
   return select_all(s, W, counts, NQ, top_p, top_k, mask, list, count, online, nullptr, floors, st);

@@ -41,7 +41,8 @@ Shape make_shape(int dtype, int B, int H, int N, int d, int nk) {
 int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
                   const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k, float scale,
                   float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count, void* workspace,
-                  size_t workspace_bytes, void* stream, float* probs = nullptr) {
+                  size_t workspace_bytes, void* stream, float* probs = nullptr, void* ev_begin = nullptr,
+                  void* ev_end = nullptr) {
   bool uns;
   int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
   if (st != PARK_OK) return st;
@@ -54,7 +55,7 @@ int retrieve_impl(bool pooled, const void* Q, int dtype, int B, int H, int N, in
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   hipError_t e = park::launch_retrieve(s, Q, centroids, counts, scale, top_p, top_k, pooled, scores, mask,
                                        block_list, block_count, workspace, static_cast<hipStream_t>(stream), false,
-                                       probs);
+                                       probs, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end));
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
@@ -164,10 +165,10 @@ int park_cluster_queries(const void* Q, int dtype, int B, int H, int N, int d, i
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
-int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int N, int d, int n_clusters,
-                      int iters, int metric, float alpha, const int32_t* init_idx, float* centroids,
-                      int32_t* counts, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+int park_cluster_keys_timed(const void* Q, const void* K, int dtype, int B, int H, int N, int d, int n_clusters,
+                            int iters, int metric, float alpha, const int32_t* init_idx, float* centroids,
+                            int32_t* counts, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
+                            void* workspace, size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end) {
   bool uns;
   int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
   if (st != PARK_OK) return st;
@@ -178,8 +179,18 @@ int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int
   st = check_ws(workspace, workspace_bytes, park::cluster_workspace(s));
   if (st != PARK_OK) return st;
   hipError_t e = park::launch_cluster(s, Q, K, iters, metric, alpha, init_idx, centroids, counts, labels, perm,
-                                      offsets, status, workspace, static_cast<hipStream_t>(stream));
+                                      offsets, status, workspace, static_cast<hipStream_t>(stream),
+                                      static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end));
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+
+int park_cluster_keys(const void* Q, const void* K, int dtype, int B, int H, int N, int d, int n_clusters,
+                      int iters, int metric, float alpha, const int32_t* init_idx, float* centroids,
+                      int32_t* counts, int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return park_cluster_keys_timed(Q, K, dtype, B, H, N, d, n_clusters, iters, metric, alpha, init_idx, centroids,
+                                 counts, labels, perm, offsets, status, workspace, workspace_bytes, stream, nullptr,
+                                 nullptr);
 }
 
 int park_retrieve_blocks(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
@@ -188,6 +199,15 @@ int park_retrieve_blocks(const void* Q, int dtype, int B, int H, int N, int d, c
                          size_t workspace_bytes, void* stream) {
   return retrieve_impl(false, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
                        scores, mask, block_list, block_count, workspace, workspace_bytes, stream);
+}
+
+int park_retrieve_blocks_timed(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,
+                               const int32_t* counts, int n_clusters, int q_block, float top_p, int top_k,
+                               float scale, float* scores, uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                               void* workspace, size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end) {
+  return retrieve_impl(false, Q, dtype, B, H, N, d, centroids, counts, n_clusters, q_block, top_p, top_k, scale,
+                       scores, mask, block_list, block_count, workspace, workspace_bytes, stream, nullptr, ev_begin,
+                       ev_end);
 }
 
 int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H, int N, int d, const float* centroids,

@@ -38,10 +38,12 @@ size_t retrieve_workspace(const Shape& s, bool need_scores);
 // online: SCOPE's online per-head top-k floor on top of the fixed one; probs [BH][N][nk] (or
 // NULL): the unfused ablation, which materialises the probabilities there and averages them in
 // a second kernel
+// ev_begin / ev_end (optional): recorded on st right before and after the fused PAMA kernel
 hipError_t launch_retrieve(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
                            float scale, float top_p, int top_k, bool pooled, float* scores,
                            uint8_t* mask, int32_t* list, int32_t* count, void* ws, hipStream_t st,
-                           bool online = false, float* probs = nullptr);
+                           bool online = false, float* probs = nullptr, hipEvent_t ev_begin = nullptr,
+                           hipEvent_t ev_end = nullptr);
 // PAMA and the same selection over clustered query blocks
 size_t retrieve_clustered_workspace(const Shape& s, int NQ, bool need_scores);
 hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float* cent, const int32_t* counts,
@@ -70,9 +72,11 @@ hipError_t launch_logmass(const Shape& s, const void* Q, const void* K, const in
 
 // ----- key clustering
 size_t cluster_workspace(const Shape& s);
+// ev_begin / ev_end (optional): recorded on st right before and after the last step's
+// assignment kernel
 hipError_t launch_cluster(const Shape& s, const void* Q, const void* K, int iters, int metric,
                           float alpha, const int32_t* init_idx, float* cent, int32_t* counts,
                           int32_t* labels, int32_t* perm, int32_t* offsets, int32_t* status,
-                          void* ws, hipStream_t st);
+                          void* ws, hipStream_t st, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 }  // namespace park

@@ -114,6 +114,19 @@ PARK_API int park_cluster_keys(const void* Q, const void* K, int dtype, int B, i
                       void* stream);
 
 /*
+ * park_cluster_keys_timed - park_cluster_keys for measurement: records the HIP events ev_begin
+ * and ev_end (hipEvent_t, created by the caller; either may be NULL) on `stream` immediately
+ * before and after the assignment kernel of the last k-means step, so that
+ * hipEventElapsedTime gives one assignment launch's duration.  Otherwise identical to
+ * park_cluster_keys (arguments, results, errors); a failed hipEventRecord is reported as HIP.
+ */
+PARK_API int park_cluster_keys_timed(const void* Q, const void* K, int dtype, int B, int H, int N, int d,
+                                     int n_clusters, int iters, int metric, float alpha, const int32_t* init_idx,
+                                     float* centroids, int32_t* counts, int32_t* labels, int32_t* perm,
+                                     int32_t* offsets, int32_t* status, void* workspace, size_t workspace_bytes,
+                                     void* stream, void* ev_begin, void* ev_end);
+
+/*
  * park_retrieve_blocks - per-query attention-mass aggregation (PAMA, section 5.1, E7/E8)
  * followed by top-p selection with a top-k floor (section 6.1; the floor as in SCOPE,
  * paperpeel.com/paper/2608.12780, appendix "Online Per-Head Top-k Selection"), per (b, h):
@@ -138,6 +151,20 @@ PARK_API int park_retrieve_blocks(const void* Q, int dtype, int B, int H, int N,
                          int q_block, float top_p, int top_k, float scale, float* scores,
                          uint8_t* mask, int32_t* block_list, int32_t* block_count,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * park_retrieve_blocks_timed - park_retrieve_blocks for measurement: records the HIP events
+ * ev_begin and ev_end (hipEvent_t, created by the caller; either may be NULL) on `stream`
+ * immediately before and after the fused PAMA kernel (after the centroid preparation, before
+ * the selection).  Otherwise identical to park_retrieve_blocks; a failed hipEventRecord is
+ * reported as HIP.
+ */
+PARK_API int park_retrieve_blocks_timed(const void* Q, int dtype, int B, int H, int N, int d,
+                                        const float* centroids, const int32_t* counts, int n_clusters,
+                                        int q_block, float top_p, int top_k, float scale, float* scores,
+                                        uint8_t* mask, int32_t* block_list, int32_t* block_count,
+                                        void* workspace, size_t workspace_bytes, void* stream, void* ev_begin,
+                                        void* ev_end);
 
 /*
  * park_retrieve_blocks_pooled - the query-centroid estimate that PAMA replaces (section 4.1

@@ -204,6 +204,27 @@ def test_attention_rejects(lib):
     assert _attn(lib, wsb=100) == WORKSPACE
 
 
+def test_timed_cluster_and_retrieve_reject_like_the_plain_calls(lib):
+    # the measurement variants run the same host checks before they record any event
+    for over, want in ((dict(Q=None), INVALID), (dict(d=96), UNSUPPORTED), (dict(ws=None), WORKSPACE)):
+        a = dict(Q=FAKE, K=FAKE, dtype=1, B=1, H=1, N=256, d=128, nk=8, iters=2, metric=0, alpha=0.05, init=None,
+                 cent=FAKE, counts=FAKE, labels=FAKE, perm=FAKE, offsets=FAKE, status=None, ws=FAKE, wsb=1 << 40)
+        a.update(over)
+        st = lib.park_cluster_keys_timed(a["Q"], a["K"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["nk"],
+                                         a["iters"], a["metric"], a["alpha"], a["init"], a["cent"], a["counts"],
+                                         a["labels"], a["perm"], a["offsets"], a["status"], a["ws"], a["wsb"], None,
+                                         FAKE, FAKE)
+        assert st == want, (over, st)
+    for over, want in ((dict(mask=None), INVALID), (dict(qb=32), UNSUPPORTED), (dict(ws=None), WORKSPACE)):
+        a = dict(Q=FAKE, dtype=1, B=1, H=1, N=256, d=128, cent=FAKE, counts=FAKE, nk=8, qb=64, p=0.9, k=2,
+                 scale=-1.0, scores=FAKE, mask=FAKE, lst=FAKE, cnt=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(over)
+        st = lib.park_retrieve_blocks_timed(a["Q"], a["dtype"], a["B"], a["H"], a["N"], a["d"], a["cent"],
+                                            a["counts"], a["nk"], a["qb"], a["p"], a["k"], a["scale"], a["scores"],
+                                            a["mask"], a["lst"], a["cnt"], a["ws"], a["wsb"], None, FAKE, FAKE)
+        assert st == want, (over, st)
+
+
 def test_timed_attention_rejects_like_attention(lib):
     # the measurement variant runs the same host checks before it records any event
     base = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=1, B=1, H=1, N=128, d=128, perm=FAKE, off=FAKE, nk=2, lst=FAKE,
