@@ -31,7 +31,7 @@ struct ClusterWs {
   double* cmean;  // [BH][nkp][D] original-space member means
   uint32_t* hmax; // [BH][4] float bits of max |R c~|, max bf16 error of R c~, max |c~|^2
   int32_t* hist;  // [BH][nch_s][nk] counting-sort histograms, then bases
-  int32_t* plab;  // [BH][N] label of each position of the key permutation (labels in sorted order)
+  int32_t* wlab;  // [BH][ceil(N / kAsgKeys)] label at the first position of each assignment workgroup
   int nch_g, nch_s, nkp;
 };
 
@@ -56,7 +56,7 @@ static ClusterWs carve(const Shape& s, void* base) {
   w.cmean = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
   w.hmax = reinterpret_cast<uint32_t*>(take(BH * 4 * sizeof(uint32_t)));
   w.hist = reinterpret_cast<int32_t*>(take(BH * (size_t)w.nch_s * s.nk * sizeof(int32_t)));
-  w.plab = reinterpret_cast<int32_t*>(take(BH * (size_t)s.N * sizeof(int32_t)));
+  w.wlab = reinterpret_cast<int32_t*>(take(BH * (size_t)((s.N + 255) / 256) * sizeof(int32_t)));
   if (base == nullptr) w.gpart = reinterpret_cast<double*>(p);  // total size in the pointer
   return w;
 }
@@ -468,6 +468,7 @@ __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ ci
 // overflowed compares every cluster.
 constexpr int kAsgWaves = 4;
 constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
+static_assert(kAsgKeys == 256, "the workspace sizes the per-workgroup start labels for 256 keys per workgroup");
 constexpr int kAsgCap = 10;                // list entries per key and lane half (compacted when half full)
 
 // global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
                                                       const bf16* __restrict__ gneg2, const float* __restrict__ ccv,
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
                                                       const int32_t* __restrict__ order,
-                                                      const int32_t* __restrict__ plab, int32_t* __restrict__ labels) {
+                                                      const int32_t* __restrict__ wlab, int32_t* __restrict__ labels) {
   constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
   __shared__ int lcnt[kAsgKeys][2];
   __shared__ int lovf[kAsgKeys];
@@ -559,14 +560,14 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   // Running minimum and candidate lists.  From the second step on the keys are visited in the
   // previous step's label order, so the workgroup's keys share a few consecutive previous
   // clusters; the screen starts at the 32-cluster tile holding the previous cluster of the
-  // workgroup's first key (plab), which makes the running minimum tight from the first tile
+  // workgroup's first key (wlab), which makes the running minimum tight from the first tile
   // on.  The candidate set does not depend on the tile order: every score within the final
   // window is recorded whatever its turn (the window only shrinks).
   float mr[2] = {INFINITY, INFINITY};
   int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
   bool ovf[2] = {false, false};
   int t0 = 0;
-  if (plab) t0 = __builtin_amdgcn_readfirstlane(min(max(plab[(size_t)bh * N + k0], 0), nkp - 1) >> 5);
+  if (wlab) t0 = __builtin_amdgcn_readfirstlane(min(max(wlab[(size_t)bh * gridDim.x + blockIdx.x], 0), nkp - 1) >> 5);
 #pragma unroll
   for (int i = 0; i < MV; ++i)
     if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
@@ -834,7 +835,8 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
 }
 
 __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, int N, int nk, int nch,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ wlab) {
   extern __shared__ int tot[];
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, bh = blockIdx.x;
@@ -862,10 +864,13 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   int base = 0;
   for (int i = 0; i < w; ++i) base += wsum[i];
   int ex = base + incl - s;
+  const int nwg = (N + kAsgKeys - 1) / kAsgKeys;
   for (int v = b0; v < b1; ++v) {
     const int t = tot[v];
     tot[v] = ex;
     offsets[(size_t)bh * (nk + 1) + v] = ex;
+    // the next step's assignment workgroups whose first position lies in cluster v
+    for (int g = (ex + kAsgKeys - 1) / kAsgKeys; g < nwg && g * kAsgKeys < ex + t; ++g) wlab[(size_t)bh * nwg + g] = v;
     ex += t;
   }
   if (tid == 0) offsets[(size_t)bh * (nk + 1) + nk] = N;
@@ -882,8 +887,7 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
 }
 
 __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__ labels, const int32_t* __restrict__ hist,
-                                                     int N, int nk, int nch, int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ plab) {
+                                                     int N, int nk, int nch, int32_t* __restrict__ perm) {
   extern __shared__ int cur[];
   const int lane = threadIdx.x, bh = blockIdx.y, ch = blockIdx.x;
   const int nbits = nk > 1 ? 32 - __builtin_clz((unsigned)(nk - 1)) : 0;   // bits of a label
@@ -914,7 +918,6 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__
     if (lab >= 0) {
       const int pos = cur[lab] + rank;
       perm[(size_t)bh * N + pos] = j;
-      plab[(size_t)bh * N + pos] = lab;
       if (last) cur[lab] = pos + 1;
     }
     __syncthreads();
@@ -1099,14 +1102,14 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
 // ---------------------------------------------------------------------------------------
 template <int D>
 static hipError_t launch_assign(const Shape& s, const ClusterWs& w, const void* K, const int32_t* order,
-                                const int32_t* plab, int32_t* labels, hipStream_t st) {
+                                const int32_t* wlab, int32_t* labels, hipStream_t st) {
   dim3 grid((s.N + kAsgKeys - 1) / kAsgKeys, s.BH);
   if (s.dtype == 0)
     k_km_assign<D, true><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N, s.nk,
-                                                         w.nkp, order, plab, labels);
+                                                         w.nkp, order, wlab, labels);
   else
     k_km_assign<D, false><<<grid, 64 * kAsgWaves, 0, st>>>(K, w.Kt, w.knorm, w.ctil, w.gneg2, w.ccv, w.hmax, s.N,
-                                                          s.nk, w.nkp, order, plab, labels);
+                                                          s.nk, w.nkp, order, wlab, labels);
   return hipGetLastError();
 }
 
@@ -1156,14 +1159,14 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     // from the second step on, the keys are visited in the previous step's label order (perm)
     const bool timed = it == iters - 1;
     if (timed && ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-    e = launch_assign<D>(s, w, K, it > 0 ? perm : nullptr, it > 0 ? w.plab : nullptr, labels, st);
+    e = launch_assign<D>(s, w, K, it > 0 ? perm : nullptr, it > 0 ? w.wlab : nullptr, labels, st);
     if (e != hipSuccess) return e;
     if (timed && ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
-    k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets);
+    k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets, w.wlab);
     PARK_CHECK();
-    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64, shm_nk, st>>>(labels, w.hist, s.N, s.nk, w.nch_s, perm, w.plab);
+    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64, shm_nk, st>>>(labels, w.hist, s.N, s.nk, w.nch_s, perm);
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
     if (f32)
