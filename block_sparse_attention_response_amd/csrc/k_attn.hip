@@ -1,8 +1,9 @@
 // Block-sparse attention (PARK section 3.1, E1/E2 with the softmax renormalised over the
 // selected keys): every query block attends to the union of its selected key clusters.  The
-// bf16 path packs the clusters' keys and values, splits each head's clusters into key ranges
-// (one per XCD), computes a partial softmax state per (query block, key range) and merges
-// them; the float path walks the selected clusters through the cluster permutation.
+// bf16 path packs the clusters' keys and values, splits each head's clusters into four key
+// ranges (each computed on two XCDs), computes a partial softmax state per (query block, key
+// range) and merges them; the float path walks the selected clusters through the cluster
+// permutation.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -64,14 +65,18 @@ __device__ __forceinline__ int selected_key(int p, const int* pre, int cnt, cons
 //  * the keys and values of every cluster are packed, in cluster order, into 8-key groups
 //    in the operand layouts of the two MFMA products;
 //  * the clusters of every head are dealt to kRanges key ranges of about equal work;
-//    range r of every head is computed on XCD r (the dispatcher deals consecutive
-//    workgroups to the 8 XCDs in turn), so each XCD's L2 serves one eighth of a head's keys
-//    and values to all query blocks of that head;
+//    range r of every head is computed on XCDs r and r + 4 (the dispatcher deals consecutive
+//    workgroups to the 8 XCDs in turn), so each XCD's L2 serves a quarter of a head's keys
+//    and values to the query blocks of that head it runs.  Four ranges rather than eight:
+//    the partial states (written once, read once by the merge) halve, which outweighs the
+//    L2 holding a larger share of the keys (measured at 75.6k tokens x 40 heads: attention
+//    call 15.5 ms with eight ranges, 14.6 ms with four, 16.5 ms with two);
 //  * every (query block, range) pair is a work item: the groups of its selected clusters in
 //    that range, in list order, cut into 32-key tiles of 4 groups.
 // One wave per item computes a partial softmax state over its tiles (k_attn_items) and a last
 // kernel merges the kRanges partial states of every query (k_attn_merge).
-constexpr int kRanges = 8;
+constexpr int kRanges = 4;
+static_assert(8 % kRanges == 0, "range r runs on the XCDs x with x % kRanges == r");
 
 // Step 1: gstart[v] = first group of cluster v (exclusive scan of ceil(n_v / 8)); a cluster
 // of n keys takes ceil(n / 8) groups and the tail of its last group is zero padding.
@@ -940,8 +945,9 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
 }
 
 // Persistent waves, one per workgroup: wave b starts with item b and then takes items of its
-// key range r = b % kRanges (items of range r run on XCD r: workgroups are dealt to the XCDs
-// round robin and the grid size is a multiple of kRanges) from a per-range counter, in item
+// key range r = b % kRanges (items of range r run on the XCDs x with x % kRanges == r:
+// workgroups are dealt to the XCDs round robin and the grid size is a multiple of kRanges,
+// and of 8 whenever there are enough items to fill the chip) from a per-range counter, in item
 // order: items gridDim.x + r + kRanges k for k = 0, 1, ...  The next index is taken as an
 // item starts and used when it ends.  A wave whose range is exhausted moves on to the next
 // ranges' counters (the ranges' total work differs a little).  No wave waits for another, so

@@ -188,10 +188,10 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  * an empty J_u gives O_i = 0 and lse_i = -inf.  O is in the original query order.
  * For bf16 inputs the call first copies every cluster's keys and values, in cluster order, into
  * the workspace as 8-key groups in matrix-operand order (the last group of a cluster
- * zero-padded), deals each head's clusters to 8 key ranges of about equal work (range r is
- * computed on XCD r, so each XCD's L2 holds one eighth of a head's keys), lists the 32-key
- * tiles of every (query block, range) pair, computes a partial softmax state per pair and
- * merges the 8 partial states of every query; float inputs are read in place through perm.
+ * zero-padded), deals each head's clusters to 4 key ranges of about equal work (range r is
+ * computed on XCDs r and r + 4, so each XCD's L2 holds a quarter of a head's keys), lists the
+ * 32-key tiles of every (query block, range) pair, computes a partial softmax state per pair
+ * and merges the 4 partial states of every query; float inputs are read in place through perm.
  * Inputs: Q, K, V [B,H,N,d] of `dtype`; perm/offsets from park_cluster_keys; block_list /
  * block_count from park_retrieve_blocks (ids must lie in [0, n_clusters); listing every
  * cluster gives dense attention).  scale <= 0 selects 1/sqrt(d).

@@ -70,7 +70,8 @@ def test_clustered_attention_workspace_has_no_partial_states(lib):
     BH, maxc = B * H, (N + 63) // 64 + NQ
     w64 = lib.park_workspace_bytes(2, B, H, N, d, nk)
     wcl = lib.park_workspace_bytes_clustered(2, B, H, N, d, nk, NQ)
-    partial = a256(BH * N * 8 * d * 2) + a256(BH * N * 8 * 8)
+    R = 4                        # key ranges of the 64-token path
+    partial = a256(BH * N * R * d * 2) + a256(BH * N * R * 8)
     tables = a256(BH * maxc * 16) + a256(BH * (NQ + 1) * 4) + a256(BH * 4)
     assert w64 - wcl == partial - tables
 
