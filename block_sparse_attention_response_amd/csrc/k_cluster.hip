@@ -937,24 +937,46 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   }
 }
 
-__global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__ labels, const int32_t* __restrict__ hist,
-                                                     int N, int nk, int nch, int32_t* __restrict__ perm) {
-  extern __shared__ int cur[];
-  const int lane = threadIdx.x, bh = blockIdx.y, ch = blockIdx.x;
+// Stable scatter of one chunk by four waves: wave w takes the chunk's keys [256 w, 256 w + 256)
+// and counts them per label in LDS; the counts are turned into each wave's starting position
+// per label (the chunk's base, then the waves in order), and each wave ranks its keys among
+// equal labels with one ballot per label bit, 64 keys at a time, in key order.
+constexpr int kScatWaves = 4;
+__global__ __launch_bounds__(64 * kScatWaves) void k_sort_scatter(const int32_t* __restrict__ labels,
+                                                                  const int32_t* __restrict__ hist, int N, int nk,
+                                                                  int nch, int32_t* __restrict__ perm) {
+  extern __shared__ int wpos[];   // [kScatWaves][nk]: keys per label, then starting positions
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, bh = blockIdx.y, ch = blockIdx.x;
   const int nbits = nk > 1 ? 32 - __builtin_clz((unsigned)(nk - 1)) : 0;   // bits of a label
-  // every label of the chunk is loaded before the first is ranked
-  constexpr int kSteps = kSortChunk / 64;
+  constexpr int kSteps = kSortChunk / (64 * kScatWaves);
+  static_assert(kSteps * 64 * kScatWaves == kSortChunk, "chunk split");
+  const int j0 = ch * kSortChunk + w * (kSortChunk / kScatWaves);
   int labs[kSteps];
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
-    const int j = ch * kSortChunk + 64 * st + lane;
+    const int j = j0 + 64 * st + lane;
     labs[st] = j < N ? labels[(size_t)bh * N + j] : -1;
   }
-  for (int v = lane; v < nk; v += 64) cur[v] = hist[((size_t)bh * nch + ch) * nk + v];
+  for (int v = tid; v < kScatWaves * nk; v += 64 * kScatWaves) wpos[v] = 0;
   __syncthreads();
 #pragma unroll
+  for (int st = 0; st < kSteps; ++st)
+    if (labs[st] >= 0) atomicAdd(&wpos[w * nk + labs[st]], 1);
+  __syncthreads();
+  for (int v = tid; v < nk; v += 64 * kScatWaves) {
+    int b = hist[((size_t)bh * nch + ch) * nk + v];
+#pragma unroll
+    for (int ww = 0; ww < kScatWaves; ++ww) {
+      const int t = wpos[ww * nk + v];
+      wpos[ww * nk + v] = b;
+      b += t;
+    }
+  }
+  __syncthreads();
+  int* cur = wpos + w * nk;   // this wave's next position per label
+#pragma unroll
   for (int st = 0; st < kSteps; ++st) {
-    const int j = ch * kSortChunk + 64 * st + lane;
+    const int j = j0 + 64 * st + lane;
     const int lab = labs[st];
     // lanes holding the same label: one ballot per label bit (and one for validity)
     uint64_t same = __ballot(lab >= 0);
@@ -966,12 +988,13 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const int32_t* __restrict__
     const uint64_t below = (1ull << lane) - 1;
     const int rank = __builtin_popcountll(same & below);
     const bool last = (same & ~below & ~(1ull << lane)) == 0;
+    // (a wave's LDS accesses complete in order: every lane reads its label's position before
+    // the last lane of the label moves it, and the next step reads the moved value)
     if (lab >= 0) {
       const int pos = cur[lab] + rank;
       perm[(size_t)bh * N + pos] = j;
       if (last) cur[lab] = pos + 1;
     }
-    __syncthreads();
   }
 }
 
@@ -1217,7 +1240,8 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
     PARK_CHECK();
     k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets, w.wlab);
     PARK_CHECK();
-    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64, shm_nk, st>>>(labels, w.hist, s.N, s.nk, w.nch_s, perm);
+    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64 * kScatWaves, kScatWaves * shm_nk, st>>>(labels, w.hist, s.N, s.nk,
+                                                                                   w.nch_s, perm);
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
     if (f32)
