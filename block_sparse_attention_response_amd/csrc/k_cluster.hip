@@ -455,41 +455,21 @@ __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ ci
 // (a_j = |k_j|, e_j = |k_j - bf16(k_j)|, t_j = |k~_j|, G = max |R c~|, F = max bf16 error of
 // R c~, CC = max |c~|^2).  Every cluster whose score is within 2 E_j of the key's minimum is
 // a candidate; the true argmin always is one.
-// One workgroup: 4 waves x 64 keys.  The products are 16x16x32 MFMAs (the same work as the
-// 32x32x16 shape, but the chip holds a higher clock under them): a wave's keys are four
-// groups of 16 (B operands held in registers for the whole screen), a 32-cluster tile is two
-// 16-row halves.  The cluster operand streams through a three-slot LDS ring in 32-cluster
-// tiles (LDS DMA, each wave copying a quarter of every tile, one barrier per tile), shared by
-// the 4 waves.  Each wave keeps a running minimum per key and records every score within
-// 2 E_j of the running minimum in small per-key lists, one per lane group of 16 (a value
-// that ends within 2 E_j of the final minimum was within 2 E_j of the running minimum when it
-// was seen).  From the second step on, keys are visited in the previous step's label order
-// and the screen starts at the tile of the workgroup's first previous cluster, so the running
-// minimum is tight from the first tile on.  A single surviving candidate is the answer;
-// otherwise the candidates are compared with exact float distances (k~ and c~ as stored,
-// summed in dimension order), then by id; a key whose list overflowed compares every cluster.
+// One workgroup: 4 waves x 64 keys.  The cluster operand streams through a three-slot LDS ring
+// in 32-cluster tiles (LDS DMA, each wave copying a quarter of every tile, one barrier per
+// tile), shared by the 4 waves; each wave keeps its keys' B fragments in registers and a
+// running minimum per key, and records every score within 2 E_j of the running minimum in a
+// small per-key list (a value that ends within 2 E_j of the final minimum was within 2 E_j of
+// the running minimum when it was seen).  From the second step on, keys are visited in the
+// previous step's label order and the screen starts at the tile of the workgroup's first
+// previous cluster, so the running minimum is tight from the first tile on.  A single
+// surviving candidate is the answer; otherwise the candidates are compared with exact float
+// distances (k~ and c~ as stored, summed in dimension order), then by id; a key whose list
+// overflowed compares every cluster.
 constexpr int kAsgWaves = 4;
 constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
 static_assert(kAsgKeys == 256, "the workspace sizes the per-workgroup start labels for 256 keys per workgroup");
-constexpr int kAsgCap = 5;                 // list entries per key and lane group (compacted when over half full)
-
-// Fragment-major layout of the screen operand for 16x16x32 fragments: the 64 lanes' 16-byte
-// pieces of one (16-row half tile, 32-column chunk) sit in 1 KB; lane l holds row l % 16 of
-// the half tile, columns 32 kc + 8 (l / 16) .. + 7.  A 32-row tile is D / 16 consecutive
-// fragments (half 0's chunks, then half 1's).
-__device__ __forceinline__ size_t frag16_offset(int row, int col, int D) {
-  const int t2 = row >> 4, r = row & 15, kc = col >> 5, g = (col >> 3) & 3, e = col & 7;
-  return ((size_t)(t2 * (D / 32) + kc) * 64 + 16 * g + r) * 8 + e;
-}
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// min of x over lanes l and l ^ 16 (v_permlane16_swap exchanges rows of 16 lanes pairwise)
-__device__ __forceinline__ float xor16_min(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+constexpr int kAsgCap = 10;                // list entries per key and lane half (compacted when half full)
 
 // global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
 // Inline assembly, so that the compiler does not guard later LDS reads with a wait for all
@@ -513,11 +493,10 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
                                                       const int32_t* __restrict__ order,
                                                       const int32_t* __restrict__ wlab, int32_t* __restrict__ labels) {
-  constexpr int KC = D / 32;      // 32-column chunks
-  constexpr int NF = 2 * KC;      // 1 KB fragments per 32-cluster tile: (half ch, chunk kc) at ch KC + kc
-  __shared__ int lcnt[kAsgKeys][4];
+  constexpr int NF = D / 16;  // 16-column fragments per 32-cluster tile
+  __shared__ int lcnt[kAsgKeys][2];
   __shared__ int lovf[kAsgKeys];
-  __shared__ int2 lst[kAsgKeys][4][kAsgCap];   // one list per key and lane group (one writer each)
+  __shared__ int2 lst[kAsgKeys][2][kAsgCap];   // one list per key and lane half (one writer each)
   __shared__ float ths[kAsgKeys];
   __shared__ unsigned long long best[kAsgKeys];
   // the three-slot ring of screen tiles; after the screen it holds the refine pairs
@@ -528,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   __shared__ int npairs;
   __shared__ __attribute__((aligned(16))) float ccs[PARK_MAX_CLUSTERS];
   __shared__ int kidx[kAsgKeys];   // key index of each slot (-1 past N)
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, k0 = blockIdx.x * kAsgKeys;
   const int nT = nkp >> 5;
@@ -547,35 +526,35 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   }
   if (tid == 0) npairs = 0;
 
-  // B fragments of this wave's 64 keys: group kg holds slot 64 w + 16 kg + l % 16, columns
-  // 32 kc + 8 (l / 16) .. + 7
-  bf16x8 bfr[4][KC];
-  float E[4];
+  // B fragments of this wave's 64 keys (two 32-key tiles)
+  bf16x8 bfr[2][NF];
+  float E[2];
   const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
   const float CC = __uint_as_float(hmax[4 * bh + 2]);
+  // the keys of slots 64 w + l32 and 64 w + 32 + l32 (-1 past N)
+  const int keyi[2] = {__shfl(kslot, l32), __shfl(kslot, 32 + l32)};
 #pragma unroll
-  for (int kg = 0; kg < 4; ++kg) {
-    const int pos = k0 + 64 * w + 16 * kg + l16;
-    const int ks = __shfl(kslot, 16 * kg + l16);
-    const int key = pos < N ? ks : 0;
+  for (int kt = 0; kt < 2; ++kt) {
+    const int pos = k0 + 64 * w + 32 * kt + l32;
+    const int key = pos < N ? keyi[kt] : 0;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
+    for (int kc = 0; kc < NF; ++kc) {
       if (pos < N) {
-        const size_t off = ((size_t)bh * N + key) * D + 32 * kc + 8 * g4;
-        if constexpr (KF32) bfr[kg][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
-        else bfr[kg][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
+        const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
+        if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
+        else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bfr[kg][kc][i] = (bf16)0.0f;
+        for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = (bf16)0.0f;
       }
     }
-    E[kg] = 0.0f;
+    E[kt] = 0.0f;
     if (pos < N) {
       const float4 kn = knorm[(size_t)bh * N + key];
       // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
       // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
-      E[kg] = 2.0f * (kn.y * G + kn.x * F + kn.y * F) + (1.0f / 16384.0f) * (2.0f * kn.x * G + CC + kn.z * kn.z);
-      E[kg] *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
+      E[kt] = 2.0f * (kn.y * G + kn.x * F + kn.y * F) + (1.0f / 16384.0f) * (2.0f * kn.x * G + CC + kn.z * kn.z);
+      E[kt] *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
     }
   }
   // Running minimum and candidate lists.  From the second step on the keys are visited in the
@@ -584,9 +563,9 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   // workgroup's first key (wlab), which makes the running minimum tight from the first tile
   // on.  The candidate set does not depend on the tile order: every score within the final
   // window is recorded whatever its turn (the window only shrinks).
-  float mr[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-  int cnt[4] = {0, 0, 0, 0};    // entries in this lane group's list of each key (in registers)
-  bool ovf[4] = {false, false, false, false};
+  float mr[2] = {INFINITY, INFINITY};
+  int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
+  bool ovf[2] = {false, false};
   int t0 = 0;
   if (wlab) t0 = __builtin_amdgcn_readfirstlane(min(max(wlab[(size_t)bh * gridDim.x + blockIdx.x], 0), nkp - 1) >> 5);
 #pragma unroll
@@ -617,69 +596,63 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       dma16(src + kc * 1024, (uint32_t)lane * 16u, dst + (uint32_t)kc * 1024u);
     }
   };
-  // |c~|^2 of the rows 16 ch + 4 (l / 16) + 0..3 of turn i's tile as the start of the
-  // accumulators of all four key groups; each group reads them at an offset the compiler
-  // cannot fold (zoff is zero), so that no register copies are needed
-  int zoff;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(zoff));
-  auto start_acc = [&](int i, f32x4 (&acc)[2][4]) {
+  // the screen products of turn i's tile into acc
+  auto products = [&](int i, const bf16x8 (&a)[NF], f32x16 (&acc)[2]) {
     const int t = tile_of(i);
+    f32x16 init;
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
+    for (int g = 0; g < 4; ++g) {  // rows 8g + 4h + 0..3 of the tile
+      const f32x4 c = *reinterpret_cast<const f32x4*>(&ccs[32 * t + 8 * g + 4 * h]);
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-        acc[ch][kg] = *reinterpret_cast<const f32x4*>(&ccs[32 * t + 16 * ch + 4 * g4 + kg * zoff]);
+      for (int i2 = 0; i2 < 4; ++i2) init[4 * g + i2] = c[i2];
+    }
+    acc[0] = mfma32(a[0], bfr[0][0], init);
+    acc[1] = mfma32(a[0], bfr[1][0], init);
+#pragma unroll
+    for (int kc = 1; kc < NF; ++kc) {
+      acc[0] = mfma32(a[kc], bfr[0][kc], acc[0]);
+      acc[1] = mfma32(a[kc], bfr[1][kc], acc[1]);
+    }
   };
-  // the screen products of a tile, accumulated onto the start values in acc
-  auto products = [&](const bf16x8 (&a)[NF], f32x4 (&acc)[2][4]) {
+  // minima of turn i's products per key (lane halves combined), into tm
+  auto minima = [&](const f32x16 (&acc)[2], float (&tm)[2]) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
+    for (int kt = 0; kt < 2; ++kt) {
+      float x = fminf(fminf(acc[kt][0], acc[kt][1]), acc[kt][2]);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg) acc[ch][kg] = mfma16(a[ch * KC + kc], bfr[kg][kc], acc[ch][kg]);
-  };
-  // minimum over the tile per key: this lane's 8 rows, then the 4 lane groups
-  auto minima = [&](const f32x4 (&acc)[2][4], float (&tm)[4]) {
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      float x = fminf(fminf(acc[0][kg][0], acc[0][kg][1]), acc[0][kg][2]);
-      x = fminf(fminf(x, acc[0][kg][3]), acc[1][kg][0]);
-      x = fminf(fminf(x, acc[1][kg][1]), acc[1][kg][2]);
-      tm[kg] = xor32_min(xor16_min(fminf(x, acc[1][kg][3])));
+      for (int r = 3; r < 15; r += 2) x = fminf(fminf(x, acc[kt][r]), acc[kt][r + 1]);
+      tm[kt] = xor32_min(fminf(x, acc[kt][15]));
     }
   };
   // running minimum and candidate lists from turn i's products and minima
-  auto candidates = [&](int i, const f32x4 (&acc)[2][4], const float (&tm)[4]) {
+  auto candidates = [&](int i, const f32x16 (&acc)[2], const float (&tm)[2]) {
     const int t = tile_of(i);
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      mr[kg] = fminf(mr[kg], tm[kg]);
-      const float th = mr[kg] + E[kg];
-      if (__any(tm[kg] <= th)) {
-        const int slot = 64 * w + 16 * kg + l16;
-        int c = cnt[kg];
+    for (int kt = 0; kt < 2; ++kt) {
+      mr[kt] = fminf(mr[kt], tm[kt]);
+      const float th = mr[kt] + E[kt];
+      if (__any(tm[kt] <= th)) {
+        const int slot = 64 * w + 32 * kt + l32;
+        int c = cnt[kt];
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = 32 * t + 16 * ch + 4 * g4 + r;
-            if (acc[ch][kg][r] <= th && v < nk) {
-              if (c < kAsgCap) lst[slot][g4][c] = make_int2(v, __float_as_int(acc[ch][kg][r]));
-              else ovf[kg] = true;
-              ++c;
-            }
+        for (int r = 0; r < 16; ++r) {
+          const int v = 32 * t + c_row(r, lane);
+          if (acc[kt][r] <= th && v < nk) {
+            if (c < kAsgCap) lst[slot][h][c] = make_int2(v, __float_as_int(acc[kt][r]));
+            else ovf[kt] = true;
+            ++c;
           }
-        // the window only shrinks: drop entries that left it once a list is over half full
-        if (c > kAsgCap / 2 && !ovf[kg]) {
+        }
+        // the window only shrinks: drop entries that left it once a list is half full
+        if (c > kAsgCap / 2 && !ovf[kt]) {
           int m = 0;
           for (int e = 0; e < c; ++e) {
-            const int2 x = lst[slot][g4][e];
-            if (__int_as_float(x.y) <= th) lst[slot][g4][m++] = x;
+            const int2 x = lst[slot][h][e];
+            if (__int_as_float(x.y) <= th) lst[slot][h][m++] = x;
           }
           c = m;
         }
-        cnt[kg] = c;
+        cnt[kt] = c;
       }
     }
   };
@@ -687,54 +660,38 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   auto read_turn = [&](int i, bf16x8 (&a)[NF]) {
     const bf16x8* tl = reinterpret_cast<const bf16x8*>(ring + (i % 3) * NF * 1024);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) a[f] = tl[f * 64 + lane];
+    for (int kc = 0; kc < NF; ++kc) a[kc] = tl[kc * 64 + lane];
   };
   // Software pipeline over the turns (two named sets of fragment and product registers, the
-  // loop unrolled by two).  Iteration i (a turn with two more after it): a barrier (before it
-  // every wave has its LDS reads returned and its copies of turn i + 2 landed; after it turn
-  // i + 2 is whole and the slot of turn i + 1, read an iteration earlier, is free for the copy
-  // of turn i + 4); then steps that each issue the four MFMAs of one fragment of turn i + 1,
-  // a share of turn i's minima and one fragment read of turn i + 2, fenced so that the vector
-  // work runs while the matrix instructions execute; then the candidate lists of turn i (a
-  // branch taken only when a score falls inside a key's window) and the start values of turn
-  // i + 2 into the registers that held turn i's products.
+  // loop unrolled by two).  Iteration i: a barrier (before it every wave has its LDS reads
+  // returned and its copies of turn i + 2 landed; after it turn i + 2 is whole and the slot of
+  // turn i + 1, read an iteration earlier, is free for the copy of turn i + 4); then, as one
+  // block whose instructions are interleaved (scheduling group barriers), the products of turn
+  // i + 1, the LDS reads of turn i + 2 and the minima of turn i's products, so the matrix
+  // unit works on the next tile while the vector unit reduces this one; last the candidate
+  // lists of turn i (a branch taken only when a score falls inside a key's window).
   bf16x8 fa[NF], fb[NF];
-  f32x4 pa[2][4], pb[2][4];
-  constexpr int SPK = NF / 4;   // steps per key group of the minima
-  static_assert(SPK * 4 == NF && (SPK == 1 || SPK == 2), "minima steps");
-  auto iteration = [&](int i, bf16x8 (&fi)[NF], bf16x8 (&fn)[NF], f32x4 (&pi)[2][4], f32x4 (&pn)[2][4]) {
-    wait_lds();
-    if (i + 3 < nT) wait_copies<FPW>(); else wait_copies<0>();
-    __syncthreads();
-    if (i + 4 < nT) copy_turn(i + 4);
-    const bf16x8* tl = reinterpret_cast<const bf16x8*>(ring + ((i + 2) % 3) * NF * 1024);
-    float x[4];
+  f32x16 pa[2], pb[2];
+  auto iteration = [&](int i, bf16x8 (&fi)[NF], bf16x8 (&fn)[NF], f32x16 (&pi)[2], f32x16 (&pn)[2]) {
+    float tm[2];
+    if (i + 2 < nT) {
+      wait_lds();
+      if (i + 3 < nT) wait_copies<FPW>(); else wait_copies<0>();
+      __syncthreads();
+      if (i + 4 < nT) copy_turn(i + 4);
+      products(i + 1, fn, pn);
+      read_turn(i + 2, fi);
+      minima(pi, tm);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int kc = f % KC, ch = f / KC;
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg) pn[ch][kg] = mfma16(fn[f], bfr[kg][kc], pn[ch][kg]);
-      const int kg = f / SPK;
-#pragma unroll
-      for (int c2 = (f % SPK) * 2 / SPK; c2 < ((f % SPK) + 1) * 2 / SPK; ++c2) {
-        const f32x4 p = pi[c2][kg];
-        const float m = fminf(fminf(p[0], p[1]), fminf(p[2], p[3]));
-        x[kg] = (c2 == 0) ? m : fminf(x[kg], m);
+      for (int k = 0; k < 2 * NF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+        if (k < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      fi[f] = tl[f * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (i + 1 < nT) products(i + 1, fn, pn);
+      minima(pi, tm);
     }
-    float tm[4];
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) tm[kg] = xor32_min(xor16_min(x[kg]));
-    candidates(i, pi, tm);
-    start_acc(i + 2, pi);   // the products of turn i are consumed
-  };
-  // one of the last two turns (their tiles are in LDS and their fragments read)
-  auto last_turn = [&](int i, const bf16x8 (&fn)[NF], f32x4 (&pi)[2][4], f32x4 (&pn)[2][4]) {
-    float tm[4];
-    if (i + 1 < nT) products(fn, pn);
-    minima(pi, tm);
     candidates(i, pi, tm);
   };
   copy_turn(0);
@@ -743,37 +700,29 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   if (nT > 2) wait_copies<FPW>(); else wait_copies<0>();
   __syncthreads();
   read_turn(0, fa);
-  start_acc(0, pa);
   if (nT > 1) read_turn(1, fb);
-  products(fa, pa);
-  if (nT > 1) start_acc(1, pb);
+  products(0, fa, pa);
   if (nT > 3) {   // turn 3 goes to the slot of turn 0, once every wave has read it
     wait_lds();
     __syncthreads();
     copy_turn(3);
   }
   int i = 0;
-  for (; i + 3 < nT; i += 2) {
+  for (; i + 1 < nT; i += 2) {
     iteration(i, fa, fb, pa, pb);
     iteration(i + 1, fb, fa, pb, pa);
   }
-  if (i + 2 < nT) {
-    iteration(i, fa, fb, pa, pb);
-    last_turn(i + 1, fa, pb, pa);
-    last_turn(i + 2, fb, pa, pb);
-  } else if (i + 1 < nT) {
-    last_turn(i, fb, pa, pb);
-    last_turn(i + 1, fa, pb, pa);
-  } else if (i < nT) {
-    last_turn(i, fb, pa, pb);
-  }
+  if (i < nT) iteration(i, fa, fb, pa, pb);
   wait_copies<0>();
 #pragma unroll
-  for (int kg = 0; kg < 4; ++kg) {
-    const int slot = 64 * w + 16 * kg + l16;
-    lcnt[slot][g4] = min(cnt[kg], kAsgCap);
-    if (ovf[kg]) lovf[slot] = 1;
-    if (g4 == 0) ths[slot] = mr[kg] + E[kg];
+  for (int kt = 0; kt < 2; ++kt) {
+    const int slot = 64 * w + 32 * kt + l32;
+    lcnt[slot][h] = min(cnt[kt], kAsgCap);
+    if (ovf[kt]) lovf[slot] = 1;
+  }
+  if (h == 0) {
+    ths[64 * w + l32] = mr[0] + E[0];
+    ths[64 * w + 32 + l32] = mr[1] + E[1];
   }
   __syncthreads();
   // survivors per key: list entries within the window of the final minimum; keys with two
@@ -782,20 +731,20 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   const int j = k0 + tid;
   {
     const float th = ths[tid];
-    for (int gg = 0; gg < 4; ++gg) {
-      const int n = lcnt[tid][gg];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int n = lcnt[tid][hh];
       for (int c = 0; c < n; ++c) {
-        const int2 e = lst[tid][gg][c];
+        const int2 e = lst[tid][hh][c];
         if (__int_as_float(e.y) <= th) { ++n_surv; only = e.x; }
       }
     }
     if (j < N && !lovf[tid] && n_surv >= 2) {
       const int base = atomicAdd(&npairs, n_surv);
       int m = 0;
-      for (int gg = 0; gg < 4; ++gg) {
-        const int n = lcnt[tid][gg];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int n = lcnt[tid][hh];
         for (int c = 0; c < n; ++c) {
-          const int2 e = lst[tid][gg][c];
+          const int2 e = lst[tid][hh][c];
           if (__int_as_float(e.y) <= th) {
             if (base + m < kAsgKeys * 4) pairs[base + m] = make_int2(tid, e.x);
             ++m;
@@ -1134,9 +1083,9 @@ __global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean
         ms[vv][i] = g[c][d];
         if (live_s[vv]) {
           ctil[((size_t)bh * nkp + v) * D + i] = cs[vv][i];
-          gneg2[(size_t)bh * nkp * D + frag16_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[c][d]);
+          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[c][d]);
         } else if (v >= nk) {
-          gneg2[(size_t)bh * nkp * D + frag16_offset(v, i, D)] = (bf16)0.0f;
+          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
         }
       }
     }
