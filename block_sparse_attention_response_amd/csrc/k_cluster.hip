@@ -471,12 +471,13 @@ constexpr int kAsgKeys = 64 * kAsgWaves;   // keys per workgroup
 static_assert(kAsgKeys == 256, "the workspace sizes the per-workgroup start labels for 256 keys per workgroup");
 constexpr int kAsgCap = 10;                // list entries per key and lane half (compacted when half full)
 
-// global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i.
-// Inline assembly, so that the compiler does not guard later LDS reads with a wait for all
+// global -> LDS copy of 16 bytes per lane: lane i reads base + off_i and writes lds + 16 i
+// (the LDS address goes in m0, bound as an operand so that the compiler sets it).  Inline
+// assembly, so that the compiler does not guard later LDS reads with a wait for all
 // outstanding copies; the kernel waits for exactly the copies it needs (copies complete in
 // issue order).  The instruction has no register results.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_copies() {
