@@ -22,9 +22,8 @@ std::mutex scratch_mtx;
 
 // Device address of the current device's copy of `scratch` (looked up on the first call on
 // that device, with the device current); nullptr if the lookup fails.
-void* device_scratch() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
   void* p = scratch_ptr[dev].load(std::memory_order_acquire);
   if (p) return p;
   std::lock_guard<std::mutex> lock(scratch_mtx);
@@ -69,7 +68,15 @@ int park_retrieve_blocks_noalloc(const void* Q, int dtype, int B, int H, int N, 
   park::Shape s;
   s.BH = B * H; s.N = N; s.d = d; s.nk = n_clusters; s.dtype = dtype;
   if (park::retrieve_workspace(s, false) > PARK_NOALLOC_SCRATCH_BYTES) return PARK_ERR_WORKSPACE;
-  void* ws = device_scratch();
+  // the scratch is the current device's: the stream must run on that device
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PARK_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return PARK_ERR_HIP;
+    if (sdev != dev) return PARK_ERR_INVALID;
+  }
+  void* ws = device_scratch(dev);
   if (!ws) return PARK_ERR_HIP;
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   const hipError_t e = park::launch_retrieve(s, Q, centroids, counts, scale, top_p, top_k, false, scores, mask,

@@ -400,11 +400,14 @@ PARK_API size_t park_noalloc_scratch_bytes(int B, int H, int N, int d, int n_clu
  * operands of the fused PAMA kernel) is the library's static per-GPU array of
  * PARK_NOALLOC_SCRATCH_BYTES.  `scores` is required here (W is an output in caller memory,
  * not scratch).  The device address of the array is looked up once per device, on the first
- * call with that device current.  Every call on one GPU uses the same array and overwrites
+ * call with that device current; `stream` (NULL: the current device's null stream) must
+ * belong to the current device, whose copy of the array the call uses.  Every call on one
+ * GPU uses the same array and overwrites
  * all of it that it reads, so calls that overlap on one GPU (several host threads, or
  * several streams running at once) race and must be serialised by the caller.
- * Errors: as park_retrieve_blocks; INVALID also for a NULL scores; WORKSPACE when the sizes
- * need more than PARK_NOALLOC_SCRATCH_BYTES (park_noalloc_scratch_bytes); HIP also when the
+ * Errors: as park_retrieve_blocks; INVALID also for a NULL scores and for a stream of another
+ * device; WORKSPACE when the sizes need more than PARK_NOALLOC_SCRATCH_BYTES
+ * (park_noalloc_scratch_bytes); HIP also when the current device, the stream's device or the
  * scratch address cannot be obtained.
  */
 PARK_API int park_retrieve_blocks_noalloc(const void* Q, int dtype, int B, int H, int N, int d,
