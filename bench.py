@@ -126,6 +126,55 @@ def traffic_bytes(tag, source, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
+def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4):
+    """HBM roofline entries of the step's streaming kernels, from the committed kernel trace and
+    counters (profiles/streaming_kernels_<workload>_traffic.txt): profiled, not timed in this
+    run.  Algorithmic bytes are each kernel's minimum reads and writes at these sizes; an entry
+    whose kernel source changed since the profile was taken carries no measured figures."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"streaming_kernels_{workload}_traffic.txt")))
+    except (OSError, ValueError):
+        return []
+    nkp = (nk + 31) // 32 * 32
+    alg = {
+        "park::k_km_sums<128, bf16>": ("the keys once (by perm), perm once, the means (double) once",
+                                       BH * N * d * esz + BH * N * 4 + BH * nkp * d * 8),
+        "park::k_km_ctx<128>": ("the means (double) and R, R^T once; c~ (float), the bf16 screen operand and "
+                                "the per-cluster figures once", BH * nkp * d * 8 + 2 * BH * d * d * 8 + BH * nkp * (d * 6 + 20)),
+        "park::k_transform_bf16<128>": ("the keys once; K~ (float) and the key norms once",
+                                        BH * N * d * esz + BH * N * d * 4 + BH * N * 16),
+        "park::k_gram_bf16<128>": ("the queries once", BH * N * d * esz),
+        "park::k_sort_scatter": ("the labels once, perm once", 2 * BH * N * 4),
+        "park::k_select<16>": ("W once; mask, list and count once", BH * NQ * nk * (4 + 1 + 4) + BH * NQ * 4),
+        "park::k_pack_kv<128>": ("K, V and perm once; the packed groups once",
+                                 2 * BH * N * d * esz + BH * N * 4 + 2 * BH * (N + 8 * nk) * d * esz),
+        "park::k_attn_merge<128>": ("the partial states once (an upper bound: negligible ones are skipped); O and lse once",
+                                    BH * N * ranges * (d * 2 + 8) + BH * N * (d * esz + 4)),
+    }
+    out = []
+    for k in rec.get("kernels", []):
+        if k["kernel"] not in alg:
+            continue
+        desc, nbytes = alg[k["kernel"]]
+        e = {"kernel": k["kernel"].replace("park::", ""), "bound": "hbm", "algorithmic": desc,
+             "dispatches_per_step": k["dispatches_per_step"],
+             "over": "profiled: kernel trace average and FETCH_SIZE + WRITE_SIZE per dispatch (profiles/)"}
+        sha = hashlib.sha256(open(os.path.join(ROOT, k["source"]), "rb").read()).hexdigest()
+        if sha != k["source_sha256"]:
+            e["stale"] = "the kernel's source changed since the profile was taken"
+        else:
+            sec = k["average_us"] * 1e-6
+            meas = k["fetch_bytes_per_dispatch"] + k["write_bytes_per_dispatch"]
+            e.update({"kernel_ms": round(k["average_us"] / 1e3, 4),
+                      "hbm_algorithmic": {"bytes": int(nbytes), "GBps": round(nbytes / sec / 1e9, 1),
+                                          "frac": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4)},
+                      "traffic": int(meas),
+                      "hbm_measured": {"GBps": round(meas / sec / 1e9, 1), "frac": round(meas / sec / 1e9 / PEAK_HBM_GBS, 4)}})
+        out.append(e)
+    return out
+
+
 def kernel_roofline(name, bound, flops, kernel_ms, algorithmic, alg_bytes, traffic, extra=None):
     """One kernel's roofline entry from its launch's algorithmic work and live duration."""
     sec = kernel_ms * 1e-3
@@ -563,6 +612,8 @@ def main():
                         BH * N * d * esz + BH * nk * d * 2 + BH * N * 4,
                         traffic_bytes("k_km_assign", "k_cluster.hip", cfg.name)),
     ]
+    # the streaming kernels of the step against the HBM roofline (from the committed profiles)
+    result["streaming_kernels"] = streaming_rooflines(cfg.name, BH, N, d, nk, NQ, esz)
 
     if args.recall == "on":
         allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()

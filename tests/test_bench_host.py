@@ -1,5 +1,6 @@
-"""Host-side pieces of bench.py that need no GPU: the refusal of more than one GPU and the
-count of selected (query, key) pairs that the throughput is computed from."""
+"""Host-side pieces of bench.py that need no GPU: the refusal of more than one GPU, the count
+of selected (query, key) pairs that the throughput is computed from, and the streaming
+kernels' HBM entries taken from the committed profile."""
 import importlib.util
 import os
 import subprocess
@@ -52,3 +53,38 @@ def test_effective_pairs_brute_force():
                                          torch.from_numpy(cnt), N, None if qc is None else torch.from_numpy(qc))
         assert got == want
         assert kpb.shape == (B, H, NQ)
+
+
+def test_streaming_rooflines_follow_the_committed_profile(tmp_path, monkeypatch):
+    """The streaming kernels' HBM entries come from the committed profile record; an entry
+    whose kernel source no longer matches the recorded SHA-256 carries no measured figures."""
+    bench = _bench()
+    wl = "wan2.1-14b-720p-21x45x80"
+    rec_path = os.path.join(bench.ROOT, "profiles", f"streaming_kernels_{wl}_traffic.txt")
+    if not os.path.exists(rec_path):
+        import pytest
+        pytest.skip("no streaming-kernel profile for this workload")
+    BH, N, d, nk = 40, 75600, 128, 1024
+    entries = bench.streaming_rooflines(wl, BH, N, d, nk, (N + 63) // 64, 2)
+    assert entries and all(e["bound"] == "hbm" for e in entries)
+    sums = next(e for e in entries if e["kernel"].startswith("k_km_sums"))
+    if "stale" not in sums:
+        # the sums read every key once: at least B H N d bf16 bytes
+        assert sums["hbm_algorithmic"]["bytes"] >= BH * N * d * 2
+        assert abs(sums["hbm_measured"]["GBps"] - sums["traffic"] / (sums["kernel_ms"] * 1e-3) / 1e9) < 1.0
+    # a record whose hashes do not match the sources gives stale entries only
+    import json
+    rec = json.load(open(rec_path))
+    for k in rec["kernels"]:
+        k["source_sha256"] = "0" * 64
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / f"streaming_kernels_{wl}_traffic.txt").write_text(json.dumps(rec))
+    real_root = bench.ROOT
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for k in rec["kernels"]:   # the sources are read relative to ROOT as well
+        src = tmp_path / k["source"]
+        src.parent.mkdir(parents=True, exist_ok=True)
+        src.write_bytes(open(os.path.join(real_root, k["source"]), "rb").read())
+    stale = bench.streaming_rooflines(wl, BH, N, d, nk, (N + 63) // 64, 2)
+    assert stale and all("stale" in e and "kernel_ms" not in e for e in stale)
