@@ -92,58 +92,77 @@ __device__ __forceinline__ float reduce_scatter16(float (&v)[16], int l32) {
   return v[0] + __shfl_xor(v[0], 1);
 }
 
+// One wave per 32x32 output tile ((D/32)^2 waves per workgroup), so a lane holds the double
+// sums of one tile only and the workgroup has many waves to hide the loads; every thread
+// loads its share of each 64-token sub-chunk kGramAhead sub-chunks ahead into registers.
+// The sums are taken in the same order as ever: per sub-chunk the MFMA's float sum over the
+// 64 tokens, then the sub-chunks in order in double.
+constexpr int kGramAhead = 4;
 template <int D>
-__global__ __launch_bounds__(256) void k_gram_bf16(const bf16* __restrict__ Q, int N, int nch, double* __restrict__ gpart) {
+__global__ __launch_bounds__(64 * (D / 32) * (D / 32)) void k_gram_bf16(const bf16* __restrict__ Q, int N, int nch,
+                                                                        double* __restrict__ gpart) {
   constexpr int TP = 64 + 8;
   constexpr int NT = D / 32;
-  constexpr int TPW = NT * NT / 4;  // output tiles per wave
+  constexpr int NTH = 64 * NT * NT;            // threads
+  constexpr int LPT = (64 * (D / 8)) / NTH;    // 16-byte loads per thread and sub-chunk
+  static_assert(LPT * NTH == 64 * (D / 8) && LPT >= 1, "sub-chunk split");
   __shared__ bf16 Qt[D * TP];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), mt = w / NT, nt = w % NT;
   const int bh = blockIdx.y, ch = blockIdx.x;
   const int c0 = ch * kGramChunk, c1 = min(c0 + kGramChunk, N);
-  double acc64[TPW][16];
+  const int nsub = (c1 - c0 + 63) / 64;
+  // this thread's loads of a sub-chunk: element e = tid + NTH l, token e % 64, 8 columns at 8 (e / 64)
+  auto load_sub = [&](int sidx, bf16x8 (&v)[LPT]) {
 #pragma unroll
-  for (int j = 0; j < TPW; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc64[j][r] = 0.0;
-  for (int sub = c0; sub < c1; sub += 64) {
-    for (int e = tid; e < 64 * (D / 8); e += 256) {
-      const int tok = e & 63, sg = e >> 6;
-      bf16x8 val;
-      if (sub + tok < c1) {
-        val = load_bf16x8(Q + ((size_t)bh * N + sub + tok) * D + sg * 8);
+    for (int l = 0; l < LPT; ++l) {
+      const int e = tid + NTH * l, tok = e & 63, sg = e >> 6;
+      const int t = c0 + 64 * sidx + tok;
+      if (sidx < nsub && t < c1) {
+        v[l] = load_bf16x8(Q + ((size_t)bh * N + t) * D + sg * 8);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) val[i] = (bf16)0.0f;
+        for (int i = 0; i < 8; ++i) v[l][i] = (bf16)0.0f;
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Qt[(sg * 8 + i) * TP + tok] = val[i];
     }
-    __syncthreads();
+  };
+  bf16x8 ring[kGramAhead][LPT];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int id = w * TPW + j, mt = id / NT, nt = id % NT;
-      f32x16 acc;
+  for (int a = 0; a < kGramAhead; ++a) load_sub(a, ring[a]);
+  double acc64[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc64[r] = 0.0;
+  for (int s0 = 0; s0 < nsub; s0 += kGramAhead) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qt[(32 * mt + l32) * TP + 16 * kc + 8 * h]);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&Qt[(32 * nt + l32) * TP + 16 * kc + 8 * h]);
-        acc = mfma32(a, b, acc);
+    for (int a = 0; a < kGramAhead; ++a) {
+      const int sidx = s0 + a;
+      if (sidx < nsub) {   // uniform over the workgroup
+#pragma unroll
+        for (int l = 0; l < LPT; ++l) {
+          const int e = tid + NTH * l, tok = e & 63, sg = e >> 6;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) Qt[(sg * 8 + i) * TP + tok] = ring[a][l][i];
+        }
+        __syncthreads();
+        load_sub(sidx + kGramAhead, ring[a]);   // the slot is free: kGramAhead sub-chunks ahead
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Qt[(32 * mt + l32) * TP + 16 * kc + 8 * h]);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Qt[(32 * nt + l32) * TP + 16 * kc + 8 * h]);
+          acc = mfma32(av, bv, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc64[r] += (double)acc[r];
+        __syncthreads();
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc64[j][r] += (double)acc[r];
     }
-    __syncthreads();
   }
   double* out = gpart + ((size_t)bh * nch + ch) * D * D;
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int id = w * TPW + j, mt = id / NT, nt = id % NT;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) out[(32 * mt + c_row(r, lane)) * D + 32 * nt + l32] = acc64[j][r];
-  }
+  for (int r = 0; r < 16; ++r) out[(32 * mt + c_row(r, lane)) * D + 32 * nt + l32] = acc64[r];
 }
 
 // a1 for float queries: plain double sums (small workloads only).
@@ -1148,7 +1167,7 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   if (metric == 0) {
     dim3 grid(w.nch_g, s.BH);
     if (f32) k_gram_f32<D><<<grid, 256, 0, st>>>(reinterpret_cast<const float*>(Q), s.N, w.nch_g, w.gpart);
-    else k_gram_bf16<D><<<grid, 256, 0, st>>>(reinterpret_cast<const bf16*>(Q), s.N, w.nch_g, w.gpart);
+    else k_gram_bf16<D><<<grid, 64 * (D / 32) * (D / 32), 0, st>>>(reinterpret_cast<const bf16*>(Q), s.N, w.nch_g, w.gpart);
     PARK_CHECK();
   }
   if (metric == 0) {
