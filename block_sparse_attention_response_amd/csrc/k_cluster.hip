@@ -207,73 +207,101 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ 
   G[(size_t)bh * D * D + e] = s / (double)N;
 }
 
-// a2: shrinkage and Cholesky factor, one workgroup per head, double precision in LDS.
+// a2: shrinkage and Cholesky factor, one workgroup per head, double precision in registers.
 //   s = max(tr G / D, s_min);  Gs = (1-alpha) G + (alpha+eps) s I;  Gs = R R^T computed
-//   right-looking in place (row pitch D+1): for each column the pivot is square-rooted, the
-//   column below it scaled, and the trailing lower triangle updated by all threads at once.
-//   On failure (non-positive or non-finite pivot) the head gets R = I and status 1.
-//   metric 1 (Euclidean) writes R = I.  G may alias Rt64 (it is read before Rt64 is written).
+//   right-looking: thread (ty, tx) of a 16 x 16 grid holds the entries (ty + 16a, tx + 16b) of
+//   the matrix.  For each column j the threads holding it publish it in LDS, every thread takes
+//   the square root of the pivot and one thread per row divides its entry by it, and then every
+//   thread updates its entries to the right of column j with the new column (each entry gets its
+//   updates one FMA at a time in column order).  Entries above the diagonal are updated too and
+//   ignored.  On failure (non-positive or non-finite pivot) the head gets R = I and status 1.
+//   metric 1 (Euclidean) writes R = I.  G may alias Rt64 (every read of G precedes the first
+//   barrier, every write of Rt64 follows the last).
 template <int D>
 __global__ __launch_bounds__(256) void k_chol(const double* G, int metric, double alpha, double* __restrict__ R64,
                                               double* Rt64, bf16* __restrict__ Rsp, int32_t* __restrict__ status) {
-  constexpr int P = D + 1;
-  __shared__ double A[D * P];
+  constexpr int NB = D / 16;  // rows (and columns) per thread
+  __shared__ double col[D], lcol[D];
   __shared__ double red[4];
-  __shared__ int fail;
-  const int tid = threadIdx.x, bh = blockIdx.x;
-  if (tid == 0) fail = 0;
+  const int tid = threadIdx.x, bh = blockIdx.x, ty = tid >> 4, tx = tid & 15;
+  double acc[NB][NB];
+  bool fail = false;
   if (metric == 0) {
-    for (int e = tid; e < D * D; e += 256) A[(e / D) * P + e % D] = G[(size_t)bh * D * D + e];
-    __syncthreads();
-    double tr = 0.0;
-    for (int i = tid; i < D; i += 256) tr += A[i * P + i];
+    const double* g = G + (size_t)bh * D * D;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = g[(ty + 16 * a) * D + tx + 16 * b];
+    double tr = tid < D ? g[tid * D + tid] : 0.0;
     tr = sum64d(tr);
     if ((tid & 63) == 0) red[tid >> 6] = tr;
     __syncthreads();
     double sq = (red[0] + red[1] + red[2] + red[3]) / D;
     if (!(sq > kSMin)) sq = kSMin;
-    for (int e = tid; e < D * D; e += 256) {
-      const int i = e / D, j = e % D;
-      A[i * P + j] = (1.0 - alpha) * A[i * P + j] + (i == j ? (alpha + kEps) * sq : 0.0);
-    }
-    __syncthreads();
-    for (int j = 0; j < D; ++j) {
-      double piv = A[j * P + j];
-      if (!(piv > 0.0) || !isfinite(piv)) {
-        if (tid == 0) fail = 1;
-        piv = 1.0;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = ty + 16 * a, j = tx + 16 * b;
+        acc[a][b] = (1.0 - alpha) * acc[a][b] + (i == j ? (alpha + kEps) * sq : 0.0);
       }
-      const double dj = sqrt(piv);
-      __syncthreads();
-      if (tid == 0) A[j * P + j] = dj;
-      for (int i = j + 1 + tid; i < D; i += 256) A[i * P + j] /= dj;
-      __syncthreads();
-      // trailing lower triangle, 16 x 16 thread grid
-      const int ty = tid >> 4, tx = tid & 15;
-      for (int i = j + 1 + ty; i < D; i += 16) {
-        const double lij = A[i * P + j];
-        for (int k = j + 1 + tx; k <= i; k += 16) A[i * P + k] -= lij * A[k * P + j];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll 1
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = 16 * jb + jj;
+        if (tx == jj) {
+#pragma unroll
+          for (int a = 0; a < NB; ++a) col[ty + 16 * a] = acc[a][jb];
+        }
+        __syncthreads();
+        double piv = col[j];
+        if (!(piv > 0.0) || !isfinite(piv)) {
+          fail = true;
+          piv = 1.0;
+        }
+        const double dj = sqrt(piv);
+        if (tid < D) lcol[tid] = tid > j ? col[tid] / dj : (tid == j ? dj : 0.0);
+        __syncthreads();
+        double li[NB];
+#pragma unroll
+        for (int a = 0; a < NB; ++a) li[a] = lcol[ty + 16 * a];
+        if (tx == jj) {
+#pragma unroll
+          for (int a = 0; a < NB; ++a)
+            if (ty + 16 * a >= j) acc[a][jb] = li[a];
+        }
+        // columns k = tx + 16 b > j: b > jb always, b == jb when tx > jj
+#pragma unroll
+        for (int b = jb; b < NB; ++b) {
+          if (b == jb && tx <= jj) continue;
+          const double lk = lcol[tx + 16 * b];
+#pragma unroll
+          for (int a = 0; a < NB; ++a) acc[a][b] -= li[a] * lk;
+        }
       }
-      __syncthreads();
     }
   }
   const bool ident = metric != 0 || fail;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    const double r = ident ? (i == j ? 1.0 : 0.0) : (j <= i ? A[i * P + j] : 0.0);
-    R64[(size_t)bh * D * D + e] = r;                       // R[i][j]
-    Rt64[(size_t)bh * D * D + (size_t)j * D + i] = r;      // Rt[j][i] = R[i][j]
-    // Rsp[s][out a][in c] = split of Rt[a][c] = R[c][a]: here a = j, c = i
-    const bf16 s0 = (bf16)(float)r;
-    const double r1 = r - (double)(float)s0;
-    const bf16 s1 = (bf16)(float)r1;
-    const double r2 = r1 - (double)(float)s1;
-    const bf16 s2 = (bf16)(float)r2;
-    bf16* rs = Rsp + (size_t)bh * 3 * D * D + (size_t)j * D + i;
-    rs[0] = s0;
-    rs[(size_t)D * D] = s1;
-    rs[(size_t)2 * D * D] = s2;
-  }
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = ty + 16 * a, j = tx + 16 * b;
+      const double r = ident ? (i == j ? 1.0 : 0.0) : (j <= i ? acc[a][b] : 0.0);
+      R64[(size_t)bh * D * D + (size_t)i * D + j] = r;       // R[i][j]
+      Rt64[(size_t)bh * D * D + (size_t)j * D + i] = r;      // Rt[j][i] = R[i][j]
+      // Rsp[s][out a][in c] = split of Rt[a][c] = R[c][a]: here a = j, c = i
+      const bf16 s0 = (bf16)(float)r;
+      const double r1 = r - (double)(float)s0;
+      const bf16 s1 = (bf16)(float)r1;
+      const double r2 = r1 - (double)(float)s1;
+      const bf16 s2 = (bf16)(float)r2;
+      bf16* rs = Rsp + (size_t)bh * 3 * D * D + (size_t)j * D + i;
+      rs[0] = s0;
+      rs[(size_t)D * D] = s1;
+      rs[(size_t)2 * D * D] = s2;
+    }
   if (status && tid == 0) status[bh] = (metric == 0 && fail) ? 1 : 0;
 }
 
