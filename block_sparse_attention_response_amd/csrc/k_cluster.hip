@@ -1054,118 +1054,171 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
 // initial centroids, c~_v as stored), then the screen operand g_v = R c~_v in double,
 // gneg2 = bf16(-2 g) (fragment-major), |c~|^2, |g|, |g - bf16(g)|.  Clusters without keys
 // keep everything from the previous step; padding rows (v >= nk) get |c~|^2 = +inf.
-// Thread (i, vh) owns dimension i of the clusters NVH j + vh of the tile, so each R element
-// read from memory serves several clusters.
+// Both products are double GEMMs on the matrix cores (16 x 16 x 4 double MFMAs): wave w takes
+// the 16 clusters v0 + 16 (w & 1) .. + 15 and the D / 2 columns of half w >> 1, as D / 32
+// output blocks of 16 columns.  Lane l holds the A element (cluster l % 16, k) and the B
+// element (k, column l % 16) for k in [(l / 16) KS, (l / 16 + 1) KS), KS = D / 4, one k of
+// that range per MFMA step, so each lane reads contiguous rows: the means (or c~), and rows
+// of R^T (first product) or R (second).  The MFMA output element (cluster 4 r + l / 16,
+// column l % 16) sits in lane l, register r.
 template <int D>
-__global__ __launch_bounds__(256) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
-                                                 int nk, int nkp, int init_mode, const double* __restrict__ R64,
-                                                 const double* __restrict__ Rt64, float* __restrict__ ctil,
-                                                 bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
-                                                 float* __restrict__ ccv) {
-  // thread (cg, dg): clusters 4 cg .. 4 cg + 3 of the 32-cluster tile, columns DPT dg .. + DPT - 1
-  constexpr int DPT = D / 32;
-  __shared__ double ms[32][D + 1];     // means, then g
-  __shared__ float cs[32][D + 1];
-  __shared__ int live_s[32];
-  const int tid = threadIdx.x, bh = blockIdx.y, v0 = blockIdx.x * 32;
-  const int cg = tid >> 5, dg = tid & 31, c0 = 4 * cg, i0 = DPT * dg;
-  if (tid < 32) {
-    const int v = v0 + tid;
-    live_s[tid] = v < nk && (init_mode || counts[(size_t)bh * nk + v] > 0);
-  }
-  // acc[c][d] = sum_k M[k][i0 + d] rhs(c0 + c, k), 8 rows of M loaded ahead of their use
-  auto matvec = [&](const double* M, auto&& rhs, double (&acc)[4][DPT]) {
+__global__ __launch_bounds__(256, 2) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
+                                                    int nk, int nkp, int init_mode, const double* __restrict__ R64,
+                                                    const double* __restrict__ Rt64, float* __restrict__ ctil,
+                                                    bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
+                                                    float* __restrict__ ccv) {
+  constexpr int NBW = D / 32;  // 16-column output blocks per wave
+  constexpr int KS = D / 4;    // MFMA steps
+  constexpr int SP = 2;        // steps per B load (16 bytes per lane and block)
+  __shared__ __attribute__((aligned(16))) float cs[32][D + 4];   // c~ of the tile's clusters
+  __shared__ __attribute__((aligned(16))) bf16 gs[32][D + 8];    // bf16(-2 g) of the tile's clusters
+  __shared__ double red[2][32][2];     // per column half: |g|^2 and residual sums of each cluster
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int cg = w & 1, ch = w >> 1;
+  const int bh = blockIdx.y, t0 = blockIdx.x * 32, v0 = t0 + 16 * cg;
+  const int k0 = lg * KS;
+  // live32 bit c: cluster t0 + c has keys (or is an initial centroid); write32 bit c: its
+  // outputs are written (live, or a padding row)
+  const int vl = t0 + (lane & 31);
+  const bool lv = vl < nk && (init_mode || counts[(size_t)bh * nk + vl] > 0);
+  const uint32_t live32 = (uint32_t)__ballot(lv && lane < 32);
+  const uint32_t write32 = (uint32_t)__ballot((lv || vl >= nk) && lane < 32);
+  // out[b] = A (a[s], step s) x B (row 16 (NBW ch + b) + l % 16 of M, columns k0 + s)
+  auto gemm = [&](const double (&a)[KS], const double* __restrict__ M, f64x4 (&out)[NBW]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int b = 0; b < NBW; ++b) out[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const double* mrow = M + (size_t)bh * D * D + (size_t)(16 * NBW * ch + li) * D + k0;
+    // B in chunks of SP steps (16 bytes per lane and block), kAhead chunks in flight; scheduling
+    // fences keep each chunk's loads together and ahead of the MFMAs
+    constexpr int kAhead = 3, NC = KS / SP;
+    f64x2 bq[kAhead + 1][NBW];
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) acc[c][d] = 0.0;
-    for (int k0 = 0; k0 < D; k0 += 8) {
-      double r[8][DPT];
+    for (int c = 0; c < kAhead; ++c)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int b = 0; b < NBW; ++b) bq[c][b] = *reinterpret_cast<const f64x2*>(mrow + (size_t)16 * b * D + SP * c);
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) r[u][d] = M[(size_t)(k0 + u) * D + i0 + d];
+    for (int c = 0; c < NC; ++c) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + kAhead < NC) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        double x[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = rhs(c0 + c, k0 + u);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int d = 0; d < DPT; ++d) acc[c][d] = fma(r[u][d], x[c], acc[c][d]);
+        for (int b = 0; b < NBW; ++b)
+          bq[(c + kAhead) % (kAhead + 1)][b] = *reinterpret_cast<const f64x2*>(mrow + (size_t)16 * b * D + SP * (c + kAhead));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ss = 0; ss < SP; ++ss)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+          out[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[SP * c + ss], bq[c % (kAhead + 1)][b][ss], out[b], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
+  double a[KS];
   if (init_mode) {
-    for (int e = tid; e < 32 * D; e += 256) {
-      const int vv = e / D, k = e % D;
-      cs[vv][k] = ctil[((size_t)bh * nkp + v0 + vv) * D + k];
+    const float* src = ctil + ((size_t)bh * nkp + v0 + li) * D + k0;
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + s);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[s + u] = (double)x[u];
     }
-    __syncthreads();
   } else {
-    for (int e = tid; e < 32 * D; e += 256) {
-      const int vv = e / D, k = e % D;
-      const int v = v0 + vv;
-      ms[vv][k] = v < nk ? cmean[((size_t)bh * nkp + v) * D + k] : 0.0;
+    // first product: c~ = R^T m, i.e. c~[v][i] = sum_k m[v][k] Rt[i][k]
+    const bool real = v0 + li < nk;
+    const double* src = cmean + ((size_t)bh * nkp + v0 + li) * D + k0;
+#pragma unroll
+    for (int s = 0; s < KS; s += 2) {
+      const f64x2 x = real ? *reinterpret_cast<const f64x2*>(src + s) : f64x2{0.0, 0.0};
+      a[s] = x[0];
+      a[s + 1] = x[1];
     }
-    __syncthreads();
-    double t[4][DPT];   // (R^T m)_i = sum_k R[k][i] m_k
-    matvec(R64 + (size_t)bh * D * D, [&](int vv, int k) { return ms[vv][k]; }, t);
+    f64x4 t[NBW];
+    gemm(a, Rt64, t);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int b = 0; b < NBW; ++b)
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) cs[c0 + c][i0 + d] = (float)t[c][d];
+      for (int r = 0; r < 4; ++r) cs[16 * cg + 4 * r + lg][16 * (NBW * ch + b) + li] = (float)t[b][r];
     __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&cs[16 * cg + li][k0 + s]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[s + u] = (double)x[u];
+    }
+    // c~ of the live clusters to ctil, 16 bytes per store (piece p: row p / (D / 4), columns
+    // 4 (p % (D / 4)) .. + 3)
+#pragma unroll
+    for (int q = 0; q < (32 * D / 4) / 256; ++q) {
+      const int p = tid + 256 * q, row = p / (D / 4), c4 = 4 * (p % (D / 4));
+      if ((live32 >> row) & 1)
+        *reinterpret_cast<f32x4*>(ctil + ((size_t)bh * nkp + t0 + row) * D + c4) =
+            *reinterpret_cast<const f32x4*>(&cs[row][c4]);
+    }
   }
-  {
-    double g[4][DPT];   // Rt[k][i] = R[i][k]: (R c~)_i
-    matvec(Rt64 + (size_t)bh * D * D, [&](int vv, int k) { return (double)cs[vv][k]; }, g);
-    __syncthreads();  // ms is reused for g
+  // |c~|^2 of cluster v0 + li: this lane's KS columns in order, then the four column ranges
+  double cc = 0.0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int vv = c0 + c, v = v0 + vv;
+  for (int s = 0; s < KS; ++s) cc += a[s] * a[s];
+  cc += __shfl_xor(cc, 16);
+  cc += __shfl_xor(cc, 32);
+  // second product: g = R c~, i.e. g[v][i] = sum_k c~[v][k] R[i][k]
+  f64x4 g[NBW];
+  gemm(a, R64, g);
+  // bf16(-2 g) into LDS; the per-cluster |g|^2 and residual sums of this column half: columns
+  // in block order per lane, then the 16 lanes of the cluster's group by a fixed butterfly
+  double gn[4] = {0.0, 0.0, 0.0, 0.0}, fr[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) {
-        const int i = i0 + d;
-        ms[vv][i] = g[c][d];
-        if (live_s[vv]) {
-          ctil[((size_t)bh * nkp + v) * D + i] = cs[vv][i];
-          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)(-2.0f * (float)(bf16)(float)g[c][d]);
-        } else if (v >= nk) {
-          gneg2[(size_t)bh * nkp * D + frag_offset(v, i, D)] = (bf16)0.0f;
-        }
-      }
+  for (int b = 0; b < NBW; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 16 * cg + 4 * r + lg, i = 16 * (NBW * ch + b) + li;
+      const double gv = g[b][r];
+      const bf16 gb = (bf16)(float)gv;
+      const double df = gv - (double)(float)gb;
+      gn[r] += gv * gv;
+      fr[r] += df * df;
+      gs[c][i] = t0 + c < nk ? (bf16)(-2.0f * (float)gb) : (bf16)0.0f;
     }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      gn[r] += __shfl_xor(gn[r], o);
+      fr[r] += __shfl_xor(fr[r], o);
+    }
+  if (li < 4) {   // lane (li = r, lg) holds cluster 4 r + lg's sums
+    double gsel = gn[0], fsel = fr[0];
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      gsel = li == r ? gn[r] : gsel;
+      fsel = li == r ? fr[r] : fsel;
+    }
+    red[ch][16 * cg + 4 * li + lg][0] = gsel;
+    red[ch][16 * cg + 4 * li + lg][1] = fsel;
   }
   __syncthreads();
-  // per cluster |c~|^2, |g| and the bf16 rounding residual of g: 8 threads per cluster, each
-  // summing D/8 consecutive columns in order, then a fixed butterfly
-  {
-    const int vv = tid >> 3, part = tid & 7;
-    double cc = 0.0, gn = 0.0, f = 0.0;
-    for (int k = part * (D / 8); k < (part + 1) * (D / 8); ++k) {
-      const double c = cs[vv][k], g = ms[vv][k];
-      const double df = g - (double)(float)(bf16)(float)g;
-      cc += c * c; gn += g * g; f += df * df;
-    }
+  // gneg2 of the written rows: the tile's D / 16 fragments (1 KB each, contiguous), 16 bytes
+  // per store: lane l of fragment kc holds row l % 32, columns 16 kc + 8 (l / 32) .. + 7
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      cc += __shfl_xor(cc, o);
-      gn += __shfl_xor(gn, o);
-      f += __shfl_xor(f, o);
-    }
-    const int v = v0 + vv;
-    if (part == 0) {
-      if (v >= nk) {
-        cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
-        ccv[(size_t)bh * nkp + v] = INFINITY;
-      } else if (live_s[vv]) {
-        const float up = 1.0f + 1.0f / 1048576.0f;
-        const float4 ci = make_float4((float)cc, (float)sqrt(gn) * up, (float)sqrt(f) * up, 0.0f);
-        cinfo[(size_t)bh * nkp + v] = ci;
-        ccv[(size_t)bh * nkp + v] = ci.x;
-      }
+  for (int q = 0; q < (32 * D / 8) / 256; ++q) {
+    const int p = tid + 256 * q, kc = p >> 6, l = p & 63, row = l & 31, col = 16 * kc + 8 * (l >> 5);
+    if ((write32 >> row) & 1)
+      *reinterpret_cast<bf16x8*>(gneg2 + (size_t)bh * nkp * D + frag_lane(blockIdx.x, kc, l, D)) =
+          *reinterpret_cast<const bf16x8*>(&gs[row][col]);
+  }
+  // lane c < 16 of the first column half writes cluster v0 + c (column halves added in order)
+  if (ch == 0 && lg == 0) {
+    const int v = v0 + li, c = 16 * cg + li;
+    const double gnc = red[0][c][0] + red[1][c][0];
+    const double frc = red[0][c][1] + red[1][c][1];
+    if (v >= nk) {
+      cinfo[(size_t)bh * nkp + v] = make_float4(INFINITY, 0.0f, 0.0f, 0.0f);
+      ccv[(size_t)bh * nkp + v] = INFINITY;
+    } else if ((live32 >> c) & 1) {
+      const float up = 1.0f + 1.0f / 1048576.0f;
+      const float4 ci = make_float4((float)cc, (float)sqrt(gnc) * up, (float)sqrt(frc) * up, 0.0f);
+      cinfo[(size_t)bh * nkp + v] = ci;
+      ccv[(size_t)bh * nkp + v] = ci.x;
     }
   }
 }
