@@ -327,17 +327,27 @@ __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int ct = w % NT, par = w / NT;
   const int bh = blockIdx.y, k0 = blockIdx.x * kTfKeys;
-  // the keys: 16-byte pieces, consecutive threads on consecutive pieces of a row
-  for (int e = tid; e < kTfKeys * (D / 8); e += 256) {
-    const int r = e / (D / 8), c = e % (D / 8);
-    bf16x8 x;
-    if (k0 + r < N) {
-      x = load_bf16x8(K + ((size_t)bh * N + k0 + r) * D + 8 * c);
-    } else {
+  // the keys: 16-byte pieces, consecutive threads on consecutive pieces of a row; every load
+  // of a thread is issued before the first is written to LDS
+  constexpr int PPT = kTfKeys * (D / 8) / 256;   // pieces per thread
+  static_assert(PPT * 256 == kTfKeys * (D / 8), "key pieces");
+  {
+    bf16x8 x[PPT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (bf16)0.0f;
+    for (int j = 0; j < PPT; ++j) {
+      const int e = tid + 256 * j, r = e / (D / 8), c = e % (D / 8);
+      if (k0 + r < N) {
+        x[j] = load_bf16x8(K + ((size_t)bh * N + k0 + r) * D + 8 * c);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[j][i] = (bf16)0.0f;
+      }
     }
-    *reinterpret_cast<bf16x8*>(&ks[r * KP + 8 * c]) = x;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int e = tid + 256 * j, r = e / (D / 8), c = e % (D / 8);
+      *reinterpret_cast<bf16x8*>(&ks[r * KP + 8 * c]) = x[j];
+    }
   }
   const bf16* rs = Rsp + (size_t)bh * 3 * D * D + (size_t)(32 * ct + l32) * D + 8 * h;
   bf16x8 bfr[3][KC];
