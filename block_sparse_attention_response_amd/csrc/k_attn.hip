@@ -150,33 +150,53 @@ __global__ __launch_bounds__(128) void k_pack_kv(const bf16* __restrict__ K, con
       *reinterpret_cast<bf16x8*>(Vph + (size_t)Gcap * 8 * D + e * 8) = z;
     }
   }
+  // Branch-free copies (a branch around each access makes the compiler wait for every
+  // earlier load and store before the next one): member indices are clamped to the cluster,
+  // padding slots are zeroed by a select, and the stores of slots past the cluster's groups
+  // go to the head's all-zero filler group (writing zeros there changes nothing).
+  const bf16* Kz = Kph + (size_t)Gcap * 8 * D;
   Kph += (size_t)g0 * 8 * D;
   Vph += (size_t)g0 * 8 * D;
-  for (int e = tid; e < ng * 8 * NS; e += 128) {
-    const int slot = e / NS, sg = e % NS;
-    bf16x8 val;
-    if (slot < n) {
-      val = load_bf16x8(Kh + (size_t)pm[slot] * D + sg * 8);
-    } else {
+  bf16x8 zero8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) val[i] = (bf16)0.0f;
+  for (int i = 0; i < 8; ++i) zero8[i] = (bf16)0.0f;
+  // keys: thread t copies the 16-byte piece sg = t % NS of key slots t / NS + SPI u, U slots in
+  // flight (their member indices, then their rows, then the stores)
+  {
+    constexpr int SPI = 128 / NS, U = 8;
+    const int sg = tid % NS, s0 = tid / NS;
+    const uint32_t in_group = (uint32_t)((sg >> 1) * 128 + (sg & 1) * 8);
+    for (int base = 0; base < ng * 8; base += SPI * U) {
+      int src[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) src[u] = pm[min(base + s0 + SPI * u, n - 1)];
+      bf16x8 val[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bf16x8 x = load_bf16x8(Kh + (size_t)src[u] * D + sg * 8);
+        val[u] = base + s0 + SPI * u < n ? x : zero8;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int slot = base + s0 + SPI * u, j = slot >> 3, sl = slot & 7;
+        bf16* dst = slot < ng * 8 ? Kph + (size_t)j * 8 * D : const_cast<bf16*>(Kz);
+        *reinterpret_cast<bf16x8*>(dst + in_group + sl * 16) = val[u];
+      }
     }
-    const int j = slot >> 3, s = slot & 7;
-    *reinterpret_cast<bf16x8*>(Kph + (size_t)j * 8 * D + (sg >> 1) * 128 + s * 16 + (sg & 1) * 8) = val;
   }
+  // values: thread t transposes the 8 x 8 block (group j, columns 8 sg .. + 7): 8 member rows
+  // in, 8 rows of V^T out
   float amax = 0.0f;
   for (int e = tid; e < ng * NS; e += 128) {
     const int j = e / NS, sg = e % NS;
+    int src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) src[i] = pm[min(8 * j + i, n - 1)];
     bf16x8 rows[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int slot = 8 * j + i;
-      if (slot < n) {
-        rows[i] = load_bf16x8(Vh + (size_t)pm[slot] * D + sg * 8);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) rows[i][t] = (bf16)0.0f;
-      }
+      const bf16x8 x = load_bf16x8(Vh + (size_t)src[i] * D + sg * 8);
+      rows[i] = 8 * j + i < n ? x : zero8;
     }
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
