@@ -545,10 +545,31 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     nq = min(64, N - p0);
   }
   const size_t hrow = (size_t)bh * N;
+  // the head's largest |value| (the partial states' unit), loaded early: it is used at the end
+  const float vmax_h = fused ? 0.0f : vmax[bh];
   // query index of position i < nq of the item
   auto query = [&](int i) __attribute__((always_inline)) {
     return qperm ? min(max(qperm[hrow + p0 + i], 0), N - 1) : p0 + i;
   };
+  // Q^T fragments of query halves 0 and 1 in registers (qrow: this lane's query of each
+  // half, -1 past the item's queries), issued before the item's tile range is read
+  bf16x8 qf[2][KC];
+  int qrow[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) qrow[h2] = 32 * h2 + l32 < nq ? query(32 * h2 + l32) : -1;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (qrow[h2] >= 0) {
+        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow[h2]) * D + kc * 16 + 8 * h);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[h2][kc][i] = (bf16)0.0f;
+      }
+    }
+  }
+
   const int t0 = tbase[(size_t)prow * kRanges + rr];
   const int nt = tbase[(size_t)prow * kRanges + (fused ? kRanges : rr + 1)] - t0;
   if (nt <= 0) {
@@ -611,25 +632,6 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
       for (int dt = 0; dt < DT; ++dt) vf[c * DT + dt] = *reinterpret_cast<const bf16x8*>(src + dt * 512);
     }
   };
-
-  // Q^T fragments of query halves 0 and 1 in registers (qrow: this lane's query of each
-  // half, -1 past the item's queries)
-  bf16x8 qf[2][KC];
-  int qrow[2];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) qrow[h2] = 32 * h2 + l32 < nq ? query(32 * h2 + l32) : -1;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (qrow[h2] >= 0) {
-        qf[h2][kc] = load_bf16x8(Q + (hrow + qrow[h2]) * D + kc * 16 + 8 * h);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[h2][kc][i] = (bf16)0.0f;
-      }
-    }
-  }
 
   f32x16 oacc[2][DT];
 #pragma unroll
@@ -942,7 +944,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   }
   // partial state: O_r = O^T / lb stored as fp16 in units of the head's value unit (so
   // |stored| <= 1), and (m, l) in float
-  const float unit = value_unit(vmax[bh]);
+  const float unit = value_unit(vmax_h);
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     const float l = lsum[h2] + __shfl_xor(lsum[h2], 32);
