@@ -1031,22 +1031,34 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
-#pragma unroll 4
-  for (int r = rg; r < n; r += RPI) {
-    const T* src = Kh + (size_t)pm[r] * D + c8;
-    float x[8];
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 q = load_bf16x8(reinterpret_cast<const bf16*>(src));
+  // rows rg, rg + RPI, ... in order, U at a time: their member indices, then their values,
+  // all in flight together (branch-free: indices clamped to the cluster, rows past it add 0)
+  constexpr int U = 8;
+  for (int r0 = rg; r0 < n; r0 += U * RPI) {
+    int src[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)q[i];
-    } else {
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(src + 4);
+    for (int u = 0; u < U; ++u) src[u] = pm[min(r0 + u * RPI, n - 1)];
+    float x[U][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { x[i] = q0[i]; x[4 + i] = q1[i]; }
+    for (int u = 0; u < U; ++u) {
+      const T* row = Kh + (size_t)src[u] * D + c8;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 q = load_bf16x8(reinterpret_cast<const bf16*>(row));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = (float)q[i];
+      } else {
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(row);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[u][i] = q0[i]; x[u][4 + i] = q1[i]; }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += (double)x[i];
+    for (int u = 0; u < U; ++u) {
+      const bool in = r0 + u * RPI < n;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += in ? (double)x[u][i] : 0.0;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[rg][c8 + i] = acc[i];
