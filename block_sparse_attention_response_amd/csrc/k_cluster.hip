@@ -583,62 +583,15 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     cvv[i] = v < nkp ? ccv[(size_t)bh * nkp + v] : 0.0f;
   }
   if (tid == 0) npairs = 0;
-
-  // B fragments of this wave's 64 keys (two 32-key tiles)
-  bf16x8 bfr[2][NF];
-  float E[2];
-  const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
-  const float CC = __uint_as_float(hmax[4 * bh + 2]);
-  // the keys of slots 64 w + l32 and 64 w + 32 + l32 (-1 past N)
-  const int keyi[2] = {__shfl(kslot, l32), __shfl(kslot, 32 + l32)};
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int pos = k0 + 64 * w + 32 * kt + l32;
-    const int key = pos < N ? keyi[kt] : 0;
-#pragma unroll
-    for (int kc = 0; kc < NF; ++kc) {
-      if (pos < N) {
-        const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
-        if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
-        else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = (bf16)0.0f;
-      }
-    }
-    E[kt] = 0.0f;
-    if (pos < N) {
-      const float4 kn = knorm[(size_t)bh * N + key];
-      // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
-      // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
-      E[kt] = 2.0f * (kn.y * G + kn.x * F + kn.y * F) + (1.0f / 16384.0f) * (2.0f * kn.x * G + CC + kn.z * kn.z);
-      E[kt] *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
-    }
-  }
-  // Running minimum and candidate lists.  From the second step on the keys are visited in the
-  // previous step's label order, so the workgroup's keys share a few consecutive previous
-  // clusters; the screen starts at the 32-cluster tile holding the previous cluster of the
-  // workgroup's first key (wlab), which makes the running minimum tight from the first tile
-  // on.  The candidate set does not depend on the tile order: every score within the final
-  // window is recorded whatever its turn (the window only shrinks).
-  float mr[2] = {INFINITY, INFINITY};
-  int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
-  bool ovf[2] = {false, false};
   int t0 = 0;
   if (wlab) t0 = __builtin_amdgcn_readfirstlane(min(max(wlab[(size_t)bh * gridDim.x + blockIdx.x], 0), nkp - 1) >> 5);
-#pragma unroll
-  for (int i = 0; i < MV; ++i)
-    if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
-  kidx[tid] = kslot;
-  lovf[tid] = 0;
-  best[tid] = ~0ull;
-  __syncthreads();
 
   // The 32-cluster tiles of the screen operand (fragment-major: 1 KB per fragment) pass through
   // a three-slot LDS ring shared by the workgroup's waves: the tile of turn i sits in slot
   // i % 3, each wave copies NF / 4 of its fragments two turns ahead, and one barrier per turn
   // both publishes a tile and frees the slot the next copy refills.  Every fragment crosses
-  // the memory path once per workgroup instead of once per wave.
+  // the memory path once per workgroup instead of once per wave.  The first three turns are
+  // copied before the keys are loaded, so that the two overlap.
   // tile of turn i (rotated start)
   auto tile_of = [&](int i) { const int j = t0 + i; return j >= nT ? j - nT : j; };
   constexpr int FPW = NF / kAsgWaves;   // fragments each wave copies per turn
@@ -654,6 +607,62 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
       dma16(src + kc * 1024, (uint32_t)lane * 16u, dst + (uint32_t)kc * 1024u);
     }
   };
+  copy_turn(0);
+  if (nT > 1) copy_turn(1);
+  if (nT > 2) copy_turn(2);
+
+  // B fragments of this wave's 64 keys (two 32-key tiles) and their bounds: every load in
+  // flight at once (branch-free: slots past N load key 0 and take zeros)
+  bf16x8 bfr[2][NF];
+  float E[2];
+  const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
+  const float CC = __uint_as_float(hmax[4 * bh + 2]);
+  // the keys of slots 64 w + l32 and 64 w + 32 + l32 (-1 past N)
+  const int keyi[2] = {__shfl(kslot, l32), __shfl(kslot, 32 + l32)};
+  float4 kn[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int pos = k0 + 64 * w + 32 * kt + l32;
+    const int key = pos < N ? keyi[kt] : 0;
+    kn[kt] = knorm[(size_t)bh * N + key];
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc) {
+      const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
+      if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
+      else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const bool real = k0 + 64 * w + 32 * kt + l32 < N;
+#pragma unroll
+    for (int kc = 0; kc < NF; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = real ? bfr[kt][kc][i] : (bf16)0.0f;
+    // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
+    // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
+    const float4 k4 = kn[kt];
+    float e = 2.0f * (k4.y * G + k4.x * F + k4.y * F) + (1.0f / 16384.0f) * (2.0f * k4.x * G + CC + k4.z * k4.z);
+    e *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
+    E[kt] = real ? e : 0.0f;
+  }
+  // Running minimum and candidate lists.  From the second step on the keys are visited in the
+  // previous step's label order, so the workgroup's keys share a few consecutive previous
+  // clusters; the screen starts at the 32-cluster tile holding the previous cluster of the
+  // workgroup's first key (wlab), which makes the running minimum tight from the first tile
+  // on.  The candidate set does not depend on the tile order: every score within the final
+  // window is recorded whatever its turn (the window only shrinks).
+  float mr[2] = {INFINITY, INFINITY};
+  int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
+  bool ovf[2] = {false, false};
+#pragma unroll
+  for (int i = 0; i < MV; ++i)
+    if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
+  kidx[tid] = kslot;
+  lovf[tid] = 0;
+  best[tid] = ~0ull;
+  __syncthreads();
+
   // the screen products of turn i's tile into acc
   auto products = [&](int i, const bf16x8 (&a)[NF], f32x16 (&acc)[2]) {
     const int t = tile_of(i);
@@ -752,9 +761,6 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     }
     candidates(i, pi, tm);
   };
-  copy_turn(0);
-  if (nT > 1) copy_turn(1);
-  if (nT > 2) copy_turn(2);
   if (nT > 2) wait_copies<FPW>(); else wait_copies<0>();
   __syncthreads();
   read_turn(0, fa);
