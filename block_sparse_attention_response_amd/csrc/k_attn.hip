@@ -232,12 +232,34 @@ __global__ __launch_bounds__(1024) void k_range_assign(const int32_t* __restrict
   __syncthreads();
   const int32_t* L = list + (size_t)bh * NQ * nk;
   const int32_t* C = count + (size_t)bh * NQ;
-  for (int e = tid; e < NQ * 64; e += 1024) {
-    const int u = e >> 6;
-    const int cnt = min(max(C[u], 0), nk);
-    for (int i = e & 63; i < cnt; i += 64) {
-      const int v = L[(size_t)u * nk + i];
-      if (v >= 0 && v < nk) atomicAdd(&freq[v], 1);
+  // wave w counts blocks w, w + 16, ...: kB blocks at a time, their counts and the first 128
+  // entries of each loaded together (entries past a block's count are masked, not skipped);
+  // the rare blocks with more than 128 entries finish in a second loop
+  {
+    constexpr int kB = 8, W = 1024 / 64;
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int u0 = wv; u0 < NQ; u0 += W * kB) {
+      int cnt[kB], v0[kB], v1[kB];
+      // lane b loads the count of block u0 + W b (one load for the wave)
+      const int cl = C[min(u0 + W * (lane & (kB - 1)), NQ - 1)];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int u = min(u0 + W * b, NQ - 1);
+        const int cu = __builtin_amdgcn_readlane(cl, b);
+        cnt[b] = u0 + W * b < NQ ? min(max(cu, 0), nk) : 0;
+        v0[b] = L[(size_t)u * nk + min(lane, nk - 1)];
+        v1[b] = L[(size_t)u * nk + min(64 + lane, nk - 1)];
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (lane < cnt[b] && v0[b] >= 0 && v0[b] < nk) atomicAdd(&freq[v0[b]], 1);
+        if (64 + lane < cnt[b] && v1[b] >= 0 && v1[b] < nk) atomicAdd(&freq[v1[b]], 1);
+        const int u = u0 + W * b;
+        for (int i = 128 + lane; i < cnt[b]; i += 64) {
+          const int v = L[(size_t)u * nk + i];
+          if (v >= 0 && v < nk) atomicAdd(&freq[v], 1);
+        }
+      }
     }
   }
   __syncthreads();

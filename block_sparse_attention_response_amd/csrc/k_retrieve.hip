@@ -438,14 +438,23 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ W, con
   uint64_t key[EPL], ms[EPL];
   int ne = 0;
   uint64_t msum = 0;
+  // every count and weight of the row loaded at once (branch-free: indices clamped to the
+  // row, entries past it or of empty clusters masked afterwards)
+  int cn[EPL];
+  float wr[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int i = min(lane + 64 * j, nk - 1);
+    cn[j] = counts[(size_t)bh * nk + i];
+    wr[j] = Wr[i];
+  }
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int i = lane + 64 * j;
     uint32_t hi = 0xFFFFFFFFu;
     uint64_t m = 0;
-    if (i < nk && counts[(size_t)bh * nk + i] > 0) {
-      float wv = Wr[i];
-      wv = (wv > 0.0f) ? wv : 0.0f;   // also maps NaN to 0
+    if (i < nk && cn[j] > 0) {
+      const float wv = (wr[j] > 0.0f) ? wr[j] : 0.0f;   // also maps NaN to 0
       hi = 0x7F800000u - __float_as_uint(wv);
       m = (uint64_t)((double)fminf(wv, 64.0f) * 72057594037927936.0);   // 2^56
       ++ne;
