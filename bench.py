@@ -213,6 +213,64 @@ def copy_calibration(gib):
                       "GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def attn_clocks(args):
+    """The attention kernel's per-item clock stamps (libpark_clocks.so, the build compiled with
+    PARK_ATTN_CLOCKS; record layout in include/park_clocks.h) on the workload's inputs: where an
+    item's time goes (prologue, tiles, epilogue, the gap to the workgroup's next item) and the
+    cycles per 32-key tile.  Every call runs through the clocked build; prints one JSON line."""
+    import ctypes
+    import numpy as np
+    import park_synth
+    import torch
+    import block_sparse_attention_response_amd as park
+    clocked = os.path.join(os.path.dirname(park.LIB_PATH), "libpark_clocks.so")
+    if not os.path.exists(clocked):
+        raise SystemExit(f"{clocked} is missing: build it with __graft_entry__.build()")
+    park.LIB_PATH, park._lib = clocked, None
+    L = park.lib()
+    cfg = park_synth.WORKLOADS[args.workload]
+    log(f"clock stamps: generating {cfg.name}")
+    Q, K, V = park_synth.generate(cfg, seed=0, workers=16)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (Q, K, V))
+    del Q, K, V
+    B, H, N, d = q.shape
+    cl = park.park_cluster_keys(q, k, cfg.n_clusters, cfg.iters)
+    rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], cfg.top_p, cfg.top_k, scores=False)
+    ev = park.HipEvents()
+    times = []
+    for _ in range(3):
+        park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
+                                    events=ev.handles)
+        times.append(ev.elapsed_ms())
+    torch.cuda.synchronize()
+    items = B * H * ((N + 63) // 64) * 4
+    L.park_attn_clock_words.restype = ctypes.c_size_t
+    words = min(5 * items, int(L.park_attn_clock_words()))
+    buf = np.zeros(words, np.uint64)
+    L.park_attn_clock_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    if L.park_attn_clock_read(buf.ctypes.data, words) != 0:
+        raise RuntimeError("park_attn_clock_read failed")
+    c = buf.reshape(-1, 5).astype(np.int64)
+    c = c[c[:, 0] > 0]                     # items with tiles (the last call's stamps)
+    wg, nt = c[:, 4] >> 32, c[:, 4] & 0xFFFFFFFF
+    pro, til, epi = c[:, 1] - c[:, 0], c[:, 2] - c[:, 1], c[:, 3] - c[:, 2]
+    o = np.lexsort((c[:, 0], wg))          # a workgroup's items in time order (one XCD's clock)
+    same = wg[o][1:] == wg[o][:-1]
+    gap = (c[o, 0][1:] - c[o, 3][:-1])[same]
+    total = pro.sum() + til.sum() + epi.sum() + gap.sum()
+    many = nt >= 8
+    out = {"mode": "attn_clocks", "workload": cfg.name, "library": os.path.basename(clocked),
+           "kernel_ms": round(float(np.median(times)), 3), "items": int(len(c)), "tiles": int(nt.sum()),
+           "share": {"prologue": round(float(pro.sum() / total), 4), "tiles": round(float(til.sum() / total), 4),
+                     "epilogue": round(float(epi.sum() / total), 4), "gap": round(float(gap.sum() / total), 4)},
+           "cycles_median": {"prologue": float(np.median(pro)), "epilogue": float(np.median(epi)),
+                             "gap": float(np.median(gap)) if len(gap) else None},
+           "cycles_per_tile": {"median": round(float(np.median(til[many] / nt[many])), 1),
+                               "mean": round(float(til[many].sum() / nt[many].sum()), 1)}}
+    print(json.dumps(out), flush=True)
+
+
 def clustered_leg(args, park, torch, np, cfg, q, k, v, top_p, top_k, stream, lse_dense):
     """PARK's own configuration: query blocks by Euclidean k-means of the queries (NQ blocks,
     the same k-means steps as the keys), timed like the main leg on the same inputs."""
@@ -472,9 +530,15 @@ def main():
                     help="clustered: time only the clustered-query-block step (for kernel traces of it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
+    ap.add_argument("--attn-clocks", action="store_true",
+                    help="only run the attention kernel's clock-stamped build (libpark_clocks.so) and "
+                         "print where its items' time goes, then exit")
     args = ap.parse_args()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.attn_clocks:
+        attn_clocks(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (heads would be "

@@ -76,6 +76,19 @@ __device__ __forceinline__ int selected_key(int p, const int* pre, int cnt, cons
 // One wave per item computes a partial softmax state over its tiles (k_attn_items) and a last
 // kernel merges the kRanges partial states of every query (k_attn_merge).
 constexpr int kRanges = 4;
+
+// Clock-stamped measurement build (compiled with PARK_ATTN_CLOCKS into a separate library; the
+// product build has none of it): per 64-token-block item, the shader clock (s_memtime) at the
+// item's start, before its tile loop, after it and after its stores, and (wave, tiles), five
+// words per item, written by lane 0.  The stamps add four scalar reads and one store per item
+// and change no other instruction.
+#ifdef PARK_ATTN_CLOCKS
+constexpr size_t kAttnClockWords = size_t(1) << 21;
+__device__ unsigned long long attn_clock[kAttnClockWords];
+#define PARK_ATTN_STAMP(x) const unsigned long long x = __builtin_amdgcn_s_memtime()
+#else
+#define PARK_ATTN_STAMP(x) do { } while (0)
+#endif
 static_assert(8 % kRanges == 0, "range r runs on the XCDs x with x % kRanges == r");
 
 // Step 1: gstart[v] = first group of cluster v (exclusive scan of ceil(n_v / 8)); a cluster
@@ -592,6 +605,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
     }
   }
 
+  PARK_ATTN_STAMP(clk_start);
   const int t0 = tbase[(size_t)prow * kRanges + rr];
   const int nt = tbase[(size_t)prow * kRanges + (fused ? kRanges : rr + 1)] - t0;
   if (nt <= 0) {
@@ -928,6 +942,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   to_bf16(pb);
   weight_sums(pb, lb, 0);
   weight_sums(pb, lb, 1);
+  PARK_ATTN_STAMP(clk_loop);
   int t = 0;
   for (; t + 2 < nt; t += 2) {
     step(P0{}, t);
@@ -939,6 +954,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   } else {
     last(P0{}, t);
   }
+  PARK_ATTN_STAMP(clk_tiles);
 
   if constexpr (FUSED) {
     // the whole row: O = O^T / lb in bf16, lse = ln 2 (m + log2 l) (what the merge gives for
@@ -986,6 +1002,17 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
       if (h == 0) ML[(hrow + qrow[h2]) * kRanges + rr] = make_float2(m[h2], l);
     }
   }
+#ifdef PARK_ATTN_CLOCKS
+  PARK_ATTN_STAMP(clk_end);
+  if (lane == 0 && (size_t)item * 5 + 5 <= kAttnClockWords) {
+    unsigned long long* o = attn_clock + (size_t)item * 5;
+    o[0] = clk_start;
+    o[1] = clk_loop;
+    o[2] = clk_tiles;
+    o[3] = clk_end;
+    o[4] = ((unsigned long long)blockIdx.x << 32) | (unsigned)nt;
+  }
+#endif
 }
 
 // Persistent waves, one per workgroup: wave b starts with item b and then takes items of its
@@ -1598,3 +1625,14 @@ hipError_t launch_logmass(const Shape& s, const void* Q, const void* K, const in
 }
 
 }  // namespace park
+
+#ifdef PARK_ATTN_CLOCKS
+extern "C" __attribute__((visibility("default"))) size_t park_attn_clock_words(void) {
+  return park::kAttnClockWords;
+}
+extern "C" __attribute__((visibility("default"))) int park_attn_clock_read(void* host, size_t words) {
+  if (!host || words > park::kAttnClockWords) return PARK_ERR_INVALID;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(park::attn_clock), words * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? PARK_OK : PARK_ERR_HIP;
+}
+#endif

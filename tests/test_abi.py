@@ -41,6 +41,27 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_clock_build_exports_only_its_declared_symbols(lib):
+    """libpark_clocks.so exports the measurement entry points of include/park_clocks.h beside
+    every entry point of park.h; the product library exports none of them."""
+    clocks = os.path.join(ROOT, "block_sparse_attention_response_amd", "libpark_clocks.so")
+    if not os.path.exists(clocks):
+        pytest.fail("libpark_clocks.so is not built (run __graft_entry__.build())")
+    text = open(os.path.join(ROOT, "include", "park_clocks.h")).read()
+    names = re.findall(r"PARK_CLOCKS_API\s+[\w\s\*]+?\b(park_\w+)\s*\(", text)
+    assert sorted(names) == ["park_attn_clock_read", "park_attn_clock_words"]
+    L = ctypes.CDLL(clocks)
+    for n in names + declared_functions():
+        assert hasattr(L, n), n
+    for n in names:
+        assert not hasattr(lib, n), n
+    L.park_attn_clock_words.restype = ctypes.c_size_t
+    assert L.park_attn_clock_words() == 1 << 21
+    L.park_attn_clock_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert L.park_attn_clock_read(None, 5) == INVALID                      # no host buffer
+    assert L.park_attn_clock_read(FAKE, (1 << 21) + 1) == INVALID          # beyond the record
+
+
 def test_version_and_status_strings(lib):
     assert lib.park_abi_version() == 1
     names = [lib.park_status_string(i).decode() for i in range(6)]
