@@ -474,29 +474,43 @@ __global__ __launch_bounds__(256) void k_plan_fill(const int32_t* __restrict__ l
   int run[kRanges];   // groups placed so far in each range
 #pragma unroll
   for (int j = 0; j < kRanges; ++j) run[j] = 0;
-  for (int i0 = 0; i0 < cnt; i0 += 64) {
-    const int i = i0 + lane;
-    int n = 0, g0 = 0, r = 0;
-    if (i < cnt) {
-      const int v = lst[i];
-      if (v >= 0 && v < nk) { n = off[v + 1] - off[v]; g0 = gs[v]; r = rg[v]; }
+  // two chunks of 64 entries per pass, all of their loads in flight together (branch-free:
+  // indices clamped, entries past the count or out of range count as empty)
+  for (int i00 = 0; i00 < cnt; i00 += 128) {
+    int vv[2], nn[2], gg[2], rr[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) vv[k] = lst[min(i00 + 64 * k + lane, nk - 1)];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool ok = i00 + 64 * k + lane < cnt && vv[k] >= 0 && vv[k] < nk;
+      const int v = ok ? vv[k] : 0;
+      const int o0 = off[v], o1 = off[v + 1];
+      gg[k] = gs[v];
+      rr[k] = ok ? rg[v] : 0;
+      nn[k] = ok ? o1 - o0 : 0;
     }
-    const int ng = (n + 7) >> 3;
-    int pos = 0;
 #pragma unroll
-    for (int j = 0; j < kRanges; ++j) {
-      const int x = r == j ? ng : 0;
-      int incl = x;
+    for (int k = 0; k < 2; ++k) {
+      const int i0 = i00 + 64 * k;
+      if (i0 >= cnt) break;
+      const int n = nn[k], g0 = gg[k], r = rr[k];
+      const int ng = (n + 7) >> 3;
+      int pos = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
+      for (int j = 0; j < kRanges; ++j) {
+        const int x = r == j ? ng : 0;
+        int incl = x;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        if (r == j) pos = run[j] + incl - x;
+        run[j] += __shfl(incl, 63);
       }
-      if (r == j) pos = run[j] + incl - x;
-      run[j] += __shfl(incl, 63);
+      int32_t* pl = plan + (size_t)tb[r] * 4 + pos;
+      for (int jj = 0; jj < ng; ++jj) pl[jj] = ((g0 + jj) << 4) | min(8, n - 8 * jj);
     }
-    int32_t* pl = plan + (size_t)tb[r] * 4 + pos;
-    for (int jj = 0; jj < ng; ++jj) pl[jj] = ((g0 + jj) << 4) | min(8, n - 8 * jj);
   }
   // fill the tail of each range's last tile
   if (lane < kRanges) {
@@ -1083,6 +1097,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const f16* __restrict__ Opar
   const int gt = blockIdx.x * 256 + threadIdx.x;
   const int q = gt / TPQ, part = gt % TPQ;
   if (q >= rows) return;
+  const float vm = vmax[q / N];
   float2 st[kRanges];
   float M = -INFINITY;
 #pragma unroll
@@ -1097,18 +1112,22 @@ __global__ __launch_bounds__(256) void k_attn_merge(const f16* __restrict__ Opar
     wsum += w[j];
   }
   const float cut = wsum * 0x1p-20f;
+  // every range's piece loaded at once (branch-free): a skipped range reads the first piece of
+  // the buffer instead (cached, so no memory traffic) and its value is discarded
+  f16x8 o[kRanges];
+#pragma unroll
+  for (int j = 0; j < kRanges; ++j)
+    o[j] = *reinterpret_cast<const f16x8*>(Opart + (w[j] > cut ? ((size_t)q * kRanges + j) * D + part * 8 : 0));
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < kRanges; ++j) {
-    if (w[j] > cut) {
-      const f16x8 o = *reinterpret_cast<const f16x8*>(Opart + ((size_t)q * kRanges + j) * D + part * 8);
+    const bool use = w[j] > cut;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], (float)o[i], acc[i]);
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = use ? fmaf(w[j], (float)o[j][i], acc[i]) : acc[i];
   }
-  const float scale = wsum > 0.0f ? value_unit(vmax[q / N]) / wsum : 0.0f;
+  const float scale = wsum > 0.0f ? value_unit(vm) / wsum : 0.0f;
   bf16x8 out;
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = (bf16)(acc[i] * scale);
