@@ -149,8 +149,10 @@ def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4):
         "park::k_select<16>": ("W once; mask, list and count once", BH * NQ * nk * (4 + 1 + 4) + BH * NQ * 4),
         "park::k_pack_kv<128>": ("K, V and perm once; the packed groups once",
                                  2 * BH * N * d * esz + BH * N * 4 + 2 * BH * (N + 8 * nk) * d * esz),
-        "park::k_attn_merge<128>": ("the partial states once (an upper bound: negligible ones are skipped); O and lse once",
-                                    BH * N * ranges * (d * 2 + 8) + BH * N * (d * esz + 4)),
+        "park::k_attn_merge<128>": ("every range's (m, l) and one range's partial output per query (the ranges "
+                                    "below 2^-20 of a row's weight are skipped, so the reads lie between this and "
+                                    "all ranges' outputs); O and lse once",
+                                    BH * N * (ranges * 8 + d * 2) + BH * N * (d * esz + 4)),
     }
     out = []
     for k in rec.get("kernels", []):
