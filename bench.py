@@ -24,7 +24,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (fp16 is the same)
 PEAK_HBM_GBS = 8000.0
 EXP_PER_S = 9.8e12          # v_exp_f32 throughput of the chip (256 CUs), estimated
 
@@ -140,7 +140,7 @@ def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4):
     alg = {
         "park::k_km_sums<128, bf16>": ("the keys once (by perm), perm once, the means (double) once",
                                        BH * N * d * esz + BH * N * 4 + BH * nkp * d * 8),
-        "park::k_km_ctx<128>": ("the means (double) and R, R^T once; c~ (float), the bf16 screen operand and "
+        "park::k_km_ctx<128>": ("the means (double) and R, R^T once; c~ (float), the fp16 screen operand and "
                                 "the per-cluster figures once", BH * nkp * d * 8 + 2 * BH * d * d * 8 + BH * nkp * (d * 6 + 20)),
         "park::k_transform_bf16<128>": ("the keys once; K~ (float) and the key norms once",
                                         BH * N * d * esz + BH * N * d * 4 + BH * N * 16),
@@ -673,7 +673,8 @@ def main():
                         {"mfma_issued_frac": round(2 * pama_flops / (pama_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "exp_floor_ms": round(BH * N * nk / EXP_PER_S * 1e3, 3)}),
         kernel_roofline("k_km_assign<128, false>", "mfma", assign_flops, assign_ms,
-                        "2 N_K d FLOP per key (the bf16 distance screen of one k-means step; the last step's "
+                        "2 N_K d FLOP per key (the fp16 distance screen of one k-means step, against the fp16 peak, which equals "
+                        "the bf16 one; the last step's "
                         "launch); bytes: the keys once, the screen operand once per head, the labels once",
                         BH * N * d * esz + BH * nk * d * 2 + BH * N * 4,
                         traffic_bytes("k_km_assign", "k_cluster.hip", cfg.name)),

@@ -23,13 +23,13 @@ struct ClusterWs {
   double* Rt64;   // [BH][D][D] its transpose
   bf16* Rsp;      // [BH][3][D][D] Rt as a sum of three bf16 matrices
   float* Kt;      // [BH][N][D] transformed keys
-  float4* knorm;  // [BH][N] (|k|, |k - bf16(k)|, |k~|, 0)
+  float4* knorm;  // [BH][N] (|k|, |k - fp16(k)|, |k~|, 0)
   float* ctil;    // [BH][nkp][D] centroids in the transformed space
-  bf16* gneg2;    // [BH][nkp][D] bf16(-2 R c~)
-  float4* cinfo;  // [BH][nkp] (|c~|^2, |R c~|, |R c~ - bf16(R c~)|, 0)
+  f16* gneg2;     // [BH][nkp][D] fp16(-2 R c~)
+  float4* cinfo;  // [BH][nkp] (|c~|^2, |R c~|, |R c~ - fp16(R c~)|, 0)
   float* ccv;     // [BH][nkp] |c~|^2 (+inf for padding rows)
   double* cmean;  // [BH][nkp][D] original-space member means
-  uint32_t* hmax; // [BH][4] float bits of max |R c~|, max bf16 error of R c~, max |c~|^2
+  uint32_t* hmax; // [BH][4] float bits of max |R c~|, max fp16 error of R c~, max |c~|^2
   int32_t* hist;  // [BH][nch_s][nk] counting-sort histograms, then bases
   int32_t* wlab;  // [BH][ceil(N / kAsgKeys)] label at the first position of each assignment workgroup
   int nch_g, nch_s, nkp;
@@ -50,7 +50,7 @@ static ClusterWs carve(const Shape& s, void* base) {
   w.Kt = reinterpret_cast<float*>(take(BH * (size_t)s.N * D * sizeof(float)));
   w.knorm = reinterpret_cast<float4*>(take(BH * (size_t)s.N * sizeof(float4)));
   w.ctil = reinterpret_cast<float*>(take(BH * w.nkp * D * sizeof(float)));
-  w.gneg2 = reinterpret_cast<bf16*>(take(BH * w.nkp * D * sizeof(bf16)));
+  w.gneg2 = reinterpret_cast<f16*>(take(BH * w.nkp * D * sizeof(f16)));
   w.cinfo = reinterpret_cast<float4*>(take(BH * w.nkp * sizeof(float4)));
   w.ccv = reinterpret_cast<float*>(take(BH * w.nkp * sizeof(float)));
   w.cmean = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
@@ -311,7 +311,8 @@ __global__ __launch_bounds__(256) void k_chol(const double* G, int metric, doubl
 template <int D>
 __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__ K, const bf16* __restrict__ Rsp,
                                                         int N, float* __restrict__ Kt, float4* __restrict__ knorm) {
-  // k~ = R^T k for kTfKeys keys per workgroup, and the key norms (|k|, 0, |k~|) on the way.
+  // k~ = R^T k for kTfKeys keys per workgroup, and the key norms (|k|, |k - fp16(k)|, |k~|) on
+  // the way.
   // The workgroup's keys are copied to LDS once (rows padded by 16 bytes: the 16 rows one
   // 16-lane pass of a fragment read touches start in distinct banks); wave w computes output
   // columns [32 ct, 32 ct + 32) (ct = w % NT) of the key tiles with parity w / NT, with its B
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__
   __shared__ bf16 ks[kTfKeys * KP];
   __shared__ float tpart[NT][kTfKeys];  // |k~|^2 partial sums per output tile
   __shared__ float ksq[kTfKeys];        // |k|^2
+  __shared__ float kerr[kTfKeys];       // |k - fp16(k)|^2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int ct = w % NT, par = w / NT;
   const int bh = blockIdx.y, k0 = blockIdx.x * kTfKeys;
@@ -378,14 +380,19 @@ __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__
     // row sums of squares over this wave's 32 columns: lanes l and l ^ 1 get row my_row
     const float t = reduce_scatter16(sq, l32);
     if ((l32 & 1) == 0) tpart[ct][32 * kt + my_row] = t;
-    if (ct == 0) {   // |k|^2 from the A fragments: this lane's half of key l32's row
-      float s2 = 0.0f;
+    if (ct == 0) {   // |k|^2 and |k - fp16(k)|^2 from the A fragments: this lane's half of key l32's row
+      float s2 = 0.0f, e2 = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { const float x = (float)a[kc][i]; s2 = fmaf(x, x, s2); }
+        for (int i = 0; i < 8; ++i) {
+          const float x = (float)a[kc][i], dx = x - (float)(f16)x;
+          s2 = fmaf(x, x, s2);
+          e2 = fmaf(dx, dx, e2);
+        }
       s2 += __shfl_xor(s2, 32);
-      if (h == 0) ksq[32 * kt + l32] = s2;
+      e2 += __shfl_xor(e2, 32);
+      if (h == 0) { ksq[32 * kt + l32] = s2; kerr[32 * kt + l32] = e2; }
     }
   }
   __syncthreads();
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(256) void k_transform_bf16(const bf16* __restrict__
       float t2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NT; ++c) t2 += tpart[c][i];
-      knorm[(size_t)bh * N + key] = make_float4(sqrtf(ksq[i]), 0.0f, sqrtf(t2), 0.0f);
+      knorm[(size_t)bh * N + key] = make_float4(sqrtf(ksq[i]), sqrtf(kerr[i]), sqrtf(t2), 0.0f);
     }
   }
 }
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(256) void k_copy_keys_bf16(const bf16* __restrict__
   const int sub = tid / TPK, c = tid % TPK;
   for (int r = sub; r < 64; r += KPS) {
     const int j = blockIdx.x * 64 + r;
-    float s2 = 0.0f;
+    float s2 = 0.0f, e2 = 0.0f;
     if (j < N) {
       const size_t off = ((size_t)bh * N + j) * D + 8 * c;
       const bf16x8 x = load_bf16x8(K + off);
@@ -419,15 +426,22 @@ __global__ __launch_bounds__(256) void k_copy_keys_bf16(const bf16* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) { lo[i] = (float)x[i]; hi[i] = (float)x[4 + i]; }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s2 = fmaf((float)x[i], (float)x[i], s2);
+      for (int i = 0; i < 8; ++i) {
+        const float xf = (float)x[i], dx = xf - (float)(f16)xf;
+        s2 = fmaf(xf, xf, s2);
+        e2 = fmaf(dx, dx, e2);
+      }
       *reinterpret_cast<f32x4*>(Kt + off) = lo;
       *reinterpret_cast<f32x4*>(Kt + off + 4) = hi;
     }
 #pragma unroll
-    for (int o = 1; o < TPK; o <<= 1) s2 += __shfl_xor(s2, o);
+    for (int o = 1; o < TPK; o <<= 1) {
+      s2 += __shfl_xor(s2, o);
+      e2 += __shfl_xor(e2, o);
+    }
     if (j < N && c == 0) {
       const float n = sqrtf(s2);
-      knorm[(size_t)bh * N + j] = make_float4(n, 0.0f, n, 0.0f);
+      knorm[(size_t)bh * N + j] = make_float4(n, sqrtf(e2), n, 0.0f);
     }
   }
 }
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(256) void k_transform_f32(const float* __restrict__
   Kt[((size_t)bh * N + j) * D + a] = (float)s;
 }
 
-// Per-key norms for the screening bound: |k|, |k - bf16(k)| (0 for bf16 keys), |k~|.
+// Per-key norms for the screening bound: |k|, |k - fp16(k)|, |k~|.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ K, const float* __restrict__ Kt, int N,
                                                    float4* __restrict__ knorm) {
@@ -458,7 +472,7 @@ __global__ __launch_bounds__(256) void k_key_norms(const T* __restrict__ K, cons
     double a2 = 0.0, e2 = 0.0, t2 = 0.0;
     for (int c = lane; c < D; c += 64) {
       const float x = to_f32(K[((size_t)bh * N + j) * D + c]);
-      const float xb = (float)(bf16)x;
+      const float xb = (float)(f16)x;
       const float y = Kt[((size_t)bh * N + j) * D + c];
       a2 += (double)x * x;
       e2 += (double)(x - xb) * (x - xb);
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(D) void k_km_init(const float* __restrict__ Kt, con
   ctil[((size_t)bh * nkp + v) * D + i] = x;
 }
 
-// Per-head maxima of |R c~|, its bf16 error and |c~|^2 over all clusters (empty ones
+// Per-head maxima of |R c~|, its fp16 error and |c~|^2 over all clusters (empty ones
 // included: they keep their centroid and stay candidates), read by the next assignment.
 __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ cinfo, int nk, int nkp,
                                                    uint32_t* __restrict__ hmax) {
@@ -506,11 +520,14 @@ __global__ __launch_bounds__(256) void k_bound_max(const float4* __restrict__ ci
 
 // ---------------------------------------------------------------------------------------
 // a5: assignment a_j = argmin_v |k~_j - c~_v|^2, ties to the lowest v.
-// Screen: score_jv = |c~_v|^2 - 2 k_j . bf16(R c~_v) on bf16 MFMA (S^T layout: rows are
+// Screen: score_jv = |c~_v|^2 + fp16(k_j) . fp16(-2 R c~_v) on fp16 MFMA (S^T layout: rows are
 // clusters, columns keys), which equals |k~_j - c~_v|^2 - |k~_j|^2 up to a per-key bound
 //   E_j = 2 (e_j G + a_j F + e_j F) + 2^-14 (2 a_j G + CC + t_j^2)
-// (a_j = |k_j|, e_j = |k_j - bf16(k_j)|, t_j = |k~_j|, G = max |R c~|, F = max bf16 error of
-// R c~, CC = max |c~|^2).  Every cluster whose score is within 2 E_j of the key's minimum is
+// (a_j = |k_j|, e_j = |k_j - fp16(k_j)|, t_j = |k~_j|, G = max |R c~|, F = max fp16 error of
+// R c~, CC = max |c~|^2).  fp16 operands rather than bf16 (the same MFMA rate) make the first
+// term, the larger one, about 8 times smaller, and with it the keys left with several
+// candidates.  A key whose bound is not finite (values beyond the fp16 range), or any key of
+// a head with G >= 2^14 (where -2 R c~ could leave it), compares every cluster exactly.  Every cluster whose score is within 2 E_j of the key's minimum is
 // a candidate; the true argmin always is one.
 // One workgroup: 4 waves x 64 keys.  The cluster operand streams through a three-slot LDS ring
 // in 32-cluster tiles (LDS DMA, each wave copying a quarter of every tile, one barrier per
@@ -547,7 +564,7 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 template <int D, bool KF32>
 __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ Kv, const float* __restrict__ Kt,
                                                       const float4* __restrict__ knorm, const float* __restrict__ ctil,
-                                                      const bf16* __restrict__ gneg2, const float* __restrict__ ccv,
+                                                      const f16* __restrict__ gneg2, const float* __restrict__ ccv,
                                                       const uint32_t* __restrict__ hmax, int N, int nk, int nkp,
                                                       const int32_t* __restrict__ order,
                                                       const int32_t* __restrict__ wlab, int32_t* __restrict__ labels) {
@@ -613,8 +630,9 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
 
   // B fragments of this wave's 64 keys (two 32-key tiles) and their bounds: every load in
   // flight at once (branch-free: slots past N load key 0 and take zeros)
-  bf16x8 bfr[2][NF];
+  f16x8 bfr[2][NF];
   float E[2];
+  bool exact_all[2];
   const float G = __uint_as_float(hmax[4 * bh]), F = __uint_as_float(hmax[4 * bh + 1]);
   const float CC = __uint_as_float(hmax[4 * bh + 2]);
   // the keys of slots 64 w + l32 and 64 w + 32 + l32 (-1 past N)
@@ -628,8 +646,8 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
 #pragma unroll
     for (int kc = 0; kc < NF; ++kc) {
       const size_t off = ((size_t)bh * N + key) * D + 16 * kc + 8 * h;
-      if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_bf16(reinterpret_cast<const float*>(Kv) + off);
-      else bfr[kt][kc] = load_bf16x8(reinterpret_cast<const bf16*>(Kv) + off);
+      if constexpr (KF32) bfr[kt][kc] = load_f32x8_as_f16(reinterpret_cast<const float*>(Kv) + off);
+      else bfr[kt][kc] = load_bf16x8_as_f16(reinterpret_cast<const bf16*>(Kv) + off);
     }
   }
 #pragma unroll
@@ -638,13 +656,15 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
 #pragma unroll
     for (int kc = 0; kc < NF; ++kc)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = real ? bfr[kt][kc][i] : (bf16)0.0f;
+      for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = real ? bfr[kt][kc][i] : (f16)0.0f;
     // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
     // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
     const float4 k4 = kn[kt];
     float e = 2.0f * (k4.y * G + k4.x * F + k4.y * F) + (1.0f / 16384.0f) * (2.0f * k4.x * G + CC + k4.z * k4.z);
     e *= 2.0f * (1.0f + 1.0f / 65536.0f);  // the window is twice the bound
-    E[kt] = real ? e : 0.0f;
+    // no finite bound: no candidates, the exact comparison of every cluster instead
+    exact_all[kt] = real && !(e <= 3.0e38f && G < 16384.0f);
+    E[kt] = !real ? 0.0f : (exact_all[kt] ? -INFINITY : e);
   }
   // Running minimum and candidate lists.  From the second step on the keys are visited in the
   // previous step's label order, so the workgroup's keys share a few consecutive previous
@@ -654,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   // window is recorded whatever its turn (the window only shrinks).
   float mr[2] = {INFINITY, INFINITY};
   int cnt[2] = {0, 0};          // entries in this lane's list of each key (kept in registers)
-  bool ovf[2] = {false, false};
+  bool ovf[2] = {exact_all[0], exact_all[1]};
 #pragma unroll
   for (int i = 0; i < MV; ++i)
     if (tid + i * kAsgKeys < nkp) ccs[tid + i * kAsgKeys] = cvv[i];
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   __syncthreads();
 
   // the screen products of turn i's tile into acc
-  auto products = [&](int i, const bf16x8 (&a)[NF], f32x16 (&acc)[2]) {
+  auto products = [&](int i, const f16x8 (&a)[NF], f32x16 (&acc)[2]) {
     const int t = tile_of(i);
     f32x16 init;
 #pragma unroll
@@ -724,8 +744,8 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
     }
   };
   // fragments of turn i from its slot
-  auto read_turn = [&](int i, bf16x8 (&a)[NF]) {
-    const bf16x8* tl = reinterpret_cast<const bf16x8*>(ring + (i % 3) * NF * 1024);
+  auto read_turn = [&](int i, f16x8 (&a)[NF]) {
+    const f16x8* tl = reinterpret_cast<const f16x8*>(ring + (i % 3) * NF * 1024);
 #pragma unroll
     for (int kc = 0; kc < NF; ++kc) a[kc] = tl[kc * 64 + lane];
   };
@@ -737,9 +757,9 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
   // i + 1, the LDS reads of turn i + 2 and the minima of turn i's products, so the matrix
   // unit works on the next tile while the vector unit reduces this one; last the candidate
   // lists of turn i (a branch taken only when a score falls inside a key's window).
-  bf16x8 fa[NF], fb[NF];
+  f16x8 fa[NF], fb[NF];
   f32x16 pa[2], pb[2];
-  auto iteration = [&](int i, bf16x8 (&fi)[NF], bf16x8 (&fn)[NF], f32x16 (&pi)[2], f32x16 (&pn)[2]) {
+  auto iteration = [&](int i, f16x8 (&fi)[NF], f16x8 (&fn)[NF], f32x16 (&pi)[2], f32x16 (&pn)[2]) {
     float tm[2];
     if (i + 2 < nT) {
       wait_lds();
@@ -1080,7 +1100,7 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
 
 // Step 2, per (32-cluster tile, head): c~_v = R^T mean_v rounded to float (or, for the
 // initial centroids, c~_v as stored), then the screen operand g_v = R c~_v in double,
-// gneg2 = bf16(-2 g) (fragment-major), |c~|^2, |g|, |g - bf16(g)|.  Clusters without keys
+// gneg2 = fp16(-2 g) (fragment-major), |c~|^2, |g|, |g - fp16(g)|.  Clusters without keys
 // keep everything from the previous step; padding rows (v >= nk) get |c~|^2 = +inf.
 // Both products are double GEMMs on the matrix cores (16 x 16 x 4 double MFMAs): wave w takes
 // the 16 clusters v0 + 16 (w & 1) .. + 15 and the D / 2 columns of half w >> 1, as D / 32
@@ -1093,13 +1113,13 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void k_km_ctx(const double* __restrict__ cmean, const int32_t* __restrict__ counts,
                                                     int nk, int nkp, int init_mode, const double* __restrict__ R64,
                                                     const double* __restrict__ Rt64, float* __restrict__ ctil,
-                                                    bf16* __restrict__ gneg2, float4* __restrict__ cinfo,
+                                                    f16* __restrict__ gneg2, float4* __restrict__ cinfo,
                                                     float* __restrict__ ccv) {
   constexpr int NBW = D / 32;  // 16-column output blocks per wave
   constexpr int KS = D / 4;    // MFMA steps
   constexpr int SP = 2;        // steps per B load (16 bytes per lane and block)
   __shared__ __attribute__((aligned(16))) float cs[32][D + 4];   // c~ of the tile's clusters
-  __shared__ __attribute__((aligned(16))) bf16 gs[32][D + 8];    // bf16(-2 g) of the tile's clusters
+  __shared__ __attribute__((aligned(16))) f16 gs[32][D + 8];     // fp16(-2 g) of the tile's clusters
   __shared__ double red[2][32][2];     // per column half: |g|^2 and residual sums of each cluster
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
   const int cg = w & 1, ch = w >> 1;
@@ -1192,7 +1212,7 @@ __global__ __launch_bounds__(256, 2) void k_km_ctx(const double* __restrict__ cm
   // second product: g = R c~, i.e. g[v][i] = sum_k c~[v][k] R[i][k]
   f64x4 g[NBW];
   gemm(a, R64, g);
-  // bf16(-2 g) into LDS; the per-cluster |g|^2 and residual sums of this column half: columns
+  // fp16(-2 g) into LDS; the per-cluster |g|^2 and residual sums of this column half: columns
   // in block order per lane, then the 16 lanes of the cluster's group by a fixed butterfly
   double gn[4] = {0.0, 0.0, 0.0, 0.0}, fr[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -1201,11 +1221,11 @@ __global__ __launch_bounds__(256, 2) void k_km_ctx(const double* __restrict__ cm
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * cg + 4 * r + lg, i = 16 * (NBW * ch + b) + li;
       const double gv = g[b][r];
-      const bf16 gb = (bf16)(float)gv;
+      const f16 gb = (f16)(float)gv;
       const double df = gv - (double)(float)gb;
       gn[r] += gv * gv;
       fr[r] += df * df;
-      gs[c][i] = t0 + c < nk ? (bf16)(-2.0f * (float)gb) : (bf16)0.0f;
+      gs[c][i] = t0 + c < nk ? (f16)(-2.0f * (float)gb) : (f16)0.0f;
     }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1)
@@ -1231,8 +1251,8 @@ __global__ __launch_bounds__(256, 2) void k_km_ctx(const double* __restrict__ cm
   for (int q = 0; q < (32 * D / 8) / 256; ++q) {
     const int p = tid + 256 * q, kc = p >> 6, l = p & 63, row = l & 31, col = 16 * kc + 8 * (l >> 5);
     if ((write32 >> row) & 1)
-      *reinterpret_cast<bf16x8*>(gneg2 + (size_t)bh * nkp * D + frag_lane(blockIdx.x, kc, l, D)) =
-          *reinterpret_cast<const bf16x8*>(&gs[row][col]);
+      *reinterpret_cast<f16x8*>(gneg2 + (size_t)bh * nkp * D + frag_lane(blockIdx.x, kc, l, D)) =
+          *reinterpret_cast<const f16x8*>(&gs[row][col]);
   }
   // lane c < 16 of the first column half writes cluster v0 + c (column halves added in order)
   if (ch == 0 && lg == 0) {

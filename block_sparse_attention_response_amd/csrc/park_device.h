@@ -66,12 +66,20 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-__device__ __forceinline__ bf16x8 load_f32x8_as_bf16(const float* p) {
+// 8 float or bf16 values as fp16 (round to nearest even; beyond the fp16 range they become inf)
+__device__ __forceinline__ f16x8 load_f32x8_as_f16(const float* p) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
   const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  bf16x8 r;
-  r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3];
-  r[4] = (bf16)b[0]; r[5] = (bf16)b[1]; r[6] = (bf16)b[2]; r[7] = (bf16)b[3];
+  f16x8 r;
+  r[0] = (f16)a[0]; r[1] = (f16)a[1]; r[2] = (f16)a[2]; r[3] = (f16)a[3];
+  r[4] = (f16)b[0]; r[5] = (f16)b[1]; r[6] = (f16)b[2]; r[7] = (f16)b[3];
+  return r;
+}
+__device__ __forceinline__ f16x8 load_bf16x8_as_f16(const bf16* p) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (f16)(float)x[i];
   return r;
 }
 

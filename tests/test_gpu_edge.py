@@ -93,3 +93,39 @@ def test_degenerate_sizes(dev, orc, N, d, dtype, nk, nq):
                                             gc["block_list"][0, 0], gc["block_count"][0, 0], scale)
     assert np.abs(host(O2)[0, 0] - Oo2).max() <= tol
     assert np.abs(host(lse2)[0, 0] - lo2).max() <= 1e-3
+
+
+# The assignment screens in fp16.  A key with a component beyond the fp16 range has no finite
+# screening bound, and a head whose |R c~| reaches 2^14 could overflow the screen operand: such
+# keys compare every cluster exactly.  Queries scaled down keep R small, so the first two cases
+# reach only the key condition (the first half of the keys scaled past the range, beside keys
+# screened as usual, then every key); the third reaches only the head condition.  12 clusters
+# fit a key's candidate lists, 40 do not.  (query scale, key scale, keys scaled)
+RANGE_CASES = [(2.0 ** -10, 2.0 ** 15, 300), (2.0 ** -10, 2.0 ** 15, 600), (1.0, 2.0 ** 12, 600)]
+
+
+@pytest.mark.parametrize("qscale,kscale,nscaled", RANGE_CASES)
+@pytest.mark.parametrize("nk", [12, 40])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_screen_beyond_fp16_range(dev, orc, qscale, kscale, nscaled, nk, dtype):
+    N, d, iters = 600, 128, 3
+    Q, K, _ = _inputs(N, d, dtype, 11 * nk + nscaled)
+    Q = Q * np.float32(qscale)
+    K[0, 0, :nscaled] *= np.float32(kscale)   # powers of two: still exact in bf16
+    _, _, R, ok = orc.query_metric(Q[0, 0])
+    C0 = orc.init_centroids(orc.transform(K[0, 0], R), nk)
+    beyond = int((np.abs(K[0, 0]) > 65504.0).any(axis=1).sum())
+    G = float(np.linalg.norm(C0 @ R.T, axis=1).max())
+    if qscale < 1.0:
+        assert beyond == nscaled and G < 2.0 ** 14
+    else:
+        assert beyond == 0 and G >= 2.0 ** 14
+    q, k = to_dev(Q, dtype), to_dev(K, dtype)
+    runs = [{kk: host(vv) for kk, vv in dev.park_cluster_keys(q, k, nk, t).items()} for t in range(1, iters + 1)]
+    assert all(r["status"][0, 0] == 0 for r in runs)
+    n_diff, n_keys, _ = teacher_forced_chain(orc, Q[0, 0], K[0, 0], nk, [r["labels"][0, 0] for r in runs])
+    print(f"keys beyond fp16 {beyond}/{N}, max |R c~| {G:.3g}: {n_diff} near-tie label differences over {n_keys} keys")
+    lab = runs[-1]["labels"][0, 0]
+    cent, counts, perm, offsets = orc.finalize(K[0, 0], lab, nk)
+    assert np.array_equal(runs[-1]["counts"][0, 0], counts) and np.array_equal(runs[-1]["perm"][0, 0], perm)
+    assert np.array_equal(runs[-1]["offsets"][0, 0], offsets)
