@@ -71,7 +71,9 @@ def test_streaming_rooflines_follow_the_committed_profile(tmp_path, monkeypatch)
     if "stale" not in sums:
         # the sums read every key once: at least B H N d bf16 bytes
         assert sums["hbm_algorithmic"]["bytes"] >= BH * N * d * 2
-        assert abs(sums["hbm_measured"]["GBps"] - sums["traffic"] / (sums["kernel_ms"] * 1e-3) / 1e9) < 1.0
+        # kernel_ms is rounded to 1 us, so the rate recomputed from it agrees to that rounding
+        rate = sums["traffic"] / (sums["kernel_ms"] * 1e-3) / 1e9
+        assert abs(sums["hbm_measured"]["GBps"] - rate) <= rate * 0.0006 / sums["kernel_ms"] + 0.1
     # a record whose hashes do not match the sources gives stale entries only
     import json
     rec = json.load(open(rec_path))
