@@ -579,6 +579,29 @@ def test_logmass_rmse_closed_form_and_translation(orc):
     assert abs(orc.logmass_rmse(Q, K2, lab, cent2, counts, s) - got) < 1e-6
 
 
+
+@pytest.mark.parametrize("seed", range(4))
+def test_qrkc_lowers_logmass_error_for_anisotropic_queries(orc, seed):
+    """PARK section 5.2 and appendix B (M2): within a cluster, the log-mass error of a query
+    grows with the variance of q . (k - c_v), whose mean over the queries is the query-metric
+    norm (k - c_v)^T G (k - c_v) that QRKC minimises; Euclidean k-means minimises |k - c_v|^2.
+    With class-centred keys and queries whose spread is concentrated on a few coordinates, the
+    QRKC clustering must give a clearly lower centred log-mass RMSE than the Euclidean one (the
+    ratio is 0.61-0.81 on these seeds)."""
+    rng = np.random.default_rng(seed)
+    N, d, M, nk, iters = 2000, 32, 8, 32, 8
+    mu = rng.normal(0, 2, (M, d))
+    z = rng.integers(0, M, N)
+    s = np.r_[np.full(4, 4.0), np.full(d - 4, 0.25)]
+    Q = ((mu[z] + rng.normal(0, 0.5, (N, d))) * s).astype(np.float32)
+    K = (mu[z] + rng.normal(0, 0.5, (N, d))).astype(np.float32)
+    rows = np.arange(0, N, 4)
+    err = {}
+    for metric in ("qrkc", "euclidean"):
+        cl = orc.cluster_keys(Q, K, nk, iters, metric=metric)
+        err[metric] = orc.logmass_rmse(Q, K, cl["labels"], cl["centroids"], cl["counts"], 1 / np.sqrt(d), rows=rows)
+    assert err["qrkc"] < 0.9 * err["euclidean"], err
+
 # ---------------------------------------------------------------- SCOPE online per-head top-k
 
 def test_select_online_hand_example(orc):
