@@ -126,11 +126,13 @@ def traffic_bytes(tag, source, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4):
+def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4, attn_passes=1):
     """HBM roofline entries of the step's streaming kernels, from the committed kernel trace and
     counters (profiles/streaming_kernels_<workload>_traffic.txt): profiled, not timed in this
-    run.  Algorithmic bytes are each kernel's minimum reads and writes at these sizes; an entry
-    whose kernel source changed since the profile was taken carries no measured figures."""
+    run.  Algorithmic bytes are each kernel's minimum reads and writes per launch at these sizes
+    (the attention call's kernels run once per pass over the heads, attn_passes launches of
+    BH / attn_passes heads each); an entry whose kernel source changed since the profile was
+    taken carries no measured figures."""
     import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", f"streaming_kernels_{workload}_traffic.txt")))
@@ -147,12 +149,12 @@ def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4):
         "park::k_gram_bf16<128>": ("the queries once", BH * N * d * esz),
         "park::k_sort_scatter": ("the labels once, perm once", 2 * BH * N * 4),
         "park::k_select<16>": ("W once; mask, list and count once", BH * NQ * nk * (4 + 1 + 4) + BH * NQ * 4),
-        "park::k_pack_kv<128>": ("K, V and perm once; the packed groups once",
-                                 2 * BH * N * d * esz + BH * N * 4 + 2 * BH * (N + 8 * nk) * d * esz),
+        "park::k_pack_kv<128>": ("K, V and perm once; the packed groups once (one pass's heads)",
+                                 (2 * BH * N * d * esz + BH * N * 4 + 2 * BH * (N + 8 * nk) * d * esz) / attn_passes),
         "park::k_attn_merge<128>": ("every range's (m, l) and one range's partial output per query (the ranges "
                                     "below 2^-20 of a row's weight are skipped, so the reads lie between this and "
-                                    "all ranges' outputs); O and lse once",
-                                    BH * N * (ranges * 8 + d * 2) + BH * N * (d * esz + 4)),
+                                    "all ranges' outputs); O and lse once (one pass's heads)",
+                                    (BH * N * (ranges * 8 + d * 2) + BH * N * (d * esz + 4)) / attn_passes),
     }
     out = []
     for k in rec.get("kernels", []):
@@ -239,14 +241,17 @@ def attn_clocks(args):
     B, H, N, d = q.shape
     cl = park.park_cluster_keys(q, k, cfg.n_clusters, cfg.iters)
     rb = park.park_retrieve_blocks(q, cl["centroids"], cl["counts"], cfg.top_p, cfg.top_k, scores=False)
-    ev = park.HipEvents()
+    passes = park.attn_passes(B, H, N, d, cfg.n_clusters)
+    hpp = -(-B * H // passes)              # heads per pass
+    ev = park.HipEvents(passes)
     times = []
     for _ in range(3):
         park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
-                                    events=ev.handles)
+                                    events=ev)
         times.append(ev.elapsed_ms())
     torch.cuda.synchronize()
-    items = B * H * ((N + 63) // 64) * 4
+    NQ = (N + 63) // 64
+    items = B * H * NQ * 4
     L.park_attn_clock_words.restype = ctypes.c_size_t
     words = min(5 * items, int(L.park_attn_clock_words()))
     buf = np.zeros(words, np.uint64)
@@ -254,8 +259,10 @@ def attn_clocks(args):
     if L.park_attn_clock_read(buf.ctypes.data, words) != 0:
         raise RuntimeError("park_attn_clock_read failed")
     c = buf.reshape(-1, 5).astype(np.int64)
-    c = c[c[:, 0] > 0]                     # items with tiles (the last call's stamps)
+    idx = np.nonzero(c[:, 0] > 0)[0]       # items with tiles (the last call's stamps)
+    c = c[idx]
     wg, nt = c[:, 4] >> 32, c[:, 4] & 0xFFFFFFFF
+    wg = wg + (idx // (4 * NQ) // hpp) * (1 << 20)   # the workgroups of each pass apart
     pro, til, epi = c[:, 1] - c[:, 0], c[:, 2] - c[:, 1], c[:, 3] - c[:, 2]
     o = np.lexsort((c[:, 0], wg))          # a workgroup's items in time order (one XCD's clock)
     same = wg[o][1:] == wg[o][:-1]
@@ -586,7 +593,7 @@ def main():
                                        events=rev.handles if rev else None)
         if ev: ev[2].record(stream)
         O, lse = park.park_block_sparse_attn(q, k, v, cl["perm"], cl["offsets"], rb["block_list"], rb["block_count"],
-                                             workspace=ws_a, events=kev.handles if kev else None)
+                                             workspace=ws_a, events=kev)
         if ev: ev[3].record(stream)
         return cl, rb, O, lse
 
@@ -595,7 +602,8 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    kevs = [park.HipEvents() for _ in range(args.steps)]   # around the attention kernel itself
+    passes = park.attn_passes(B, H, N, d, nk)
+    kevs = [park.HipEvents(passes) for _ in range(args.steps)]   # around the attention kernel of each pass
     cevs = [park.HipEvents() for _ in range(args.steps)]   # around the last k-means assignment kernel
     revs = [park.HipEvents() for _ in range(args.steps)]   # around the fused PAMA kernel
     log(f"timing {args.steps} steps")
@@ -651,9 +659,14 @@ def main():
         "pair_density": round(pair_density, 4),
         "roofline": {"bound": "mfma", "kernel": "k_attn_items<128, false>", "achieved": round(kernel_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes("k_attn_items", "k_attn.hip", cfg.name), "kernel_ms": round(kernel_ms, 3),
-                     "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch" % (attn_flops / 1e12)},
+                     "traffic": traffic_bytes("k_attn_items", "k_attn.hip", cfg.name),
+                     "kernel_ms": round(kernel_ms / passes, 3), "launches_per_call": passes,
+                     "algorithmic": "4 d FLOP per selected (query, key) pair, %.4g TFLOP per launch (the call's "
+                                    "%.4g TFLOP over its %d passes of %d heads or fewer)"
+                                    % (attn_flops / passes / 1e12, attn_flops / 1e12, passes, -(-B * H // passes))},
     }
+    result["workspace_bytes"] = {"cluster": int(ws_c.numel()), "retrieval": int(ws_r.numel()),
+                                 "attention": int(ws_a.numel()), "attention_passes": passes}
     # the three heavy kernels of the step, each timed live (HIP events around one launch)
     BH, NQ = B * H, (N + 63) // 64
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -661,9 +674,10 @@ def main():
     pama_flops = 2.0 * BH * N * nk * d
     assign_flops = 2.0 * BH * N * nk * d
     result["kernels"] = [
-        kernel_roofline("k_attn_items<128, false>", "mfma", attn_flops, kernel_ms,
+        kernel_roofline("k_attn_items<128, false>", "mfma", attn_flops / passes, kernel_ms / passes,
                         "4 d FLOP per selected (query, key) pair; bytes: Q and O once, K and V once per "
-                        "(query block, selected key)", BH * N * d * esz * 2 + kv_bytes,
+                        "(query block, selected key); per launch: the call's work over its %d passes" % passes,
+                        (BH * N * d * esz * 2 + kv_bytes) / passes,
                         traffic_bytes("k_attn_items", "k_attn.hip", cfg.name)),
         kernel_roofline("k_pama<128, 4, false, false>", "mfma", pama_flops, pama_ms,
                         "2 N_K d FLOP per query (the score product; the kernel runs it twice on the matrix unit, "
@@ -680,7 +694,7 @@ def main():
                         traffic_bytes("k_km_assign", "k_cluster.hip", cfg.name)),
     ]
     # the streaming kernels of the step against the HBM roofline (from the committed profiles)
-    result["streaming_kernels"] = streaming_rooflines(cfg.name, BH, N, d, nk, NQ, esz)
+    result["streaming_kernels"] = streaming_rooflines(cfg.name, BH, N, d, nk, NQ, esz, attn_passes=passes)
 
     if args.recall == "on":
         allb = torch.arange(nk, dtype=torch.int32, device="cuda").expand(B, H, rb["block_list"].shape[2], nk).contiguous()

@@ -33,7 +33,7 @@ import os
 
 __all__ = [
     "ParkError", "lib", "workspace_bytes", "park_abi_version", "park_cluster_keys",
-    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_retrieve_blocks_unfused", "park_block_sparse_attn", "HipEvents",
+    "park_retrieve_blocks", "park_retrieve_blocks_pooled", "park_retrieve_blocks_unfused", "park_block_sparse_attn", "HipEvents", "attn_passes",
     "workspace_bytes_clustered", "park_cluster_queries", "park_retrieve_blocks_clustered",
     "park_block_sparse_attn_clustered", "park_retrieve_blocks_online", "park_block_importance_exact", "OP_BLOCK_IMPORTANCE", "park_logmass_rmse",
     "PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
@@ -88,8 +88,10 @@ def lib():
         L.park_block_sparse_attn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _F, _P, _P,
                                              _P, _S, _P]
         L.park_block_sparse_attn.restype = _I
-        L.park_block_sparse_attn_timed.argtypes = L.park_block_sparse_attn.argtypes + [_P, _P]
+        L.park_block_sparse_attn_timed.argtypes = L.park_block_sparse_attn.argtypes + [_P, _P, _I]
         L.park_block_sparse_attn_timed.restype = _I
+        L.park_attn_passes.argtypes = [_I, _I, _I, _I, _I, _I]
+        L.park_attn_passes.restype = _I
         L.park_workspace_bytes_clustered.argtypes = [_I, _I, _I, _I, _I, _I, _I]
         L.park_workspace_bytes_clustered.restype = _S
         L.park_cluster_queries.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P]
@@ -328,8 +330,8 @@ def park_retrieve_blocks_pooled(Q, centroids, counts, top_p: float, top_k: int, 
 def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scale=None, want_lse: bool = True,
                            out=None, lse=None, workspace=None, events=None):
     """Attention over the selected blocks.  Returns (O [B,H,N,d] in Q's dtype, lse [B,H,N]
-    float32 or None).  `events` = (begin, end) raw hipEvent_t handles selects
-    park_block_sparse_attn_timed, which records them around the attention kernel itself."""
+    float32 or None).  `events` = a HipEvents with one pair per pass (attn_passes()) selects
+    park_block_sparse_attn_timed, which records pair p around pass p's attention kernel."""
     torch = _torch()
     for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (perm, "perm"), (offsets, "offsets"),
                  (block_list, "block_list"), (block_count, "block_count")):
@@ -353,7 +355,8 @@ def park_block_sparse_attn(Q, K, V, perm, offsets, block_list, block_count, scal
     if events is None:
         _check(lib().park_block_sparse_attn(*args), "park_block_sparse_attn")
     else:
-        _check(lib().park_block_sparse_attn_timed(*args, events[0], events[1]), "park_block_sparse_attn_timed")
+        begins, ends, n = events.arrays
+        _check(lib().park_block_sparse_attn_timed(*args, begins, ends, n), "park_block_sparse_attn_timed")
     return O, (lse if want_lse else None)
 
 
@@ -527,34 +530,57 @@ def park_logmass_rmse(Q, K, perm, offsets, centroids, counts, scale=None, worksp
     return out
 
 
+def attn_passes(B: int, H: int, N: int, d: int, n_clusters: int, dtype: str = "bf16") -> int:
+    """Passes over the heads that park_block_sparse_attn makes for these sizes."""
+    return lib().park_attn_passes(1 if dtype == "bf16" else 0, B, H, N, d, n_clusters)
+
+
 class HipEvents:
-    """Two HIP events for timing one kernel through park_block_sparse_attn(events=...):
+    """`n` pairs of HIP events for timing one kernel through the *_timed entry points (one pair
+    for park_cluster_keys and park_retrieve_blocks, one per pass for park_block_sparse_attn):
     created and read through libamdhip64 directly (torch's events only see its own calls)."""
 
-    def __init__(self):
+    def __init__(self, n: int = 1):
         import ctypes.util
         name = ctypes.util.find_library("amdhip64") or "libamdhip64.so"
         self._hip = ctypes.CDLL(name)
-        self.begin, self.end = ctypes.c_void_p(), ctypes.c_void_p()
-        for ev in (self.begin, self.end):
-            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+        self.begins = (ctypes.c_void_p * n)()
+        self.ends = (ctypes.c_void_p * n)()
+        self.n = n
+        for arr in (self.begins, self.ends):
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev.value
 
     @property
     def handles(self):
-        return (self.begin, self.end)
+        """(begin, end) of the first pair."""
+        return (ctypes.c_void_p(self.begins[0]), ctypes.c_void_p(self.ends[0]))
+
+    @property
+    def arrays(self):
+        """(begin handles, end handles, n) as host arrays."""
+        return (self.begins, self.ends, self.n)
 
     def elapsed_ms(self) -> float:
-        ms = ctypes.c_float()
-        if self._hip.hipEventSynchronize(self.end) != 0 or \
-                self._hip.hipEventElapsedTime(ctypes.byref(ms), self.begin, self.end) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
+        """Sum over the pairs of the time between begin and end."""
+        total = 0.0
+        for i in range(self.n):
+            ms = ctypes.c_float()
+            b, e = ctypes.c_void_p(self.begins[i]), ctypes.c_void_p(self.ends[i])
+            if self._hip.hipEventSynchronize(e) != 0 or \
+                    self._hip.hipEventElapsedTime(ctypes.byref(ms), b, e) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            total += ms.value
+        return total
 
     def __del__(self):
         try:
-            for ev in (self.begin, self.end):
-                self._hip.hipEventDestroy(ev)
+            for arr in (self.begins, self.ends):
+                for i in range(self.n):
+                    self._hip.hipEventDestroy(ctypes.c_void_p(arr[i]))
         except Exception:  # pragma: no cover - interpreter shutdown
             pass
 

@@ -6,6 +6,7 @@
 // permutation.
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <type_traits>
 
 #include "park_device.h"
@@ -562,7 +563,7 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
                                           f16* __restrict__ Opart, float2* __restrict__ ML,
                                           const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
                                           const int32_t* __restrict__ qperm, int maxc, bf16* __restrict__ Ofin,
-                                          float* __restrict__ lse) {
+                                          float* __restrict__ lse, int item0) {
   constexpr bool fused = FUSED;
   constexpr int KC = D / 16, DT = D / 32;
   constexpr uint32_t GB = 16 * D;   // bytes per packed group (K or V)
@@ -1018,8 +1019,8 @@ __device__ __forceinline__ void attn_item(const int item, AttnLds<D>& sm, const 
   }
 #ifdef PARK_ATTN_CLOCKS
   PARK_ATTN_STAMP(clk_end);
-  if (lane == 0 && (size_t)item * 5 + 5 <= kAttnClockWords) {
-    unsigned long long* o = attn_clock + (size_t)item * 5;
+  if (lane == 0 && ((size_t)item0 + item) * 5 + 5 <= kAttnClockWords) {
+    unsigned long long* o = attn_clock + ((size_t)item0 + item) * 5;
     o[0] = clk_start;
     o[1] = clk_loop;
     o[2] = clk_tiles;
@@ -1048,7 +1049,7 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
                                                    float2* __restrict__ ML, int items, int32_t* __restrict__ ictr,
                                                    const int4* __restrict__ chunks, const int32_t* __restrict__ ctotal,
                                                    const int32_t* __restrict__ qperm, int maxc, int frows,
-                                                   bf16* __restrict__ Ofin, float* __restrict__ lse) {
+                                                   bf16* __restrict__ Ofin, float* __restrict__ lse, int item0) {
   __shared__ AttnLds<D> sm;
   const int lane = threadIdx.x;
   for (int i = lane; i < 72; i += 64) sm.btab[i >> 3][i & 7] = (i & 7) < (i >> 3) ? 0.0f : -INFINITY;
@@ -1074,10 +1075,10 @@ __global__ __launch_bounds__(64) void k_attn_items(const bf16* __restrict__ Q, c
       const int row = (item % kRanges) * per + item / kRanges;
       if (row < frows)
         attn_item<D, true>(row, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
-                           qperm, maxc, Ofin, lse);
+                           qperm, maxc, Ofin, lse, item0);
     } else {
       attn_item<D, false>(item, sm, Q, Kp, Vp, plan, tbase, vmax, N, NQ, Gcap, scale2, Opart, ML, chunks, ctotal,
-                          qperm, maxc, Ofin, lse);
+                          qperm, maxc, Ofin, lse, item0);
     }
     item = (int)gridDim.x + xr + kRanges * __builtin_amdgcn_readfirstlane(nxt);
   }
@@ -1291,16 +1292,43 @@ static int compute_units() {
   return n;
 }
 
+// The call walks the heads in passes; the workspace holds one pass's packed keys and values,
+// tile plan and partial states (every one of them per head), so a pass takes as many heads as
+// fit in kAttnPassBytes (at least one), and the passes are balanced.  Each pass is the whole
+// computation for its heads: heads are independent.
+constexpr size_t kAttnPassBytes = size_t(5) << 29;   // 2.5 GiB
+
+int attn_heads_per_pass(const Shape& s, const QueryBlocks* qb) {
+  Shape one = s;
+  one.BH = 1;
+  size_t per = 0;
+  carve_attn(one, qb, nullptr, &per);
+  const long long fit = std::max<long long>(1, (long long)(kAttnPassBytes / std::max<size_t>(per, 1)));
+  const long long passes = (s.BH + fit - 1) / fit;
+  return (int)((s.BH + passes - 1) / passes);
+}
+
+int attn_passes(const Shape& s, const QueryBlocks* qb) {
+  const int hpp = attn_heads_per_pass(s, qb);
+  return (s.BH + hpp - 1) / hpp;
+}
+
+// (carve_attn of h heads is at most h times carve_attn of one head: each buffer is per head,
+// rounded up to 256 bytes)
 size_t attn_workspace(const Shape& s, const QueryBlocks* qb) {
+  Shape sp = s;
+  sp.BH = attn_heads_per_pass(s, qb);
   size_t total = 0;
-  carve_attn(s, qb, nullptr, &total);
+  carve_attn(sp, qb, nullptr, &total);
   return total;
 }
 
-hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
-                       const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
-                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                       const QueryBlocks* qb) {
+// One pass: the heads of s (pointers already offset to the pass's first head); item0 = the
+// first head's first item, for the clock-stamped build's record.
+static hipError_t attn_pass(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
+                            const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
+                            void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
+                            const QueryBlocks* qb, int item0) {
   // query blocks per head (plan rows) and chunk slots per head (clustered blocks)
   const int NQ = qb ? qb->NQ : n_qblocks(s.N);
   const int maxc = qb ? chunk_slots(s.N, qb->NQ) : 0;
@@ -1353,7 +1381,8 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
     const int waves = (int)std::min<long long>(aitems, 4 * compute_units() / kRanges * kRanges);
 #define PARK_ITEMS(DD, FF)                                                                                  \
   k_attn_items<DD, FF><<<waves, 64, 0, st>>>(q, w.Kp, w.Vp, w.plan, w.tbase, w.vmax, s.N, NQ, Gcap, scale2, w.Opart, \
-                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc, (int)frows, o, lse)
+                                             w.ML, (int)aitems, w.ictr, w.chunks, w.ctotal, qperm, maxc, (int)frows, o, lse, \
+                                             item0)
     if (s.d == 128) {
       if (qb) PARK_ITEMS(128, true); else PARK_ITEMS(128, false);
     } else {
@@ -1385,6 +1414,31 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
                                            w.chunks, w.ctotal, qperm, maxc);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
+                       const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
+                       void* O, float* lse, void* ws, hipStream_t st, const hipEvent_t* ev_begin,
+                       const hipEvent_t* ev_end, int n_events, const QueryBlocks* qb) {
+  const int hpp = attn_heads_per_pass(s, qb);
+  const int NQ = qb ? qb->NQ : n_qblocks(s.N);
+  const size_t esz = s.dtype == 1 ? 2 : 4, N = s.N, d = s.d;
+  for (int h0 = 0, p = 0; h0 < s.BH; h0 += hpp, ++p) {
+    Shape sp = s;
+    sp.BH = std::min(hpp, s.BH - h0);
+    const size_t tok = (size_t)h0 * N;
+    QueryBlocks qp{};
+    if (qb) qp = QueryBlocks{qb->qperm + tok, qb->qoffsets + (size_t)h0 * (NQ + 1), NQ};
+    const hipError_t e = attn_pass(
+        sp, static_cast<const char*>(Q) + tok * d * esz, static_cast<const char*>(K) + tok * d * esz,
+        static_cast<const char*>(V) + tok * d * esz, perm + tok, offsets + (size_t)h0 * (s.nk + 1),
+        list + (size_t)h0 * NQ * s.nk, count + (size_t)h0 * NQ, scale, static_cast<char*>(O) + tok * d * esz,
+        lse ? lse + tok : nullptr, ws, st, ev_begin && p < n_events ? ev_begin[p] : nullptr,
+        ev_end && p < n_events ? ev_end[p] : nullptr, qb ? &qp : nullptr,
+        (int)std::min<long long>((long long)h0 * NQ * kRanges, INT_MAX));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -300,14 +300,15 @@ int park_block_sparse_attn_clustered(const void* Q, const void* K, const void* V
   if (st != PARK_OK) return st;
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   hipError_t e = park::launch_attn(s, Q, K, V, perm, offsets, block_list, block_count, scale, O, lse, workspace,
-                                   static_cast<hipStream_t>(stream), nullptr, nullptr, &qb);
+                                   static_cast<hipStream_t>(stream), nullptr, nullptr, 0, &qb);
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
 static int attn_impl(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N, int d,
                      const int32_t* perm, const int32_t* offsets, int n_clusters, const int32_t* block_list,
                      const int32_t* block_count, int q_block, float scale, void* O, float* lse, void* workspace,
-                     size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end) {
+                     size_t workspace_bytes, void* stream, void* const* ev_begin, void* const* ev_end,
+                     int n_events) {
   bool uns;
   int st = check_common(dtype, B, H, N, d, n_clusters, &uns);
   if (st != PARK_OK) return st;
@@ -319,8 +320,8 @@ static int attn_impl(const void* Q, const void* K, const void* V, int dtype, int
   if (st != PARK_OK) return st;
   if (scale <= 0.0f) scale = 1.0f / sqrtf((float)d);
   hipError_t e = park::launch_attn(s, Q, K, V, perm, offsets, block_list, block_count, scale, O, lse, workspace,
-                                   static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
-                                   static_cast<hipEvent_t>(ev_end));
+                                   static_cast<hipStream_t>(stream), reinterpret_cast<const hipEvent_t*>(ev_begin),
+                                   reinterpret_cast<const hipEvent_t*>(ev_end), n_events);
   return e == hipSuccess ? PARK_OK : PARK_ERR_HIP;
 }
 
@@ -329,16 +330,23 @@ int park_block_sparse_attn(const void* Q, const void* K, const void* V, int dtyp
                            const int32_t* block_count, int q_block, float scale, void* O, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return attn_impl(Q, K, V, dtype, B, H, N, d, perm, offsets, n_clusters, block_list, block_count, q_block, scale, O,
-                   lse, workspace, workspace_bytes, stream, nullptr, nullptr);
+                   lse, workspace, workspace_bytes, stream, nullptr, nullptr, 0);
 }
 
 int park_block_sparse_attn_timed(const void* Q, const void* K, const void* V, int dtype, int B, int H, int N,
                                  int d, const int32_t* perm, const int32_t* offsets, int n_clusters,
                                  const int32_t* block_list, const int32_t* block_count, int q_block, float scale,
                                  void* O, float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                                 void* ev_begin, void* ev_end) {
+                                 void* const* ev_begin, void* const* ev_end, int n_events) {
+  if (n_events < 0 || (n_events > 0 && (!ev_begin || !ev_end))) return PARK_ERR_INVALID;
   return attn_impl(Q, K, V, dtype, B, H, N, d, perm, offsets, n_clusters, block_list, block_count, q_block, scale, O,
-                   lse, workspace, workspace_bytes, stream, ev_begin, ev_end);
+                   lse, workspace, workspace_bytes, stream, ev_begin, ev_end, n_events);
+}
+
+int park_attn_passes(int dtype, int B, int H, int N, int d, int n_clusters) {
+  bool uns;
+  if (check_common(dtype, B, H, N, d, n_clusters, &uns) != PARK_OK) return 0;
+  return park::attn_passes(make_shape(dtype, B, H, N, d, n_clusters));
 }
 
 }  // extern "C"

@@ -52,12 +52,17 @@ hipError_t launch_retrieve_clustered(const Shape& s, const void* Q, const float*
                                      bool online = false);
 
 // ----- block-sparse attention
-// qb == nullptr: 64-token query blocks; otherwise clustered query blocks
+// qb == nullptr: 64-token query blocks; otherwise clustered query blocks.  The heads are
+// computed in attn_passes() passes of at most attn_heads_per_pass() heads; the workspace holds
+// one pass.  ev_begin[p] / ev_end[p] (optional, p < n_events): recorded on st right before and
+// after pass p's attention kernel.
+int attn_heads_per_pass(const Shape& s, const QueryBlocks* qb = nullptr);
+int attn_passes(const Shape& s, const QueryBlocks* qb = nullptr);
 size_t attn_workspace(const Shape& s, const QueryBlocks* qb = nullptr);
 hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                        const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
-                       void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin = nullptr,
-                       hipEvent_t ev_end = nullptr, const QueryBlocks* qb = nullptr);
+                       void* O, float* lse, void* ws, hipStream_t st, const hipEvent_t* ev_begin = nullptr,
+                       const hipEvent_t* ev_end = nullptr, int n_events = 0, const QueryBlocks* qb = nullptr);
 
 // ----- exact block importance (section 3.2, Eq. (3)) for 64-token blocks, a diagnostic
 size_t importance_workspace(const Shape& s);

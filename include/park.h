@@ -40,7 +40,7 @@ extern "C" {
 #define PARK_API
 #endif
 
-#define PARK_ABI_VERSION 1
+#define PARK_ABI_VERSION 2
 #define PARK_MAX_CLUSTERS 1536
 #define PARK_QUERY_BLOCK 64
 #define PARK_MAX_QUERY_BLOCKS 1536   /* clustered query blocks per head */
@@ -201,6 +201,9 @@ PARK_API int park_retrieve_blocks_pooled(const void* Q, int dtype, int B, int H,
  * sum of those rounded weights, lse from the float sum); here (64-token blocks) the partial
  * outputs of the key ranges are kept in fp16, scaled by the head's largest |value|, and
  * merged in range order; float inputs are computed in float throughout.
+ * The heads are computed in park_attn_passes() passes (each the whole computation for its
+ * heads, heads being independent); the workspace holds one pass's packed keys and values, tile
+ * plan and partial states, and a pass takes as many heads as fit in 2.5 GiB (at least one).
  * Workspace: park_workspace_bytes(PARK_OP_BLOCK_SPARSE_ATTN, ...) bytes (sized for any selection,
  * up to every cluster for every query block).
  * Errors: INVALID, UNSUPPORTED (d, q_block != 64, n_clusters > PARK_MAX_CLUSTERS),
@@ -212,19 +215,26 @@ PARK_API int park_block_sparse_attn(const void* Q, const void* K, const void* V,
                            int q_block, float scale, void* O, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Number of passes over the heads that park_block_sparse_attn makes for these sizes (>= 1;
+ * 0 for sizes the call rejects). */
+PARK_API int park_attn_passes(int dtype, int B, int H, int N, int d, int n_clusters);
+
 /*
- * park_block_sparse_attn_timed - park_block_sparse_attn for measurement: records the HIP
- * events ev_begin and ev_end (hipEvent_t, created by the caller; either may be NULL) on
- * `stream` immediately before and after the attention kernel itself, i.e. after the packing
- * and tile-planning launches, so that hipEventElapsedTime gives that kernel's duration.
- * Otherwise identical to park_block_sparse_attn (arguments, results, errors); a failed
+ * park_block_sparse_attn_timed - park_block_sparse_attn for measurement: for each pass p <
+ * n_events, records the HIP events ev_begin[p] and ev_end[p] (hipEvent_t, created by the
+ * caller; host arrays of n_events handles, either handle may be NULL) on `stream` immediately
+ * before and after that pass's attention kernel itself, i.e. after its packing and
+ * tile-planning launches, so that the sum of hipEventElapsedTime over the passes gives the
+ * kernel's duration.  Otherwise identical to park_block_sparse_attn (arguments, results,
+ * errors); INVALID also for n_events < 0 or a NULL array with n_events > 0; a failed
  * hipEventRecord is reported as HIP.
  */
 PARK_API int park_block_sparse_attn_timed(const void* Q, const void* K, const void* V, int dtype, int B, int H,
                                  int N, int d, const int32_t* perm, const int32_t* offsets,
                                  int n_clusters, const int32_t* block_list, const int32_t* block_count,
                                  int q_block, float scale, void* O, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream, void* ev_begin, void* ev_end);
+                                 size_t workspace_bytes, void* stream, void* const* ev_begin,
+                                 void* const* ev_end, int n_events);
 
 /*
  * park_block_importance_exact - a retrieval-accuracy diagnostic: the exact block importance
@@ -367,7 +377,8 @@ PARK_API int park_retrieve_blocks_online(const void* Q, int dtype, int B, int H,
  * tiles of every block as park_block_sparse_attn does (the tile plan of a block serves all its
  * chunks); one wave computes a whole chunk over all its selected tiles in one pass and writes
  * the final O (bf16) and lse itself, so there are no partial states and no merge.  Queries are
- * read and results written through q_perm.
+ * read and results written through q_perm.  Heads are computed in passes as in
+ * park_block_sparse_attn.
  * Workspace: park_workspace_bytes_clustered(PARK_OP_BLOCK_SPARSE_ATTN, ...).
  * Errors: as park_block_sparse_attn; INVALID also for NULL q_perm / q_offsets or n_qblocks
  * outside [1, N]; UNSUPPORTED for n_qblocks > PARK_MAX_QUERY_BLOCKS.

@@ -103,8 +103,20 @@ int main(void) {
   EXPECT(AT(F, 64, -1.0f, 32, F, big), PARK_ERR_UNSUPPORTED);
   EXPECT(AT(F, 64, -1.0f, 128, NULL, big), PARK_ERR_WORKSPACE);
   EXPECT(AT(F, 64, -1.0f, 128, F, 100), PARK_ERR_WORKSPACE);
-  EXPECT(park_block_sparse_attn_timed(F, F, F, 1, 1, 2, 256, 128, F, F, 8, F, F, 64, -1.0f, F, NULL, NULL, 0, NULL,
-                                      F, F), PARK_ERR_WORKSPACE);
+  {
+    void* evs[2] = {F, F};
+    EXPECT(park_block_sparse_attn_timed(F, F, F, 1, 1, 2, 256, 128, F, F, 8, F, F, 64, -1.0f, F, NULL, NULL, 0, NULL,
+                                        evs, evs, 2), PARK_ERR_WORKSPACE);
+    EXPECT(park_block_sparse_attn_timed(F, F, F, 1, 1, 2, 256, 128, F, F, 8, F, F, 64, -1.0f, F, NULL, F, big, NULL,
+                                        NULL, evs, 1), PARK_ERR_INVALID);
+    EXPECT(park_block_sparse_attn_timed(F, F, F, 1, 1, 2, 256, 128, F, F, 8, F, F, 64, -1.0f, F, NULL, F, big, NULL,
+                                        evs, evs, -1), PARK_ERR_INVALID);
+  }
+  /* passes over the heads: at least one for valid sizes, none for rejected ones */
+  EXPECT(park_attn_passes(1, 1, 40, 75600, 128, 1024) > 1, 1);
+  EXPECT(park_attn_passes(1, 1, 1, 2048, 64, 32), 1);
+  EXPECT(park_attn_passes(1, 1 << 20, 1 << 20, 1 << 20, 128, 8), 0);
+  EXPECT(park_attn_passes(1, 1, 1, -5, 128, 8), 0);
   EXPECT(park_block_sparse_attn_clustered(F, F, F, 1, 1, 2, 256, 128, F, F, 8, NULL, F, 4, F, F, -1.0f, F, NULL, F,
                                           big, NULL), PARK_ERR_INVALID);
   EXPECT(park_block_sparse_attn_clustered(F, F, F, 1, 1, 2, 256, 128, F, F, 8, F, F, 4, F, F, -1.0f, F, NULL, NULL,

@@ -63,7 +63,7 @@ def test_clock_build_exports_only_its_declared_symbols(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.park_abi_version() == 1
+    assert lib.park_abi_version() == 2
     names = [lib.park_status_string(i).decode() for i in range(6)]
     assert names == ["PARK_OK", "PARK_ERR_INVALID", "PARK_ERR_UNSUPPORTED", "PARK_ERR_WORKSPACE", "PARK_ERR_HIP",
                      "PARK_ERR_NUMERIC"]
@@ -86,7 +86,7 @@ def test_clustered_attention_workspace_has_no_partial_states(lib):
     workspace holds no per-range partial states (fp16 O and float (m, l) per query and key
     range), only the chunk tables that the 64-token path does not need."""
     a256 = lambda x: (x + 255) // 256 * 256
-    B, H, N, d, nk = 1, 40, 75600, 128, 1024
+    B, H, N, d, nk = 1, 4, 75600, 128, 1024    # four heads: one pass on both paths
     NQ = (N + 63) // 64          # as many clustered blocks as 64-token blocks: same plan size
     BH, maxc = B * H, (N + 63) // 64 + NQ
     w64 = lib.park_workspace_bytes(2, B, H, N, d, nk)
@@ -94,7 +94,31 @@ def test_clustered_attention_workspace_has_no_partial_states(lib):
     R = 4                        # key ranges of the 64-token path
     partial = a256(BH * N * R * d * 2) + a256(BH * N * R * 8)
     tables = a256(BH * maxc * 16) + a256(BH * (NQ + 1) * 4) + a256(BH * 4)
+    assert lib.park_attn_passes(1, B, H, N, d, nk) == 1
     assert w64 - wcl == partial - tables
+
+
+@pytest.mark.parametrize("B,H,N,nk", [(1, 40, 75600, 1024), (1, 24, 119056, 1536), (2, 12, 32760, 512)])
+def test_attention_workspace_holds_one_pass_of_heads(lib, B, H, N, nk):
+    """The attention call walks the heads in passes whose packed keys and values, tile plan and
+    partial states fit in 2.5 GiB; the workspace is that of one pass of ceil(B H / passes)
+    heads, so the 75.6k-token, 40-head layer needs under 3 GB."""
+    d = 128
+    passes = lib.park_attn_passes(1, B, H, N, d, nk)
+    assert passes >= 1
+    hpp = -(-B * H // passes)
+    assert -(-B * H // hpp) == passes                       # balanced passes
+    ws = lib.park_workspace_bytes(2, B, H, N, d, nk)
+    assert ws == lib.park_workspace_bytes(2, 1, hpp, N, d, nk)
+    assert lib.park_attn_passes(1, 1, hpp, N, d, nk) == 1
+    assert ws <= 5 << 29
+    if hpp > 1:   # one more head would not fit in 2.5 GiB... or the passes would not be balanced
+        assert lib.park_workspace_bytes(2, 1, hpp + 1, N, d, nk) > 5 << 29 or \
+            -(-B * H // (hpp + 1)) == passes
+    if (B, H, N, nk) == (1, 40, 75600, 1024):
+        assert passes > 1 and ws < 3e9
+    assert lib.park_attn_passes(1, 0, H, N, d, nk) == 0      # invalid sizes
+    assert lib.park_attn_passes(0, B, H, N, d, nk) == 1      # float inputs keep no per-head buffers
 
 
 def test_noalloc_retrieve_rejects(lib):
@@ -256,5 +280,12 @@ def test_timed_attention_rejects_like_attention(lib):
         a = dict(base, **over)
         st = lib.park_block_sparse_attn_timed(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"],
                                               a["perm"], a["off"], a["nk"], a["lst"], a["cnt"], a["qb"], a["scale"],
-                                              a["O"], a["lse"], a["ws"], a["wsb"], None, FAKE, FAKE)
+                                              a["O"], a["lse"], a["ws"], a["wsb"], None, FAKE, FAKE, 1)
         assert st == want, (over, st)
+    # the event arrays: n_events >= 0, and both arrays given when n_events > 0
+    a = dict(base, ws=FAKE, wsb=1 << 40, V=FAKE)
+    for evb, eve, n in ((FAKE, FAKE, -1), (None, FAKE, 1), (FAKE, None, 2)):
+        st = lib.park_block_sparse_attn_timed(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"],
+                                              a["perm"], a["off"], a["nk"], a["lst"], a["cnt"], a["qb"], a["scale"],
+                                              a["O"], a["lse"], a["ws"], a["wsb"], None, evb, eve, n)
+        assert st == INVALID, (evb, eve, n, st)

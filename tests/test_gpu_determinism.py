@@ -96,3 +96,35 @@ def test_non_finite_queries_flagged(dev, orc, dtype, d):
         n_diff, n_keys, _ = teacher_forced_chain(orc, Q[0, h], K[0, h], cfg.n_clusters,
                                                  [host(r["labels"])[0, h] for r in runs])
         print(f"{dtype} head {h}: {n_diff} near-tie label differences over {n_keys} keys")
+
+
+def test_attention_passes_match_single_pass_calls(dev):
+    """At 40 heads x 75,600 tokens the attention call walks the heads in several passes (its
+    workspace holds one pass); heads are independent, so each pass's heads, attended in a call
+    of their own (one pass), give bitwise the same O and lse.  Seeded random inputs: keys
+    dealt to 1024 clusters by a random permutation, 80 random clusters per query block."""
+    import torch
+    B, H, N, d, nk = 1, 40, 75600, 128, 1024
+    passes = dev.attn_passes(B, H, N, d, nk)
+    assert passes > 1
+    hpp = -(-H // passes)
+    NQ = (N + 63) // 64
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q, k, v = (torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    perm = torch.argsort(torch.rand(B, H, N, device="cuda", generator=g), dim=-1).to(torch.int32)
+    offsets = (torch.arange(nk + 1, device="cuda", dtype=torch.int64) * N // nk).to(torch.int32)
+    offsets = offsets.expand(B, H, nk + 1).contiguous()
+    pick = torch.argsort(torch.rand(B, H, NQ, nk, device="cuda", generator=g), dim=-1).to(torch.int32)
+    cnt = torch.full((B, H, NQ), 80, dtype=torch.int32, device="cuda")
+    O, lse = dev.park_block_sparse_attn(q, k, v, perm, offsets, pick, cnt)
+    torch.cuda.synchronize()
+    for h0 in range(0, H, hpp):
+        h1 = min(H, h0 + hpp)
+        assert dev.attn_passes(B, h1 - h0, N, d, nk) == 1
+        sl = lambda t: t[:, h0:h1].contiguous()
+        Op, lp = dev.park_block_sparse_attn(sl(q), sl(k), sl(v), sl(perm), sl(offsets), sl(pick), sl(cnt))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(O[:, h0:h1]), _bits(Op)), f"heads {h0}..{h1 - 1}: O differs"
+        assert torch.equal(_bits(lse[:, h0:h1]), _bits(lp)), f"heads {h0}..{h1 - 1}: lse differs"
+        del Op, lp
+    print(f"{passes} passes of {hpp} heads: outputs equal to the per-pass calls")
