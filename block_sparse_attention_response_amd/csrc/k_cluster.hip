@@ -29,6 +29,8 @@ struct ClusterWs {
   float4* cinfo;  // [BH][nkp] (|c~|^2, |R c~|, |R c~ - fp16(R c~)|, 0)
   float* ccv;     // [BH][nkp] |c~|^2 (+inf for padding rows)
   double* cmean;  // [BH][nkp][D] original-space member means
+  double* csum;   // [BH][nkp][D] original-space member sums (carried from step to step)
+  int32_t *lalt, *palt, *oalt, *calt;   // the other step's labels, perm, offsets, counts
   uint32_t* hmax; // [BH][4] float bits of max |R c~|, max fp16 error of R c~, max |c~|^2
   int32_t* hist;  // [BH][nch_s][nk] counting-sort histograms, then bases
   int32_t* wlab;  // [BH][ceil(N / kAsgKeys)] label at the first position of each assignment workgroup
@@ -54,6 +56,11 @@ static ClusterWs carve(const Shape& s, void* base) {
   w.cinfo = reinterpret_cast<float4*>(take(BH * w.nkp * sizeof(float4)));
   w.ccv = reinterpret_cast<float*>(take(BH * w.nkp * sizeof(float)));
   w.cmean = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
+  w.csum = reinterpret_cast<double*>(take(BH * w.nkp * D * sizeof(double)));
+  w.lalt = reinterpret_cast<int32_t*>(take(BH * (size_t)s.N * sizeof(int32_t)));
+  w.palt = reinterpret_cast<int32_t*>(take(BH * (size_t)s.N * sizeof(int32_t)));
+  w.oalt = reinterpret_cast<int32_t*>(take(BH * (size_t)(s.nk + 1) * sizeof(int32_t)));
+  w.calt = reinterpret_cast<int32_t*>(take(BH * (size_t)s.nk * sizeof(int32_t)));
   w.hmax = reinterpret_cast<uint32_t*>(take(BH * 4 * sizeof(uint32_t)));
   w.hist = reinterpret_cast<int32_t*>(take(BH * (size_t)w.nch_s * s.nk * sizeof(int32_t)));
   w.wlab = reinterpret_cast<int32_t*>(take(BH * (size_t)((s.N + 255) / 256) * sizeof(int32_t)));
@@ -1036,11 +1043,13 @@ __global__ __launch_bounds__(64 * kScatWaves) void k_sort_scatter(const int32_t*
 // the members (a run of perm) are read 16 bytes per thread, RPI rows at a time; each thread
 // sums its dimensions in double over its rows, and the RPI partial sums are added in a
 // fixed order, so the result does not depend on scheduling.  Writes the original-space mean
-// (double) for step 2 and, on the last iteration, the float centroid output (0 if empty).
+// (double) for step 2, the sum (csum, when given) for the next k-means step's update and,
+// on the last iteration, the float centroid output (0 if empty).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ offsets, int N, int nk, int nkp,
-                                                 double* __restrict__ cmean, float* __restrict__ cent) {
+                                                 double* __restrict__ cmean, double* __restrict__ csum,
+                                                 float* __restrict__ cent) {
   constexpr int TPR = D / 8;         // threads per row (8 dimensions each)
   constexpr int RPI = 256 / TPR;     // rows in flight per step
   __shared__ double part[RPI][D];
@@ -1049,6 +1058,7 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
   const int n = b - a;
   if (n == 0) {
     if (cent && tid < D) cent[((size_t)bh * nk + v) * D + tid] = 0.0f;
+    if (csum && tid < D) csum[((size_t)bh * nkp + v) * D + tid] = 0.0;
     return;
   }
   const int32_t* pm = perm + (size_t)bh * N + a;
@@ -1094,7 +1104,118 @@ __global__ __launch_bounds__(256) void k_km_sums(const T* __restrict__ K, const 
     for (int g = 0; g < RPI; ++g) sum += part[g][tid];
     const double m = sum / (double)n;
     cmean[((size_t)bh * nkp + v) * D + tid] = m;
+    if (csum) csum[((size_t)bh * nkp + v) * D + tid] = sum;
     if (cent) cent[((size_t)bh * nk + v) * D + tid] = (float)m;
+  }
+}
+
+// a6 from the second k-means step on, for bf16 keys: a cluster's member sum changes only by
+// the keys that joined it (members now, of another cluster before) and the keys that left it
+// (members before, of another cluster now), so csum_v += sum(joined) - sum(left), and the
+// mean is csum_v / n_v as before.  A sum of bf16 values in double is exact while the partial
+// sums stay within 53 bits of the smallest term's last place (for these key magnitudes, terms
+// of magnitude 2^-24 and up), so the carried sum equals the sum over the current members; in
+// late steps only a few percent of the keys change cluster, and only their rows are read.
+// One wave per cluster (four per workgroup), every step's loads issued together: the two
+// member runs (now, then before) are walked as one list, the member indices and labels of 256
+// positions at a time; the changed keys of each 64-position window are compacted in list
+// order into LDS, and their rows read 16 bytes per lane, four rows per instruction, up to 8
+// rows in flight; lane l adds the rows of the window's list positions = l / 16 (mod 4), in
+// order, for dimensions 8 (l % 16) .. + 7, and the four row groups are added by a fixed
+// butterfly at the end.  Writes csum and, for a
+// non-empty cluster, the mean; on the last iteration the float centroid output (0 if empty).
+template <int D>
+__global__ __launch_bounds__(256) void k_km_sums_delta(const bf16* __restrict__ K, const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ labels,
+                                                       const int32_t* __restrict__ perm_prev,
+                                                       const int32_t* __restrict__ offsets_prev,
+                                                       const int32_t* __restrict__ labels_prev, int N, int nk,
+                                                       int nkp, double* __restrict__ cmean,
+                                                       double* __restrict__ csum, float* __restrict__ cent) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int LPR = D / 8;        // lanes per row (16 bytes each)
+  constexpr int RPW = 64 / LPR;     // rows per wave instruction
+  constexpr int U = 2;              // row instructions in flight
+  __shared__ int clist[4][64];      // per wave: changed keys of the window, sign in bit 31
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, bh = blockIdx.y;
+  const int v = blockIdx.x * 4 + w;
+  if (v >= nk) return;              // (whole waves; no workgroup barrier below)
+  const int32_t* on = offsets + (size_t)bh * (nk + 1);
+  const int32_t* op = offsets_prev + (size_t)bh * (nk + 1);
+  const int an = on[v], bn = on[v + 1], ap = op[v], bp = op[v + 1];
+  const int nn = bn - an, ntot = nn + (bp - ap);
+  const int rl = lane / LPR, c8 = (lane % LPR) * 8;
+  const size_t crow = ((size_t)bh * nkp + v) * D + c8;
+  const bf16* Kh = K + (size_t)bh * N * D;
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  constexpr int XW = 4;             // list windows of 64 positions whose loads go out together
+  for (int x0 = 0; x0 < ntot; x0 += 64 * XW) {
+    int jj[XW], oth[XW];
+#pragma unroll
+    for (int q = 0; q < XW; ++q) {   // the run now (joined keys), then the run before (left keys)
+      const int x = min(x0 + 64 * q + lane, ntot - 1);
+      const bool joined = x < nn;
+      const int pos = joined ? an + x : ap + (x - nn);
+      jj[q] = min(max((joined ? perm : perm_prev)[(size_t)bh * N + pos], 0), N - 1);
+    }
+#pragma unroll
+    for (int q = 0; q < XW; ++q) {
+      const bool joined = min(x0 + 64 * q + lane, ntot - 1) < nn;
+      oth[q] = (joined ? labels_prev : labels)[(size_t)bh * N + jj[q]];
+    }
+#pragma unroll
+    for (int q = 0; q < XW; ++q) {
+    const int x = x0 + 64 * q + lane;
+    if (x0 + 64 * q >= ntot) break;   // (uniform)
+    int key = -1, neg = 0;
+    if (x < ntot && oth[q] != v) { key = jj[q]; neg = x < nn ? 0 : 1; }
+    const uint64_t m = __ballot(key >= 0);
+    const int nch = __builtin_popcountll(m);
+    if (key >= 0) clist[w][__builtin_popcountll(m & ((1ull << lane) - 1))] = key | (neg << 31);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int r0 = 0; r0 < nch; r0 += U * RPW) {
+      float xv[U][8];
+      int sg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RPW + rl;
+        const int e = clist[w][min(r, nch - 1)];
+        sg[u] = r < nch ? ((e < 0) ? -1 : 1) : 0;
+        const bf16x8 q = load_bf16x8(Kh + (size_t)(e & 0x7FFFFFFF) * D + c8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[u][i] = (float)q[i];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sg[u] > 0 ? (double)xv[u][i] : (sg[u] < 0 ? -(double)xv[u][i] : 0.0);
+    }
+    __builtin_amdgcn_wave_barrier();   // the list is rewritten by the next window
+    }
+  }
+  // the row groups' partial sums, by a fixed butterfly over the lanes of equal c8
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o);
+  if (rl == 0) {
+    const bool live = nn > 0;
+    double sm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm[i] = csum[crow + i] + acc[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) csum[crow + i] = sm[i];
+    if (live)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cmean[crow + i] = sm[i] / (double)nn;
+    if (cent)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cent[((size_t)bh * nk + v) * D + c8 + i] = live ? (float)(sm[i] / (double)nn) : 0.0f;
   }
 }
 
@@ -1327,28 +1448,43 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
   k_bound_max<<<s.BH, 256, 0, st>>>(w.cinfo, s.nk, w.nkp, w.hmax);
   PARK_CHECK();
   const size_t shm_nk = (size_t)s.nk * sizeof(int);
+  // Labels, perm, offsets and counts alternate between the caller's arrays and the workspace
+  // from step to step (the last step writes the caller's), so that each step's update sees
+  // the previous step's clustering beside its own.
+  int32_t* const lab2[2] = {labels, w.lalt};
+  int32_t* const perm2[2] = {perm, w.palt};
+  int32_t* const off2[2] = {offsets, w.oalt};
+  int32_t* const cnt2[2] = {counts, w.calt};
   for (int it = 0; it < iters; ++it) {
+    const int cur = (iters - 1 - it) & 1, prv = cur ^ 1;
     // from the second step on, the keys are visited in the previous step's label order (perm)
     const bool timed = it == iters - 1;
     if (timed && ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-    e = launch_assign<D>(s, w, K, it > 0 ? perm : nullptr, it > 0 ? w.wlab : nullptr, labels, st);
+    e = launch_assign<D>(s, w, K, it > 0 ? perm2[prv] : nullptr, it > 0 ? w.wlab : nullptr, lab2[cur], st);
     if (e != hipSuccess) return e;
     if (timed && ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
-    k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(labels, s.N, s.nk, w.nch_s, w.hist);
+    k_sort_hist<<<dim3(w.nch_s, s.BH), 256, shm_nk, st>>>(lab2[cur], s.N, s.nk, w.nch_s, w.hist);
     PARK_CHECK();
-    k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, counts, offsets, w.wlab);
+    k_sort_scan<<<s.BH, 1024, shm_nk, st>>>(w.hist, s.N, s.nk, w.nch_s, cnt2[cur], off2[cur], w.wlab);
     PARK_CHECK();
-    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64 * kScatWaves, kScatWaves * shm_nk, st>>>(labels, w.hist, s.N, s.nk,
-                                                                                   w.nch_s, perm);
+    k_sort_scatter<<<dim3(w.nch_s, s.BH), 64 * kScatWaves, kScatWaves * shm_nk, st>>>(lab2[cur], w.hist, s.N, s.nk,
+                                                                                   w.nch_s, perm2[cur]);
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
     if (f32)
-      k_km_sums<D, float><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const float*>(K), perm, offsets, s.N, s.nk, w.nkp, w.cmean, co);
+      k_km_sums<D, float><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const float*>(K), perm2[cur], off2[cur],
+                                                            s.N, s.nk, w.nkp, w.cmean, nullptr, co);
+    else if (it == 0)
+      k_km_sums<D, bf16><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm2[cur], off2[cur],
+                                                           s.N, s.nk, w.nkp, w.cmean, w.csum, co);
     else
-      k_km_sums<D, bf16><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm, offsets, s.N, s.nk, w.nkp, w.cmean, co);
+      k_km_sums_delta<D><<<dim3((s.nk + 3) / 4, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm2[cur],
+                                                                     off2[cur], lab2[cur], perm2[prv], off2[prv],
+                                                                     lab2[prv], s.N, s.nk, w.nkp, w.cmean, w.csum, co);
     PARK_CHECK();
     if (it + 1 < iters) {  // the transformed centroids only feed the next assignment
-      k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, counts, s.nk, w.nkp, 0, w.R64, w.Rt64, w.ctil, w.gneg2, w.cinfo, w.ccv);
+      k_km_ctx<D><<<dim3(w.nkp / 32, s.BH), 256, 0, st>>>(w.cmean, cnt2[cur], s.nk, w.nkp, 0, w.R64, w.Rt64, w.ctil,
+                                                          w.gneg2, w.cinfo, w.ccv);
       PARK_CHECK();
     }
     if (it + 1 < iters) {

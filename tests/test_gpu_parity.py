@@ -105,10 +105,14 @@ def test_cluster_stagewise(dev, orc, name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_cluster_outputs(dev, orc, name):
     """counts / offsets / perm bit-exact and centroids equal to the oracle's finalisation of
-    the GPU's own final labels."""
+    the GPU's own final labels.  With bf16 keys the GPU carries each cluster's member sum
+    from step to step (adding the keys that joined, subtracting those that left) while the
+    oracle sums the final members afresh; both double sums of bf16 values are exact (keys of
+    magnitude 2^-24 and up), so the float means agree bit for bit but for a rare tiny key."""
     cfg, Q, K, V = _data(name)
     g = _gpu_cluster(dev, cfg, Q, K, cfg.iters)
     B, H = Q.shape[:2]
+    n_diff = n_all = 0
     for b in range(B):
         for h in range(H):
             lab = g["labels"][b, h]
@@ -119,6 +123,11 @@ def test_cluster_outputs(dev, orc, name):
             assert np.array_equal(g["perm"][b, h], perm)
             err = np.abs(g["centroids"][b, h] - cent).max() / max(1e-30, np.abs(cent).max())
             assert err <= 1e-6, err
+            n_diff += int((g["centroids"][b, h] != cent).sum())
+            n_all += cent.size
+    print(f"{name}: {n_diff} of {n_all} centroid values not bit-equal to the oracle's")
+    if cfg.dtype == "bf16":
+        assert n_diff <= 1e-4 * n_all
 
 
 @pytest.mark.parametrize("name", list(CASES))
