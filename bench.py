@@ -140,8 +140,13 @@ def streaming_rooflines(workload, BH, N, d, nk, NQ, esz, ranges=4, attn_passes=1
         return []
     nkp = (nk + 31) // 32 * 32
     alg = {
-        "park::k_km_sums<128, bf16>": ("the keys once (by perm), perm once, the means (double) once",
-                                       BH * N * d * esz + BH * N * 4 + BH * nkp * d * 8),
+        "park::k_km_sums<128, bf16>": ("the keys once (by perm), perm once, the means and sums (double) once "
+                                       "(the first k-means step)",
+                                       BH * N * d * esz + BH * N * 4 + 2 * BH * nkp * d * 8),
+        "park::k_km_sums_delta<128>": ("the later k-means steps: both steps' perm and labels once (16 bytes per key), "
+                                       "the carried sums read and written, the means written; the rows of the keys "
+                                       "that changed cluster come on top (data-dependent, not counted)",
+                                       BH * N * 16 + 3 * BH * nkp * d * 8),
         "park::k_km_ctx<128>": ("the means (double) and R, R^T once; c~ (float), the fp16 screen operand and "
                                 "the per-cluster figures once", BH * nkp * d * 8 + 2 * BH * d * d * 8 + BH * nkp * (d * 6 + 20)),
         "park::k_transform_bf16<128>": ("the keys once; K~ (float) and the key norms once",
