@@ -34,36 +34,14 @@ __global__ void k_centroid_split(const float* __restrict__ C, const int32_t* __r
   }
 }
 
-// Reduce-scatter over the 32 lanes of a wave half: v[i] (i < 32) of every lane is combined
-// with op across the 32 lanes, and lane l ends up holding the result for i = l % 32.
-template <bool MAX>
-__device__ __forceinline__ float reduce_scatter32(float (&v)[32], int l32) {
-#pragma unroll
-  for (int step = 0; step < 5; ++step) {
-    const int mask = 16 >> step, half = 16 >> step;
-    // lanes with the mask bit keep the upper half; the choice is a bitwise select on values
-    // (a ternary on array elements would become dynamic register indexing)
-    const uint32_t sel = (l32 & mask) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + half]);
-      const float send = __uint_as_float((lo & sel) | (hi & ~sel));
-      const float keep = __uint_as_float((hi & sel) | (lo & ~sel));
-      const float recv = __shfl_xor(send, mask);
-      v[i] = MAX ? fmaxf(keep, recv) : keep + recv;
-    }
-  }
-  return v[0];
-}
-
 // ---------------------------------------------------------------------------------------
 // Fused PAMA: one workgroup per (query block, head), 64 queries, nw waves; wave w owns
 // clusters [32 VT w, 32 VT (w+1)).  The 64 x (32 VT) logit slab of a wave stays in
 // registers (MFMA accumulators) through the softmax and the block mean; only W goes out.
 //   P_iv = 2^(S_iv - max_r S_ir) / sum_r 2^(S_ir - max_r S_ir)
 //   W_uv = (1/n_u) sum_i P_iv
-// Row maxima and sums: in-lane over the wave's tiles, a 32-lane reduce-scatter (one query
-// row per lane), then across the waves through LDS.
+// Row maxima and sums: in-lane over the wave's tiles, over the wave's 32 columns by a
+// transpose through LDS (one query row per lane), then across the waves through LDS.
 // PROBS (the unfused ablation, 64-token blocks only): instead of the block's column sums, every
 // query row's normalised probabilities P_i. go to W, laid out [BH][N][nk]; k_rows_mean then
 // forms the block means from them in a second pass over HBM.
@@ -82,6 +60,9 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
   __shared__ float red[8][64];
   __shared__ float rowm[64];
   __shared__ float rowinv[64];
+  // per wave: a 64-row transpose buffer for the row reductions over the wave's 32 columns
+  constexpr int TP = 36;   // row pitch in floats (16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) float tbuf[8][64 * TP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int u = blockIdx.x, bh = blockIdx.y;
@@ -229,8 +210,29 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[qt][vt][r] = -INFINITY;
 
-  // this lane's query row after the reduce-scatter: index l32 = 16 qt + r
-  const int my_row = 32 * (l32 >> 4) + c_row(l32 & 15, lane);
+  // Row reductions over the wave's 32 cluster columns through LDS: lane (h, l32) holds
+  // t[16 qt + r] for query row 32 qt + c_row(r, lane) and column l32; the values are written
+  // transposed (row-major, one row per query), and lane L then combines row L's 32 values in
+  // column order.  Two LDS rounds instead of five dependent shuffle rounds and their selects.
+  float* tb = tbuf[w];
+  const auto row_reduce = [&](const float (&t)[32], bool is_max) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tb[(32 * (i >> 4) + c_row(i & 15, lane)) * TP + l32] = t[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float x = is_max ? -INFINITY : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&tb[lane * TP + 4 * k]);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) x = is_max ? fmaxf(x, v[z]) : x + v[z];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return x;
+  };
   float t[32];
 
   // row maxima
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       for (int vt = 1; vt < VT; ++vt) mx = fmaxf(mx, acc[qt][vt][r]);
       t[16 * qt + r] = mx;
     }
-  red[w][my_row] = reduce_scatter32<true>(t, l32);
+  red[w][lane] = row_reduce(t, true);
   __syncthreads();
   if (tid < 64) {
     float m = -INFINITY;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
         t[16 * qt + r] = ps;
       }
     }
-  red[w][my_row] = reduce_scatter32<false>(t, l32);
+  red[w][lane] = row_reduce(t, false);
   __syncthreads();
   if (tid < 64) {
     float l = 0.0f;
