@@ -119,8 +119,9 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qt][vt][r] = l2n;
   }
-  // B operand fragments (fragment-major Chi / Clo); spare tiles past nkp re-read tile 0
-  // and are masked to -inf below
+  // B operand fragments (fragment-major Chi / Clo); spare tiles past nkp re-read tile 0: their
+  // accumulators start at -inf, as an empty cluster's do, and the finite products leave them
+  // there
   size_t crow[VT];
 #pragma unroll
   for (int vt = 0; vt < VT; ++vt) {
@@ -202,13 +203,6 @@ __global__ __launch_bounds__(512) void k_pama(const void* __restrict__ Qv, const
       }
     }
   }
-#pragma unroll
-  for (int vt = 0; vt < VT; ++vt)
-    if (v0 + 32 * vt >= nkp)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[qt][vt][r] = -INFINITY;
 
   // Row reductions over the wave's 32 cluster columns through LDS: lane (h, l32) holds
   // t[16 qt + r] for query row 32 qt + c_row(r, lane) and column l32; the values are written

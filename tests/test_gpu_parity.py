@@ -222,6 +222,29 @@ def test_retrieve_edge_parameters(dev, orc, p, k):
                           g["block_count"][0, h], orc)
 
 
+@pytest.mark.parametrize("nk", [288, 544, 1312])
+def test_pama_spare_cluster_tiles(dev, orc, nk):
+    """Cluster counts whose 32-cluster tiles do not fill the fused kernel's waves evenly (288:
+    5 waves of two tiles for 9; 544: 6 of three for 17; 1312: 7 of six for 41): the spare
+    tiles' logits start at -inf, as an empty cluster's do, and stay there.  W and the selection
+    against the oracle, with some empty clusters."""
+    import torch
+    cfg = Config("spare", 1, 2, (2, 24, 30), 5, 128, "bf16", 8, (44, 42, 42), nk, 1, 0.9, 3)
+    Q, _, _ = park_synth.generate(cfg, seed=11)
+    rng = np.random.default_rng(nk)
+    cent = rng.normal(0, 0.7, (1, 2, nk, 128)).astype(np.float32)
+    counts = rng.integers(0, 40, (1, 2, nk)).astype(np.int32)
+    counts[0, :, rng.integers(0, nk, 7)] = 0
+    out = dev.park_retrieve_blocks(to_dev(Q, "bf16"), to_dev(cent, "f32"), to_dev(counts, "f32"), 0.9, 3)
+    torch.cuda.synchronize()
+    g = {kk: host(v) for kk, v in out.items()}
+    for h in range(2):
+        W_ref = orc.pama(Q[0, h], cent[0, h], counts[0, h], 64, 1.0 / np.sqrt(128))
+        check_scores(g["scores"][0, h], W_ref)
+        compare_selection(g["scores"][0, h], W_ref, counts[0, h], 0.9, 3, g["mask"][0, h], g["block_list"][0, h],
+                          g["block_count"][0, h], orc)
+
+
 def _attn_case(dev, orc, name, lists=None):
     import torch
     cfg, Q, K, V = _data(name)
