@@ -1257,9 +1257,6 @@ static AttnWs carve_attn(const Shape& s, const QueryBlocks* qb, void* base, size
   // plan entries of one query block: at most every group of its head, plus the filler of
   // one partial tile per range
   const size_t per_row = (size_t)group_cap(s) + 4 * kRanges;
-  w.gstart = reinterpret_cast<int32_t*>(take((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)));
-  w.rng = reinterpret_cast<int32_t*>(take((size_t)s.BH * s.nk * sizeof(int32_t)));
-  w.vmax = reinterpret_cast<float*>(take((size_t)s.BH * sizeof(float)));
   w.ntiles = reinterpret_cast<int32_t*>(take(items * sizeof(int32_t)));
   w.tbase = reinterpret_cast<int32_t*>(take((items + 1) * sizeof(int32_t)));
   w.bsum = reinterpret_cast<int32_t*>(take(((items + kScanBlock - 1) / kScanBlock) * sizeof(int32_t)));
@@ -1292,6 +1289,15 @@ static int compute_units() {
   return n;
 }
 
+// Per-head tables computed once for all heads before the passes (bf16 only): each cluster's
+// first packed group (gstart [BH][nk+1]), its key range (rng [BH][nk]) and the head's largest
+// |value| (vmax [BH]).  They sit at the front of the workspace.
+static size_t head_tabs_bytes(const Shape& s) {
+  if (s.dtype != 1) return 0;
+  return align256((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)) + align256((size_t)s.BH * s.nk * sizeof(int32_t)) +
+         align256((size_t)s.BH * sizeof(float));
+}
+
 // The call walks the heads in passes; the workspace holds one pass's packed keys and values,
 // tile plan and partial states (every one of them per head), so a pass takes as many heads as
 // fit in kAttnPassBytes (at least one), and the passes are balanced.  Each pass is the whole
@@ -1320,7 +1326,7 @@ size_t attn_workspace(const Shape& s, const QueryBlocks* qb) {
   sp.BH = attn_heads_per_pass(s, qb);
   size_t total = 0;
   carve_attn(sp, qb, nullptr, &total);
-  return total;
+  return head_tabs_bytes(s) + total;
 }
 
 // One pass: the heads of s (pointers already offset to the pass's first head); item0 = the
@@ -1328,12 +1334,15 @@ size_t attn_workspace(const Shape& s, const QueryBlocks* qb) {
 static hipError_t attn_pass(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* perm,
                             const int32_t* offsets, const int32_t* list, const int32_t* count, float scale,
                             void* O, float* lse, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                            const QueryBlocks* qb, int item0) {
+                            const QueryBlocks* qb, int item0, int32_t* gstart, int32_t* rng, float* vmax) {
   // query blocks per head (plan rows) and chunk slots per head (clustered blocks)
   const int NQ = qb ? qb->NQ : n_qblocks(s.N);
   const int maxc = qb ? chunk_slots(s.N, qb->NQ) : 0;
   const float scale2 = scale * kLog2e;
   AttnWs w = carve_attn(s, qb, ws, nullptr);
+  w.gstart = gstart;   // (the pass's heads of the per-head tables)
+  w.rng = rng;
+  w.vmax = vmax;
   const int32_t* qperm = qb ? qb->qperm : nullptr;
   if (qb) {
     hipError_t e = launch_qchunks(qb->qoffsets, s.BH, s.N, NQ, maxc, w.chunks, w.cbase, w.ctotal, st);
@@ -1355,13 +1364,9 @@ static hipError_t attn_pass(const Shape& s, const void* Q, const void* K, const 
     auto o = reinterpret_cast<bf16*>(O);
     hipError_t e;
 #define PARK_CHECK() do { e = hipGetLastError(); if (e != hipSuccess) return e; } while (0)
-    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, w.gstart, w.vmax);
-    PARK_CHECK();
     dim3 pgrid(s.nk, s.BH);
     if (s.d == 128) k_pack_kv<128><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp, w.vmax);
     else k_pack_kv<64><<<pgrid, 128, 0, st>>>(k, v, perm, offsets, w.gstart, s.N, s.nk, Gcap, w.Kp, w.Vp, w.vmax);
-    PARK_CHECK();
-    k_range_assign<<<s.BH, 1024, 0, st>>>(list, count, offsets, s.nk, NQ, w.rng);
     PARK_CHECK();
     k_plan_count<<<(rows + 3) / 4, 256, 0, st>>>(list, count, offsets, w.rng, s.nk, NQ, rows, w.ntiles);
     PARK_CHECK();
@@ -1423,6 +1428,22 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
   const int hpp = attn_heads_per_pass(s, qb);
   const int NQ = qb ? qb->NQ : n_qblocks(s.N);
   const size_t esz = s.dtype == 1 ? 2 : 4, N = s.N, d = s.d;
+  // the per-head tables of every head, then the passes' workspace
+  char* const tabs = static_cast<char*>(ws);
+  int32_t* const gstart = reinterpret_cast<int32_t*>(tabs);
+  int32_t* const rng = reinterpret_cast<int32_t*>(tabs + align256((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)));
+  float* const vmax = reinterpret_cast<float*>(tabs + align256((size_t)s.BH * (s.nk + 1) * sizeof(int32_t)) +
+                                               align256((size_t)s.BH * s.nk * sizeof(int32_t)));
+  void* const pws = tabs + head_tabs_bytes(s);
+  if (s.dtype == 1) {
+    // each cluster's first packed group and the head's |value| maximum (reset here, raised by
+    // the packing), and the clusters' key ranges, for all heads at once
+    k_group_scan<<<s.BH, 256, 0, st>>>(offsets, s.nk, gstart, vmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_range_assign<<<s.BH, 1024, 0, st>>>(list, count, offsets, s.nk, NQ, rng);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   for (int h0 = 0, p = 0; h0 < s.BH; h0 += hpp, ++p) {
     Shape sp = s;
     sp.BH = std::min(hpp, s.BH - h0);
@@ -1433,9 +1454,10 @@ hipError_t launch_attn(const Shape& s, const void* Q, const void* K, const void*
         sp, static_cast<const char*>(Q) + tok * d * esz, static_cast<const char*>(K) + tok * d * esz,
         static_cast<const char*>(V) + tok * d * esz, perm + tok, offsets + (size_t)h0 * (s.nk + 1),
         list + (size_t)h0 * NQ * s.nk, count + (size_t)h0 * NQ, scale, static_cast<char*>(O) + tok * d * esz,
-        lse ? lse + tok : nullptr, ws, st, ev_begin && p < n_events ? ev_begin[p] : nullptr,
+        lse ? lse + tok : nullptr, pws, st, ev_begin && p < n_events ? ev_begin[p] : nullptr,
         ev_end && p < n_events ? ev_end[p] : nullptr, qb ? &qp : nullptr,
-        (int)std::min<long long>((long long)h0 * NQ * kRanges, INT_MAX));
+        (int)std::min<long long>((long long)h0 * NQ * kRanges, INT_MAX), gstart + (size_t)h0 * (s.nk + 1),
+        rng + (size_t)h0 * s.nk, vmax + h0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
