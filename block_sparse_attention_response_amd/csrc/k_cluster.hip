@@ -660,10 +660,14 @@ __global__ __launch_bounds__(256, 2) void k_km_assign(const void* __restrict__ K
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const bool real = k0 + 64 * w + 32 * kt + l32 < N;
+    // (only a key tile that runs past N has slots to clear: a wave-uniform test, so the other
+    // tiles skip the 64 selects)
+    if (k0 + 64 * w + 32 * kt + 32 > N) {
 #pragma unroll
-    for (int kc = 0; kc < NF; ++kc)
+      for (int kc = 0; kc < NF; ++kc)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = real ? bfr[kt][kc][i] : (f16)0.0f;
+        for (int i = 0; i < 8; ++i) bfr[kt][kc][i] = real ? bfr[kt][kc][i] : (f16)0.0f;
+    }
     // the second term covers the float accumulation of 129 terms (< 2^-16.9 of their
     // magnitudes), the rounding of |c~|^2 and of the stored k~, with a factor-7 margin
     const float4 k4 = kn[kt];
