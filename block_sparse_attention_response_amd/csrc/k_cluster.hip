@@ -1475,10 +1475,14 @@ static hipError_t launch_cluster_d(const Shape& s, const void* Q, const void* K,
                                                                                    w.nch_s, perm2[cur]);
     PARK_CHECK();
     float* co = (it == iters - 1) ? cent : nullptr;
+    // carried sums (one wave per cluster walks both member runs) pay off for small clusters;
+    // clusters of more than 128 keys on average (the query blocks' k-means, say) are summed
+    // afresh by a workgroup each
+    const bool carry = (long long)s.N <= 128LL * s.nk;
     if (f32)
       k_km_sums<D, float><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const float*>(K), perm2[cur], off2[cur],
                                                             s.N, s.nk, w.nkp, w.cmean, nullptr, co);
-    else if (it == 0)
+    else if (it == 0 || !carry)
       k_km_sums<D, bf16><<<dim3(s.nk, s.BH), 256, 0, st>>>(reinterpret_cast<const bf16*>(K), perm2[cur], off2[cur],
                                                            s.N, s.nk, w.nkp, w.cmean, w.csum, co);
     else

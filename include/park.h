@@ -103,9 +103,9 @@ PARK_API size_t park_workspace_bytes(int op, int B, int H, int N, int d, int n_c
  *             that needs the outcome synchronises and reports PARK_ERR_NUMERIC for a non-zero
  *             flag (the Python binding's numeric_status does so).
  * init_idx: NULL or device int32 [n_clusters] of key indices in [0, N), shared by all heads.
- * With bf16 keys each cluster's member sum is carried from step to step (plus the keys that
- * joined, minus those that left), which is exact in double and gives the plain Lloyd step's
- * means.
+ * With bf16 keys and clusters of at most 128 keys on average, each cluster's member sum is
+ * carried from step to step (plus the keys that joined, minus those that left), which is exact
+ * in double and gives the plain Lloyd step's means.
  * Errors: INVALID for NULL required pointers, B,H < 1, N < 1, n_clusters outside [1, N],
  * iters < 1, alpha outside [0, 1] or not finite, unknown dtype/metric; UNSUPPORTED for d
  * not in {64,128} or n_clusters > PARK_MAX_CLUSTERS; WORKSPACE; HIP.
